@@ -1,0 +1,277 @@
+// C ABI of the SparsePR call: argument validation, workspace planning and launch order.
+// The operations themselves are documented in include/sparsepr.h.
+#include <cmath>
+
+#include "sp_common.hpp"
+#include "sp_launch.hpp"
+
+namespace sp {
+
+Dims dims_of(const sparsepr_params& p) {
+  Dims d;
+  d.hq = p.heads_q;
+  d.hkv = p.heads_kv;
+  d.g = p.heads_q / p.heads_kv;
+  d.n = p.n;
+  d.d = p.d;
+  d.gq = p.groups_q;
+  d.gk = p.groups_k;
+  d.rk = p.r_k;
+  d.m = p.n_probe;
+  d.r = p.rank;
+  d.iters = p.kmeans_iters;
+  d.scale = p.softmax_scale > 0.f ? p.softmax_scale : (float)(1.0 / std::sqrt((double)p.d));
+  d.lambda = p.lambda;
+  d.bf16 = p.dtype == SPARSEPR_BF16;
+  return d;
+}
+
+static size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+Workspace plan_workspace(const sparsepr_params& p) {
+  Workspace w{};
+  const size_t n = (size_t)p.n, hkv = (size_t)p.heads_kv, hq = (size_t)p.heads_q;
+  w.fpk = round_up4(p.r_k);
+  w.fpq = round_up4(p.groups_k);
+  const int fpmax = w.fpk > w.fpq ? w.fpk : w.fpq;
+  size_t o = 0;
+  w.maxbits = o; o = align_up(o + hkv * 2 * 4);
+  w.xk = o; o = align_up(o + hkv * n * w.fpk);
+  w.xq = o; o = align_up(o + hkv * n * w.fpq);
+  w.centroids = o; o = align_up(o + hkv * kMaxGroups * fpmax * 4);
+  w.sums = o; o = align_up(o + 2 * hkv * kMaxGroups * (fpmax + 1) * 4);
+  w.usum = o; if (p.heads_q != p.heads_kv) o = align_up(o + hkv * n * p.groups_k * 4);
+  w.total_partition = o;
+  w.nchunks = (int)ceil_div(p.n, kProbeChunk);
+  o = 0;
+  w.probe_alloc = o; o = align_up(o + hkv * n * 4);
+  w.partials = o; o = align_up(o + hq * w.nchunks * p.n_probe * 2 * (p.d + 2) * 4);
+  w.fitbuf = o; o = align_up(o + hq * (3 * kMaxProbe * p.d + p.d * kMaxRank) * 8);
+  w.total_probe = o;
+  w.dense_meta = 0;
+  w.total_dense = 0;
+  w.total = w.total_partition;
+  if (w.total_probe > w.total) w.total = w.total_probe;
+  if (w.total_dense > w.total) w.total = w.total_dense;
+  return w;
+}
+
+static sparsepr_status check_params(const sparsepr_params* p) {
+  if (!p) return SPARSEPR_ERR_NULL;
+  if (p->dtype != SPARSEPR_BF16 && p->dtype != SPARSEPR_FP32) return SPARSEPR_ERR_DTYPE;
+  if (p->n < 1 || p->n > (1 << 22)) return SPARSEPR_ERR_SHAPE;
+  if (p->d != 64 && p->d != 128) return SPARSEPR_ERR_SHAPE;
+  if (p->heads_q < 1 || p->heads_kv < 1 || p->heads_q % p->heads_kv != 0) return SPARSEPR_ERR_SHAPE;
+  if (p->heads_q / p->heads_kv > 16) return SPARSEPR_ERR_SHAPE;
+  if (p->groups_q < 1 || p->groups_q > kMaxGroups || p->groups_k < 1 || p->groups_k > kMaxGroups)
+    return SPARSEPR_ERR_SHAPE;
+  if (p->groups_q > p->n || p->groups_k > p->n) return SPARSEPR_ERR_SHAPE;
+  if (p->r_q < 1 || p->groups_k > p->r_q) return SPARSEPR_ERR_PARAM;
+  if (p->r_k < 1 || p->r_k > kMaxFeat) return SPARSEPR_ERR_PARAM;
+  if (p->n_probe < 1 || p->n_probe > kMaxProbe || p->n_probe > p->n) return SPARSEPR_ERR_PARAM;
+  if (p->rank < 1 || p->rank > kMaxRank || p->rank > p->n_probe || p->rank > p->d) return SPARSEPR_ERR_PARAM;
+  if (!(p->lambda > 0.f) || !std::isfinite(p->lambda)) return SPARSEPR_ERR_PARAM;
+  if (!(p->rho_exec <= 1.f) || !((double)p->rho_exec > (double)p->n_probe / (double)p->n)) return SPARSEPR_ERR_PARAM;
+  if (p->kmeans_iters < 0 || p->kmeans_iters > 64) return SPARSEPR_ERR_PARAM;
+  if (p->block != 64) return SPARSEPR_ERR_PARAM;
+  if (!(p->softmax_scale >= 0.f) || !std::isfinite(p->softmax_scale)) return SPARSEPR_ERR_PARAM;
+  return SPARSEPR_OK;
+}
+
+static bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
+
+static sparsepr_status check_ws(const sparsepr_params* p, const void* ws, size_t bytes, size_t need_of_part) {
+  (void)p;
+  if (need_of_part > 0 && ws == nullptr) return SPARSEPR_ERR_NULL;
+  if (bytes < need_of_part) return SPARSEPR_ERR_WORKSPACE;
+  if (ws && ((uintptr_t)ws & 255u) != 0) return SPARSEPR_ERR_ALIGN;
+  return SPARSEPR_OK;
+}
+
+static sparsepr_status hip_status() {
+  return hipGetLastError() == hipSuccess ? SPARSEPR_OK : SPARSEPR_ERR_HIP;
+}
+
+// Route budget in pairs per head: floor(rho_ppm n^2 / 10^6) - M n with rho_ppm the
+// target density rounded once to integer parts per million.
+static int64_t route_budget(const sparsepr_params& p) {
+  const int64_t ppm = (int64_t)std::floor((double)p.rho_exec * 1e6 + 0.5);
+  const int64_t n = p.n;
+  return (ppm * n * n) / 1000000 - (int64_t)p.n_probe * n;
+}
+
+}  // namespace sp
+
+using namespace sp;
+
+extern "C" {
+
+sparsepr_status sparsepr_workspace_size(const sparsepr_params* params, size_t* bytes) {
+  sparsepr_status st = check_params(params);
+  if (st != SPARSEPR_OK) return st;
+  if (!bytes) return SPARSEPR_ERR_NULL;
+  *bytes = plan_workspace(*params).total;
+  return SPARSEPR_OK;
+}
+
+sparsepr_status sparsepr_partition(const sparsepr_params* params, const void* q, const void* k, const void* v,
+                                   const sparsepr_partition_t* out, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  sparsepr_status st = check_params(params);
+  if (st != SPARSEPR_OK) return st;
+  if (!q || !k || !v || !out) return SPARSEPR_ERR_NULL;
+  const sparsepr_partition_t& o = *out;
+  if (!o.responses_s || !o.responses_u || !o.exponents || !o.key_labels || !o.key_centroids_int || !o.key_perm ||
+      !o.key_offsets || !o.key_centroids || !o.query_features || !o.query_labels || !o.query_centroids ||
+      !o.query_perm || !o.query_offsets || !o.q_gm || !o.k_gm || !o.v_gm)
+    return SPARSEPR_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o.q_gm) || !aligned16(o.k_gm) ||
+      !aligned16(o.v_gm))
+    return SPARSEPR_ERR_ALIGN;
+  const Workspace wp = plan_workspace(*params);
+  st = check_ws(params, workspace, workspace_bytes, wp.total_partition);
+  if (st != SPARSEPR_OK) return st;
+  (void)hipGetLastError();
+  launch_partition(dims_of(*params), wp, q, k, v, o, static_cast<char*>(workspace), (hipStream_t)stream);
+  return hip_status();
+}
+
+sparsepr_status sparsepr_route(const sparsepr_params* params, const sparsepr_partition_t* part,
+                               const sparsepr_route_t* out, void* workspace, size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  sparsepr_status st = check_params(params);
+  if (st != SPARSEPR_OK) return st;
+  if (!part || !out) return SPARSEPR_ERR_NULL;
+  if (!part->responses_u || !part->query_labels || !part->query_offsets || !part->key_offsets)
+    return SPARSEPR_ERR_NULL;
+  if (!out->row_ptr || !out->cols || !out->kept_mask || !out->pairs || !out->cell_mass) return SPARSEPR_ERR_NULL;
+  if (((uintptr_t)out->cell_mass & 7u) != 0) return SPARSEPR_ERR_ALIGN;
+  (void)hipGetLastError();
+  if (ensure_exp_table() != hipSuccess) return SPARSEPR_ERR_HIP;
+  launch_route(dims_of(*params), route_budget(*params), *part, *out, (hipStream_t)stream);
+  return hip_status();
+}
+
+sparsepr_status sparsepr_attend(const sparsepr_params* params, const sparsepr_partition_t* part,
+                                const sparsepr_route_t* route, float* o_gm, float* lse, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  sparsepr_status st = check_params(params);
+  if (st != SPARSEPR_OK) return st;
+  if (!part || !route || !o_gm) return SPARSEPR_ERR_NULL;
+  if (!part->q_gm || !part->k_gm || !part->v_gm || !part->query_offsets || !part->key_offsets || !route->row_ptr ||
+      !route->cols)
+    return SPARSEPR_ERR_NULL;
+  if (!aligned16(part->q_gm) || !aligned16(part->k_gm) || !aligned16(part->v_gm) || !aligned16(o_gm))
+    return SPARSEPR_ERR_ALIGN;
+  const Dims dm = dims_of(*params);
+  AttnArgs a{};
+  a.q = part->q_gm;
+  a.k = part->k_gm;
+  a.v = part->v_gm;
+  a.q_skv = (int64_t)dm.n * dm.g * dm.d;
+  a.q_sp = (int64_t)dm.g * dm.d;
+  a.q_sj = dm.d;
+  a.kv_skv = (int64_t)dm.n * dm.d;
+  a.qoff = part->query_offsets;
+  a.koff = part->key_offsets;
+  a.row_ptr = route->row_ptr;
+  a.cols = route->cols;
+  a.o = o_gm;
+  a.o_skv = a.q_skv;
+  a.o_sp = a.q_sp;
+  a.o_sj = a.q_sj;
+  a.lse = lse;
+  a.n = dm.n;
+  a.g = dm.g;
+  a.gq = dm.gq;
+  a.gk = dm.gk;
+  a.scale = dm.scale;
+  (void)hipGetLastError();
+  launch_attention(dm, a, false, (hipStream_t)stream);
+  return hip_status();
+}
+
+sparsepr_status sparsepr_probe_fit(const sparsepr_params* params, const void* q, const sparsepr_partition_t* part,
+                                   const sparsepr_route_t* route, const sparsepr_fit_t* out, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  sparsepr_status st = check_params(params);
+  if (st != SPARSEPR_OK) return st;
+  if (!q || !part || !route || !out) return SPARSEPR_ERR_NULL;
+  if (!part->query_features || !part->query_centroids || !part->query_perm || !part->query_offsets ||
+      !part->key_offsets || !part->k_gm || !part->v_gm || !route->kept_mask)
+    return SPARSEPR_ERR_NULL;
+  if (!out->probe_tokens || !out->probe_groups || !out->probe_weights || !out->o_dense || !out->o_sparse ||
+      !out->A || !out->B || !out->c0 || !out->r_eff || !out->eig)
+    return SPARSEPR_ERR_NULL;
+  if (!aligned16(q) || !aligned16(part->k_gm) || !aligned16(part->v_gm)) return SPARSEPR_ERR_ALIGN;
+  const Workspace wp = plan_workspace(*params);
+  st = check_ws(params, workspace, workspace_bytes, wp.total_probe);
+  if (st != SPARSEPR_OK) return st;
+  (void)hipGetLastError();
+  launch_probe_fit(dims_of(*params), wp, q, *part, *route, *out, static_cast<char*>(workspace), (hipStream_t)stream);
+  return hip_status();
+}
+
+sparsepr_status sparsepr_apply(const sparsepr_params* params, const float* o_gm, const sparsepr_partition_t* part,
+                               const sparsepr_fit_t* fit, void* o, void* stream) {
+  sparsepr_status st = check_params(params);
+  if (st != SPARSEPR_OK) return st;
+  if (!o_gm || !part || !fit || !o) return SPARSEPR_ERR_NULL;
+  if (!part->query_perm || !fit->A || !fit->B || !fit->c0 || !fit->r_eff || !fit->o_dense || !fit->probe_tokens)
+    return SPARSEPR_ERR_NULL;
+  if (!aligned16(o_gm) || !aligned16(o)) return SPARSEPR_ERR_ALIGN;
+  (void)hipGetLastError();
+  launch_apply(dims_of(*params), o_gm, *part, *fit, o, (hipStream_t)stream);
+  return hip_status();
+}
+
+sparsepr_status sparsepr_dense_attention(const sparsepr_params* params, const void* q, const void* k,
+                                         const void* v, void* o, void* workspace, size_t workspace_bytes,
+                                         void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  sparsepr_status st = check_params(params);
+  if (st != SPARSEPR_OK) return st;
+  if (!q || !k || !v || !o) return SPARSEPR_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return SPARSEPR_ERR_ALIGN;
+  const Dims dm = dims_of(*params);
+  AttnArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.q_skv = (int64_t)dm.g * dm.n * dm.d;
+  a.q_sp = dm.d;
+  a.q_sj = (int64_t)dm.n * dm.d;
+  a.kv_skv = (int64_t)dm.n * dm.d;
+  a.o = o;
+  a.o_skv = a.q_skv;
+  a.o_sp = a.q_sp;
+  a.o_sj = a.q_sj;
+  a.n = dm.n;
+  a.g = dm.g;
+  a.gq = 1;
+  a.gk = 1;
+  a.scale = dm.scale;
+  (void)hipGetLastError();
+  launch_attention(dm, a, true, (hipStream_t)stream);
+  return hip_status();
+}
+
+const char* sparsepr_status_string(sparsepr_status status) {
+  switch (status) {
+    case SPARSEPR_OK: return "ok";
+    case SPARSEPR_ERR_NULL: return "a required pointer is NULL";
+    case SPARSEPR_ERR_SHAPE: return "shape out of range (n, d, heads or groups)";
+    case SPARSEPR_ERR_DTYPE: return "unsupported dtype";
+    case SPARSEPR_ERR_ALIGN: return "misaligned pointer";
+    case SPARSEPR_ERR_WORKSPACE: return "workspace too small";
+    case SPARSEPR_ERR_PARAM: return "parameter out of range";
+    case SPARSEPR_ERR_HIP: return "HIP runtime or launch failure";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

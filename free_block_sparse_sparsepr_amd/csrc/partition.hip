@@ -1,0 +1,513 @@
+// Response-coupled Q/K partition (summary page of "Partition the Support, Reconstruct the
+// Residual", response-coupled partition paragraph): sampled-query key responses, integer
+// key features, online k-means over keys (values follow keys), key centroids in the
+// original space, query responses to those centroids, integer response-direction
+// features, online k-means over queries (one asymmetric pass), stable group-major
+// permutations and the gathers of Q, K and V into group-major order (execution
+// paragraph).
+//
+// Every integer decision is exact: features are integers in [-127, 127], distances and
+// sums are exact 32-bit integer arithmetic, ties go to the smallest index and the
+// partition is a stable counting sort, so the result is deterministic and independent
+// of scheduling.
+#include "sp_common.hpp"
+#include "sp_launch.hpp"
+
+namespace sp {
+
+__global__ void fill_u32_kernel(uint32_t* p, size_t n, uint32_t v) {
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (; i < n; i += stride) p[i] = v;
+}
+
+void fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t s) {
+  if (n == 0) return;
+  int blocks = (int)std::min<size_t>(4096, (n + 255) / 256);
+  hipLaunchKernelGGL(fill_u32_kernel, dim3(blocks), dim3(256), 0, s, p, n, v);
+}
+
+// ---------------------------------------------------------------------------------------
+// S = Q_s K^T * scale for the r_k sampled query rows (token floor((2s+1) n / (2 r_k)),
+// query head s mod g of the KV head).  One thread per key; fp32 accumulation in
+// ascending d.  Also the per-head max |S| (float bits are monotone for |x|).
+// grid (ceil(n / 256), Hkv), block 256.
+// ---------------------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(256) void resp_s_kernel(const T* __restrict__ q, const T* __restrict__ k,
+                                                     int n, int g, int rk, float scale,
+                                                     float* __restrict__ S, uint32_t* maxbits) {
+  __shared__ float qs[kMaxFeat][D];
+  __shared__ float red[4];
+  const int kv = blockIdx.y;
+  for (int idx = threadIdx.x; idx < rk * D; idx += 256) {
+    int s = idx / D, c = idx % D;
+    int64_t tok = ((int64_t)(2 * s + 1) * n) / (2 * rk);
+    int h = kv * g + (s % g);
+    qs[s][c] = to_f32(q[((int64_t)h * n + tok) * D + c]);
+  }
+  __syncthreads();
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  float acc[kMaxFeat];
+#pragma unroll
+  for (int s = 0; s < kMaxFeat; ++s) acc[s] = 0.f;
+  float mx = 0.f;
+  if (j < n) {
+    const T* kr = k + ((int64_t)kv * n + j) * D;
+    for (int c0 = 0; c0 < D; c0 += 8) {
+      float kf[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) kf[e] = to_f32(kr[c0 + e]);
+#pragma unroll
+      for (int s = 0; s < kMaxFeat; ++s) {
+        if (s < rk) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[s] = fmaf(qs[s][c0 + e], kf[e], acc[s]);
+        }
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < kMaxFeat; ++s) {
+      if (s < rk) {
+        float v = acc[s] * scale;
+        S[((int64_t)kv * rk + s) * n + j] = v;
+        mx = fmaxf(mx, fabsf(v));
+      }
+    }
+  }
+  mx = wave_max(mx);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    atomicMax(&maxbits[kv], __float_as_uint(m));
+  }
+}
+
+// X^K[j][s] = clamp(rint(S[s][j] * 2^e_S), -127, 127), e_S the largest e with
+// max|S| 2^e <= 127.  Features stored point-major with a padded stride fp (zeros).
+__global__ __launch_bounds__(256) void key_features_kernel(const float* __restrict__ S,
+                                                           const uint32_t* maxbits, int n, int rk,
+                                                           int fp, int8_t* __restrict__ X,
+                                                           int32_t* exps) {
+  const int kv = blockIdx.y;
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  const int e = pow2_exponent(__uint_as_float(maxbits[kv]), 127.f);
+  if (blockIdx.x == 0 && threadIdx.x == 0) exps[kv * 2 + 0] = e;
+  if (j >= n) return;
+  int8_t* xr = X + ((int64_t)kv * n + j) * fp;
+  for (int s = 0; s < fp; ++s) {
+    float v = 0.f;
+    if (s < rk) v = fminf(fmaxf(rintf(ldexpf(S[((int64_t)kv * rk + s) * n + j], e)), -127.f), 127.f);
+    xr[s] = (int8_t)(int)v;
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Online Lloyd k-means on integer features (exact).  Centroids C [H][G][fp] int32.
+// ---------------------------------------------------------------------------------------
+__global__ void kmeans_init_kernel(const int8_t* __restrict__ X, int n, int G, int fp,
+                                   int32_t* __restrict__ C) {
+  const int h = blockIdx.x;
+  for (int idx = threadIdx.x; idx < G * fp; idx += blockDim.x) {
+    int gi = idx / fp, f = idx % fp;
+    int64_t tok = ((int64_t)(2 * gi + 1) * n) / (2 * G);
+    C[((int64_t)h * kMaxGroups + gi) * fp + f] = X[((int64_t)h * n + tok) * fp + f];
+  }
+}
+
+// Assignment argmin_g ||c_g||^2 - 2 <x, c_g> (ties: smallest g) with 4-way int8 dot
+// products, plus exact per-group feature sums and counts (block-local in LDS, then
+// global atomics).  sums: [H][G][fp + 1] (last column = count), zeroed by the caller.
+// grid (ceil(n / 256), H), block 256.
+template <int FP>
+__global__ __launch_bounds__(256) void kmeans_assign_kernel(const int8_t* __restrict__ X, int n,
+                                                            int G, const int32_t* __restrict__ C,
+                                                            int32_t* __restrict__ labels,
+                                                            int32_t* __restrict__ sums) {
+  constexpr int W = FP / 4;
+  __shared__ int32_t cw[kMaxGroups][W];
+  __shared__ int32_t cn[kMaxGroups];
+  __shared__ int32_t acc[kMaxGroups * (FP + 1)];
+  const int h = blockIdx.y;
+  for (int idx = threadIdx.x; idx < G * W; idx += 256) {
+    int gi = idx / W, w = idx % W;
+    const int32_t* c = C + ((int64_t)h * kMaxGroups + gi) * FP + 4 * w;
+    uint32_t packed = (uint32_t)(uint8_t)(int8_t)c[0] | ((uint32_t)(uint8_t)(int8_t)c[1] << 8) |
+                      ((uint32_t)(uint8_t)(int8_t)c[2] << 16) | ((uint32_t)(uint8_t)(int8_t)c[3] << 24);
+    cw[gi][w] = (int32_t)packed;
+  }
+  for (int gi = threadIdx.x; gi < G; gi += 256) {
+    int s = 0;
+    const int32_t* c = C + ((int64_t)h * kMaxGroups + gi) * FP;
+    for (int f = 0; f < FP; ++f) s += c[f] * c[f];
+    cn[gi] = s;
+  }
+  for (int idx = threadIdx.x; idx < G * (FP + 1); idx += 256) acc[idx] = 0;
+  __syncthreads();
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  if (j < n) {
+    int32_t xw[W];
+    const int32_t* xr = reinterpret_cast<const int32_t*>(X + ((int64_t)h * n + j) * FP);
+#pragma unroll
+    for (int w = 0; w < W; ++w) xw[w] = xr[w];
+    int best = 0x7fffffff, bi = 0;
+    for (int gi = 0; gi < G; ++gi) {
+      int dot = 0;
+#pragma unroll
+      for (int w = 0; w < W; ++w) dot = __builtin_amdgcn_sdot4(xw[w], cw[gi][w], dot, false);
+      int score = cn[gi] - 2 * dot;
+      if (score < best) { best = score; bi = gi; }
+    }
+    labels[(int64_t)h * n + j] = bi;
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        int v = (int)(int8_t)((uint32_t)xw[w] >> (8 * b));
+        if (v) atomicAdd(&acc[bi * (FP + 1) + 4 * w + b], v);
+      }
+    }
+    atomicAdd(&acc[bi * (FP + 1) + FP], 1);
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < G * (FP + 1); idx += 256) {
+    int v = acc[idx];
+    if (v) atomicAdd(&sums[(int64_t)h * kMaxGroups * (FP + 1) + idx], v);
+  }
+}
+
+// c_g = div_rhaz(sum_g, count_g); an empty group keeps its centroid.  Also clears the
+// other sums buffer for the next assignment.  grid H, block 256.
+__global__ void kmeans_update_kernel(const int32_t* __restrict__ sums, int G, int F, int fp,
+                                     int32_t* __restrict__ C, int32_t* __restrict__ next_sums) {
+  const int h = blockIdx.x;
+  const int32_t* sh = sums + (int64_t)h * kMaxGroups * (fp + 1);
+  for (int idx = threadIdx.x; idx < G * fp; idx += blockDim.x) {
+    int gi = idx / fp, f = idx % fp;
+    int cnt = sh[gi * (fp + 1) + fp];
+    if (cnt > 0 && f < F) C[((int64_t)h * kMaxGroups + gi) * fp + f] = div_rhaz(sh[gi * (fp + 1) + f], cnt);
+  }
+  int32_t* nh = next_sums + (int64_t)h * kMaxGroups * (fp + 1);
+  for (int idx = threadIdx.x; idx < kMaxGroups * (fp + 1); idx += blockDim.x) nh[idx] = 0;
+}
+
+__global__ void copy_centroids_kernel(const int32_t* __restrict__ C, int G, int F, int fp,
+                                      int32_t* __restrict__ out) {
+  const int h = blockIdx.x;
+  for (int idx = threadIdx.x; idx < G * F; idx += blockDim.x) {
+    int gi = idx / F, f = idx % F;
+    out[((int64_t)h * G + gi) * F + f] = C[((int64_t)h * kMaxGroups + gi) * fp + f];
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Stable counting sort of labels: offsets (exclusive scan of counts) and perm (token at
+// each group-major position, tokens ascending within a group).  One block per head.
+// Within a 1024-token chunk a token's rank among equal labels comes from wave ballots
+// plus the counts of earlier waves.
+// ---------------------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void group_major_kernel(const int32_t* __restrict__ labels, int n,
+                                                           int G, int32_t* __restrict__ perm,
+                                                           int32_t* __restrict__ offsets) {
+  __shared__ int cnt[kMaxGroups];
+  __shared__ int base[kMaxGroups];
+  __shared__ int wcnt[16][kMaxGroups];
+  const int h = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int32_t* lh = labels + (int64_t)h * n;
+  for (int i = tid; i < kMaxGroups; i += 1024) cnt[i] = 0;
+  for (int i = tid; i < 16 * kMaxGroups; i += 1024) (&wcnt[0][0])[i] = 0;
+  __syncthreads();
+  for (int j = tid; j < n; j += 1024) atomicAdd(&cnt[lh[j]], 1);
+  __syncthreads();
+  if (tid == 0) {
+    int s = 0;
+    for (int b = 0; b < G; ++b) { base[b] = s; offsets[(int64_t)h * (G + 1) + b] = s; s += cnt[b]; }
+    offsets[(int64_t)h * (G + 1) + G] = s;
+  }
+  __syncthreads();
+  const uint64_t lt = (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
+  for (int c0 = 0; c0 < n; c0 += 1024) {
+    const int j = c0 + tid;
+    const bool valid = j < n;
+    const int lab = valid ? lh[j] : -1;
+    uint64_t active = __ballot(valid);
+    int rank = 0;
+    while (active) {
+      int leader = __ffsll((long long)active) - 1;
+      int L = __shfl(lab, leader);
+      uint64_t m = __ballot(lab == L) & active;
+      if (valid && lab == L) rank = __popcll(m & lt);
+      if (lane == leader) wcnt[w][L] = __popcll(m);
+      active &= ~m;
+    }
+    __syncthreads();
+    if (valid) {
+      int pre = 0;
+      for (int ww = 0; ww < w; ++ww) pre += wcnt[ww][lab];
+      perm[(int64_t)h * n + base[lab] + pre + rank] = j;
+    }
+    __syncthreads();
+    if (tid < G) {
+      int s = 0;
+      for (int ww = 0; ww < 16; ++ww) { s += wcnt[ww][tid]; wcnt[ww][tid] = 0; }
+      base[tid] += s;
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Row gather into group-major order: dst row (kv, p, j) <- src head kv*g + j, token
+// perm[kv][p].  16-byte vector copies; dst layout [Hkv][n][g][D].
+// ---------------------------------------------------------------------------------------
+template <int ROW_BYTES>
+__global__ __launch_bounds__(256) void gather_rows_kernel(const uint4* __restrict__ src,
+                                                          const int32_t* __restrict__ perm, int n,
+                                                          int g, int64_t rows, uint4* __restrict__ dst) {
+  constexpr int VPR = ROW_BYTES / 16;
+  int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  int64_t r = t / VPR;
+  int c = (int)(t % VPR);
+  if (r >= rows) return;
+  int64_t kvp = r / g;
+  int jh = (int)(r % g);
+  int64_t kv = kvp / n;
+  int64_t p = kvp % n;
+  int64_t tok = perm[kv * n + p];
+  int64_t srow = (kv * g + jh) * n + tok;
+  dst[r * VPR + c] = src[srow * VPR + c];
+}
+
+// C^K_b = mean of the group-major key rows of group b in fixed order (fp32).  grid
+// (G, Hkv), block 256.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void segment_mean_kernel(const T* __restrict__ kgm,
+                                                           const int32_t* __restrict__ offsets, int n,
+                                                           int G, float* __restrict__ C) {
+  constexpr int P = 256 / D;
+  __shared__ float red[P][D];
+  const int b = blockIdx.x, h = blockIdx.y;
+  const int col = threadIdx.x % D, ph = threadIdx.x / D;
+  const int start = offsets[(int64_t)h * (G + 1) + b], end = offsets[(int64_t)h * (G + 1) + b + 1];
+  float s = 0.f;
+  for (int r = start + ph; r < end; r += P) s += to_f32(kgm[((int64_t)h * n + r) * D + col]);
+  red[ph][col] = s;
+  __syncthreads();
+  if (ph == 0) {
+    float tot = 0.f;
+    for (int i = 0; i < P; ++i) tot += red[i][col];
+    int cnt = end - start;
+    C[((int64_t)h * G + b) * D + col] = cnt > 0 ? tot / (float)cnt : 0.f;
+  }
+}
+
+// U^(h) = Q^(h) C^K^T * scale for the g query heads of a KV head over a 64-token tile;
+// the head sum (fp32, ascending head order) is kept for the direction features, with
+// its per-head max |.|.  Lanes run over key groups so U rows are written coalesced.
+// grid (ceil(n / 64), Hkv), block 256.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void resp_u_kernel(const T* __restrict__ q, const float* __restrict__ Ck,
+                                                     int n, int g, int Gk, float scale,
+                                                     float* __restrict__ U, float* __restrict__ Usum,
+                                                     uint32_t* maxbits) {
+  __shared__ float cs[kMaxGroups][D + 1];
+  __shared__ float qs[64][D];
+  __shared__ float red[4];
+  const int kv = blockIdx.y;
+  const int t0 = blockIdx.x * 64;
+  for (int idx = threadIdx.x; idx < Gk * D; idx += 256) {
+    int b = idx / D, c = idx % D;
+    cs[b][c] = Ck[((int64_t)kv * Gk + b) * D + c];
+  }
+  const int b = threadIdx.x & 63;
+  const int rg = threadIdx.x >> 6;
+  float usum[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) usum[i] = 0.f;
+  for (int jh = 0; jh < g; ++jh) {
+    const int h = kv * g + jh;
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < 64 * D; idx += 256) {
+      int r = idx / D, c = idx % D;
+      int t = t0 + r;
+      qs[r][c] = t < n ? to_f32(q[((int64_t)h * n + t) * D + c]) : 0.f;
+    }
+    __syncthreads();
+    if (b < Gk) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = rg + 4 * i;
+        float acc = 0.f;
+        for (int c = 0; c < D; ++c) acc = fmaf(qs[r][c], cs[b][c], acc);
+        const float u = acc * scale;
+        usum[i] = (jh == 0) ? u : usum[i] + u;
+        const int t = t0 + r;
+        if (t < n) U[((int64_t)h * n + t) * Gk + b] = u;
+      }
+    }
+  }
+  float mx = 0.f;
+  if (b < Gk) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int t = t0 + rg + 4 * i;
+      if (t < n) {
+        mx = fmaxf(mx, fabsf(usum[i]));
+        if (Usum) Usum[((int64_t)kv * n + t) * Gk + b] = usum[i];
+      }
+    }
+  }
+  mx = wave_max(mx);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    atomicMax(&maxbits[kv], __float_as_uint(m));
+  }
+}
+
+// Response-direction features: u = rint(Usum 2^e_U) (e_U: largest e with
+// max|Usum| 2^e <= 2^14), c_b = G_K u_b - sum u, x_b = div_rhaz(127 c_b, max|c|).
+// Written to the caller's [Hkv][n][G_K] buffer and to a stride-fp copy for the k-means.
+__global__ __launch_bounds__(256) void query_features_kernel(const float* __restrict__ Usrc,
+                                                             const uint32_t* maxbits, int n, int Gk,
+                                                             int fp, int8_t* __restrict__ Xout,
+                                                             int8_t* __restrict__ Xpad, int32_t* exps) {
+  const int kv = blockIdx.y;
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  const int e = pow2_exponent(__uint_as_float(maxbits[kv]), 16384.f);
+  if (blockIdx.x == 0 && threadIdx.x == 0) exps[kv * 2 + 1] = e;
+  if (i >= n) return;
+  const float* ur = Usrc + ((int64_t)kv * n + i) * Gk;
+  int u[kMaxGroups];
+  int sum = 0;
+#pragma unroll
+  for (int b = 0; b < kMaxGroups; ++b) {
+    if (b < Gk) { u[b] = (int)rintf(ldexpf(ur[b], e)); sum += u[b]; }
+  }
+  int mx = 0;
+#pragma unroll
+  for (int b = 0; b < kMaxGroups; ++b) {
+    if (b < Gk) { u[b] = Gk * u[b] - sum; int a = u[b] < 0 ? -u[b] : u[b]; mx = a > mx ? a : mx; }
+  }
+  int8_t* xo = Xout + ((int64_t)kv * n + i) * Gk;
+  int8_t* xp = Xpad + ((int64_t)kv * n + i) * fp;
+#pragma unroll
+  for (int b = 0; b < kMaxGroups; ++b) {
+    if (b < fp) {
+      int x = (b < Gk && mx > 0) ? div_rhaz(127 * u[b], mx) : 0;
+      xp[b] = (int8_t)x;
+      if (b < Gk) xo[b] = (int8_t)x;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------------------
+template <int FP>
+static void launch_assign(const int8_t* X, int n, int H, int G, const int32_t* C, int32_t* labels,
+                          int32_t* sums, hipStream_t s) {
+  hipLaunchKernelGGL(kmeans_assign_kernel<FP>, dim3((unsigned)ceil_div(n, 256), H), dim3(256), 0, s,
+                     X, n, G, C, labels, sums);
+}
+
+static void assign_dispatch(int fp, const int8_t* X, int n, int H, int G, const int32_t* C,
+                            int32_t* labels, int32_t* sums, hipStream_t s) {
+  switch (fp) {
+#define SP_FP_CASE(V) case V: launch_assign<V>(X, n, H, G, C, labels, sums, s); break;
+    SP_FP_CASE(4) SP_FP_CASE(8) SP_FP_CASE(12) SP_FP_CASE(16) SP_FP_CASE(20) SP_FP_CASE(24)
+    SP_FP_CASE(28) SP_FP_CASE(32) SP_FP_CASE(36) SP_FP_CASE(40) SP_FP_CASE(44) SP_FP_CASE(48)
+    SP_FP_CASE(52) SP_FP_CASE(56) SP_FP_CASE(60) SP_FP_CASE(64)
+#undef SP_FP_CASE
+    default: break;
+  }
+}
+
+void run_kmeans(const int8_t* X, int n, int H, int G, int F, int fp, int iters, int32_t* C,
+                int32_t* sums2, int32_t* labels, int32_t* centroids_out, hipStream_t s) {
+  const size_t sums_elems = (size_t)H * kMaxGroups * (fp + 1);
+  int32_t* sums[2] = {sums2, sums2 + sums_elems};
+  hipLaunchKernelGGL(kmeans_init_kernel, dim3(H), dim3(256), 0, s, X, n, G, fp, C);
+  fill_u32(reinterpret_cast<uint32_t*>(sums[0]), sums_elems, 0, s);
+  for (int t = 0; t < iters; ++t) {
+    assign_dispatch(fp, X, n, H, G, C, labels, sums[t & 1], s);
+    hipLaunchKernelGGL(kmeans_update_kernel, dim3(H), dim3(256), 0, s, sums[t & 1], G, F, fp, C,
+                       sums[(t + 1) & 1]);
+  }
+  assign_dispatch(fp, X, n, H, G, C, labels, sums[iters & 1], s);
+  hipLaunchKernelGGL(copy_centroids_kernel, dim3(H), dim3(256), 0, s, C, G, F, fp, centroids_out);
+}
+
+void run_group_major(const int32_t* labels, int n, int H, int G, int32_t* perm, int32_t* offsets,
+                     hipStream_t s) {
+  hipLaunchKernelGGL(group_major_kernel, dim3(H), dim3(1024), 0, s, labels, n, G, perm, offsets);
+}
+
+void run_gather(const void* src, const int32_t* perm, int n, int hkv, int g, int d, bool bf16,
+                void* dst, hipStream_t s) {
+  const int row_bytes = d * (bf16 ? 2 : 4);
+  const int64_t rows = (int64_t)hkv * n * g;
+  const int64_t threads = rows * (row_bytes / 16);
+  const dim3 grid((unsigned)ceil_div(threads, 256));
+  const uint4* sp = static_cast<const uint4*>(src);
+  uint4* dp = static_cast<uint4*>(dst);
+  switch (row_bytes) {
+    case 128: hipLaunchKernelGGL(gather_rows_kernel<128>, grid, dim3(256), 0, s, sp, perm, n, g, rows, dp); break;
+    case 256: hipLaunchKernelGGL(gather_rows_kernel<256>, grid, dim3(256), 0, s, sp, perm, n, g, rows, dp); break;
+    case 512: hipLaunchKernelGGL(gather_rows_kernel<512>, grid, dim3(256), 0, s, sp, perm, n, g, rows, dp); break;
+    default: break;
+  }
+}
+
+template <typename T, int D>
+static void partition_typed(const Dims& dm, const Workspace& wp, const T* q, const T* k, const T* v,
+                            const sparsepr_partition_t& out, char* ws, hipStream_t s) {
+  uint32_t* maxbits = reinterpret_cast<uint32_t*>(ws + wp.maxbits);
+  int8_t* xk = reinterpret_cast<int8_t*>(ws + wp.xk);
+  int8_t* xq = reinterpret_cast<int8_t*>(ws + wp.xq);
+  int32_t* C = reinterpret_cast<int32_t*>(ws + wp.centroids);
+  int32_t* sums = reinterpret_cast<int32_t*>(ws + wp.sums);
+  float* usum = dm.g > 1 ? reinterpret_cast<float*>(ws + wp.usum) : nullptr;
+  const int n = dm.n, hkv = dm.hkv;
+  fill_u32(maxbits, (size_t)hkv * 2, 0, s);
+  // keys
+  hipLaunchKernelGGL((resp_s_kernel<T, D>), dim3((unsigned)ceil_div(n, 256), hkv), dim3(256), 0, s, q, k,
+                     n, dm.g, dm.rk, dm.scale, out.responses_s, maxbits);
+  hipLaunchKernelGGL(key_features_kernel, dim3((unsigned)ceil_div(n, 256), hkv), dim3(256), 0, s,
+                     out.responses_s, maxbits, n, dm.rk, wp.fpk, xk, out.exponents);
+  run_kmeans(xk, n, hkv, dm.gk, dm.rk, wp.fpk, dm.iters, C, sums, out.key_labels, out.key_centroids_int, s);
+  run_group_major(out.key_labels, n, hkv, dm.gk, out.key_perm, out.key_offsets, s);
+  run_gather(k, out.key_perm, n, hkv, 1, D, dm.bf16, out.k_gm, s);
+  run_gather(v, out.key_perm, n, hkv, 1, D, dm.bf16, out.v_gm, s);
+  hipLaunchKernelGGL((segment_mean_kernel<T, D>), dim3(dm.gk, hkv), dim3(256), 0, s,
+                     static_cast<const T*>(out.k_gm), out.key_offsets, n, dm.gk, out.key_centroids);
+  // queries
+  hipLaunchKernelGGL((resp_u_kernel<T, D>), dim3((unsigned)ceil_div(n, 64), hkv), dim3(256), 0, s, q,
+                     out.key_centroids, n, dm.g, dm.gk, dm.scale, out.responses_u, usum, maxbits + hkv);
+  hipLaunchKernelGGL(query_features_kernel, dim3((unsigned)ceil_div(n, 256), hkv), dim3(256), 0, s,
+                     usum ? usum : out.responses_u, maxbits + hkv, n, dm.gk, wp.fpq, out.query_features,
+                     xq, out.exponents);
+  run_kmeans(xq, n, hkv, dm.gq, dm.gk, wp.fpq, dm.iters, C, sums, out.query_labels, out.query_centroids, s);
+  run_group_major(out.query_labels, n, hkv, dm.gq, out.query_perm, out.query_offsets, s);
+  run_gather(q, out.query_perm, n, hkv, dm.g, D, dm.bf16, out.q_gm, s);
+}
+
+void launch_partition(const Dims& dm, const Workspace& wp, const void* q, const void* k, const void* v,
+                      const sparsepr_partition_t& out, char* ws, hipStream_t s) {
+  if (dm.bf16) {
+    if (dm.d == 128)
+      partition_typed<bf16_t, 128>(dm, wp, (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, out, ws, s);
+    else
+      partition_typed<bf16_t, 64>(dm, wp, (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, out, ws, s);
+  } else {
+    if (dm.d == 128)
+      partition_typed<float, 128>(dm, wp, (const float*)q, (const float*)k, (const float*)v, out, ws, s);
+    else
+      partition_typed<float, 64>(dm, wp, (const float*)q, (const float*)k, (const float*)v, out, ws, s);
+  }
+}
+
+}  // namespace sp

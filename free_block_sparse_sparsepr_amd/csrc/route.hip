@@ -1,0 +1,245 @@
+// Routing of (query group x key group) cells to a target execution density (summary page
+// of "Partition the Support, Reconstruct the Residual", execution paragraph: rho_exec =
+// rho_route + M / N, the router subtracts the probe cost first, cells are indivisible so
+// the realised density deviates slightly from the target).
+//
+// Cell masses are exact fixed-point integers: every query row's mass on key group b is
+// the size-weighted softmax of its responses to the key centroids, with logits rounded
+// to 1/64 units and exponentiated through a 1024-entry table, floor-divided to 2^20
+// units and summed with 64-bit integer atomics (order-free, hence deterministic).
+// Selection is one block per KV head: a mandatory heaviest cell per non-empty query
+// group, a bitonic sort of the other cells by mass per pair (exact 128-bit
+// cross-multiplication, ties to the smaller cell index), a prefix scan of their costs
+// and the longest prefix that fits the budget.
+#include <climits>
+#include <cmath>
+#include <mutex>
+
+#include "sp_common.hpp"
+#include "sp_launch.hpp"
+
+namespace sp {
+
+__constant__ uint32_t c_exp_table[kExpTable];
+
+// E[k] = rint(2^20 exp(-k / 64)), built on the host in double precision (round half to
+// even) and uploaded once per device.
+hipError_t ensure_exp_table() {
+  static std::mutex mu;
+  static bool done[64] = {false};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (done[dev]) return hipSuccess;
+  uint32_t table[kExpTable];
+  for (int k = 0; k < kExpTable; ++k) table[k] = (uint32_t)std::nearbyint(1048576.0 * std::exp(-k / 64.0));
+  e = hipMemcpyToSymbol(HIP_SYMBOL(c_exp_table), table, sizeof(table), 0, hipMemcpyHostToDevice);
+  if (e == hipSuccess) done[dev] = true;
+  return e;
+}
+
+// grid (ceil(n / 256), Hq), block 256.  mass [Hkv][Gq][Gk] must be zero on entry.
+__global__ __launch_bounds__(256) void route_mass_kernel(const float* __restrict__ U,
+                                                         const int32_t* __restrict__ qlabels,
+                                                         const int32_t* __restrict__ koff, int n,
+                                                         int g, int Gq, int Gk,
+                                                         unsigned long long* __restrict__ mass) {
+  __shared__ unsigned long long acc[kMaxGroups * kMaxGroups];
+  __shared__ int nb[kMaxGroups];
+  const int h = blockIdx.y, kv = h / g;
+  for (int i = threadIdx.x; i < Gq * Gk; i += 256) acc[i] = 0ull;
+  for (int b = threadIdx.x; b < Gk; b += 256)
+    nb[b] = koff[(int64_t)kv * (Gk + 1) + b + 1] - koff[(int64_t)kv * (Gk + 1) + b];
+  __syncthreads();
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) {
+    const int a = qlabels[(int64_t)kv * n + i];
+    const float* ur = U + ((int64_t)h * n + i) * Gk;
+    int z[kMaxGroups];
+    int mu = INT_MIN;
+#pragma unroll
+    for (int b = 0; b < kMaxGroups; ++b) {
+      if (b < Gk) {
+        float t = fminf(fmaxf(rintf(64.f * ur[b]), -1073741824.f), 1073741824.f);
+        z[b] = (int)t;
+        if (nb[b] > 0 && z[b] > mu) mu = z[b];
+      }
+    }
+    uint64_t e[kMaxGroups];
+    uint64_t tot = 0;
+#pragma unroll
+    for (int b = 0; b < kMaxGroups; ++b) {
+      if (b < Gk) {
+        int64_t dz = (int64_t)mu - (int64_t)z[b];
+        int k = dz > kExpTable - 1 ? kExpTable - 1 : (int)dz;
+        e[b] = nb[b] > 0 ? (uint64_t)nb[b] * (uint64_t)c_exp_table[k] : 0ull;
+        tot += e[b];
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < kMaxGroups; ++b) {
+      if (b < Gk && e[b]) atomicAdd(&acc[a * Gk + b], (unsigned long long)udiv_exact(e[b] << 20, tot));
+    }
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < Gq * Gk; idx += 256) {
+    unsigned long long v = acc[idx];
+    if (v) atomicAdd(&mass[(int64_t)kv * Gq * Gk + idx], v);
+  }
+}
+
+struct CellKey {
+  uint64_t m;
+  uint64_t c;
+};
+
+// a precedes b: valid first, then larger m/c, then smaller index
+__device__ __forceinline__ bool cell_before(const uint64_t* m, const uint64_t* cost, const uint8_t* valid,
+                                            int x, int y) {
+  if (valid[x] != valid[y]) return valid[x] > valid[y];
+  if (!valid[x]) return x < y;
+  unsigned __int128 l = (unsigned __int128)m[x] * cost[y];
+  unsigned __int128 r = (unsigned __int128)m[y] * cost[x];
+  if (l != r) return l > r;
+  return x < y;
+}
+
+// One block (1024 threads) per KV head.
+__global__ __launch_bounds__(1024) void route_select_kernel(const unsigned long long* __restrict__ mass,
+                                                            const int32_t* __restrict__ qoff,
+                                                            const int32_t* __restrict__ koff, int Gq,
+                                                            int Gk, int64_t budget,
+                                                            int32_t* __restrict__ row_ptr,
+                                                            int32_t* __restrict__ cols,
+                                                            uint64_t* __restrict__ kept_mask,
+                                                            int64_t* __restrict__ pairs) {
+  constexpr int CELLS = kMaxGroups * kMaxGroups;
+  __shared__ uint64_t sm[CELLS];
+  __shared__ uint64_t sc[CELLS];
+  __shared__ uint8_t valid[CELLS];
+  __shared__ uint8_t kept[CELLS];
+  __shared__ uint16_t order[CELLS];
+  __shared__ int64_t part[1024];
+  __shared__ int na[kMaxGroups], nbk[kMaxGroups], mand[kMaxGroups], rcount[kMaxGroups];
+  __shared__ int64_t left_s;
+  const int kv = blockIdx.x, tid = threadIdx.x;
+  const int ncell = Gq * Gk;
+  int P = 1;
+  while (P < ncell) P <<= 1;
+  if (tid < Gq) na[tid] = qoff[(int64_t)kv * (Gq + 1) + tid + 1] - qoff[(int64_t)kv * (Gq + 1) + tid];
+  if (tid < Gk) nbk[tid] = koff[(int64_t)kv * (Gk + 1) + tid + 1] - koff[(int64_t)kv * (Gk + 1) + tid];
+  __syncthreads();
+  for (int c = tid; c < P; c += 1024) {
+    if (c < ncell) {
+      int a = c / Gk, b = c % Gk;
+      sm[c] = mass[(int64_t)kv * ncell + c];
+      sc[c] = (uint64_t)na[a] * (uint64_t)nbk[b];
+    } else {
+      sm[c] = 0; sc[c] = 0;
+    }
+    kept[c] = 0;
+    order[c] = (uint16_t)c;
+  }
+  __syncthreads();
+  // mandatory heaviest non-empty key group of every non-empty query group (ties: smaller b)
+  if (tid < Gq) {
+    int best = -1;
+    if (na[tid] > 0) {
+      for (int b = 0; b < Gk; ++b) {
+        if (nbk[b] == 0) continue;
+        if (best < 0 || sm[tid * Gk + b] > sm[tid * Gk + best]) best = b;
+      }
+    }
+    mand[tid] = best;
+    if (best >= 0) kept[tid * Gk + best] = 1;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int64_t mc = 0;
+    for (int a = 0; a < Gq; ++a)
+      if (mand[a] >= 0) mc += (int64_t)sc[a * Gk + mand[a]];
+    left_s = budget - mc;
+  }
+  for (int c = tid; c < P; c += 1024) valid[c] = (c < ncell && sc[c] > 0 && !kept[c]) ? 1 : 0;
+  __syncthreads();
+  // bitonic sort of cell indices
+  for (int size = 2; size <= P; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int t = tid; t < P / 2; t += 1024) {
+        int lo = 2 * t - (t & (stride - 1));
+        int hi = lo + stride;
+        bool up = ((lo & size) == 0);
+        int x = order[lo], y = order[hi];
+        bool swap = up ? cell_before(sm, sc, valid, y, x) : cell_before(sm, sc, valid, x, y);
+        if (swap) { order[lo] = (uint16_t)y; order[hi] = (uint16_t)x; }
+      }
+      __syncthreads();
+    }
+  }
+  // inclusive prefix sum of costs in sorted order (valid cells come first)
+  const int per = (P + 1023) / 1024;
+  int64_t local = 0;
+  for (int i = 0; i < per; ++i) {
+    int pos = tid * per + i;
+    if (pos < P) { int c = order[pos]; if (valid[c]) local += (int64_t)sc[c]; }
+  }
+  part[tid] = local;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    int64_t v = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int64_t run = tid > 0 ? part[tid - 1] : 0;
+  const int64_t left = left_s;
+  for (int i = 0; i < per; ++i) {
+    int pos = tid * per + i;
+    if (pos < P) {
+      int c = order[pos];
+      if (valid[c]) {
+        run += (int64_t)sc[c];
+        if (run <= left) kept[c] = 1;
+      }
+    }
+  }
+  __syncthreads();
+  // CSR (columns ascending), kept masks, routed pairs
+  if (tid < Gq) {
+    int cnt = 0;
+    uint64_t msk = 0;
+    for (int b = 0; b < Gk; ++b)
+      if (kept[tid * Gk + b]) { ++cnt; msk |= 1ull << b; }
+    rcount[tid] = cnt;
+    kept_mask[(int64_t)kv * Gq + tid] = msk;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int s = 0;
+    int64_t pr = 0;
+    for (int a = 0; a < Gq; ++a) {
+      row_ptr[(int64_t)kv * (Gq + 1) + a] = s;
+      int w = s;
+      for (int b = 0; b < Gk; ++b)
+        if (kept[a * Gk + b]) { cols[(int64_t)kv * ncell + w++] = b; pr += (int64_t)sc[a * Gk + b]; }
+      s += rcount[a];
+    }
+    row_ptr[(int64_t)kv * (Gq + 1) + Gq] = s;
+    pairs[kv] = pr;
+  }
+}
+
+void launch_route(const Dims& dm, int64_t budget, const sparsepr_partition_t& part, const sparsepr_route_t& out,
+                  hipStream_t s) {
+  fill_u32(reinterpret_cast<uint32_t*>(out.cell_mass), (size_t)dm.hkv * dm.gq * dm.gk * 2, 0, s);
+  hipLaunchKernelGGL(route_mass_kernel, dim3((unsigned)ceil_div(dm.n, 256), dm.hq), dim3(256), 0, s,
+                     part.responses_u, part.query_labels, part.key_offsets, dm.n, dm.g, dm.gq, dm.gk,
+                     reinterpret_cast<unsigned long long*>(out.cell_mass));
+  hipLaunchKernelGGL(route_select_kernel, dim3(dm.hkv), dim3(1024), 0, s,
+                     reinterpret_cast<const unsigned long long*>(out.cell_mass), part.query_offsets,
+                     part.key_offsets, dm.gq, dm.gk, budget, out.row_ptr, out.cols, out.kept_mask, out.pairs);
+}
+
+}  // namespace sp

@@ -1,0 +1,93 @@
+// Shared device/host helpers of the SparsePR library (gfx950, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/sparsepr.h"
+
+namespace sp {
+
+typedef uint16_t bf16_t;
+
+constexpr int kWave = 64;
+constexpr int kMaxGroups = 64;      // G_Q, G_K <= 64 (one 64-bit kept mask per query group)
+constexpr int kMaxFeat = 64;        // r_k and G_K feature widths <= 64
+constexpr int kMaxProbe = 64;
+constexpr int kMaxRank = 32;
+constexpr int kExpTable = 1024;     // route exponential table entries
+constexpr int kProbeChunk = 1024;   // keys per probe-attention work item
+
+__host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+__host__ __device__ inline int round_up4(int x) { return (x + 3) & ~3; }
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t x) { return __uint_as_float(((uint32_t)x) << 16); }
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  __bf16 h = (__bf16)f;  // round to nearest even (v_cvt_pk_bf16_f32)
+  return __builtin_bit_cast(bf16_t, h);
+}
+
+template <typename T> __device__ __forceinline__ float to_f32(T x);
+template <> __device__ __forceinline__ float to_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ float to_f32<bf16_t>(bf16_t x) { return bf16_to_f32(x); }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) { return f32_to_bf16(x); }
+
+// Largest integer e with m * 2^e <= limit (0 when m == 0).  Power-of-two scaling of a
+// float is exact, so this decision is identical in float32 and float64.
+// Non-finite or non-positive maxima give 0; the adjustment loops are bounded.
+__device__ __forceinline__ int pow2_exponent(float m, float limit) {
+  if (!(m > 0.f) || !(m < INFINITY)) return 0;
+  int e;
+  frexpf(limit / m, &e);
+  e -= 1;
+  for (int it = 0; it < 320 && ldexpf(m, e + 1) <= limit; ++it) ++e;
+  for (int it = 0; it < 320 && ldexpf(m, e) > limit; ++it) --e;
+  return e;
+}
+
+// Integer a / b (b > 0) rounded half away from zero.
+__device__ __forceinline__ int div_rhaz(int a, int b) {
+  int q = (2 * (a < 0 ? -a : a) + b) / (2 * b);
+  return a < 0 ? -q : q;
+}
+
+// Exact floor(num / den) for 64-bit unsigned operands below 2^62.
+__device__ __forceinline__ uint64_t udiv_exact(uint64_t num, uint64_t den) {
+  if (den == 0) return 0;
+  uint64_t q = (uint64_t)((double)num / (double)den);
+  while (q > 0 && q * den > num) --q;
+  while ((q + 1) * den <= num) ++q;
+  return q;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+// A zero-fill kernel (used instead of hipMemsetAsync so the call can be captured).
+__global__ void fill_u32_kernel(uint32_t* p, size_t n, uint32_t v);
+void fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t s);
+
+// Workspace layout shared by the entry points (regions may overlap across entry
+// points because calls on one stream never run concurrently).
+struct Workspace {
+  size_t maxbits, xk, xq, centroids, sums, usum, total_partition;
+  size_t partials, fitbuf, probe_alloc, total_probe;
+  size_t dense_meta, total_dense;
+  size_t total;
+  int fpk, fpq, nchunks;
+};
+Workspace plan_workspace(const sparsepr_params& p);
+
+struct Dims {
+  int hq, hkv, g, n, d, gq, gk, rk, m, r, iters;
+  float scale, lambda;
+  bool bf16;
+};
+Dims dims_of(const sparsepr_params& p);
+
+}  // namespace sp

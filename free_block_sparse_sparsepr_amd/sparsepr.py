@@ -1,0 +1,162 @@
+"""Python front end of the SparsePR call (thin wrapper over include/sparsepr.h).
+
+torch allocates the device buffers and supplies the current HIP stream; the five entry
+points (partition, route, attend, probe_fit, apply) and the dense baseline all run in
+libsparsepr.so.  There is no fallback: without the library every call raises.
+"""
+import ctypes
+from dataclasses import dataclass
+
+import torch
+
+from . import _binding as B
+
+
+@dataclass
+class Config:
+    heads_q: int
+    heads_kv: int
+    n: int
+    d: int
+    dtype: str = "bf16"          # "bf16" or "fp32"
+    groups_q: int = 64
+    groups_k: int = 64
+    rho_exec: float = 0.22
+    r_k: int = 48
+    r_q: int = 64
+    n_probe: int = 64
+    rank: int = 16
+    lam: float = 0.1
+    kmeans_iters: int = 10
+    softmax_scale: float = 0.0
+
+    @property
+    def g(self):
+        return self.heads_q // self.heads_kv
+
+    @property
+    def torch_dtype(self):
+        return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+
+    def params(self) -> B.Params:
+        return B.Params(self.heads_q, self.heads_kv, self.n, self.d,
+                        B.BF16 if self.dtype == "bf16" else B.FP32, self.groups_q, self.groups_k,
+                        self.r_k, self.r_q, self.n_probe, self.rank, self.lam, self.rho_exec, 64,
+                        self.kmeans_iters, self.softmax_scale)
+
+
+def _p(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def workspace_bytes(cfg: Config) -> int:
+    lib = B.load()
+    out = ctypes.c_size_t(0)
+    prm = cfg.params()
+    B.check(lib.sparsepr_workspace_size(ctypes.byref(prm), ctypes.byref(out)))
+    return out.value
+
+
+class SparsePR:
+    """Owns the device buffers of one call shape; `__call__` runs the unfused order
+    partition -> route -> attend -> probe_fit -> apply on the current stream."""
+
+    def __init__(self, cfg: Config, device="cuda"):
+        self.cfg = cfg
+        self.lib = B.load()
+        self.prm = cfg.params()
+        dev = torch.device(device)
+        c = cfg
+        i32, f32 = torch.int32, torch.float32
+        e = lambda *shape, dt=i32: torch.empty(shape, dtype=dt, device=dev)  # noqa: E731
+        self.ws = e(max(workspace_bytes(cfg), 256), dt=torch.uint8)
+        self.part = dict(
+            responses_s=e(c.heads_kv, c.r_k, c.n, dt=f32), responses_u=e(c.heads_q, c.n, c.groups_k, dt=f32),
+            exponents=e(c.heads_kv, 2), key_labels=e(c.heads_kv, c.n),
+            key_centroids_int=e(c.heads_kv, c.groups_k, c.r_k), key_perm=e(c.heads_kv, c.n),
+            key_offsets=e(c.heads_kv, c.groups_k + 1), key_centroids=e(c.heads_kv, c.groups_k, c.d, dt=f32),
+            query_features=e(c.heads_kv, c.n, c.groups_k, dt=torch.int8), query_labels=e(c.heads_kv, c.n),
+            query_centroids=e(c.heads_kv, c.groups_q, c.groups_k), query_perm=e(c.heads_kv, c.n),
+            query_offsets=e(c.heads_kv, c.groups_q + 1),
+            q_gm=e(c.heads_kv, c.n, c.g, c.d, dt=c.torch_dtype), k_gm=e(c.heads_kv, c.n, c.d, dt=c.torch_dtype),
+            v_gm=e(c.heads_kv, c.n, c.d, dt=c.torch_dtype))
+        self.route_buf = dict(
+            row_ptr=e(c.heads_kv, c.groups_q + 1), cols=e(c.heads_kv, c.groups_q * c.groups_k),
+            kept_mask=e(c.heads_kv, c.groups_q, dt=torch.int64), pairs=e(c.heads_kv, dt=torch.int64),
+            cell_mass=e(c.heads_kv, c.groups_q, c.groups_k, dt=torch.int64))
+        self.fit = dict(
+            probe_tokens=e(c.heads_kv, c.n_probe), probe_groups=e(c.heads_kv, c.n_probe),
+            probe_weights=e(c.heads_kv, c.n_probe, dt=torch.float64),
+            o_dense=e(c.heads_q, c.n_probe, c.d, dt=f32), o_sparse=e(c.heads_q, c.n_probe, c.d, dt=f32),
+            A=e(c.heads_q, c.d, c.rank, dt=f32), B=e(c.heads_q, c.rank, c.d, dt=f32), c0=e(c.heads_q, c.d, dt=f32),
+            r_eff=e(c.heads_q), eig=e(c.heads_q, c.rank + 1, dt=f32))
+        self.o_gm = e(c.heads_kv, c.n, c.g, c.d, dt=f32)
+        self.lse = e(c.heads_kv, c.n, c.g, dt=f32)
+        self._part_t = B.PartitionT(*[self.part[k].data_ptr() for k in B.PARTITION_FIELDS])
+        self._route_t = B.RouteT(*[self.route_buf[k].data_ptr() for k in B.ROUTE_FIELDS])
+        self._fit_t = B.FitT(*[self.fit[k].data_ptr() for k in B.FIT_FIELDS])
+
+    # -- input checks (shape/dtype/device only; the library validates everything else)
+    def _check_qkv(self, q, k, v):
+        c = self.cfg
+        for t, h in ((q, c.heads_q), (k, c.heads_kv), (v, c.heads_kv)):
+            if t is None:
+                continue
+            if t.shape != (h, c.n, c.d) or t.dtype != c.torch_dtype or not t.is_cuda or not t.is_contiguous():
+                raise ValueError(f"expected contiguous {c.torch_dtype} cuda tensor of shape {(h, c.n, c.d)}, "
+                                 f"got {tuple(t.shape)} {t.dtype} {t.device}")
+
+    def partition(self, q, k, v):
+        self._check_qkv(q, k, v)
+        B.check(self.lib.sparsepr_partition(ctypes.byref(self.prm), _p(q), _p(k), _p(v),
+                                            ctypes.byref(self._part_t), _p(self.ws), self.ws.numel(), _stream()))
+
+    def route(self):
+        B.check(self.lib.sparsepr_route(ctypes.byref(self.prm), ctypes.byref(self._part_t),
+                                        ctypes.byref(self._route_t), _p(self.ws), self.ws.numel(), _stream()))
+
+    def attend(self):
+        B.check(self.lib.sparsepr_attend(ctypes.byref(self.prm), ctypes.byref(self._part_t),
+                                         ctypes.byref(self._route_t), _p(self.o_gm), _p(self.lse), _p(self.ws),
+                                         self.ws.numel(), _stream()))
+
+    def probe_fit(self, q):
+        self._check_qkv(q, None, None)
+        B.check(self.lib.sparsepr_probe_fit(ctypes.byref(self.prm), _p(q), ctypes.byref(self._part_t),
+                                            ctypes.byref(self._route_t), ctypes.byref(self._fit_t), _p(self.ws),
+                                            self.ws.numel(), _stream()))
+
+    def apply(self, out=None):
+        c = self.cfg
+        if out is None:
+            out = torch.empty((c.heads_q, c.n, c.d), dtype=c.torch_dtype, device=self.o_gm.device)
+        B.check(self.lib.sparsepr_apply(ctypes.byref(self.prm), _p(self.o_gm), ctypes.byref(self._part_t),
+                                        ctypes.byref(self._fit_t), _p(out), _stream()))
+        return out
+
+    def __call__(self, q, k, v, out=None):
+        self.partition(q, k, v)
+        self.route()
+        self.attend()
+        self.probe_fit(q)
+        return self.apply(out)
+
+    def dense(self, q, k, v, out=None):
+        self._check_qkv(q, k, v)
+        c = self.cfg
+        if out is None:
+            out = torch.empty((c.heads_q, c.n, c.d), dtype=c.torch_dtype, device=q.device)
+        B.check(self.lib.sparsepr_dense_attention(ctypes.byref(self.prm), _p(q), _p(k), _p(v), _p(out),
+                                                  _p(self.ws), self.ws.numel(), _stream()))
+        return out
+
+
+def config_from_workload(w) -> Config:
+    """Config of a sparsepr_workloads.Workload."""
+    return Config(heads_q=w.heads_q, heads_kv=w.heads_kv, n=w.n, d=w.d, dtype=w.dtype, groups_q=w.groups_q,
+                  groups_k=w.groups_k, rho_exec=w.rho_exec, r_k=w.r_k, r_q=w.r_q, n_probe=w.n_probe,
+                  rank=w.rank, lam=w.lam, kmeans_iters=w.kmeans_iters)

@@ -1,0 +1,192 @@
+/*
+ * sparsepr.h — C ABI of the SparsePR attention call on AMD Instinct MI355X (gfx950).
+ *
+ * SparsePR (summary page of "Partition the Support, Reconstruct the Residual:
+ * Training-Free Sparse Attention for Video Generation and World Models", Taghavi,
+ * Langari, Pandey; cited below as PSRR with the paragraph's topic) replaces one dense
+ * self-attention call with, in one call:
+ *   1. a response-coupled Q/K partition (PSRR, response-coupled partition paragraph),
+ *   2. routing of (query group x key group) cells to a target execution density with
+ *      the probe cost subtracted first (PSRR, execution paragraph),
+ *   3. a group-major permutation of Q, K and V (PSRR, execution paragraph),
+ *   4. a variable-length block-sparse attention, exact on the kept cells and
+ *      renormalised over the kept K/V groups (PSRR, execution paragraph),
+ *   5. probe-row residual reconstruction: exact probe rows, a coverage-weighted ridge
+ *      fit and a rank-r output-subspace projection, then write-back
+ *      (PSRR, probe-fit residual reconstruction paragraph).
+ * Under grouped-query attention the K/V partition and the route are shared by the
+ * query heads of one KV head (PSRR, execution paragraph).
+ *
+ * Conventions for every entry point
+ *  - All tensor pointers are DEVICE pointers allocated and owned by the caller; the
+ *    library allocates nothing and keeps no state between calls, except an immutable
+ *    1024-entry exponential table uploaded once per device on the first call made on
+ *    that device (so do not make the very first call inside a stream capture).
+ *  - `stream` is a hipStream_t (NULL = the null stream).  All work is asynchronous on
+ *    it; no entry point synchronises the host.
+ *  - Tensors are contiguous, row-major, 16-byte aligned.  Element type of Q/K/V and of
+ *    the final output is params->dtype (bf16 or fp32).
+ *  - Every argument is checked on the host before any launch.  On error a negative
+ *    sparsepr_status is returned and nothing is written.  Kernel launch failures
+ *    return SPARSEPR_ERR_HIP.  No C++ exception crosses this interface.
+ *  - Calls that share workspace or outputs must be ordered on one stream.
+ *  - Limits: 1 <= n <= 2^22, d in {64, 128}, heads_q % heads_kv == 0,
+ *    heads_q / heads_kv <= 16, 1 <= groups_q, groups_k <= 64, groups <= n,
+ *    groups_k <= r_q, 1 <= r_k <= 64, 1 <= n_probe <= min(64, n),
+ *    1 <= rank <= min(32, n_probe, d), lambda > 0, n_probe / n < rho_exec <= 1,
+ *    0 <= kmeans_iters <= 64, block == 64.
+ *
+ * Unfused call order: partition -> route -> attend -> probe_fit -> apply.
+ */
+#ifndef SPARSEPR_H
+#define SPARSEPR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SPARSEPR_OK = 0,
+  SPARSEPR_ERR_NULL = -1,      /* a required pointer is NULL */
+  SPARSEPR_ERR_SHAPE = -2,     /* n, d, heads or groups out of range */
+  SPARSEPR_ERR_DTYPE = -3,     /* dtype not bf16 / fp32 */
+  SPARSEPR_ERR_ALIGN = -4,     /* a tensor pointer is not 16-byte aligned */
+  SPARSEPR_ERR_WORKSPACE = -5, /* workspace smaller than sparsepr_workspace_size() */
+  SPARSEPR_ERR_PARAM = -6,     /* r_k, r_q, n_probe, rank, lambda, rho_exec, iters, block */
+  SPARSEPR_ERR_HIP = -7        /* a HIP runtime call or kernel launch failed */
+} sparsepr_status;
+
+typedef enum { SPARSEPR_BF16 = 0, SPARSEPR_FP32 = 1 } sparsepr_dtype;
+
+/* Problem and hyper-parameters.  Defaults on the page: r_k = 48, r_q = 64, n_probe = 64,
+ * rank = 16, lambda = 0.1 (PSRR, partition and probe-fit paragraphs); rho_exec is the
+ * target total execution density rho_route + n_probe / n (PSRR, execution paragraph). */
+typedef struct sparsepr_params {
+  int32_t heads_q;       /* query heads Hq; Q is [Hq, n, d] */
+  int32_t heads_kv;      /* KV heads Hkv; K, V are [Hkv, n, d]; query head h uses KV head h / g */
+  int32_t n;             /* tokens */
+  int32_t d;             /* head dimension (64 or 128) */
+  int32_t dtype;         /* sparsepr_dtype of Q, K, V and the output */
+  int32_t groups_q;      /* query groups G_Q */
+  int32_t groups_k;      /* key groups G_K */
+  int32_t r_k;           /* sampled queries = key response feature width */
+  int32_t r_q;           /* cap on the query feature width (features use G_K <= r_q) */
+  int32_t n_probe;       /* probe rows M per query head */
+  int32_t rank;          /* output-subspace rank r */
+  float lambda;          /* ridge penalty */
+  float rho_exec;        /* target execution density (pairs / n^2, probes included) */
+  int32_t block;         /* tile height in tokens; must be 64 */
+  int32_t kmeans_iters;  /* Lloyd iterations before the final assignment */
+  float softmax_scale;   /* 0 -> 1 / sqrt(d) */
+} sparsepr_params;
+
+/* Partition outputs (all caller-allocated device buffers).  g = heads_q / heads_kv.
+ * perm[p] is the token at group-major position p; offsets[b] is where group b starts. */
+typedef struct sparsepr_partition_t {
+  float* responses_s;        /* [Hkv, r_k, n] fp32: sampled-query responses S */
+  float* responses_u;        /* [Hq, n, G_K] fp32: query responses to key centroids U */
+  int32_t* exponents;        /* [Hkv, 2]: power-of-two exponents e_S, e_U */
+  int32_t* key_labels;       /* [Hkv, n] */
+  int32_t* key_centroids_int;/* [Hkv, G_K, r_k] integer feature centroids (final) */
+  int32_t* key_perm;         /* [Hkv, n] */
+  int32_t* key_offsets;      /* [Hkv, G_K + 1] */
+  float* key_centroids;      /* [Hkv, G_K, d] fp32 mean key vector of each group */
+  int8_t* query_features;    /* [Hkv, n, G_K] integer direction features in [-127, 127] */
+  int32_t* query_labels;     /* [Hkv, n] */
+  int32_t* query_centroids;  /* [Hkv, G_Q, G_K] centroids used by the final assignment */
+  int32_t* query_perm;       /* [Hkv, n] */
+  int32_t* query_offsets;    /* [Hkv, G_Q + 1] */
+  void* q_gm;                /* [Hkv, n, g, d] dtype: Q in group-major order */
+  void* k_gm;                /* [Hkv, n, d] dtype: K in group-major order */
+  void* v_gm;                /* [Hkv, n, d] dtype: V in group-major order (follows K) */
+} sparsepr_partition_t;
+
+/* Route outputs.  Row a of the CSR lists the kept key groups of query group a,
+ * ascending. */
+typedef struct sparsepr_route_t {
+  int32_t* row_ptr;          /* [Hkv, G_Q + 1] */
+  int32_t* cols;             /* [Hkv, G_Q * G_K] (first row_ptr[G_Q] entries used) */
+  uint64_t* kept_mask;       /* [Hkv, G_Q] bit b set when cell (a, b) is kept */
+  int64_t* pairs;            /* [Hkv] routed query-key pairs per query head (unpadded) */
+  uint64_t* cell_mass;       /* [Hkv, G_Q, G_K] fixed-point cell masses m_ab */
+} sparsepr_route_t;
+
+/* Probe and fit outputs. */
+typedef struct sparsepr_fit_t {
+  int32_t* probe_tokens;     /* [Hkv, n_probe] token index of each probe row */
+  int32_t* probe_groups;     /* [Hkv, n_probe] query group of each probe row */
+  double* probe_weights;     /* [Hkv, n_probe] group-coverage weights (sum n_probe) */
+  float* o_dense;            /* [Hq, n_probe, d] exact probe rows over all keys */
+  float* o_sparse;           /* [Hq, n_probe, d] probe rows over the kept cells */
+  float* A;                  /* [Hq, d, rank]  W V_r (zero beyond r_eff) */
+  float* B;                  /* [Hq, rank, d]  V_r^T (zero beyond r_eff) */
+  float* c0;                 /* [Hq, d]        ybar - xbar A B */
+  int32_t* r_eff;            /* [Hq] eigenpairs kept (lambda_k > 1e-8 lambda_1) */
+  float* eig;                /* [Hq, rank + 1] leading eigenvalues of Yt Yt^T */
+} sparsepr_fit_t;
+
+/* Bytes of scratch workspace every entry point below needs for these params. */
+sparsepr_status sparsepr_workspace_size(const sparsepr_params* params, size_t* bytes);
+
+/* Response-coupled partition (PSRR, response-coupled partition paragraph), per KV head:
+ * sample r_k query rows, S = Q_s K^T * scale, quantise to integer key features, online
+ * k-means over keys (V follows K), key centroids in the original space, U = Q C^T *
+ * scale per query head, integer response-direction features of the head-summed U,
+ * online k-means over queries (one asymmetric pass), stable group-major permutations,
+ * and the gathers of Q, K and V into group-major order.
+ * q: [Hq, n, d]; k, v: [Hkv, n, d] (dtype, token order). */
+sparsepr_status sparsepr_partition(const sparsepr_params* params, const void* q, const void* k,
+                                   const void* v, const sparsepr_partition_t* out, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+/* Routing to the target execution density (PSRR, execution paragraph): fixed-point cell
+ * masses from the size-weighted centroid softmax of every query row (summed over the
+ * KV head's query heads), budget rho_exec n^2 - n_probe n pairs per head, one mandatory
+ * heaviest cell per non-empty query group, the rest by mass per pair until the budget
+ * is spent.  Reads responses_u, query_labels, query_offsets, key_offsets. */
+sparsepr_status sparsepr_route(const sparsepr_params* params, const sparsepr_partition_t* part,
+                               const sparsepr_route_t* out, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/* Block-sparse attention over the kept cells, renormalised over the kept K/V groups
+ * (PSRR, execution paragraph).  Reads q_gm, k_gm, v_gm, offsets and the CSR.
+ * o_gm: [Hkv, n, g, d] fp32, group-major rows; lse: [Hkv, n, g] fp32 (natural log). */
+sparsepr_status sparsepr_attend(const sparsepr_params* params, const sparsepr_partition_t* part,
+                                const sparsepr_route_t* route, float* o_gm, float* lse,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Probe selection, exact probe rows and the fit (PSRR, probe-fit residual reconstruction
+ * paragraph): n_probe rows per KV head stratified over query groups in radial order
+ * about each group centroid, their dense and sparse outputs against all keys,
+ * R = O_dense - O_sparse, the group-coverage-weighted ridge fit of R on O_sparse and
+ * the rank-r subspace of the probe residuals.  q: [Hq, n, d] token order. */
+sparsepr_status sparsepr_probe_fit(const sparsepr_params* params, const void* q,
+                                   const sparsepr_partition_t* part, const sparsepr_route_t* route,
+                                   const sparsepr_fit_t* out, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+/* Write-back: o_hat = o + c0 + (o A) B for every row, probe rows replaced by their exact
+ * dense output, inverse permutation to token order, cast to dtype.
+ * o_gm: [Hkv, n, g, d] fp32 from sparsepr_attend; o: [Hq, n, d] dtype, token order. */
+sparsepr_status sparsepr_apply(const sparsepr_params* params, const float* o_gm,
+                               const sparsepr_partition_t* part, const sparsepr_fit_t* fit, void* o,
+                               void* stream);
+
+/* Dense softmax attention O = softmax(Q K^T * scale) V on the same tile machinery (the
+ * baseline; dense formula as in the lmnt.cn SparsePR article, section 2.1).
+ * q: [Hq, n, d]; k, v: [Hkv, n, d]; o: [Hq, n, d], all dtype and token order. */
+sparsepr_status sparsepr_dense_attention(const sparsepr_params* params, const void* q,
+                                         const void* k, const void* v, void* o,
+                                         void* workspace, size_t workspace_bytes,
+                                         void* stream);
+
+/* Static description of a status code. */
+const char* sparsepr_status_string(sparsepr_status status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SPARSEPR_H */

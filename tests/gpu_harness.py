@@ -1,0 +1,66 @@
+"""Helpers for the GPU parity tests: run the library on a seeded workload and recompute
+each stage with the oracle on the same inputs (integer stages fed the GPU's response
+matrices; float stages fed the GPU's labels, cells and probes)."""
+import numpy as np
+
+from oracle import sparsepr as O
+from sparsepr_workloads import generator as gen
+
+BF16_MAX_ABS, BF16_MEAN_ABS, FP32_MAX_ABS = 2e-2, 2e-3, 1e-4
+
+
+def torch_mod():
+    import torch
+    return torch
+
+
+def device_tensor(x, cfg):
+    torch = torch_mod()
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    return torch.from_numpy(np.ascontiguousarray(x)).to(device="cuda").to(dt).contiguous()
+
+
+def oracle_params(cfg):
+    return O.Params(groups_q=cfg.groups_q, groups_k=cfg.groups_k, rho_exec=float(np.float32(cfg.rho_exec)),
+                    r_k=cfg.r_k, r_q=cfg.r_q, n_probe=cfg.n_probe, rank=cfg.rank,
+                    lam=float(np.float32(cfg.lam)), kmeans_iters=cfg.kmeans_iters)
+
+
+def host(t):
+    torch = torch_mod()
+    if t.dtype == torch.bfloat16:
+        t = t.float()
+    return t.detach().cpu().numpy()
+
+
+def run_gpu(cfg, Q, K, V):
+    """Runs the unfused call and returns every buffer as numpy, plus the dense output."""
+    import free_block_sparse_sparsepr_amd as S
+    torch = torch_mod()
+    sp = S.SparsePR(S.config_from_workload(cfg))
+    q, k, v = device_tensor(Q, cfg), device_tensor(K, cfg), device_tensor(V, cfg)
+    out = sp(q, k, v)
+    dense = sp.dense(q, k, v)
+    torch.cuda.synchronize()
+    res = {k_: host(t) for k_, t in {**sp.part, **sp.route_buf, **sp.fit}.items()}
+    res["o_gm"] = host(sp.o_gm)
+    res["lse"] = host(sp.lse)
+    res["out"] = host(out)
+    res["dense"] = host(dense)
+    return res, sp, (q, k, v)
+
+
+def kept_from_mask(mask, gq, gk):
+    m = np.asarray(mask).astype(np.uint64)
+    return np.array([[(int(m[a]) >> b) & 1 for b in range(gk)] for a in range(gq)], dtype=bool)
+
+
+def compare_float(got, want, fp32):
+    err = np.abs(np.asarray(got, np.float64) - np.asarray(want, np.float64))
+    if fp32:
+        return err.max() <= FP32_MAX_ABS, err.max(), err.mean()
+    return (err.max() <= BF16_MAX_ABS and err.mean() <= BF16_MEAN_ABS), err.max(), err.mean()
+
+
+def oracle_inputs(cfg):
+    return gen.make_inputs(cfg, threads=4)

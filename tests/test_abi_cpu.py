@@ -1,0 +1,103 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports every entry
+point include/sparsepr.h declares, and rejects bad arguments before touching a device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sparsepr.h")
+
+B = pytest.importorskip("free_block_sparse_sparsepr_amd._binding")
+
+
+def lib_or_skip():
+    try:
+        return B.load()
+    except ImportError as e:
+        pytest.skip(str(e))
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:sparsepr_status|const char\*)\s+(sparsepr_\w+)\(", text, re.M)))
+
+
+def test_header_declares_the_five_calls_and_helpers():
+    names = declared_functions()
+    for n in ["sparsepr_partition", "sparsepr_route", "sparsepr_attend", "sparsepr_probe_fit",
+              "sparsepr_apply", "sparsepr_workspace_size", "sparsepr_dense_attention",
+              "sparsepr_status_string"]:
+        assert n in names
+    assert sorted(B.EXPORTS) == names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = lib_or_skip()
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+
+
+def _params(**kw):
+    base = dict(heads_q=4, heads_kv=2, n=4096, d=128, dtype=B.BF16, groups_q=64, groups_k=64, r_k=48,
+                r_q=64, n_probe=64, rank=16, lam=0.1, rho_exec=0.22, block=64, kmeans_iters=10,
+                softmax_scale=0.0)
+    base.update(kw)
+    return B.Params(**base)
+
+
+def _ws(p):
+    lib = lib_or_skip()
+    out = ctypes.c_size_t(0)
+    return lib.sparsepr_workspace_size(ctypes.byref(p), ctypes.byref(out)), out.value
+
+
+def test_workspace_size_valid():
+    st, n = _ws(_params())
+    assert st == 0 and n > 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=96), -2), (dict(n=0), -2), (dict(n=(1 << 22) + 1), -2), (dict(heads_q=3), -2),
+    (dict(heads_q=34, heads_kv=2), -2), (dict(groups_q=65), -2), (dict(groups_k=0), -2),
+    (dict(n=32, groups_q=33, n_probe=16, rho_exec=0.9), -2), (dict(dtype=7), -3),
+    (dict(groups_k=64, r_q=32), -6), (dict(r_k=65), -6), (dict(n_probe=65), -6),
+    (dict(n=60, groups_q=8, groups_k=8, n_probe=61, rank=4), -6), (dict(rank=33), -6),
+    (dict(rank=17, n_probe=16), -6), (dict(lam=0.0), -6), (dict(lam=float("nan")), -6),
+    (dict(rho_exec=1.5), -6), (dict(rho_exec=0.01, n=4096), -6), (dict(kmeans_iters=-1), -6),
+    (dict(block=32), -6), (dict(softmax_scale=-1.0), -6),
+])
+def test_invalid_params_rejected(kw, code):
+    st, _ = _ws(_params(**kw))
+    assert st == code
+
+
+def test_entry_points_reject_before_any_launch():
+    lib = lib_or_skip()
+    bad = _params(d=96)
+    good = _params()
+    part, route, fit = B.PartitionT(), B.RouteT(), B.FitT()
+    nul = ctypes.c_void_p(0)
+    # invalid params
+    assert lib.sparsepr_partition(ctypes.byref(bad), nul, nul, nul, ctypes.byref(part), nul, 0, nul) == -2
+    # null inputs / outputs
+    assert lib.sparsepr_partition(ctypes.byref(good), nul, nul, nul, ctypes.byref(part), nul, 0, nul) == -1
+    assert lib.sparsepr_route(ctypes.byref(good), ctypes.byref(part), ctypes.byref(route), nul, 0, nul) == -1
+    assert lib.sparsepr_attend(ctypes.byref(good), ctypes.byref(part), ctypes.byref(route), nul, nul, nul, 0,
+                               nul) == -1
+    assert lib.sparsepr_probe_fit(ctypes.byref(good), nul, ctypes.byref(part), ctypes.byref(route),
+                                  ctypes.byref(fit), nul, 0, nul) == -1
+    assert lib.sparsepr_apply(ctypes.byref(good), nul, ctypes.byref(part), ctypes.byref(fit), nul, nul) == -1
+    assert lib.sparsepr_dense_attention(ctypes.byref(good), nul, nul, nul, nul, nul, 0, nul) == -1
+    # misaligned pointer, and a workspace that is too small (fake non-null pointers are
+    # never dereferenced: validation fails first)
+    fake = ctypes.c_void_p(0x1000)
+    odd = ctypes.c_void_p(0x1008)
+    fields = {f: 0x2000 for f in B.PARTITION_FIELDS}
+    full = B.PartitionT(**fields)
+    assert lib.sparsepr_partition(ctypes.byref(good), odd, fake, fake, ctypes.byref(full), fake, 1 << 40,
+                                  nul) == -4
+    assert lib.sparsepr_partition(ctypes.byref(good), fake, fake, fake, ctypes.byref(full), fake, 16,
+                                  nul) == -5
+    assert lib.sparsepr_status_string(-5) == b"workspace too small"
