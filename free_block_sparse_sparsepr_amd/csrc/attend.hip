@@ -38,7 +38,7 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs A) {
   float o[CPT];
 #pragma unroll
   for (int c = 0; c < CPT; ++c) o[c] = 0.f;
-  int ci = 0, k0 = 0, k1 = 0;
+  int ci = ti.kbeg < 0 ? 0 : ti.kbeg, k0 = 0, k1 = 0;
   while (next_run(A, kv, ti, ci, k0, k1)) {
     for (int kt = k0; kt < k1; kt += BN) {
       const int nk = min(BN, k1 - kt);

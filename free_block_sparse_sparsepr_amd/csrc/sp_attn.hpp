@@ -63,7 +63,8 @@ __device__ __forceinline__ bool find_tile(const AttnArgs& A, int kv, int t, int 
 }
 
 // Next contiguous key run [k0, k1) of the tile: consecutive kept key groups are adjacent
-// in group-major order and merge into one run.  `ci` walks the CSR columns.
+// in group-major order and merge into one run.  `ci` walks the CSR columns and must start
+// at ti.kbeg (0 for the dense schedule).
 __device__ __forceinline__ bool next_run(const AttnArgs& A, int kv, const TileInfo& ti, int& ci, int& k0,
                                          int& k1) {
   if (ti.kbeg < 0) {

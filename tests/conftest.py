@@ -6,5 +6,11 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 
+try:  # import once at collection so a slow first import is not charged to a test's timeout
+    import torch  # noqa: F401
+except ImportError:  # pragma: no cover
+    torch = None
+
+
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
