@@ -1,0 +1,171 @@
+"""Benchmark of the SparsePR attention call on one MI355X.
+
+One step = one whole SparsePR call (partition, route, attend, probe_fit, apply: every
+stage the summary page of "Partition the Support, Reconstruct the Residual" counts in its
+timed latency) over the HunyuanVideo-shaped 720p workload: N = 118,800 tokens
+(T=33, H=45, W=80), 24 heads, d = 128, bf16, target rho_exec = 22 %, seeded synthetic
+inputs resident in HBM before the timed region.
+
+Prints one JSON line: calls/s (value), the sparse kernel's effective TFLOP/s on executed
+(unpadded) pairs and its fraction of the bf16 MFMA peak (roofline), the speedup over
+the same-GPU dense attention, a per-stage breakdown, and the CPU oracle timed on a
+bounded sample (cpu_baseline).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3] [--no-dense] [--no-cpu]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sparse attention calls/sec + effective TFLOPS (% bf16 MFMA peak) vs dense attn"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3
+STAGES = ["partition", "route", "attend", "probe_fit", "apply"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(cfg):
+    """The oracle as it stands on one KV head of the workload, scaled to the call."""
+    import numpy as np
+    from oracle import sparsepr as O
+    from sparsepr_workloads import generator as gen
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        cores = max([i.get("num_threads", 1) for i in info] or [os.cpu_count() or 1])
+        blas = ",".join(sorted({i.get("internal_api", "?") for i in info}))
+    except Exception:  # pragma: no cover
+        cores, blas = os.cpu_count() or 1, "?"
+    q, k, v = gen.head_inputs(cfg, 0)
+    p = O.Params(cfg.groups_q, cfg.groups_k, float(np.float32(cfg.rho_exec)), lam=float(np.float32(cfg.lam)))
+    t0 = time.perf_counter()
+    O.sparsepr_kv_head(q, k, v, p)
+    dt = time.perf_counter() - t0
+    per_call = dt * cfg.heads_kv
+    return {"value": 1.0 / per_call, "unit": "calls/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"KV head 0 of {cfg.heads_kv} ({cfg.g} query head(s)): whole oracle call "
+                      f"(partition, route, sparse attention of all {cfg.n} rows, probes, fit, apply) "
+                      f"in {dt:.1f} s, scaled x{cfg.heads_kv}; float64 NumPy, BLAS {blas}, "
+                      f"nproc {os.cpu_count()}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=3)
+    ap.add_argument("--dense-steps", type=int, default=2)
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for {args.gpus}); the SparsePR call "
+              "shards by head with no exchange step, but no multi-GPU path is built.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import free_block_sparse_sparsepr_amd as S
+    from sparsepr_workloads import CONFIGS, make_inputs
+
+    cfg = CONFIGS[args.workload]
+    dev = torch.device("cuda:0")
+    log(f"[bench] generating {cfg.name} inputs")
+    t0 = time.perf_counter()
+    Q, K, V = make_inputs(cfg, threads=16)
+    tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    q, k, v = (torch.from_numpy(x).to(dev).to(tdt).contiguous() for x in (Q, K, V))
+    del Q, K, V
+    log(f"[bench] inputs ready in {time.perf_counter() - t0:.1f} s")
+    sp = S.SparsePR(S.config_from_workload(cfg), device=dev)
+    out = torch.empty((cfg.heads_q, cfg.n, cfg.d), dtype=tdt, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        fns = [lambda: sp.partition(q, k, v), sp.route, sp.attend, lambda: sp.probe_fit(q),
+               lambda: sp.apply(out)]
+        for i, fn in enumerate(fns):
+            if ev is not None:
+                ev[i][0].record(stream)
+            fn()
+            if ev is not None:
+                ev[i][1].record(stream)
+
+    for i in range(args.warmup):
+        step()
+        log(f"[bench] warmup {i + 1}/{args.warmup}")
+    torch.cuda.synchronize()
+    events = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+               for _ in STAGES] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(events[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    log(f"[bench] timed {args.steps} calls in {wall:.3f} s")
+    stage_ms = {name: float(np.mean([events[s][i][0].elapsed_time(events[s][i][1]) for s in range(args.steps)]))
+                for i, name in enumerate(STAGES)}
+    ms_per_step = wall * 1e3 / args.steps
+
+    pairs_kv = sp.route_buf["pairs"].cpu().numpy().astype(np.int64)
+    routed = int(pairs_kv.sum()) * cfg.g                     # summed over query heads
+    executed = routed + cfg.heads_q * cfg.n_probe * cfg.n
+    flop_attend = 4.0 * cfg.d * routed
+    flop_call = 4.0 * cfg.d * executed
+    attend_tflops = flop_attend / (stage_ms["attend"] * 1e-3) / 1e12
+    call_tflops = flop_call / (ms_per_step * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_FP32_TFLOPS
+    rho_route = float(pairs_kv.mean()) / cfg.n ** 2
+    rho_exec = rho_route + cfg.n_probe / cfg.n
+
+    dense = None
+    if not args.no_dense:
+        sp.dense(q, k, v, out)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.dense_steps):
+            sp.dense(q, k, v, out)
+        torch.cuda.synchronize()
+        dense_ms = (time.perf_counter() - t0) * 1e3 / args.dense_steps
+        dense_flop = 4.0 * cfg.d * cfg.n * cfg.n * cfg.heads_q
+        dense = {"ms_per_call": dense_ms, "tflops": dense_flop / (dense_ms * 1e-3) / 1e12,
+                 "speedup_sparsepr_vs_dense": dense_ms / ms_per_step}
+        log(f"[bench] dense {dense_ms:.2f} ms/call")
+
+    cpu = None
+    if not args.no_cpu:
+        log("[bench] timing the CPU oracle on one head")
+        cpu = cpu_baseline(cfg)
+
+    res = {
+        "metric": METRIC, "value": args.steps / wall, "unit": "calls/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded Fourier-feature Q/K, Gaussian V; no model weights)",
+        "config": {"workload": cfg.name, "grid_thw": list(cfg.grid), "n": cfg.n, "heads_q": cfg.heads_q,
+                   "heads_kv": cfg.heads_kv, "d": cfg.d, "rho_exec_target": cfg.rho_exec,
+                   "groups_q": cfg.groups_q, "groups_k": cfg.groups_k, "n_probe": cfg.n_probe,
+                   "rank": cfg.rank, "r_k": cfg.r_k, "r_q": cfg.r_q, "lambda": cfg.lam},
+        "roofline": {"bound": "mfma", "kernel": "sparse attention (sparsepr_attend)",
+                     "achieved": attend_tflops, "peak": peak, "unit": "TFLOP/s", "frac": attend_tflops / peak,
+                     "traffic": None},
+        "effective_tflops_call": call_tflops, "effective_frac_call": call_tflops / peak,
+        "realised_rho_route": rho_route, "realised_rho_exec": rho_exec,
+        "routed_pairs": routed, "stage_ms": stage_ms, "dense": dense, "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
