@@ -105,13 +105,10 @@ static void launch_valu(AttnArgs a, int hkv, hipStream_t s) {
   hipLaunchKernelGGL((attn_valu_kernel<T, D, OutT>), dim3(a.tiles_per_head, hkv), dim3(256), 0, s, a);
 }
 
+// bf16 inputs run on the matrix cores (attend_mfma.hip); fp32 inputs on the vector ALUs.
 void launch_attention(const Dims& dm, AttnArgs a, bool out_is_input_dtype, hipStream_t s) {
   if (dm.bf16) {
-    if (out_is_input_dtype) {
-      if (dm.d == 128) launch_valu<bf16_t, 128, bf16_t>(a, dm.hkv, s); else launch_valu<bf16_t, 64, bf16_t>(a, dm.hkv, s);
-    } else {
-      if (dm.d == 128) launch_valu<bf16_t, 128, float>(a, dm.hkv, s); else launch_valu<bf16_t, 64, float>(a, dm.hkv, s);
-    }
+    launch_attention_mfma(dm, a, out_is_input_dtype, s);
   } else {
     if (dm.d == 128) launch_valu<float, 128, float>(a, dm.hkv, s); else launch_valu<float, 64, float>(a, dm.hkv, s);
   }

@@ -22,7 +22,8 @@ struct AttnArgs {
   float* lse;                  // [Hkv][n][g] or NULL
   int n, g, gq, gk;
   float scale;
-  int tiles_per_head;          // grid.x
+  int tiles_per_head;          // tiles scheduled per KV head
+  int n_heads_kv;
 };
 
 struct TileInfo {

@@ -13,6 +13,7 @@ void launch_route(const Dims& dm, int64_t budget, const sparsepr_partition_t& pa
                   hipStream_t s);
 // out_is_input_dtype: output element type equals Q's (dense baseline); otherwise fp32.
 void launch_attention(const Dims& dm, AttnArgs a, bool out_is_input_dtype, hipStream_t s);
+void launch_attention_mfma(const Dims& dm, AttnArgs a, bool out_is_input_dtype, hipStream_t s);
 void launch_probe_fit(const Dims& dm, const Workspace& wp, const void* q, const sparsepr_partition_t& part,
                       const sparsepr_route_t& route, const sparsepr_fit_t& out, char* ws, hipStream_t s);
 void launch_apply(const Dims& dm, const float* o_gm, const sparsepr_partition_t& part, const sparsepr_fit_t& fit,
