@@ -9,50 +9,78 @@
 
 namespace sp {
 
-// grid (ceil(n / 64), Hq), block 256 (4 waves x 16 rows).
+// One block = 64 group-major rows of one query head.  The rows are staged in LDS, the
+// rank-r coordinates T = O A are a 64 x r product, then o + c0 + T B is written to the
+// token-order rows (4 threads per row, 16-byte stores).  grid (ceil(n / 64), Hq), block 256.
 template <typename OutT, int D>
 __global__ __launch_bounds__(256) void apply_kernel(const float* __restrict__ o_gm, const int32_t* __restrict__ qperm,
                                                     const float* __restrict__ A, const float* __restrict__ B,
                                                     const float* __restrict__ c0, const int32_t* __restrict__ r_eff,
                                                     int n, int g, int rank, OutT* __restrict__ out) {
-  __shared__ float As[D][kMaxRank + 1];
+  constexpr int R = 64;
+  __shared__ float Os[R][D + 4];
+  __shared__ float As[D][kMaxRank];
   __shared__ float Bs[kMaxRank][D];
+  __shared__ float Ts[R][kMaxRank + 1];
   __shared__ float cs[D];
-  __shared__ float orow[4][D];
-  __shared__ float tk[4][kMaxRank];
   const int h = blockIdx.y, kv = h / g, j = h % g;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int tid = threadIdx.x;
+  const int p0 = blockIdx.x * R;
   const int re = r_eff[h];
   for (int idx = tid; idx < D * kMaxRank; idx += 256) {
     const int c = idx / kMaxRank, k = idx % kMaxRank;
     As[c][k] = k < re ? A[((int64_t)h * D + c) * rank + k] : 0.f;
-    Bs[k][c % D] = 0.f;
+    const int kb = idx / D, cb = idx % D;
+    Bs[kb][cb] = kb < re ? B[((int64_t)h * rank + kb) * D + cb] : 0.f;
+  }
+  for (int c = tid; c < D; c += 256) cs[c] = c0[(int64_t)h * D + c];
+  for (int idx = tid; idx < R * (D / 4); idx += 256) {
+    const int r = idx / (D / 4), c4 = idx % (D / 4);
+    const int p = p0 + r;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (p < n) v = *reinterpret_cast<const float4*>(o_gm + (((int64_t)kv * n + p) * g + j) * D + 4 * c4);
+    Os[r][4 * c4] = v.x; Os[r][4 * c4 + 1] = v.y; Os[r][4 * c4 + 2] = v.z; Os[r][4 * c4 + 3] = v.w;
   }
   __syncthreads();
-  for (int idx = tid; idx < re * D; idx += 256) Bs[idx / D][idx % D] = B[((int64_t)h * rank) * D + idx];
-  for (int c = tid; c < D; c += 256) cs[c] = c0[(int64_t)h * D + c];
-  __syncthreads();
-  for (int rr = 0; rr < 16; ++rr) {
-    const int p = blockIdx.x * 64 + w * 16 + rr;
-    const bool valid = p < n;
-    if (valid)
-      for (int c = l; c < D; c += 64) orow[w][c] = o_gm[(((int64_t)kv * n + p) * g + j) * D + c];
-    __syncthreads();
-    if (valid) {
-      const int k = l & 31, half = l >> 5;
-      float t = 0.f;
-      for (int c = half * (D / 2); c < (half + 1) * (D / 2); ++c) t = fmaf(orow[w][c], As[c][k], t);
-      t += __shfl_xor(t, 32);
-      if (half == 0) tk[w][k] = t;
+  const int r = tid >> 2, q4 = tid & 3;
+  {
+    float t[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) t[i] = 0.f;
+    for (int c = 0; c < D; ++c) {
+      const float x = Os[r][c];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) t[i] = fmaf(x, As[c][8 * q4 + i], t[i]);
     }
-    __syncthreads();
-    if (valid) {
-      const int64_t tok = qperm[(int64_t)kv * n + p];
-      OutT* orow_out = out + ((int64_t)h * n + tok) * D;
-      for (int c = l; c < D; c += 64) {
-        float v = orow[w][c] + cs[c];
-        for (int k = 0; k < re; ++k) v = fmaf(tk[w][k], Bs[k][c], v);
-        orow_out[c] = from_f32<OutT>(v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) Ts[r][8 * q4 + i] = t[i];
+  }
+  __syncthreads();
+  const int p = p0 + r;
+  if (p < n) {
+    constexpr int CW = D / 4;   // columns per thread
+    const int cbase = q4 * CW;
+    OutT* orow = out + ((int64_t)h * n + qperm[(int64_t)kv * n + p]) * D + cbase;
+#pragma unroll
+    for (int c8 = 0; c8 < CW; c8 += 8) {
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int c = cbase + c8 + e;
+        float x = Os[r][c] + cs[c];
+        for (int k = 0; k < re; ++k) x = fmaf(Ts[r][k], Bs[k][c], x);
+        v[e] = x;
+      }
+      if constexpr (sizeof(OutT) == 4) {
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(orow) + c8) = make_float4(v[0], v[1], v[2], v[3]);
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(orow) + c8 + 4) = make_float4(v[4], v[5], v[6], v[7]);
+      } else {
+        uint4 pk;
+        pk.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+        pk.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+        pk.z = (uint32_t)f32_to_bf16(v[4]) | ((uint32_t)f32_to_bf16(v[5]) << 16);
+        pk.w = (uint32_t)f32_to_bf16(v[6]) | ((uint32_t)f32_to_bf16(v[7]) << 16);
+        *reinterpret_cast<uint4*>(reinterpret_cast<bf16_t*>(orow) + c8) = pk;
       }
     }
   }

@@ -65,20 +65,22 @@ struct Stage {
   uint4 v[4];
 };
 
-// Global -> registers for one K/V tile.  K: thread t loads 64 contiguous bytes of key
-// t / 4; V: thread t loads 16 bytes of each of keys 4 (t / 16) .. +3 at d = 8 (t % 16).
-// Rows at or beyond k1 are zero.
+// Global -> registers for one K/V tile.  K: thread t loads D / 2 contiguous bytes of key
+// t % 64 at d = (t / 64) D / 4; V (d = 128): 16 bytes of each of keys 4 (t % 16) .. +3
+// at d = 8 (t / 16); V (d = 64): keys 2 (t % 32), +1 at d = 8 (t / 32).  Rows at or beyond
+// k1 are zero.
 template <int D>
 __device__ __forceinline__ void stage_load(const bf16_t* __restrict__ kb, const bf16_t* __restrict__ vb, int kt,
                                            int k1, int tid, Stage<D>& st) {
   static_assert(D == 128 || D == 64, "head dim");
-  if constexpr (D == 128) {
-    const int key = tid >> 2, c = (tid & 3) * 32;
-    const bool in = kt + key < k1;
-    const uint4* src = reinterpret_cast<const uint4*>(kb + (int64_t)(kt + key) * D + c);
+  constexpr int KV = D / 64;                  // 16-byte chunks per thread per operand / 2
+  const int key = tid & 63, c = (tid >> 6) * (D / 4);
+  const bool in = kt + key < k1;
+  const uint4* src = reinterpret_cast<const uint4*>(kb + (int64_t)(kt + key) * D + c);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) st.k[i] = in ? src[i] : make_uint4(0, 0, 0, 0);
-    const int kq = tid >> 4, dc = (tid & 15) * 8;
+  for (int i = 0; i < 2 * KV; ++i) st.k[i] = in ? src[i] : make_uint4(0, 0, 0, 0);
+  if constexpr (D == 128) {
+    const int kq = tid & 15, dc = (tid >> 4) * 8;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int key2 = 4 * kq + i;
@@ -86,14 +88,7 @@ __device__ __forceinline__ void stage_load(const bf16_t* __restrict__ kb, const 
                                  : make_uint4(0, 0, 0, 0);
     }
   } else {
-    // D = 64: thread t loads 32 contiguous bytes of key t / 4 (K) and 16 bytes of keys
-    // 2 (t / 8) and 2 (t / 8) + 1 at d = 8 (t % 8) (V)
-    const int key = tid >> 2, c = (tid & 3) * 16;
-    const bool in = kt + key < k1;
-    const uint4* src = reinterpret_cast<const uint4*>(kb + (int64_t)(kt + key) * D + c);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) st.k[i] = in ? src[i] : make_uint4(0, 0, 0, 0);
-    const int kp = tid >> 3, dc = (tid & 7) * 8;
+    const int kp = tid & 31, dc = (tid >> 5) * 8;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int key2 = 2 * kp + i;
@@ -103,17 +98,20 @@ __device__ __forceinline__ void stage_load(const bf16_t* __restrict__ kb, const 
   }
 }
 
-// Registers -> LDS (K row-major, V transposed).
+// Registers -> LDS (K row-major, V transposed).  Consecutive lanes write consecutive
+// keys (K rows 272 bytes apart, V^T words 8 bytes apart), so the stores are free of bank
+// conflicts.
 template <int D>
 __device__ __forceinline__ void stage_store(bf16_t* __restrict__ Ks, bf16_t* __restrict__ Vt, int tid,
                                             const Stage<D>& st) {
   using C = MfmaCfg<D>;
-  if constexpr (D == 128) {
-    const int key = tid >> 2, c = (tid & 3) * 32;
-    uint4* dst = reinterpret_cast<uint4*>(Ks + key * C::KROW + c);
+  constexpr int KV = D / 64;
+  const int key = tid & 63, c = (tid >> 6) * (D / 4);
+  uint4* dst = reinterpret_cast<uint4*>(Ks + key * C::KROW + c);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dst[i] = st.k[i];
-    const int kq = tid >> 4, dc = (tid & 15) * 8;
+  for (int i = 0; i < 2 * KV; ++i) dst[i] = st.k[i];
+  if constexpr (D == 128) {
+    const int kq = tid & 15, dc = (tid >> 4) * 8;
     const uint32_t* x0 = reinterpret_cast<const uint32_t*>(&st.v[0]);
     const uint32_t* x1 = reinterpret_cast<const uint32_t*>(&st.v[1]);
     const uint32_t* x2 = reinterpret_cast<const uint32_t*>(&st.v[2]);
@@ -126,22 +124,121 @@ __device__ __forceinline__ void stage_store(bf16_t* __restrict__ Ks, bf16_t* __r
       *reinterpret_cast<uint2*>(Vt + (dc + 2 * w + 1) * C::VROW + 4 * kq) = hi;
     }
   } else {
-    const int key = tid >> 2, c = (tid & 3) * 16;
-    uint4* dst = reinterpret_cast<uint4*>(Ks + key * C::KROW + c);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) dst[i] = st.k[i];
-    // D = 64 V: thread t holds keys 2 (t / 8) and 2 (t / 8) + 1 at d = 8 (t % 8) .. +7;
-    // each d row receives the key pair as one 32-bit word.
-    const int kp = tid >> 3, dc = (tid & 7) * 8;
-    const int keyb = 2 * kp;
+    const int kp = tid & 31, dc = (tid >> 5) * 8;
     const uint32_t* x0 = reinterpret_cast<const uint32_t*>(&st.v[0]);
     const uint32_t* x1 = reinterpret_cast<const uint32_t*>(&st.v[1]);
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      *reinterpret_cast<uint32_t*>(Vt + (dc + 2 * w) * C::VROW + keyb) = pack_lo(x0[w], x1[w]);
-      *reinterpret_cast<uint32_t*>(Vt + (dc + 2 * w + 1) * C::VROW + keyb) = pack_hi(x0[w], x1[w]);
+      *reinterpret_cast<uint32_t*>(Vt + (dc + 2 * w) * C::VROW + 2 * kp) = pack_lo(x0[w], x1[w]);
+      *reinterpret_cast<uint32_t*>(Vt + (dc + 2 * w + 1) * C::VROW + 2 * kp) = pack_hi(x0[w], x1[w]);
     }
   }
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+union PackP {
+  bf16x8_t v;
+  bf16x2_t h[4];
+};
+
+// A row max may go stale by up to this much (log2 units) before O and l are rescaled:
+// probabilities stay below 2^8 and most tiles skip the rescale entirely.
+constexpr float kStaleMax = 8.f;
+
+// One 64-key tile of the online softmax for a wave's 32 queries: S^T = K Q^T on the
+// matrix cores (two independent accumulation chains), masking (keys at or beyond nk,
+// only on partial tiles; with MASK, keys whose group bit is clear in rowmask), the row
+// max (in-register plus the partner lane), p = exp2(s c2 - m) with one FMA and the raw
+// hardware exp2, bf16 packing, the row sum as bf16 dot products of the packed p (the
+// same values the second product consumes), a lazy rescale, and O^T += V^T P^T.
+template <int D, bool MASK>
+__device__ __forceinline__ void mfma_tile_step(const bf16_t* __restrict__ ks, const bf16_t* __restrict__ vt,
+                                               const bf16x8_t* qreg, int nk, float c2,
+                                               const uint8_t* __restrict__ klab, uint64_t rowmask, float& m_i,
+                                               float& l_i, f32x16_t* o, int l32, int hf) {
+  using C = MfmaCfg<D>;
+  f32x16_t s0, s1;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) { s0[r] = 0.f; s1[r] = 0.f; }
+  {
+    const bf16_t* k0 = ks + l32 * C::KROW + 8 * hf;
+    const bf16_t* k1 = ks + (32 + l32) * C::KROW + 8 * hf;
+#pragma unroll
+    for (int kk = 0; kk < C::KSTEPS; ++kk) {
+      const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(k0 + 16 * kk);
+      const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(k1 + 16 * kk);
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[kk], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[kk], s1, 0, 0, 0);
+    }
+  }
+  f32x16_t sv[2] = {s0, s1};
+  if (MASK || nk < C::BN) {
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 32 * kb2 + 8 * (r >> 2) + 4 * hf + (r & 3);
+        bool keep = key < nk;
+        if constexpr (MASK) keep = keep && ((rowmask >> klab[key]) & 1ull);
+        sv[kb2][r] = keep ? sv[kb2][r] : -INFINITY;
+      }
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sv[kb2][r]);
+  mx = fmaxf(mx, __shfl_xor(mx, 32)) * c2;
+  const float m_use = (mx > m_i + kStaleMax) ? mx : m_i;
+  float alpha;
+  if constexpr (MASK) alpha = (m_use == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_i - m_use);
+  else alpha = __builtin_amdgcn_exp2f(m_i - m_use);
+  const float neg = -m_use;
+  bf16x2_t ones;
+  ones[0] = (__bf16)1.f;
+  ones[1] = (__bf16)1.f;
+  float rs = 0.f;
+  PackP p[2][2];
+#pragma unroll
+  for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      float e0 = __builtin_amdgcn_exp2f(fmaf(sv[kb2][r], c2, neg));
+      float e1 = __builtin_amdgcn_exp2f(fmaf(sv[kb2][r + 1], c2, neg));
+      if constexpr (MASK) {
+        e0 = (sv[kb2][r] == -INFINITY) ? 0.f : e0;
+        e1 = (sv[kb2][r + 1] == -INFINITY) ? 0.f : e1;
+      }
+      bf16x2_t pr;
+      pr[0] = (__bf16)e0;
+      pr[1] = (__bf16)e1;
+      p[kb2][r >> 3].h[(r & 7) >> 1] = pr;
+      rs = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, rs, false);
+    }
+  l_i = l_i * alpha + rs;
+  m_i = m_use;
+  if (__ballot(alpha != 1.f)) {
+#pragma unroll
+    for (int db = 0; db < C::DBLK; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+  }
+  // O^T += V^T P^T over the 4 key k-steps of the tile
+#pragma unroll
+  for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const int koff = 32 * kb2 + 16 * s2 + 4 * hf;
+#pragma unroll
+      for (int db = 0; db < C::DBLK; ++db) {
+        const bf16_t* vr = vt + (32 * db + l32) * C::VROW + koff;
+        uint2 lo = *reinterpret_cast<const uint2*>(vr);
+        uint2 hi = *reinterpret_cast<const uint2*>(vr + 8);
+        uint4 av = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av), p[kb2][s2].v, o[db], 0,
+                                                        0, 0);
+      }
+    }
 }
 
 template <int D, typename OutT>
@@ -202,71 +299,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs A) {
     iter_next(A, kv, ti, nx, C::BN);
     if (nx.valid) stage_load<D>(kb, vb, nx.kt, nx.k1, tid, st);
 
-    const bf16_t* ks = Ks[cur];
-    const bf16_t* vt = Vt[cur];
-    // S^T blocks: keys 32 kb + (8 (r / 4) + 4 hf + r % 4), query l32
-    f32x16_t s[2];
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb2][r] = 0.f;
-      const bf16_t* krow = ks + (32 * kb2 + l32) * C::KROW + 8 * hf;
-#pragma unroll
-      for (int kk = 0; kk < C::KSTEPS; ++kk) {
-        bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(krow + 16 * kk);
-        s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[kk], s[kb2], 0, 0, 0);
-      }
-    }
-    // scale to the log2 domain, mask keys beyond the run, tile max
-    const int nk = it.k1 - it.kt;
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = 32 * kb2 + 8 * (r >> 2) + 4 * hf + (r & 3);
-        float x = s[kb2][r] * c2;
-        x = key < nk ? x : -INFINITY;
-        s[kb2][r] = x;
-        mx = fmaxf(mx, x);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_i, mx);
-    const float alpha = exp2f(m_i - m_new);
-    float rs = 0.f;
-    bf16x8_t p[2][2];
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float e = exp2f(s[kb2][r] - m_new);
-        rs += e;
-        p[kb2][r >> 3][r & 7] = (__bf16)e;
-      }
-    l_i = l_i * alpha + rs;
-    m_i = m_new;
-    if (__ballot(alpha != 1.f)) {
-#pragma unroll
-      for (int db = 0; db < C::DBLK; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-    }
-    // O^T += V^T P^T over the 4 key k-steps of the tile
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const int koff = 32 * kb2 + 16 * s2 + 4 * hf;
-#pragma unroll
-        for (int db = 0; db < C::DBLK; ++db) {
-          const bf16_t* vr = vt + (32 * db + l32) * C::VROW + koff;
-          uint2 lo = *reinterpret_cast<const uint2*>(vr);
-          uint2 hi = *reinterpret_cast<const uint2*>(vr + 8);
-          uint4 av = make_uint4(lo.x, lo.y, hi.x, hi.y);
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av), p[kb2][s2], o[db],
-                                                          0, 0, 0);
-        }
-      }
+    mfma_tile_step<D, false>(Ks[cur], Vt[cur], qreg, it.k1 - it.kt, c2, nullptr, 0ull, m_i, l_i, o, l32, hf);
     if (nx.valid) stage_store<D>(Ks[cur ^ 1], Vt[cur ^ 1], tid, st);
     __syncthreads();
     cur ^= 1;
@@ -298,6 +331,121 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs A) {
       }
     if (A.lse && hf == 0) A.lse[((int64_t)kv * A.n + vrow / A.g) * A.g + vrow % A.g] = (m_i + log2f(l_tot)) * 0.6931471805599453f;
   }
+}
+
+
+// ---------------------------------------------------------------------------------------
+// Probe rows (summary page of "Partition the Support, Reconstruct the Residual",
+// probe-fit residual reconstruction paragraph): the M <= 64 probe rows of a query head
+// against one chunk of keys (group-major order), as two online softmaxes: waves 0-1 over
+// every key (dense rows) and waves 2-3 over the keys whose group is kept for the probe's
+// query group (sparse rows).  Writes unnormalised partials (o, m, l) with m in natural
+// log units: partials [Hq][chunks][M][2][D + 2].  grid (chunks, Hq), block 256.
+// ---------------------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256, 2) void probe_attn_mfma_kernel(const bf16_t* __restrict__ q,
+                                                               const bf16_t* __restrict__ kgm,
+                                                               const bf16_t* __restrict__ vgm,
+                                                               const int32_t* __restrict__ koff,
+                                                               const uint64_t* __restrict__ kept_mask,
+                                                               const int32_t* __restrict__ ptok,
+                                                               const int32_t* __restrict__ pgrp, int n, int g,
+                                                               int Gq, int Gk, int M, float scale, int chunk,
+                                                               float* __restrict__ partials) {
+  using C = MfmaCfg<D>;
+  __shared__ __attribute__((aligned(16))) bf16_t Ks[2][C::BN * C::KROW];
+  __shared__ __attribute__((aligned(16))) bf16_t Vt[2][D * C::VROW];
+  __shared__ uint8_t klab[2][C::BN];
+  __shared__ int ko[kMaxGroups + 1];
+  const int h = blockIdx.y, kv = h / g, ch = blockIdx.x, nch = gridDim.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, hf = lane >> 5;
+  const int row = 32 * (w & 1) + l32;
+  const bool sparse = (w >> 1) != 0;
+  const int k0 = ch * chunk, k1 = min(n, k0 + chunk);
+  for (int b = tid; b <= Gk; b += 256) ko[b] = koff[(int64_t)kv * (Gk + 1) + b];
+  const bool rvalid = row < M;
+  const uint64_t rowmask = rvalid ? kept_mask[(int64_t)kv * Gq + pgrp[kv * M + row]] : 0ull;
+  bf16x8_t qreg[C::KSTEPS];
+  {
+    const bf16_t* qr = q + ((int64_t)h * n + (rvalid ? ptok[kv * M + row] : 0)) * D;
+#pragma unroll
+    for (int kk = 0; kk < C::KSTEPS; ++kk) {
+      uint4 x = rvalid ? *reinterpret_cast<const uint4*>(qr + 16 * kk + 8 * hf) : make_uint4(0, 0, 0, 0);
+      qreg[kk] = __builtin_bit_cast(bf16x8_t, x);
+    }
+  }
+  const bf16_t* kb = kgm + (int64_t)kv * n * D;
+  const bf16_t* vb = vgm + (int64_t)kv * n * D;
+  const float c2 = scale * 1.4426950408889634f;
+  float m_i = -INFINITY, l_i = 0.f;
+  f32x16_t o[C::DBLK];
+#pragma unroll
+  for (int db = 0; db < C::DBLK; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
+  __syncthreads();
+  auto label_of = [&](int pos) {
+    int lo = 0, hi = Gk - 1;  // last group b with ko[b] <= pos (always non-empty)
+    while (lo < hi) { int mid = (lo + hi + 1) >> 1; if (ko[mid] <= pos) lo = mid; else hi = mid - 1; }
+    return lo;
+  };
+  Stage<D> st;
+  int kt = k0;
+  if (kt < k1) {
+    stage_load<D>(kb, vb, kt, k1, tid, st);
+    stage_store<D>(Ks[0], Vt[0], tid, st);
+    if (tid < C::BN) klab[0][tid] = (uint8_t)(kt + tid < k1 ? label_of(kt + tid) : 0);
+  }
+  __syncthreads();
+  int cur = 0;
+  while (kt < k1) {
+    const int nt = kt + C::BN;
+    if (nt < k1) stage_load<D>(kb, vb, nt, k1, tid, st);
+    if (sparse)
+      mfma_tile_step<D, true>(Ks[cur], Vt[cur], qreg, k1 - kt, c2, klab[cur], rowmask, m_i, l_i, o, l32, hf);
+    else
+      mfma_tile_step<D, false>(Ks[cur], Vt[cur], qreg, k1 - kt, c2, nullptr, 0ull, m_i, l_i, o, l32, hf);
+    if (nt < k1) {
+      stage_store<D>(Ks[cur ^ 1], Vt[cur ^ 1], tid, st);
+      if (tid < C::BN) klab[cur ^ 1][tid] = (uint8_t)(nt + tid < k1 ? label_of(nt + tid) : 0);
+    }
+    __syncthreads();
+    cur ^= 1;
+    kt = nt;
+  }
+  const float l_tot = l_i + __shfl_xor(l_i, 32);
+  if (rvalid) {
+    float* pb = partials + (((int64_t)h * nch + ch) * M + row) * 2 * (D + 2) + (sparse ? D + 2 : 0);
+#pragma unroll
+    for (int db = 0; db < C::DBLK; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d0 = 32 * db + 8 * j + 4 * hf;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pb[d0 + e] = o[db][4 * j + e];
+      }
+    if (hf == 0) {
+      pb[D] = m_i == -INFINITY ? -INFINITY : m_i * 0.6931471805599453f;
+      pb[D + 1] = l_tot;
+    }
+  }
+}
+
+void launch_probe_attn_mfma(const Dims& dm, const void* q, const sparsepr_partition_t& part,
+                            const sparsepr_route_t& route, const sparsepr_fit_t& fit, int chunk, int nchunks,
+                            float* partials, hipStream_t s) {
+  const dim3 grid(nchunks, dm.hq);
+  if (dm.d == 128)
+    hipLaunchKernelGGL(probe_attn_mfma_kernel<128>, grid, dim3(256), 0, s, (const bf16_t*)q,
+                       (const bf16_t*)part.k_gm, (const bf16_t*)part.v_gm, part.key_offsets, route.kept_mask,
+                       fit.probe_tokens, fit.probe_groups, dm.n, dm.g, dm.gq, dm.gk, dm.m, dm.scale, chunk,
+                       partials);
+  else
+    hipLaunchKernelGGL(probe_attn_mfma_kernel<64>, grid, dim3(256), 0, s, (const bf16_t*)q,
+                       (const bf16_t*)part.k_gm, (const bf16_t*)part.v_gm, part.key_offsets, route.kept_mask,
+                       fit.probe_tokens, fit.probe_groups, dm.n, dm.g, dm.gq, dm.gk, dm.m, dm.scale, chunk,
+                       partials);
 }
 
 template <int D, typename OutT>

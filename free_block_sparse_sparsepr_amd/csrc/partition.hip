@@ -86,21 +86,29 @@ __global__ __launch_bounds__(256) void resp_s_kernel(const T* __restrict__ q, co
 
 // X^K[j][s] = clamp(rint(S[s][j] * 2^e_S), -127, 127), e_S the largest e with
 // max|S| 2^e <= 127.  Features stored point-major with a padded stride fp (zeros).
+// A block converts 256 keys: coalesced reads of S rows, transpose through LDS, 16-byte
+// stores of the contiguous [256][fp] byte tile.  grid (ceil(n / 256), Hkv), block 256.
 __global__ __launch_bounds__(256) void key_features_kernel(const float* __restrict__ S,
                                                            const uint32_t* maxbits, int n, int rk,
                                                            int fp, int8_t* __restrict__ X,
                                                            int32_t* exps) {
+  __shared__ __attribute__((aligned(16))) int8_t tile[256 * kMaxFeat];
   const int kv = blockIdx.y;
-  const int j = blockIdx.x * 256 + threadIdx.x;
+  const int j0 = blockIdx.x * 256;
   const int e = pow2_exponent(__uint_as_float(maxbits[kv]), 127.f);
   if (blockIdx.x == 0 && threadIdx.x == 0) exps[kv * 2 + 0] = e;
-  if (j >= n) return;
-  int8_t* xr = X + ((int64_t)kv * n + j) * fp;
+  const int j = j0 + threadIdx.x;
   for (int s = 0; s < fp; ++s) {
     float v = 0.f;
-    if (s < rk) v = fminf(fmaxf(rintf(ldexpf(S[((int64_t)kv * rk + s) * n + j], e)), -127.f), 127.f);
-    xr[s] = (int8_t)(int)v;
+    if (s < rk && j < n) v = fminf(fmaxf(rintf(ldexpf(S[((int64_t)kv * rk + s) * n + j], e)), -127.f), 127.f);
+    tile[threadIdx.x * fp + s] = (int8_t)(int)v;
   }
+  __syncthreads();
+  const int rows = min(256, n - j0);
+  const int bytes = rows * fp;   // multiple of 4
+  int8_t* dst = X + ((int64_t)kv * n + j0) * fp;
+  for (int b = threadIdx.x * 4; b < bytes; b += 256 * 4)
+    *reinterpret_cast<int32_t*>(dst + b) = *reinterpret_cast<const int32_t*>(tile + b);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -117,8 +125,10 @@ __global__ void kmeans_init_kernel(const int8_t* __restrict__ X, int n, int G, i
 }
 
 // Assignment argmin_g ||c_g||^2 - 2 <x, c_g> (ties: smallest g) with 4-way int8 dot
-// products, plus exact per-group feature sums and counts (block-local in LDS, then
-// global atomics).  sums: [H][G][fp + 1] (last column = count), zeroed by the caller.
+// products, plus exact per-group feature sums and counts: the block's points are
+// bucketed by label (counting sort in LDS), each (group, feature) sum runs over its
+// bucket, and non-zero sums go to global memory with integer atomics (order-free).
+// sums: [H][G][fp + 1] (last column = count), zeroed by the caller.
 // grid (ceil(n / 256), H), block 256.
 template <int FP>
 __global__ __launch_bounds__(256) void kmeans_assign_kernel(const int8_t* __restrict__ X, int n,
@@ -128,7 +138,9 @@ __global__ __launch_bounds__(256) void kmeans_assign_kernel(const int8_t* __rest
   constexpr int W = FP / 4;
   __shared__ int32_t cw[kMaxGroups][W];
   __shared__ int32_t cn[kMaxGroups];
-  __shared__ int32_t acc[kMaxGroups * (FP + 1)];
+  __shared__ int32_t cnt[kMaxGroups], start[kMaxGroups];
+  __shared__ int32_t xs[256 * W];
+  __shared__ uint8_t order[256];
   const int h = blockIdx.y;
   for (int idx = threadIdx.x; idx < G * W; idx += 256) {
     int gi = idx / W, w = idx % W;
@@ -143,9 +155,10 @@ __global__ __launch_bounds__(256) void kmeans_assign_kernel(const int8_t* __rest
     for (int f = 0; f < FP; ++f) s += c[f] * c[f];
     cn[gi] = s;
   }
-  for (int idx = threadIdx.x; idx < G * (FP + 1); idx += 256) acc[idx] = 0;
+  for (int gi = threadIdx.x; gi < kMaxGroups; gi += 256) cnt[gi] = 0;
   __syncthreads();
   const int j = blockIdx.x * 256 + threadIdx.x;
+  int lab = -1, slot = 0;
   if (j < n) {
     int32_t xw[W];
     const int32_t* xr = reinterpret_cast<const int32_t*>(X + ((int64_t)h * n + j) * FP);
@@ -160,21 +173,31 @@ __global__ __launch_bounds__(256) void kmeans_assign_kernel(const int8_t* __rest
       if (score < best) { best = score; bi = gi; }
     }
     labels[(int64_t)h * n + j] = bi;
+    lab = bi;
 #pragma unroll
-    for (int w = 0; w < W; ++w) {
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        int v = (int)(int8_t)((uint32_t)xw[w] >> (8 * b));
-        if (v) atomicAdd(&acc[bi * (FP + 1) + 4 * w + b], v);
-      }
-    }
-    atomicAdd(&acc[bi * (FP + 1) + FP], 1);
+    for (int w = 0; w < W; ++w) xs[threadIdx.x * W + w] = xw[w];
+    slot = atomicAdd(&cnt[bi], 1);
   }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < G * (FP + 1); idx += 256) {
-    int v = acc[idx];
-    if (v) atomicAdd(&sums[(int64_t)h * kMaxGroups * (FP + 1) + idx], v);
+  if (threadIdx.x == 0) {
+    int s = 0;
+    for (int gi = 0; gi < G; ++gi) { start[gi] = s; s += cnt[gi]; }
   }
+  __syncthreads();
+  if (lab >= 0) order[start[lab] + slot] = (uint8_t)threadIdx.x;
+  __syncthreads();
+  // per (group, feature) sums over the group's members in this block (exact integers)
+  const int8_t* xb = reinterpret_cast<const int8_t*>(xs);
+  int32_t* sh = sums + (int64_t)h * kMaxGroups * (FP + 1);
+  for (int idx = threadIdx.x; idx < G * FP; idx += 256) {
+    const int gi = idx / FP, f = idx % FP;
+    const int m0 = start[gi], m1 = m0 + cnt[gi];
+    int acc = 0;
+    for (int m = m0; m < m1; ++m) acc += xb[order[m] * FP + f];
+    if (acc) atomicAdd(&sh[gi * (FP + 1) + f], acc);
+  }
+  for (int gi = threadIdx.x; gi < G; gi += 256)
+    if (cnt[gi]) atomicAdd(&sh[gi * (FP + 1) + FP], cnt[gi]);
 }
 
 // c_g = div_rhaz(sum_g, count_g); an empty group keeps its centroid.  Also clears the
@@ -280,25 +303,31 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint4* __restric
   dst[r * VPR + c] = src[srow * VPR + c];
 }
 
-// C^K_b = mean of the group-major key rows of group b in fixed order (fp32).  grid
-// (G, Hkv), block 256.
+// C^K_b = mean of the group-major key rows of group b in fixed order (fp32).  Thread t
+// sums 4 columns (4 * (t % (D / 4)) ..) over rows start + ph, ph + P, ... with P = 256 /
+// (D / 4) row phases, then the phases are combined in ascending order.  grid (G, Hkv),
+// block 256.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void segment_mean_kernel(const T* __restrict__ kgm,
                                                            const int32_t* __restrict__ offsets, int n,
                                                            int G, float* __restrict__ C) {
-  constexpr int P = 256 / D;
+  constexpr int CQ = D / 4;
+  constexpr int P = 256 / CQ;
   __shared__ float red[P][D];
   const int b = blockIdx.x, h = blockIdx.y;
-  const int col = threadIdx.x % D, ph = threadIdx.x / D;
+  const int cq = threadIdx.x % CQ, ph = threadIdx.x / CQ;
   const int start = offsets[(int64_t)h * (G + 1) + b], end = offsets[(int64_t)h * (G + 1) + b + 1];
-  float s = 0.f;
-  for (int r = start + ph; r < end; r += P) s += to_f32(kgm[((int64_t)h * n + r) * D + col]);
-  red[ph][col] = s;
+  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+  for (int r = start + ph; r < end; r += P) {
+    const T* src = kgm + ((int64_t)h * n + r) * D + 4 * cq;
+    s0 += to_f32(src[0]); s1 += to_f32(src[1]); s2 += to_f32(src[2]); s3 += to_f32(src[3]);
+  }
+  red[ph][4 * cq] = s0; red[ph][4 * cq + 1] = s1; red[ph][4 * cq + 2] = s2; red[ph][4 * cq + 3] = s3;
   __syncthreads();
-  if (ph == 0) {
+  for (int col = threadIdx.x; col < D; col += 256) {
     float tot = 0.f;
     for (int i = 0; i < P; ++i) tot += red[i][col];
-    int cnt = end - start;
+    const int cnt = end - start;
     C[((int64_t)h * G + b) * D + col] = cnt > 0 ? tot / (float)cnt : 0.f;
   }
 }
@@ -371,36 +400,31 @@ __global__ __launch_bounds__(256) void resp_u_kernel(const T* __restrict__ q, co
 // Response-direction features: u = rint(Usum 2^e_U) (e_U: largest e with
 // max|Usum| 2^e <= 2^14), c_b = G_K u_b - sum u, x_b = div_rhaz(127 c_b, max|c|).
 // Written to the caller's [Hkv][n][G_K] buffer and to a stride-fp copy for the k-means.
+// One wave per row (lanes over key groups, wave reductions); each wave walks 16 rows.
+// grid (ceil(n / 64), Hkv), block 256.
 __global__ __launch_bounds__(256) void query_features_kernel(const float* __restrict__ Usrc,
                                                              const uint32_t* maxbits, int n, int Gk,
                                                              int fp, int8_t* __restrict__ Xout,
                                                              int8_t* __restrict__ Xpad, int32_t* exps) {
   const int kv = blockIdx.y;
-  const int i = blockIdx.x * 256 + threadIdx.x;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int e = pow2_exponent(__uint_as_float(maxbits[kv]), 16384.f);
   if (blockIdx.x == 0 && threadIdx.x == 0) exps[kv * 2 + 1] = e;
-  if (i >= n) return;
-  const float* ur = Usrc + ((int64_t)kv * n + i) * Gk;
-  int u[kMaxGroups];
-  int sum = 0;
+  for (int rr = 0; rr < 16; ++rr) {
+    const int i = blockIdx.x * 64 + w * 16 + rr;
+    if (i >= n) break;
+    const float* ur = Usrc + ((int64_t)kv * n + i) * Gk;
+    const int u = lane < Gk ? (int)rintf(ldexpf(ur[lane], e)) : 0;
+    int sum = u;
 #pragma unroll
-  for (int b = 0; b < kMaxGroups; ++b) {
-    if (b < Gk) { u[b] = (int)rintf(ldexpf(ur[b], e)); sum += u[b]; }
-  }
-  int mx = 0;
+    for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
+    const int c = Gk * u - sum;
+    int mx = lane < Gk ? (c < 0 ? -c : c) : 0;
 #pragma unroll
-  for (int b = 0; b < kMaxGroups; ++b) {
-    if (b < Gk) { u[b] = Gk * u[b] - sum; int a = u[b] < 0 ? -u[b] : u[b]; mx = a > mx ? a : mx; }
-  }
-  int8_t* xo = Xout + ((int64_t)kv * n + i) * Gk;
-  int8_t* xp = Xpad + ((int64_t)kv * n + i) * fp;
-#pragma unroll
-  for (int b = 0; b < kMaxGroups; ++b) {
-    if (b < fp) {
-      int x = (b < Gk && mx > 0) ? div_rhaz(127 * u[b], mx) : 0;
-      xp[b] = (int8_t)x;
-      if (b < Gk) xo[b] = (int8_t)x;
-    }
+    for (int o = 32; o > 0; o >>= 1) mx = max(mx, __shfl_xor(mx, o));
+    const int x = (lane < Gk && mx > 0) ? div_rhaz(127 * c, mx) : 0;
+    if (lane < Gk) Xout[((int64_t)kv * n + i) * Gk + lane] = (int8_t)x;
+    if (lane < fp) Xpad[((int64_t)kv * n + i) * fp + lane] = (int8_t)x;
   }
 }
 
@@ -474,8 +498,11 @@ static void partition_typed(const Dims& dm, const Workspace& wp, const T* q, con
   const int n = dm.n, hkv = dm.hkv;
   fill_u32(maxbits, (size_t)hkv * 2, 0, s);
   // keys
-  hipLaunchKernelGGL((resp_s_kernel<T, D>), dim3((unsigned)ceil_div(n, 256), hkv), dim3(256), 0, s, q, k,
-                     n, dm.g, dm.rk, dm.scale, out.responses_s, maxbits);
+  if (dm.bf16)
+    launch_resp_s_mfma(dm, q, k, out.responses_s, maxbits, s);
+  else
+    hipLaunchKernelGGL((resp_s_kernel<T, D>), dim3((unsigned)ceil_div(n, 256), hkv), dim3(256), 0, s, q, k,
+                       n, dm.g, dm.rk, dm.scale, out.responses_s, maxbits);
   hipLaunchKernelGGL(key_features_kernel, dim3((unsigned)ceil_div(n, 256), hkv), dim3(256), 0, s,
                      out.responses_s, maxbits, n, dm.rk, wp.fpk, xk, out.exponents);
   run_kmeans(xk, n, hkv, dm.gk, dm.rk, wp.fpk, dm.iters, C, sums, out.key_labels, out.key_centroids_int, s);
@@ -485,9 +512,12 @@ static void partition_typed(const Dims& dm, const Workspace& wp, const T* q, con
   hipLaunchKernelGGL((segment_mean_kernel<T, D>), dim3(dm.gk, hkv), dim3(256), 0, s,
                      static_cast<const T*>(out.k_gm), out.key_offsets, n, dm.gk, out.key_centroids);
   // queries
-  hipLaunchKernelGGL((resp_u_kernel<T, D>), dim3((unsigned)ceil_div(n, 64), hkv), dim3(256), 0, s, q,
-                     out.key_centroids, n, dm.g, dm.gk, dm.scale, out.responses_u, usum, maxbits + hkv);
-  hipLaunchKernelGGL(query_features_kernel, dim3((unsigned)ceil_div(n, 256), hkv), dim3(256), 0, s,
+  if (dm.bf16)
+    launch_resp_u_mfma(dm, q, out.key_centroids, out.responses_u, usum, maxbits + hkv, s);
+  else
+    hipLaunchKernelGGL((resp_u_kernel<T, D>), dim3((unsigned)ceil_div(n, 64), hkv), dim3(256), 0, s, q,
+                       out.key_centroids, n, dm.g, dm.gk, dm.scale, out.responses_u, usum, maxbits + hkv);
+  hipLaunchKernelGGL(query_features_kernel, dim3((unsigned)ceil_div(n, 64), hkv), dim3(256), 0, s,
                      usum ? usum : out.responses_u, maxbits + hkv, n, dm.gk, wp.fpq, out.query_features,
                      xq, out.exponents);
   run_kmeans(xq, n, hkv, dm.gq, dm.gk, wp.fpq, dm.iters, C, sums, out.query_labels, out.query_centroids, s);

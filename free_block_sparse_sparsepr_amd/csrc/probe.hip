@@ -13,6 +13,8 @@
 
 namespace sp {
 
+constexpr int kSortMax = 8192;   // groups up to this size are sorted in LDS
+
 // ---------------------------------------------------------------------------------------
 // Probe selection.  grid (Gq, Hkv), block 256.
 // Allocation: one probe at a time over the non-empty groups in the order (larger group
@@ -31,6 +33,7 @@ __global__ __launch_bounds__(256) void probe_select_kernel(const int8_t* __restr
   __shared__ int alloc[kMaxGroups], start[kMaxGroups], tgt[kMaxProbe];
   __shared__ int cent[kMaxFeat];
   __shared__ int lrad[1024];
+  __shared__ uint64_t skey[kSortMax];
   const int a = blockIdx.x, kv = blockIdx.y, tid = threadIdx.x;
   const int32_t* qo = qoff + (int64_t)kv * (Gq + 1);
   if (tid == 0) {
@@ -74,10 +77,52 @@ __global__ __launch_bounds__(256) void probe_select_kernel(const int8_t* __restr
     const int tok = qperm[(int64_t)kv * n + off + i];
     const int8_t* x = XQ + ((int64_t)kv * n + tok) * Gk;
     int s = 0;
-    for (int f = 0; f < Gk; ++f) { int dd = (int)x[f] - cent[f]; s += dd * dd; }
+    if ((Gk & 15) == 0) {
+      for (int f0 = 0; f0 < Gk; f0 += 16) {
+        const uint4 v = *reinterpret_cast<const uint4*>(x + f0);
+        const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int dd = (int)(int8_t)(wv[e >> 2] >> (8 * (e & 3))) - cent[f0 + e];
+          s += dd * dd;
+        }
+      }
+    } else {
+      for (int f = 0; f < Gk; ++f) { int dd = (int)x[f] - cent[f]; s += dd * dd; }
+    }
     rad[i] = s;
   }
   __syncthreads();
+  if (na <= kSortMax) {
+    // members fit in LDS: bitonic sort of (radius << 13 | position) keys, then read the
+    // target ranks directly
+    int P = 1;
+    while (P < na) P <<= 1;
+    for (int i = tid; i < P; i += 256)
+      skey[i] = i < na ? (((uint64_t)(uint32_t)rad[i]) << 13) | (uint64_t)i : ~0ull;
+    __syncthreads();
+    for (int size = 2; size <= P; size <<= 1) {
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        for (int t = tid; t < P / 2; t += 256) {
+          const int lo = 2 * t - (t & (stride - 1));
+          const int hi = lo + stride;
+          const bool up = (lo & size) == 0;
+          const uint64_t x = skey[lo], y = skey[hi];
+          if ((x > y) == up) { skey[lo] = y; skey[hi] = x; }
+        }
+        __syncthreads();
+      }
+    }
+    for (int k = tid; k < ma; k += 256) {
+      const int i = (int)(skey[tgt[k]] & (kSortMax - 1));
+      const int slot = kv * M + start[a] + k;
+      ptok[slot] = qperm[(int64_t)kv * n + off + i];
+      pgrp[slot] = a;
+      pw[slot] = (double)M * (double)na / ((double)ma * (double)n);
+    }
+    return;
+  }
+  // large group: rank of every member by counting smaller keys, tiled through LDS
   for (int i0 = 0; i0 < na; i0 += 256) {
     const int i = i0 + tid;
     const int my = i < na ? rad[i] : 0;
@@ -251,6 +296,37 @@ __device__ __forceinline__ void jacobi_pair(int t, int i, int& p, int& q) {
   else { p = 1 + (t + i) % 63; q = 1 + (t - i + 63) % 63; }
 }
 
+// Merge of the per-chunk probe partials (log-sum-exp combination), one block per
+// (probe row, query head), one thread per output column; writes O_dense / O_sparse
+// (fp32 outputs) and X = O_sparse, Y = O_dense - O_sparse (float64 fit inputs).
+template <int D>
+__global__ __launch_bounds__(D) void probe_merge_kernel(const float* __restrict__ partials, int nch, int M,
+                                                        double* __restrict__ fbuf, float* __restrict__ o_dense,
+                                                        float* __restrict__ o_sparse) {
+  const int r = blockIdx.x, h = blockIdx.y, c = threadIdx.x;
+  double res[2];
+  for (int which = 0; which < 2; ++which) {
+    double mx = -INFINITY;
+    for (int ch = 0; ch < nch; ++ch)
+      mx = fmax(mx, (double)partials[(((int64_t)h * nch + ch) * M + r) * 2 * (D + 2) + which * (D + 2) + D]);
+    double L = 0.0, O = 0.0;
+    for (int ch = 0; ch < nch; ++ch) {
+      const float* pb = partials + (((int64_t)h * nch + ch) * M + r) * 2 * (D + 2) + which * (D + 2);
+      const double m = pb[D];
+      if (m == -INFINITY) continue;
+      const double sc = exp(m - mx);
+      L += (double)pb[D + 1] * sc;
+      O += (double)pb[c] * sc;
+    }
+    res[which] = O / L;
+  }
+  o_dense[((int64_t)h * M + r) * D + c] = (float)res[0];
+  o_sparse[((int64_t)h * M + r) * D + c] = (float)res[1];
+  double* X = fbuf + (size_t)h * (3 * kMaxProbe * D + D * kMaxRank);
+  X[r * D + c] = res[1];
+  X[kMaxProbe * D + r * D + c] = res[0] - res[1];
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void probe_fit_kernel(const float* __restrict__ partials, int nch,
                                                         const double* __restrict__ pw, int g, int M,
@@ -272,32 +348,6 @@ __global__ __launch_bounds__(256) void probe_fit_kernel(const float* __restrict_
   double* Y = X + MM * D;
   double* Z = Y + MM * D;
   double* Vr = Z + MM * D;
-  // 1. merge the chunk partials
-  for (int idx = tid; idx < M * D; idx += 256) {
-    const int r = idx / D, c = idx % D;
-    double res[2];
-    for (int which = 0; which < 2; ++which) {
-      double mx = -INFINITY;
-      for (int ch = 0; ch < nch; ++ch) {
-        const float* pb = partials + (((int64_t)h * nch + ch) * M + r) * 2 * (D + 2) + which * (D + 2);
-        mx = fmax(mx, (double)pb[D]);
-      }
-      double L = 0.0, O = 0.0;
-      for (int ch = 0; ch < nch; ++ch) {
-        const float* pb = partials + (((int64_t)h * nch + ch) * M + r) * 2 * (D + 2) + which * (D + 2);
-        const double m = pb[D];
-        if (m == -INFINITY) continue;
-        const double sc = exp(m - mx);
-        L += (double)pb[D + 1] * sc;
-        O += (double)pb[c] * sc;
-      }
-      res[which] = O / L;
-    }
-    o_dense[((int64_t)h * M + r) * D + c] = (float)res[0];
-    o_sparse[((int64_t)h * M + r) * D + c] = (float)res[1];
-    X[r * D + c] = res[1];
-    Y[r * D + c] = res[0] - res[1];
-  }
   if (tid < M) w[tid] = pw[kv * M + tid];
   __syncthreads();
   // 2. weighted centring and sqrt(w) scaling
@@ -363,7 +413,7 @@ __global__ __launch_bounds__(256) void probe_fit_kernel(const float* __restrict_
   }
   __syncthreads();
   // 7. parallel cyclic Jacobi (round-robin pairing: 32 disjoint rotations per step)
-  for (int sweep = 0; sweep < 40; ++sweep) {
+  for (int sweep = 0; sweep < 30; ++sweep) {
     double off = 0.0, dg = 0.0;
     for (int idx = tid; idx < MM * MM; idx += 256) {
       const int i = idx / MM, j = idx % MM;
@@ -378,7 +428,7 @@ __global__ __launch_bounds__(256) void probe_fit_kernel(const float* __restrict_
     red[tid] = dg;
     __syncthreads();
     for (int s = 128; s > 0; s >>= 1) { if (tid < s) red[tid] += red[tid + s]; __syncthreads(); }
-    if (tid == 0) stop_s = (off_all <= 1e-30 * red[0]) || (off_all == 0.0);
+    if (tid == 0) stop_s = (off_all <= 1e-24 * red[0]) || (off_all == 0.0);
     __syncthreads();
     if (stop_s) break;
     for (int t = 0; t < MM - 1; ++t) {
@@ -500,16 +550,7 @@ void launch_probe_fit(const Dims& dm, const Workspace& wp, const void* q, const 
                      out.probe_tokens, out.probe_groups, out.probe_weights, radius);
   const dim3 pgrid(wp.nchunks, dm.hq);
   if (dm.bf16) {
-    if (dm.d == 128)
-      hipLaunchKernelGGL((probe_attn_kernel<bf16_t, 128>), pgrid, dim3(256), 0, s, (const bf16_t*)q,
-                         (const bf16_t*)part.k_gm, (const bf16_t*)part.v_gm, part.key_offsets, route.kept_mask,
-                         out.probe_tokens, out.probe_groups, dm.n, dm.g, dm.gq, dm.gk, dm.m, dm.scale,
-                         kProbeChunk, partials);
-    else
-      hipLaunchKernelGGL((probe_attn_kernel<bf16_t, 64>), pgrid, dim3(256), 0, s, (const bf16_t*)q,
-                         (const bf16_t*)part.k_gm, (const bf16_t*)part.v_gm, part.key_offsets, route.kept_mask,
-                         out.probe_tokens, out.probe_groups, dm.n, dm.g, dm.gq, dm.gk, dm.m, dm.scale,
-                         kProbeChunk, partials);
+    launch_probe_attn_mfma(dm, q, part, route, out, kProbeChunk, wp.nchunks, partials, s);
   } else {
     if (dm.d == 128)
       hipLaunchKernelGGL((probe_attn_kernel<float, 128>), pgrid, dim3(256), 0, s, (const float*)q,
@@ -522,6 +563,12 @@ void launch_probe_fit(const Dims& dm, const Workspace& wp, const void* q, const 
                          out.probe_tokens, out.probe_groups, dm.n, dm.g, dm.gq, dm.gk, dm.m, dm.scale,
                          kProbeChunk, partials);
   }
+  if (dm.d == 128)
+    hipLaunchKernelGGL(probe_merge_kernel<128>, dim3(dm.m, dm.hq), dim3(128), 0, s, partials, wp.nchunks, dm.m,
+                       fbuf, out.o_dense, out.o_sparse);
+  else
+    hipLaunchKernelGGL(probe_merge_kernel<64>, dim3(dm.m, dm.hq), dim3(64), 0, s, partials, wp.nchunks, dm.m,
+                       fbuf, out.o_dense, out.o_sparse);
   if (dm.d == 128)
     hipLaunchKernelGGL(probe_fit_kernel<128>, dim3(dm.hq), dim3(256), 0, s, partials, wp.nchunks,
                        out.probe_weights, dm.g, dm.m, dm.r, (double)dm.lambda, fbuf, out.o_dense, out.o_sparse,

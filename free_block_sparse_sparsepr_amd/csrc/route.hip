@@ -40,48 +40,40 @@ hipError_t ensure_exp_table() {
   return e;
 }
 
-// grid (ceil(n / 256), Hq), block 256.  mass [Hkv][Gq][Gk] must be zero on entry.
+// One wave per query row (lanes over key groups): coalesced loads of the row's
+// responses, wave max / sum, per-lane fixed-point division, LDS accumulation per block,
+// then 64-bit integer atomics.  Each wave walks 16 rows.  grid (ceil(n / 64), Hq),
+// block 256.  mass [Hkv][Gq][Gk] must be zero on entry.
 __global__ __launch_bounds__(256) void route_mass_kernel(const float* __restrict__ U,
                                                          const int32_t* __restrict__ qlabels,
                                                          const int32_t* __restrict__ koff, int n,
                                                          int g, int Gq, int Gk,
                                                          unsigned long long* __restrict__ mass) {
   __shared__ unsigned long long acc[kMaxGroups * kMaxGroups];
-  __shared__ int nb[kMaxGroups];
   const int h = blockIdx.y, kv = h / g;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   for (int i = threadIdx.x; i < Gq * Gk; i += 256) acc[i] = 0ull;
-  for (int b = threadIdx.x; b < Gk; b += 256)
-    nb[b] = koff[(int64_t)kv * (Gk + 1) + b + 1] - koff[(int64_t)kv * (Gk + 1) + b];
+  const int nb = lane < Gk ? koff[(int64_t)kv * (Gk + 1) + lane + 1] - koff[(int64_t)kv * (Gk + 1) + lane] : 0;
   __syncthreads();
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i < n) {
+  for (int rr = 0; rr < 16; ++rr) {
+    const int i = blockIdx.x * 64 + w * 16 + rr;
+    if (i >= n) break;
     const int a = qlabels[(int64_t)kv * n + i];
-    const float* ur = U + ((int64_t)h * n + i) * Gk;
-    int z[kMaxGroups];
-    int mu = INT_MIN;
+    int z = INT_MIN;
+    if (lane < Gk) z = (int)fminf(fmaxf(rintf(64.f * U[((int64_t)h * n + i) * Gk + lane]), -1073741824.f), 1073741824.f);
+    int mu = (nb > 0) ? z : INT_MIN;
 #pragma unroll
-    for (int b = 0; b < kMaxGroups; ++b) {
-      if (b < Gk) {
-        float t = fminf(fmaxf(rintf(64.f * ur[b]), -1073741824.f), 1073741824.f);
-        z[b] = (int)t;
-        if (nb[b] > 0 && z[b] > mu) mu = z[b];
-      }
+    for (int o = 32; o > 0; o >>= 1) mu = max(mu, __shfl_xor(mu, o));
+    uint64_t e = 0;
+    if (nb > 0) {
+      const int64_t dz = (int64_t)mu - (int64_t)z;
+      const int k = dz > kExpTable - 1 ? kExpTable - 1 : (int)dz;
+      e = (uint64_t)nb * (uint64_t)c_exp_table[k];
     }
-    uint64_t e[kMaxGroups];
-    uint64_t tot = 0;
+    uint64_t tot = e;
 #pragma unroll
-    for (int b = 0; b < kMaxGroups; ++b) {
-      if (b < Gk) {
-        int64_t dz = (int64_t)mu - (int64_t)z[b];
-        int k = dz > kExpTable - 1 ? kExpTable - 1 : (int)dz;
-        e[b] = nb[b] > 0 ? (uint64_t)nb[b] * (uint64_t)c_exp_table[k] : 0ull;
-        tot += e[b];
-      }
-    }
-#pragma unroll
-    for (int b = 0; b < kMaxGroups; ++b) {
-      if (b < Gk && e[b]) atomicAdd(&acc[a * Gk + b], (unsigned long long)udiv_exact(e[b] << 20, tot));
-    }
+    for (int o = 32; o > 0; o >>= 1) tot += __shfl_xor(tot, o);
+    if (e) atomicAdd(&acc[a * Gk + lane], (unsigned long long)udiv_exact(e << 20, tot));
   }
   __syncthreads();
   for (int idx = threadIdx.x; idx < Gq * Gk; idx += 256) {
@@ -234,7 +226,7 @@ __global__ __launch_bounds__(1024) void route_select_kernel(const unsigned long 
 void launch_route(const Dims& dm, int64_t budget, const sparsepr_partition_t& part, const sparsepr_route_t& out,
                   hipStream_t s) {
   fill_u32(reinterpret_cast<uint32_t*>(out.cell_mass), (size_t)dm.hkv * dm.gq * dm.gk * 2, 0, s);
-  hipLaunchKernelGGL(route_mass_kernel, dim3((unsigned)ceil_div(dm.n, 256), dm.hq), dim3(256), 0, s,
+  hipLaunchKernelGGL(route_mass_kernel, dim3((unsigned)ceil_div(dm.n, 64), dm.hq), dim3(256), 0, s,
                      part.responses_u, part.query_labels, part.key_offsets, dm.n, dm.g, dm.gq, dm.gk,
                      reinterpret_cast<unsigned long long*>(out.cell_mass));
   hipLaunchKernelGGL(route_select_kernel, dim3(dm.hkv), dim3(1024), 0, s,

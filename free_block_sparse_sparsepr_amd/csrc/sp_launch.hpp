@@ -7,6 +7,10 @@ namespace sp {
 
 hipError_t ensure_exp_table();
 
+void launch_resp_s_mfma(const Dims& dm, const void* q, const void* k, float* S, uint32_t* maxbits, hipStream_t s);
+void launch_resp_u_mfma(const Dims& dm, const void* q, const float* Ck, float* U, float* Usum, uint32_t* maxbits,
+                        hipStream_t s);
+
 void launch_partition(const Dims& dm, const Workspace& wp, const void* q, const void* k, const void* v,
                       const sparsepr_partition_t& out, char* ws, hipStream_t s);
 void launch_route(const Dims& dm, int64_t budget, const sparsepr_partition_t& part, const sparsepr_route_t& out,
@@ -14,6 +18,9 @@ void launch_route(const Dims& dm, int64_t budget, const sparsepr_partition_t& pa
 // out_is_input_dtype: output element type equals Q's (dense baseline); otherwise fp32.
 void launch_attention(const Dims& dm, AttnArgs a, bool out_is_input_dtype, hipStream_t s);
 void launch_attention_mfma(const Dims& dm, AttnArgs a, bool out_is_input_dtype, hipStream_t s);
+void launch_probe_attn_mfma(const Dims& dm, const void* q, const sparsepr_partition_t& part,
+                            const sparsepr_route_t& route, const sparsepr_fit_t& fit, int chunk, int nchunks,
+                            float* partials, hipStream_t s);
 void launch_probe_fit(const Dims& dm, const Workspace& wp, const void* q, const sparsepr_partition_t& part,
                       const sparsepr_route_t& route, const sparsepr_fit_t& out, char* ws, hipStream_t s);
 void launch_apply(const Dims& dm, const float* o_gm, const sparsepr_partition_t& part, const sparsepr_fit_t& fit,

@@ -141,7 +141,10 @@ def test_attend_matches_oracle(case):
             o_s, lse, _, _ = _gpu_float_stages(case, kv, j)
             ok, mx, mean = compare_float(gpu["o_gm"][kv][:, j], o_s[perm], fp32)
             assert ok, (kv, j, mx, mean)
-            np.testing.assert_allclose(gpu["lse"][kv][:, j], lse[perm], atol=1e-3 if not fp32 else 1e-4)
+            # bf16 inputs: the row sum is taken over the bf16-rounded probabilities that
+            # the second product consumes, each within 2^-9 relative, so the log-sum-exp
+            # is within ~2^-9 absolute (4e-3 leaves a 2x margin)
+            np.testing.assert_allclose(gpu["lse"][kv][:, j], lse[perm], atol=4e-3 if not fp32 else 1e-4)
 
 
 def test_probe_rows_and_fit(case):
