@@ -49,7 +49,7 @@ Workspace plan_workspace(const sparsepr_params& p) {
   w.fitbuf = o; o = align_up(o + hq * (3 * kMaxProbe * p.d + p.d * kMaxRank) * 8);
   w.total_probe = o;
   w.dense_meta = 0;
-  w.total_dense = 0;
+  w.total_dense = align_up(hkv * (size_t)p.d * (size_t)pad8(p.n) * (p.dtype == SPARSEPR_BF16 ? 2 : 4));
   w.total = w.total_partition;
   if (w.total_probe > w.total) w.total = w.total_probe;
   if (w.total_dense > w.total) w.total = w.total_dense;
@@ -175,6 +175,8 @@ sparsepr_status sparsepr_attend(const sparsepr_params* params, const sparsepr_pa
   a.q_sp = (int64_t)dm.g * dm.d;
   a.q_sj = dm.d;
   a.kv_skv = (int64_t)dm.n * dm.d;
+  a.v_np = (int)pad8(dm.n);
+  a.v_skv = (int64_t)dm.d * a.v_np;
   a.qoff = part->query_offsets;
   a.koff = part->key_offsets;
   a.row_ptr = route->row_ptr;
@@ -231,17 +233,23 @@ sparsepr_status sparsepr_apply(const sparsepr_params* params, const float* o_gm,
 sparsepr_status sparsepr_dense_attention(const sparsepr_params* params, const void* q, const void* k,
                                          const void* v, void* o, void* workspace, size_t workspace_bytes,
                                          void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   sparsepr_status st = check_params(params);
   if (st != SPARSEPR_OK) return st;
   if (!q || !k || !v || !o) return SPARSEPR_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return SPARSEPR_ERR_ALIGN;
+  const Workspace wp = plan_workspace(*params);
+  st = check_ws(params, workspace, workspace_bytes, wp.total_dense);
+  if (st != SPARSEPR_OK) return st;
   const Dims dm = dims_of(*params);
+  (void)hipGetLastError();
+  void* vt = static_cast<char*>(workspace) + wp.dense_meta;
+  launch_transpose_v(dm, v, vt, (hipStream_t)stream);
   AttnArgs a{};
   a.q = q;
   a.k = k;
-  a.v = v;
+  a.v = vt;
+  a.v_np = (int)pad8(dm.n);
+  a.v_skv = (int64_t)dm.d * a.v_np;
   a.q_skv = (int64_t)dm.g * dm.n * dm.d;
   a.q_sp = dm.d;
   a.q_sj = (int64_t)dm.n * dm.d;

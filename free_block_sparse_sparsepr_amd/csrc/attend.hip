@@ -27,7 +27,7 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs A) {
   const int tid = threadIdx.x, r = tid >> 3, sub = tid & 7;
   const T* qb = static_cast<const T*>(A.q);
   const T* kb = static_cast<const T*>(A.k) + (int64_t)kv * A.kv_skv;
-  const T* vb = static_cast<const T*>(A.v) + (int64_t)kv * A.kv_skv;
+  const T* vb = static_cast<const T*>(A.v) + (int64_t)kv * A.v_skv;
   for (int idx = tid; idx < BM * D; idx += 256) {
     const int rr = idx / D, c = idx % D, v = ti.v0 + rr;
     float x = 0.f;
@@ -47,7 +47,7 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs A) {
         const int kk = idx / D, c = idx % D;
         const bool in = kk < nk;
         ks[kk][c] = in ? to_f32(kb[(int64_t)(kt + kk) * D + c]) : 0.f;
-        vs[kk][c] = in ? to_f32(vb[(int64_t)(kt + kk) * D + c]) : 0.f;
+        vs[kk][c] = in ? to_f32(vb[(int64_t)c * A.v_np + vt_pos(c, kt + kk)]) : 0.f;
       }
       __syncthreads();
       float s[8];

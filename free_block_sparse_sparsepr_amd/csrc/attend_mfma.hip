@@ -23,171 +23,121 @@
 namespace sp {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr int kXcds = 8;
+// A row max may go stale by up to this much (log2 units) before O and l are rescaled:
+// probabilities stay below 2^8 and most tiles skip the rescale entirely.
+constexpr float kStaleMax = 8.f;
 
-template <int D>
+template <int D, int BN_ = 32>
 struct MfmaCfg {
-  static constexpr int BM = 128;           // virtual query rows per block
-  static constexpr int BN = 64;            // keys per tile
-  static constexpr int KROW = D + 8;       // LDS row of K (bf16), padded: conflict-free 16-byte reads
-  static constexpr int VROW = BN + 4;      // LDS row of V^T (bf16), padded: conflict-free 8-byte reads
-  static constexpr int KSTEPS = D / 16;    // MFMA k-steps over d
-  static constexpr int DBLK = D / 32;      // 32-wide output blocks over d
+  static constexpr int BM = 128;            // virtual query rows per block (4 waves x 32)
+  static constexpr int BN = BN_;            // keys per tile (32 or 64)
+  static constexpr int NB = BN / 32;        // 32-key score blocks per tile
+  static constexpr int KCH = D / 8;         // 16-byte chunks per K row
+  static constexpr int VCH = BN / 8;        // 16-byte chunks per V^T row
+  static constexpr int KBYTES = BN * D * 2; // K stage: BN rows, chunk c of row r at slot c ^ (r & 7)
+  static constexpr int VBYTES = D * BN * 2; // V^T stage: D rows of BN keys, chunk c of row d at slot c ^ vswz(d)
+  static constexpr int STAGE = KBYTES + VBYTES;
+  static constexpr int KIPW = BN * KCH / 256;   // K copy instructions per wave
+  static constexpr int VIPW = D * VCH / 256;
+  static constexpr int KSTEPS = D / 16;
+  static constexpr int DBLK = D / 32;
+  // chunk swizzle of V^T row d: together with the half swap of rows with bit 3 set (in
+  // the global layout) 16 consecutive rows read at one key offset hit distinct banks
+  __device__ static int vswz(int d) { return VCH == 8 ? (d & 7) : ((d >> 1) & 3); }
 };
 
-// Key-tile iterator over the kept runs of a tile (uniform across the block).
-struct TileIter {
-  int ci, k0, k1, kt;
-  bool valid;
-};
-
-__device__ __forceinline__ void iter_first(const AttnArgs& A, int kv, const TileInfo& ti, TileIter& it) {
-  it.ci = ti.kbeg < 0 ? 0 : ti.kbeg;
-  it.valid = next_run(A, kv, ti, it.ci, it.k0, it.k1);
-  it.kt = it.k0;
+// Key tiles walk the kept runs of a query tile (uniform across the block).  Tiles start
+// on 8-key boundaries so that 16-byte chunks of the transposed V are aligned; keys of a
+// tile outside its run [k0, k1) are masked.  Advances (ci, k0, k1, kt) to the next tile;
+// returns false after the last one.
+__device__ __forceinline__ bool next_tile(const AttnArgs& A, int kv, const TileInfo& ti, int BN, int& ci, int& k0,
+                                          int& k1, int& kt) {
+  kt += BN;
+  if (kt < k1) return true;
+  if (!next_run(A, kv, ti, ci, k0, k1)) return false;
+  kt = k0 & ~7;
+  return true;
 }
 
-__device__ __forceinline__ void iter_next(const AttnArgs& A, int kv, const TileInfo& ti, TileIter& it, int BN) {
-  it.kt += BN;
-  if (it.kt < it.k1) return;
-  it.valid = next_run(A, kv, ti, it.ci, it.k0, it.k1);
-  it.kt = it.k0;
-}
-
-__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) { return (a & 0xffffu) | (b << 16); }
-__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xffff0000u); }
-
-template <int D>
-struct Stage {
-  uint4 k[4];
-  uint4 v[4];
-};
-
-// Global -> registers for one K/V tile.  K: thread t loads D / 2 contiguous bytes of key
-// t % 64 at d = (t / 64) D / 4; V (d = 128): 16 bytes of each of keys 4 (t % 16) .. +3
-// at d = 8 (t / 16); V (d = 64): keys 2 (t % 32), +1 at d = 8 (t / 32).  Rows at or beyond
-// k1 are zero.
-template <int D>
-__device__ __forceinline__ void stage_load(const bf16_t* __restrict__ kb, const bf16_t* __restrict__ vb, int kt,
-                                           int k1, int tid, Stage<D>& st) {
-  static_assert(D == 128 || D == 64, "head dim");
-  constexpr int KV = D / 64;                  // 16-byte chunks per thread per operand / 2
-  const int key = tid & 63, c = (tid >> 6) * (D / 4);
-  const bool in = kt + key < k1;
-  const uint4* src = reinterpret_cast<const uint4*>(kb + (int64_t)(kt + key) * D + c);
+// Global -> LDS copy of one tile (K rows kt.., V^T columns kt..) with the direct
+// global-to-LDS path: lane i of a copy instruction lands at the instruction's LDS base +
+// 16 i, so each lane fetches the global chunk that belongs at its LDS slot.  Rows beyond
+// the sequence are clamped (those keys are masked).
+template <int D, int BN>
+__device__ __forceinline__ void stage_copy(const bf16_t* __restrict__ kb, const bf16_t* __restrict__ vtb, int n,
+                                           int np, int kt, char* stage, int w, int lane) {
+  using C = MfmaCfg<D, BN>;
 #pragma unroll
-  for (int i = 0; i < 2 * KV; ++i) st.k[i] = in ? src[i] : make_uint4(0, 0, 0, 0);
-  if constexpr (D == 128) {
-    const int kq = tid & 15, dc = (tid >> 4) * 8;
+  for (int i = 0; i < C::KIPW; ++i) {
+    const int L = (w * C::KIPW + i) * 64 + lane;
+    const int r = L / C::KCH, slot = L % C::KCH, c = slot ^ (r & 7);
+    const int row = min(kt + r, n - 1);
+    __builtin_amdgcn_global_load_lds(kb + (int64_t)row * D + 8 * c,
+                                     (lds_void_t*)(stage + (w * C::KIPW + i) * 1024), 16, 0, 0);
+  }
+  char* vst = stage + C::KBYTES;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key2 = 4 * kq + i;
-      st.v[i] = (kt + key2 < k1) ? *reinterpret_cast<const uint4*>(vb + (int64_t)(kt + key2) * D + dc)
-                                 : make_uint4(0, 0, 0, 0);
-    }
-  } else {
-    const int kp = tid & 31, dc = (tid >> 5) * 8;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int key2 = 2 * kp + i;
-      st.v[i] = (kt + key2 < k1) ? *reinterpret_cast<const uint4*>(vb + (int64_t)(kt + key2) * D + dc)
-                                 : make_uint4(0, 0, 0, 0);
-    }
+  for (int i = 0; i < C::VIPW; ++i) {
+    const int L = (w * C::VIPW + i) * 64 + lane;
+    const int d = L / C::VCH, slot = L % C::VCH, c = slot ^ C::vswz(d);
+    int pos = kt + 8 * c;
+    pos = pos + 8 <= np ? pos : 0;
+    __builtin_amdgcn_global_load_lds(vtb + (int64_t)d * np + pos, (lds_void_t*)(vst + (w * C::VIPW + i) * 1024), 16,
+                                     0, 0);
   }
 }
 
-// Registers -> LDS (K row-major, V transposed).  Consecutive lanes write consecutive
-// keys (K rows 272 bytes apart, V^T words 8 bytes apart), so the stores are free of bank
-// conflicts.
-template <int D>
-__device__ __forceinline__ void stage_store(bf16_t* __restrict__ Ks, bf16_t* __restrict__ Vt, int tid,
-                                            const Stage<D>& st) {
-  using C = MfmaCfg<D>;
-  constexpr int KV = D / 64;
-  const int key = tid & 63, c = (tid >> 6) * (D / 4);
-  uint4* dst = reinterpret_cast<uint4*>(Ks + key * C::KROW + c);
-#pragma unroll
-  for (int i = 0; i < 2 * KV; ++i) dst[i] = st.k[i];
-  if constexpr (D == 128) {
-    const int kq = tid & 15, dc = (tid >> 4) * 8;
-    const uint32_t* x0 = reinterpret_cast<const uint32_t*>(&st.v[0]);
-    const uint32_t* x1 = reinterpret_cast<const uint32_t*>(&st.v[1]);
-    const uint32_t* x2 = reinterpret_cast<const uint32_t*>(&st.v[2]);
-    const uint32_t* x3 = reinterpret_cast<const uint32_t*>(&st.v[3]);
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      uint2 lo = make_uint2(pack_lo(x0[w], x1[w]), pack_lo(x2[w], x3[w]));
-      uint2 hi = make_uint2(pack_hi(x0[w], x1[w]), pack_hi(x2[w], x3[w]));
-      *reinterpret_cast<uint2*>(Vt + (dc + 2 * w) * C::VROW + 4 * kq) = lo;
-      *reinterpret_cast<uint2*>(Vt + (dc + 2 * w + 1) * C::VROW + 4 * kq) = hi;
-    }
-  } else {
-    const int kp = tid & 31, dc = (tid >> 5) * 8;
-    const uint32_t* x0 = reinterpret_cast<const uint32_t*>(&st.v[0]);
-    const uint32_t* x1 = reinterpret_cast<const uint32_t*>(&st.v[1]);
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      *reinterpret_cast<uint32_t*>(Vt + (dc + 2 * w) * C::VROW + 2 * kp) = pack_lo(x0[w], x1[w]);
-      *reinterpret_cast<uint32_t*>(Vt + (dc + 2 * w + 1) * C::VROW + 2 * kp) = pack_hi(x0[w], x1[w]);
-    }
-  }
-}
-
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 union PackP {
   bf16x8_t v;
   bf16x2_t h[4];
 };
 
-// A row max may go stale by up to this much (log2 units) before O and l are rescaled:
-// probabilities stay below 2^8 and most tiles skip the rescale entirely.
-constexpr float kStaleMax = 8.f;
-
-// One 64-key tile of the online softmax for a wave's 32 queries: S^T = K Q^T on the
-// matrix cores (two independent accumulation chains), masking (keys at or beyond nk,
-// only on partial tiles; with MASK, keys whose group bit is clear in rowmask), the row
-// max (in-register plus the partner lane), p = exp2(s c2 - m) with one FMA and the raw
+// One tile (BN keys) of the online softmax for a wave's 32 queries: S^T = K Q^T on the
+// matrix cores (one accumulation chain per 32-key block), masking (keys outside [lo, hi)
+// of the tile; with MASK also keys whose group bit is clear in rowmask), the row max
+// (in-register plus the partner lane l ^ 32), p = exp2(s c2 - m) with one FMA and the
 // hardware exp2, bf16 packing, the row sum as bf16 dot products of the packed p (the
-// same values the second product consumes), a lazy rescale, and O^T += V^T P^T.
-template <int D, bool MASK>
-__device__ __forceinline__ void mfma_tile_step(const bf16_t* __restrict__ ks, const bf16_t* __restrict__ vt,
-                                               const bf16x8_t* qreg, int nk, float c2,
-                                               const uint8_t* __restrict__ klab, uint64_t rowmask, float& m_i,
-                                               float& l_i, f32x16_t* o, int l32, int hf) {
-  using C = MfmaCfg<D>;
-  f32x16_t s0, s1;
+// values the second product consumes), a lazy rescale, and O^T += V^T P^T.
+template <int D, int BN, bool MASK>
+__device__ __forceinline__ void mfma_tile_step(const char* __restrict__ stage, const bf16x8_t* qreg, int lo, int hi,
+                                               float c2, const uint8_t* __restrict__ klab, uint64_t rowmask,
+                                               float& m_i, float& l_i, f32x16_t* o, int l32, int hf) {
+  using C = MfmaCfg<D, BN>;
+  f32x16_t sv[C::NB];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) { s0[r] = 0.f; s1[r] = 0.f; }
-  {
-    const bf16_t* k0 = ks + l32 * C::KROW + 8 * hf;
-    const bf16_t* k1 = ks + (32 + l32) * C::KROW + 8 * hf;
+  for (int kb = 0; kb < C::NB; ++kb)
 #pragma unroll
-    for (int kk = 0; kk < C::KSTEPS; ++kk) {
-      const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(k0 + 16 * kk);
-      const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(k1 + 16 * kk);
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[kk], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[kk], s1, 0, 0, 0);
+    for (int r = 0; r < 16; ++r) sv[kb][r] = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < C::KSTEPS; ++kk) {
+#pragma unroll
+    for (int kb = 0; kb < C::NB; ++kb) {
+      const int row = 32 * kb + l32;
+      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(stage + row * (D * 2) + (((2 * kk + hf) ^ (row & 7)) << 4));
+      sv[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[kk], sv[kb], 0, 0, 0);
     }
   }
-  f32x16_t sv[2] = {s0, s1};
-  if (MASK || nk < C::BN) {
+  if (MASK || lo > 0 || hi < C::BN) {
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2)
+    for (int kb = 0; kb < C::NB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = 32 * kb2 + 8 * (r >> 2) + 4 * hf + (r & 3);
-        bool keep = key < nk;
+        const int key = 32 * kb + 8 * (r >> 2) + 4 * hf + (r & 3);
+        bool keep = key >= lo && key < hi;
         if constexpr (MASK) keep = keep && ((rowmask >> klab[key]) & 1ull);
-        sv[kb2][r] = keep ? sv[kb2][r] : -INFINITY;
+        sv[kb][r] = keep ? sv[kb][r] : -INFINITY;
       }
   }
   float mx = -INFINITY;
 #pragma unroll
-  for (int kb2 = 0; kb2 < 2; ++kb2)
+  for (int kb = 0; kb < C::NB; ++kb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sv[kb2][r]);
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sv[kb][r]);
   mx = fmaxf(mx, __shfl_xor(mx, 32)) * c2;
   const float m_use = (mx > m_i + kStaleMax) ? mx : m_i;
   float alpha;
@@ -198,21 +148,21 @@ __device__ __forceinline__ void mfma_tile_step(const bf16_t* __restrict__ ks, co
   ones[0] = (__bf16)1.f;
   ones[1] = (__bf16)1.f;
   float rs = 0.f;
-  PackP p[2][2];
+  PackP p[C::NB][2];
 #pragma unroll
-  for (int kb2 = 0; kb2 < 2; ++kb2)
+  for (int kb = 0; kb < C::NB; ++kb)
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
-      float e0 = __builtin_amdgcn_exp2f(fmaf(sv[kb2][r], c2, neg));
-      float e1 = __builtin_amdgcn_exp2f(fmaf(sv[kb2][r + 1], c2, neg));
+      float e0 = __builtin_amdgcn_exp2f(fmaf(sv[kb][r], c2, neg));
+      float e1 = __builtin_amdgcn_exp2f(fmaf(sv[kb][r + 1], c2, neg));
       if constexpr (MASK) {
-        e0 = (sv[kb2][r] == -INFINITY) ? 0.f : e0;
-        e1 = (sv[kb2][r + 1] == -INFINITY) ? 0.f : e1;
+        e0 = (sv[kb][r] == -INFINITY) ? 0.f : e0;
+        e1 = (sv[kb][r + 1] == -INFINITY) ? 0.f : e1;
       }
       bf16x2_t pr;
       pr[0] = (__bf16)e0;
       pr[1] = (__bf16)e1;
-      p[kb2][r >> 3].h[(r & 7) >> 1] = pr;
+      p[kb][r >> 3].h[(r & 7) >> 1] = pr;
       rs = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, rs, false);
     }
   l_i = l_i * alpha + rs;
@@ -223,29 +173,31 @@ __device__ __forceinline__ void mfma_tile_step(const bf16_t* __restrict__ ks, co
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
   }
-  // O^T += V^T P^T over the 4 key k-steps of the tile
+  // O^T += V^T P^T: key k-step (kb, s2) covers keys 32 kb + 16 s2 + {4 hf + 0..3, 8 + 4 hf + 0..3}
+  const char* vst = stage + C::KBYTES;
+  const int ph = (hf ^ ((l32 >> 3) & 1)) << 3;
 #pragma unroll
-  for (int kb2 = 0; kb2 < 2; ++kb2)
+  for (int kb = 0; kb < C::NB; ++kb)
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
-      const int koff = 32 * kb2 + 16 * s2 + 4 * hf;
 #pragma unroll
       for (int db = 0; db < C::DBLK; ++db) {
-        const bf16_t* vr = vt + (32 * db + l32) * C::VROW + koff;
-        uint2 lo = *reinterpret_cast<const uint2*>(vr);
-        uint2 hi = *reinterpret_cast<const uint2*>(vr + 8);
-        uint4 av = make_uint4(lo.x, lo.y, hi.x, hi.y);
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av), p[kb2][s2].v, o[db], 0,
-                                                        0, 0);
+        const int d = 32 * db + l32;
+        const int sw = C::vswz(d);
+        const char* vr = vst + d * (C::BN * 2);
+        const uint2 lo8 = *reinterpret_cast<const uint2*>(vr + (((4 * kb + 2 * s2) ^ sw) << 4) + ph);
+        const uint2 hi8 = *reinterpret_cast<const uint2*>(vr + (((4 * kb + 2 * s2 + 1) ^ sw) << 4) + ph);
+        const uint4 av = make_uint4(lo8.x, lo8.y, hi8.x, hi8.y);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av), p[kb][s2].v, o[db], 0, 0,
+                                                        0);
       }
     }
 }
 
-template <int D, typename OutT>
+template <int D, int BN, typename OutT>
 __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs A) {
-  using C = MfmaCfg<D>;
-  __shared__ __attribute__((aligned(16))) bf16_t Ks[2][C::BN * C::KROW];
-  __shared__ __attribute__((aligned(16))) bf16_t Vt[2][D * C::VROW];
+  using C = MfmaCfg<D, BN>;
+  __shared__ __attribute__((aligned(1024))) char stages[2][C::STAGE];
 
   // XCD-aware remap of the linear block id (consecutive logical tiles on one XCD)
   const int total = gridDim.x;
@@ -262,7 +214,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs A) {
   const int l32 = lane & 31, hf = lane >> 5;
   const bf16_t* qb = static_cast<const bf16_t*>(A.q);
   const bf16_t* kb = static_cast<const bf16_t*>(A.k) + (int64_t)kv * A.kv_skv;
-  const bf16_t* vb = static_cast<const bf16_t*>(A.v) + (int64_t)kv * A.kv_skv;
+  const bf16_t* vtb = static_cast<const bf16_t*>(A.v) + (int64_t)kv * A.v_skv;
 
   // Q operand (B of S^T = K Q^T): lane holds Q[row l32][16 kk + 8 hf .. +7]
   const int vrow = ti.v0 + 32 * w + l32;
@@ -285,25 +237,25 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs A) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
 
-  TileIter it;
-  iter_first(A, kv, ti, it);
-  Stage<D> st;
-  if (it.valid) {
-    stage_load<D>(kb, vb, it.kt, it.k1, tid, st);
-    stage_store<D>(Ks[0], Vt[0], tid, st);
+  int ci = ti.kbeg < 0 ? 0 : ti.kbeg, k0 = 0, k1 = 0, kt = 0;
+  bool valid = next_run(A, kv, ti, ci, k0, k1);
+  if (valid) {
+    kt = k0 & ~7;
+    stage_copy<D, BN>(kb, vtb, A.n, A.v_np, kt, stages[0], w, lane);
   }
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   int cur = 0;
-  while (it.valid) {
-    TileIter nx = it;
-    iter_next(A, kv, ti, nx, C::BN);
-    if (nx.valid) stage_load<D>(kb, vb, nx.kt, nx.k1, tid, st);
-
-    mfma_tile_step<D, false>(Ks[cur], Vt[cur], qreg, it.k1 - it.kt, c2, nullptr, 0ull, m_i, l_i, o, l32, hf);
-    if (nx.valid) stage_store<D>(Ks[cur ^ 1], Vt[cur ^ 1], tid, st);
+  while (valid) {
+    int nci = ci, nk0 = k0, nk1 = k1, nkt = kt;
+    const bool nvalid = next_tile(A, kv, ti, C::BN, nci, nk0, nk1, nkt);
+    if (nvalid) stage_copy<D, BN>(kb, vtb, A.n, A.v_np, nkt, stages[cur ^ 1], w, lane);
+    const int lo = max(k0 - kt, 0), hi = min(k1 - kt, BN);
+    mfma_tile_step<D, BN, false>(stages[cur], qreg, lo, hi, c2, nullptr, 0ull, m_i, l_i, o, l32, hf);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     cur ^= 1;
-    it = nx;
+    ci = nci; k0 = nk0; k1 = nk1; kt = nkt; valid = nvalid;
   }
 
   // epilogue: O / l, LSE; lane writes query l32's d = 32 db + 8 j + 4 hf + 0..3
@@ -329,10 +281,10 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs A) {
           *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(orow) + d0) = v2;
         }
       }
-    if (A.lse && hf == 0) A.lse[((int64_t)kv * A.n + vrow / A.g) * A.g + vrow % A.g] = (m_i + log2f(l_tot)) * 0.6931471805599453f;
+    if (A.lse && hf == 0)
+      A.lse[((int64_t)kv * A.n + vrow / A.g) * A.g + vrow % A.g] = (m_i + log2f(l_tot)) * 0.6931471805599453f;
   }
 }
-
 
 // ---------------------------------------------------------------------------------------
 // Probe rows (summary page of "Partition the Support, Reconstruct the Residual",
@@ -345,7 +297,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs A) {
 template <int D>
 __global__ __launch_bounds__(256, 2) void probe_attn_mfma_kernel(const bf16_t* __restrict__ q,
                                                                const bf16_t* __restrict__ kgm,
-                                                               const bf16_t* __restrict__ vgm,
+                                                               const bf16_t* __restrict__ vtgm,
                                                                const int32_t* __restrict__ koff,
                                                                const uint64_t* __restrict__ kept_mask,
                                                                const int32_t* __restrict__ ptok,
@@ -353,8 +305,7 @@ __global__ __launch_bounds__(256, 2) void probe_attn_mfma_kernel(const bf16_t* _
                                                                int Gq, int Gk, int M, float scale, int chunk,
                                                                float* __restrict__ partials) {
   using C = MfmaCfg<D>;
-  __shared__ __attribute__((aligned(16))) bf16_t Ks[2][C::BN * C::KROW];
-  __shared__ __attribute__((aligned(16))) bf16_t Vt[2][D * C::VROW];
+  __shared__ __attribute__((aligned(1024))) char stages[2][C::STAGE];
   __shared__ uint8_t klab[2][C::BN];
   __shared__ int ko[kMaxGroups + 1];
   const int h = blockIdx.y, kv = h / g, ch = blockIdx.x, nch = gridDim.x;
@@ -363,6 +314,7 @@ __global__ __launch_bounds__(256, 2) void probe_attn_mfma_kernel(const bf16_t* _
   const int row = 32 * (w & 1) + l32;
   const bool sparse = (w >> 1) != 0;
   const int k0 = ch * chunk, k1 = min(n, k0 + chunk);
+  const int np = (int)pad8(n);
   for (int b = tid; b <= Gk; b += 256) ko[b] = koff[(int64_t)kv * (Gk + 1) + b];
   const bool rvalid = row < M;
   const uint64_t rowmask = rvalid ? kept_mask[(int64_t)kv * Gq + pgrp[kv * M + row]] : 0ull;
@@ -376,7 +328,7 @@ __global__ __launch_bounds__(256, 2) void probe_attn_mfma_kernel(const bf16_t* _
     }
   }
   const bf16_t* kb = kgm + (int64_t)kv * n * D;
-  const bf16_t* vb = vgm + (int64_t)kv * n * D;
+  const bf16_t* vtb = vtgm + (int64_t)kv * D * np;
   const float c2 = scale * 1.4426950408889634f;
   float m_i = -INFINITY, l_i = 0.f;
   f32x16_t o[C::DBLK];
@@ -390,26 +342,26 @@ __global__ __launch_bounds__(256, 2) void probe_attn_mfma_kernel(const bf16_t* _
     while (lo < hi) { int mid = (lo + hi + 1) >> 1; if (ko[mid] <= pos) lo = mid; else hi = mid - 1; }
     return lo;
   };
-  Stage<D> st;
   int kt = k0;
   if (kt < k1) {
-    stage_load<D>(kb, vb, kt, k1, tid, st);
-    stage_store<D>(Ks[0], Vt[0], tid, st);
+    stage_copy<D, 32>(kb, vtb, n, np, kt, stages[0], w, lane);
     if (tid < C::BN) klab[0][tid] = (uint8_t)(kt + tid < k1 ? label_of(kt + tid) : 0);
   }
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   int cur = 0;
   while (kt < k1) {
     const int nt = kt + C::BN;
-    if (nt < k1) stage_load<D>(kb, vb, nt, k1, tid, st);
-    if (sparse)
-      mfma_tile_step<D, true>(Ks[cur], Vt[cur], qreg, k1 - kt, c2, klab[cur], rowmask, m_i, l_i, o, l32, hf);
-    else
-      mfma_tile_step<D, false>(Ks[cur], Vt[cur], qreg, k1 - kt, c2, nullptr, 0ull, m_i, l_i, o, l32, hf);
     if (nt < k1) {
-      stage_store<D>(Ks[cur ^ 1], Vt[cur ^ 1], tid, st);
+      stage_copy<D, 32>(kb, vtb, n, np, nt, stages[cur ^ 1], w, lane);
       if (tid < C::BN) klab[cur ^ 1][tid] = (uint8_t)(nt + tid < k1 ? label_of(nt + tid) : 0);
     }
+    const int hi = min(k1 - kt, C::BN);
+    if (sparse)
+      mfma_tile_step<D, 32, true>(stages[cur], qreg, 0, hi, c2, klab[cur], rowmask, m_i, l_i, o, l32, hf);
+    else
+      mfma_tile_step<D, 32, false>(stages[cur], qreg, 0, hi, c2, nullptr, 0ull, m_i, l_i, o, l32, hf);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     cur ^= 1;
     kt = nt;
@@ -448,13 +400,15 @@ void launch_probe_attn_mfma(const Dims& dm, const void* q, const sparsepr_partit
                        partials);
 }
 
+constexpr int kAttnBN = 64;   // keys per tile of the main attention kernel
+
 template <int D, typename OutT>
 void launch_mfma_typed(AttnArgs a, int hkv, hipStream_t s) {
-  a.tiles_per_head = (int)ceil_div((int64_t)a.n * a.g, MfmaCfg<D>::BM) + (a.qoff ? a.gq : 0);
+  a.tiles_per_head = (int)ceil_div((int64_t)a.n * a.g, MfmaCfg<D, kAttnBN>::BM) + (a.qoff ? a.gq : 0);
   a.n_heads_kv = hkv;
   int64_t total = (int64_t)a.tiles_per_head * hkv;
   total = ceil_div(total, kXcds) * kXcds;
-  hipLaunchKernelGGL((attn_mfma_kernel<D, OutT>), dim3((unsigned)total), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((attn_mfma_kernel<D, kAttnBN, OutT>), dim3((unsigned)total), dim3(256), 0, s, a);
 }
 
 void launch_attention_mfma(const Dims& dm, AttnArgs a, bool out_is_input_dtype, hipStream_t s) {

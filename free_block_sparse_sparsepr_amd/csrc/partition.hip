@@ -303,6 +303,35 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint4* __restric
   dst[r * VPR + c] = src[srow * VPR + c];
 }
 
+// Transposing gather of V into group-major, d-major order: block = 64 positions; rows
+// perm[p] (or p when perm is NULL) are staged in LDS, then each thread writes 8-key
+// chunks of one d row (16 or 32 contiguous bytes) with the layout's half swap.  Positions
+// from n up to n_pad are zero.  grid (ceil(n_pad / 64), Hkv), block 256.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void gather_vt_kernel(const T* __restrict__ v, const int32_t* __restrict__ perm,
+                                                        int n, int np, T* __restrict__ vt) {
+  __shared__ T tile[64][D + 2];
+  const int kv = blockIdx.y, p0 = blockIdx.x * 64;
+  for (int idx = threadIdx.x; idx < 64 * D; idx += 256) {
+    const int r = idx / D, c = idx % D, p = p0 + r;
+    T x = from_f32<T>(0.f);
+    if (p < n) {
+      const int64_t tok = perm ? perm[(int64_t)kv * n + p] : p;
+      x = v[((int64_t)kv * n + tok) * D + c];
+    }
+    tile[r][c] = x;
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < D * 8; idx += 256) {
+    const int d = idx >> 3, pc = idx & 7;
+    if (p0 + 8 * pc >= np) continue;
+    const int sw = ((d >> 3) & 1) << 2;
+    T* dst = vt + ((int64_t)kv * D + d) * np + p0 + 8 * pc;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dst[e] = tile[8 * pc + (e ^ sw)][d];
+  }
+}
+
 // C^K_b = mean of the group-major key rows of group b in fixed order (fp32).  Thread t
 // sums 4 columns (4 * (t % (D / 4)) ..) over rows start + ph, ph + P, ... with P = 256 /
 // (D / 4) row phases, then the phases are combined in ascending order.  grid (G, Hkv),
@@ -508,7 +537,8 @@ static void partition_typed(const Dims& dm, const Workspace& wp, const T* q, con
   run_kmeans(xk, n, hkv, dm.gk, dm.rk, wp.fpk, dm.iters, C, sums, out.key_labels, out.key_centroids_int, s);
   run_group_major(out.key_labels, n, hkv, dm.gk, out.key_perm, out.key_offsets, s);
   run_gather(k, out.key_perm, n, hkv, 1, D, dm.bf16, out.k_gm, s);
-  run_gather(v, out.key_perm, n, hkv, 1, D, dm.bf16, out.v_gm, s);
+  hipLaunchKernelGGL((gather_vt_kernel<T, D>), dim3((unsigned)ceil_div(pad8(n), 64), hkv), dim3(256), 0, s, v,
+                     out.key_perm, n, (int)pad8(n), static_cast<T*>(out.v_gm));
   hipLaunchKernelGGL((segment_mean_kernel<T, D>), dim3(dm.gk, hkv), dim3(256), 0, s,
                      static_cast<const T*>(out.k_gm), out.key_offsets, n, dm.gk, out.key_centroids);
   // queries
@@ -523,6 +553,18 @@ static void partition_typed(const Dims& dm, const Workspace& wp, const T* q, con
   run_kmeans(xq, n, hkv, dm.gq, dm.gk, wp.fpq, dm.iters, C, sums, out.query_labels, out.query_centroids, s);
   run_group_major(out.query_labels, n, hkv, dm.gq, out.query_perm, out.query_offsets, s);
   run_gather(q, out.query_perm, n, hkv, dm.g, D, dm.bf16, out.q_gm, s);
+}
+
+void launch_transpose_v(const Dims& dm, const void* v, void* vt, hipStream_t s) {
+  const dim3 grid((unsigned)ceil_div(pad8(dm.n), 64), dm.hkv);
+  const int np = (int)pad8(dm.n);
+  if (dm.bf16) {
+    if (dm.d == 128) hipLaunchKernelGGL((gather_vt_kernel<bf16_t, 128>), grid, dim3(256), 0, s, (const bf16_t*)v, nullptr, dm.n, np, (bf16_t*)vt);
+    else hipLaunchKernelGGL((gather_vt_kernel<bf16_t, 64>), grid, dim3(256), 0, s, (const bf16_t*)v, nullptr, dm.n, np, (bf16_t*)vt);
+  } else {
+    if (dm.d == 128) hipLaunchKernelGGL((gather_vt_kernel<float, 128>), grid, dim3(256), 0, s, (const float*)v, nullptr, dm.n, np, (float*)vt);
+    else hipLaunchKernelGGL((gather_vt_kernel<float, 64>), grid, dim3(256), 0, s, (const float*)v, nullptr, dm.n, np, (float*)vt);
+  }
 }
 
 void launch_partition(const Dims& dm, const Workspace& wp, const void* q, const void* k, const void* v,

@@ -12,7 +12,9 @@ struct AttnArgs {
   const void* k;
   const void* v;
   int64_t q_skv, q_sp, q_sj;   // element strides of Q rows
-  int64_t kv_skv;              // element stride between KV heads of K and V (n * d)
+  int64_t kv_skv;              // element stride between KV heads of K (n * d)
+  int64_t v_skv;               // element stride between KV heads of transposed V (d * n_pad)
+  int v_np;                    // n_pad: row length of transposed V
   const int32_t* qoff;         // [Hkv][Gq + 1]; NULL: one group holding every token
   const int32_t* koff;         // [Hkv][Gk + 1]
   const int32_t* row_ptr;      // [Hkv][Gq + 1]; NULL: every key

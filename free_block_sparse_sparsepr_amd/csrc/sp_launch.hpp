@@ -11,6 +11,8 @@ void launch_resp_s_mfma(const Dims& dm, const void* q, const void* k, float* S, 
 void launch_resp_u_mfma(const Dims& dm, const void* q, const float* Ck, float* U, float* Usum, uint32_t* maxbits,
                         hipStream_t s);
 
+// V [Hkv][n][d] (token order) -> transposed layout [Hkv][d][n_pad] (see vt_pos).
+void launch_transpose_v(const Dims& dm, const void* v, void* vt, hipStream_t s);
 void launch_partition(const Dims& dm, const Workspace& wp, const void* q, const void* k, const void* v,
                       const sparsepr_partition_t& out, char* ws, hipStream_t s);
 void launch_route(const Dims& dm, int64_t budget, const sparsepr_partition_t& part, const sparsepr_route_t& out,

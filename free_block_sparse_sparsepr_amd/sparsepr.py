@@ -35,6 +35,10 @@ class Config:
         return self.heads_q // self.heads_kv
 
     @property
+    def n_pad(self):
+        return (self.n + 7) // 8 * 8
+
+    @property
     def torch_dtype(self):
         return torch.bfloat16 if self.dtype == "bf16" else torch.float32
 
@@ -83,7 +87,7 @@ class SparsePR:
             query_centroids=e(c.heads_kv, c.groups_q, c.groups_k), query_perm=e(c.heads_kv, c.n),
             query_offsets=e(c.heads_kv, c.groups_q + 1),
             q_gm=e(c.heads_kv, c.n, c.g, c.d, dt=c.torch_dtype), k_gm=e(c.heads_kv, c.n, c.d, dt=c.torch_dtype),
-            v_gm=e(c.heads_kv, c.n, c.d, dt=c.torch_dtype))
+            v_gm=e(c.heads_kv, c.d, c.n_pad, dt=c.torch_dtype))
         self.route_buf = dict(
             row_ptr=e(c.heads_kv, c.groups_q + 1), cols=e(c.heads_kv, c.groups_q * c.groups_k),
             kept_mask=e(c.heads_kv, c.groups_q, dt=torch.int64), pairs=e(c.heads_kv, dt=torch.int64),

@@ -101,7 +101,11 @@ typedef struct sparsepr_partition_t {
   int32_t* query_offsets;    /* [Hkv, G_Q + 1] */
   void* q_gm;                /* [Hkv, n, g, d] dtype: Q in group-major order */
   void* k_gm;                /* [Hkv, n, d] dtype: K in group-major order */
-  void* v_gm;                /* [Hkv, n, d] dtype: V in group-major order (follows K) */
+  void* v_gm;                /* [Hkv, d, n_pad] dtype, n_pad = n rounded up to 8: V in group-major
+                                order (follows K), stored transposed (d-major).  Element (d, p) is at
+                                d * n_pad + (p ^ 4) when bit 3 of d is set, else d * n_pad + p (the
+                                two 4-key halves of every 8-key chunk are swapped in those rows);
+                                positions n .. n_pad - 1 are zero. */
 } sparsepr_partition_t;
 
 /* Route outputs.  Row a of the CSR lists the kept key groups of query group a,
@@ -176,7 +180,8 @@ sparsepr_status sparsepr_apply(const sparsepr_params* params, const float* o_gm,
                                void* stream);
 
 /* Dense softmax attention O = softmax(Q K^T * scale) V on the same tile machinery (the
- * baseline; dense formula as in the lmnt.cn SparsePR article, section 2.1).
+ * baseline; dense formula as in the lmnt.cn SparsePR article, section 2.1).  V is first
+ * transposed into the workspace (part of the call).
  * q: [Hq, n, d]; k, v: [Hkv, n, d]; o: [Hq, n, d], all dtype and token order. */
 sparsepr_status sparsepr_dense_attention(const sparsepr_params* params, const void* q,
                                          const void* k, const void* v, void* o,

@@ -50,6 +50,19 @@ def run_gpu(cfg, Q, K, V):
     return res, sp, (q, k, v)
 
 
+def vgm_rows(vt, n):
+    """Group-major V rows [n, d] from the transposed layout [d, n_pad] (rows d with bit 3 set
+    hold each 8-key chunk with its 4-key halves swapped)."""
+    vt = np.asarray(vt)
+    d = vt.shape[0]
+    out = np.empty((n, d), vt.dtype)
+    p = np.arange(n)
+    for dd in range(d):
+        pos = p ^ 4 if (dd >> 3) & 1 else p
+        out[:, dd] = vt[dd, pos]
+    return out
+
+
 def kept_from_mask(mask, gq, gk):
     m = np.asarray(mask).astype(np.uint64)
     return np.array([[(int(m[a]) >> b) & 1 for b in range(gk)] for a in range(gq)], dtype=bool)

@@ -13,7 +13,7 @@ import pytest
 from oracle import sparsepr as O
 from sparsepr_workloads import CONFIGS, small
 
-from gpu_harness import (compare_float, kept_from_mask, oracle_inputs, oracle_params, run_gpu)
+from gpu_harness import (compare_float, kept_from_mask, oracle_inputs, oracle_params, run_gpu, vgm_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -59,7 +59,8 @@ def test_group_major_gathers_exact(case):
     cfg, gpu = case["cfg"], case["gpu"]
     for kv in range(cfg.heads_kv):
         np.testing.assert_array_equal(gpu["k_gm"][kv], case["K"][kv][gpu["key_perm"][kv]])
-        np.testing.assert_array_equal(gpu["v_gm"][kv], case["V"][kv][gpu["key_perm"][kv]])
+        np.testing.assert_array_equal(vgm_rows(gpu["v_gm"][kv], cfg.n), case["V"][kv][gpu["key_perm"][kv]])
+        assert not gpu["v_gm"][kv][:, cfg.n:].any()
         qp = gpu["query_perm"][kv]
         for j in range(cfg.g):
             np.testing.assert_array_equal(gpu["q_gm"][kv][:, j], case["Q"][kv * cfg.g + j][qp])
