@@ -1,8 +1,10 @@
 """Benchmark of the SparsePR attention call on one MI355X.
 
-One step = one whole SparsePR call (partition, route, attend, probe_fit, apply: every
-stage the summary page of "Partition the Support, Reconstruct the Residual" counts in its
-timed latency) over the HunyuanVideo-shaped 720p workload: N = 118,800 tokens
+One step = one whole SparsePR call in the fused order (partition, route, probe_fit,
+attend_apply), which covers every stage the summary page of "Partition the Support,
+Reconstruct the Residual" counts in its timed latency (partition, route, permutation,
+sparse kernel, probes, fit, write-back); --unfused times partition, route, attend,
+probe_fit, apply.  Workload: the HunyuanVideo-shaped 720p call, N = 118,800 tokens
 (T=33, H=45, W=80), 24 heads, d = 128, bf16, target rho_exec = 22 %, seeded synthetic
 inputs resident in HBM before the timed region.
 
@@ -11,7 +13,7 @@ Prints one JSON line: calls/s (value), the sparse kernel's effective TFLOP/s on 
 the same-GPU dense attention, a per-stage breakdown, and the CPU oracle timed on a
 bounded sample (cpu_baseline).
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3] [--no-dense] [--no-cpu]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3] [--no-dense] [--no-cpu] [--unfused]
 """
 import argparse
 import json
@@ -25,7 +27,8 @@ sys.path.insert(0, ROOT)
 METRIC = "sparse attention calls/sec + effective TFLOPS (% bf16 MFMA peak) vs dense attn"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3
-STAGES = ["partition", "route", "attend", "probe_fit", "apply"]
+STAGES_FUSED = ["partition", "route", "probe_fit", "attend_apply"]
+STAGES_UNFUSED = ["partition", "route", "attend", "probe_fit", "apply"]
 
 
 def log(*a):
@@ -66,6 +69,8 @@ def main():
     ap.add_argument("--dense-steps", type=int, default=2)
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--unfused", action="store_true",
+                    help="time the unfused order (attend -> probe_fit -> apply) instead of the fused one")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for {args.gpus}); the SparsePR call "
@@ -91,9 +96,15 @@ def main():
     out = torch.empty((cfg.heads_q, cfg.n, cfg.d), dtype=tdt, device=dev)
     stream = torch.cuda.current_stream()
 
+    if args.unfused:
+        stages = STAGES_UNFUSED
+        fns = [lambda: sp.partition(q, k, v), sp.route, sp.attend, lambda: sp.probe_fit(q), lambda: sp.apply(out)]
+    else:
+        stages = STAGES_FUSED
+        fns = [lambda: sp.partition(q, k, v), sp.route, lambda: sp.probe_fit(q), lambda: sp.attend_apply(out)]
+    attn_stage = "attend" if args.unfused else "attend_apply"
+
     def step(ev=None):
-        fns = [lambda: sp.partition(q, k, v), sp.route, sp.attend, lambda: sp.probe_fit(q),
-               lambda: sp.apply(out)]
         for i, fn in enumerate(fns):
             if ev is not None:
                 ev[i][0].record(stream)
@@ -106,7 +117,7 @@ def main():
         log(f"[bench] warmup {i + 1}/{args.warmup}")
     torch.cuda.synchronize()
     events = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-               for _ in STAGES] for _ in range(args.steps)]
+               for _ in stages] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
@@ -115,7 +126,7 @@ def main():
     wall = time.perf_counter() - t0
     log(f"[bench] timed {args.steps} calls in {wall:.3f} s")
     stage_ms = {name: float(np.mean([events[s][i][0].elapsed_time(events[s][i][1]) for s in range(args.steps)]))
-                for i, name in enumerate(STAGES)}
+                for i, name in enumerate(stages)}
     ms_per_step = wall * 1e3 / args.steps
 
     pairs_kv = sp.route_buf["pairs"].cpu().numpy().astype(np.int64)
@@ -123,7 +134,7 @@ def main():
     executed = routed + cfg.heads_q * cfg.n_probe * cfg.n
     flop_attend = 4.0 * cfg.d * routed
     flop_call = 4.0 * cfg.d * executed
-    attend_tflops = flop_attend / (stage_ms["attend"] * 1e-3) / 1e12
+    attend_tflops = flop_attend / (stage_ms[attn_stage] * 1e-3) / 1e12
     call_tflops = flop_call / (ms_per_step * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_FP32_TFLOPS
     rho_route = float(pairs_kv.mean()) / cfg.n ** 2
@@ -157,7 +168,10 @@ def main():
                    "heads_kv": cfg.heads_kv, "d": cfg.d, "rho_exec_target": cfg.rho_exec,
                    "groups_q": cfg.groups_q, "groups_k": cfg.groups_k, "n_probe": cfg.n_probe,
                    "rank": cfg.rank, "r_k": cfg.r_k, "r_q": cfg.r_q, "lambda": cfg.lam},
-        "roofline": {"bound": "mfma", "kernel": "sparse attention (sparsepr_attend)",
+        "call_order": "unfused" if args.unfused else "fused",
+        "roofline": {"bound": "mfma", "kernel": "sparse attention (" + ("sparsepr_attend" if args.unfused else
+                     "sparsepr_attend_apply: attention with the fused write-back epilogue, plus the 64-row probe "
+                     "write-back kernel") + ")",
                      "achieved": attend_tflops, "peak": peak, "unit": "TFLOP/s", "frac": attend_tflops / peak,
                      "traffic": None},
         "effective_tflops_call": call_tflops, "effective_frac_call": call_tflops / peak,

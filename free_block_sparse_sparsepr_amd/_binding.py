@@ -40,7 +40,8 @@ RouteT = _ptr_struct("RouteT", ROUTE_FIELDS)
 FitT = _ptr_struct("FitT", FIT_FIELDS)
 
 EXPORTS = ["sparsepr_workspace_size", "sparsepr_partition", "sparsepr_route", "sparsepr_attend",
-           "sparsepr_probe_fit", "sparsepr_apply", "sparsepr_dense_attention", "sparsepr_status_string"]
+           "sparsepr_probe_fit", "sparsepr_apply", "sparsepr_attend_apply", "sparsepr_dense_attention",
+           "sparsepr_status_string"]
 
 _lib = None
 
@@ -65,6 +66,7 @@ def load():
         "sparsepr_attend": [P(Params), P(PartitionT), P(RouteT), vp, vp, vp, sz, vp],
         "sparsepr_probe_fit": [P(Params), vp, P(PartitionT), P(RouteT), P(FitT), vp, sz, vp],
         "sparsepr_apply": [P(Params), vp, P(PartitionT), P(FitT), vp, vp],
+        "sparsepr_attend_apply": [P(Params), P(PartitionT), P(RouteT), P(FitT), vp, vp, sz, vp],
         "sparsepr_dense_attention": [P(Params), vp, vp, vp, vp, vp, sz, vp],
     }
     for name, args in sigs.items():

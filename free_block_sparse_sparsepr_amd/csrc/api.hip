@@ -50,7 +50,13 @@ Workspace plan_workspace(const sparsepr_params& p) {
   w.total_probe = o;
   w.dense_meta = 0;
   w.total_dense = align_up(hkv * (size_t)p.d * (size_t)pad8(p.n) * (p.dtype == SPARSEPR_BF16 ? 2 : 4));
+  // the fused write-back runs in the attention epilogue for bf16 with one query head per KV
+  // head; otherwise attend writes O_gm into the workspace and apply follows
+  w.fused_ogm = 0;
+  w.total_fused = (p.dtype == SPARSEPR_BF16 && p.heads_q == p.heads_kv)
+                      ? 0 : align_up(hkv * n * (size_t)(p.heads_q / p.heads_kv) * p.d * 4);
   w.total = w.total_partition;
+  if (w.total_fused > w.total) w.total = w.total_fused;
   if (w.total_probe > w.total) w.total = w.total_probe;
   if (w.total_dense > w.total) w.total = w.total_dense;
   return w;
@@ -98,6 +104,33 @@ static int64_t route_budget(const sparsepr_params& p) {
   const int64_t ppm = (int64_t)std::floor((double)p.rho_exec * 1e6 + 0.5);
   const int64_t n = p.n;
   return (ppm * n * n) / 1000000 - (int64_t)p.n_probe * n;
+}
+
+// Attention arguments of the block-sparse path (group-major Q, K, transposed V, CSR).
+static AttnArgs sparse_args(const Dims& dm, const sparsepr_partition_t& part, const sparsepr_route_t& route) {
+  AttnArgs a{};
+  a.q = part.q_gm;
+  a.k = part.k_gm;
+  a.v = part.v_gm;
+  a.q_skv = (int64_t)dm.n * dm.g * dm.d;
+  a.q_sp = (int64_t)dm.g * dm.d;
+  a.q_sj = dm.d;
+  a.kv_skv = (int64_t)dm.n * dm.d;
+  a.v_np = (int)pad8(dm.n);
+  a.v_skv = (int64_t)dm.d * a.v_np;
+  a.qoff = part.query_offsets;
+  a.koff = part.key_offsets;
+  a.row_ptr = route.row_ptr;
+  a.cols = route.cols;
+  a.o_skv = a.q_skv;
+  a.o_sp = a.q_sp;
+  a.o_sj = a.q_sj;
+  a.n = dm.n;
+  a.g = dm.g;
+  a.gq = dm.gq;
+  a.gk = dm.gk;
+  a.scale = dm.scale;
+  return a;
 }
 
 }  // namespace sp
@@ -167,32 +200,48 @@ sparsepr_status sparsepr_attend(const sparsepr_params* params, const sparsepr_pa
   if (!aligned16(part->q_gm) || !aligned16(part->k_gm) || !aligned16(part->v_gm) || !aligned16(o_gm))
     return SPARSEPR_ERR_ALIGN;
   const Dims dm = dims_of(*params);
-  AttnArgs a{};
-  a.q = part->q_gm;
-  a.k = part->k_gm;
-  a.v = part->v_gm;
-  a.q_skv = (int64_t)dm.n * dm.g * dm.d;
-  a.q_sp = (int64_t)dm.g * dm.d;
-  a.q_sj = dm.d;
-  a.kv_skv = (int64_t)dm.n * dm.d;
-  a.v_np = (int)pad8(dm.n);
-  a.v_skv = (int64_t)dm.d * a.v_np;
-  a.qoff = part->query_offsets;
-  a.koff = part->key_offsets;
-  a.row_ptr = route->row_ptr;
-  a.cols = route->cols;
+  AttnArgs a = sparse_args(dm, *part, *route);
   a.o = o_gm;
-  a.o_skv = a.q_skv;
-  a.o_sp = a.q_sp;
-  a.o_sj = a.q_sj;
   a.lse = lse;
-  a.n = dm.n;
-  a.g = dm.g;
-  a.gq = dm.gq;
-  a.gk = dm.gk;
-  a.scale = dm.scale;
   (void)hipGetLastError();
   launch_attention(dm, a, false, (hipStream_t)stream);
+  return hip_status();
+}
+
+sparsepr_status sparsepr_attend_apply(const sparsepr_params* params, const sparsepr_partition_t* part,
+                                      const sparsepr_route_t* route, const sparsepr_fit_t* fit, void* o,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  sparsepr_status st = check_params(params);
+  if (st != SPARSEPR_OK) return st;
+  if (!part || !route || !fit || !o) return SPARSEPR_ERR_NULL;
+  if (!part->q_gm || !part->k_gm || !part->v_gm || !part->query_offsets || !part->key_offsets ||
+      !part->query_perm || !route->row_ptr || !route->cols)
+    return SPARSEPR_ERR_NULL;
+  if (!fit->A || !fit->B || !fit->c0 || !fit->r_eff || !fit->o_dense || !fit->probe_tokens) return SPARSEPR_ERR_NULL;
+  if (!aligned16(part->q_gm) || !aligned16(part->k_gm) || !aligned16(part->v_gm) || !aligned16(o))
+    return SPARSEPR_ERR_ALIGN;
+  const Workspace wp = plan_workspace(*params);
+  st = check_ws(params, workspace, workspace_bytes, wp.total_fused);
+  if (st != SPARSEPR_OK) return st;
+  const Dims dm = dims_of(*params);
+  AttnArgs a = sparse_args(dm, *part, *route);
+  (void)hipGetLastError();
+  if (wp.total_fused == 0) {
+    a.fitA = fit->A;
+    a.fitB = fit->B;
+    a.fitc0 = fit->c0;
+    a.r_eff = fit->r_eff;
+    a.rank = dm.r;
+    a.qperm = part->query_perm;
+    a.out_tok = o;
+    launch_attention(dm, a, false, (hipStream_t)stream);
+    launch_probe_writeback(dm, *fit, o, (hipStream_t)stream);
+  } else {
+    float* ogm = reinterpret_cast<float*>(static_cast<char*>(workspace) + wp.fused_ogm);
+    a.o = ogm;
+    launch_attention(dm, a, false, (hipStream_t)stream);
+    launch_apply(dm, ogm, *part, *fit, o, (hipStream_t)stream);
+  }
   return hip_status();
 }
 

@@ -106,6 +106,15 @@ static void apply_typed(const Dims& dm, const float* o_gm, const sparsepr_partit
                      dm.n, dm.g, dm.m, D, o);
 }
 
+void launch_probe_writeback(const Dims& dm, const sparsepr_fit_t& fit, void* o, hipStream_t s) {
+  if (dm.bf16)
+    hipLaunchKernelGGL(probe_writeback_kernel<bf16_t>, dim3(dm.hq), dim3(256), 0, s, fit.o_dense, fit.probe_tokens, dm.n,
+                       dm.g, dm.m, dm.d, (bf16_t*)o);
+  else
+    hipLaunchKernelGGL(probe_writeback_kernel<float>, dim3(dm.hq), dim3(256), 0, s, fit.o_dense, fit.probe_tokens, dm.n,
+                       dm.g, dm.m, dm.d, (float*)o);
+}
+
 void launch_apply(const Dims& dm, const float* o_gm, const sparsepr_partition_t& part, const sparsepr_fit_t& fit,
                   void* o, hipStream_t s) {
   if (dm.bf16) {

@@ -194,6 +194,89 @@ __device__ __forceinline__ void mfma_tile_step(const char* __restrict__ stage, c
     }
 }
 
+// Fused write-back for one query head per KV head (summary page of "Partition the
+// Support, Reconstruct the Residual": the affine probe-fit correction, write-back):
+// o_hat = o + c0 + (o A) B on the matrix cores straight from the output accumulators.
+// O^T's accumulator layout is already a valid B operand over d (the k-index permutation
+// is applied to both operands), so t^T = A^T O^T (k x q) and then O^T += B^T t^T need no
+// data movement; A^T, B^T (bf16) and c0 are staged in the free LDS stages.  Rows are
+// scattered to token order through the query permutation.
+template <int D, int LDS_BYTES>
+__device__ __forceinline__ void fused_writeback(const AttnArgs& A, int kv, int vrow, bool qvalid, float inv,
+                                                f32x16_t* o, char* lds, int tid, int l32, int hf) {
+  constexpr int DBLK = D / 32;
+  constexpr int AROW = D + 8;      // At[k][d] bf16, padded rows (conflict-free 16-byte reads)
+  constexpr int BROW = 32 + 4;     // Bt[d][k] bf16, padded rows (conflict-free 8-byte reads)
+  static_assert((32 * AROW + D * BROW) * 2 + D * 4 <= LDS_BYTES, "fused write-back staging");
+  const int h = kv;   // one query head per KV head
+  bf16_t* At = reinterpret_cast<bf16_t*>(lds);
+  bf16_t* Bt = At + 32 * AROW;
+  float* c0s = reinterpret_cast<float*>(Bt + D * BROW);
+  const int re = A.r_eff[h];
+  const float* Ah = A.fitA + (int64_t)h * D * A.rank;
+  const float* Bh = A.fitB + (int64_t)h * A.rank * D;
+  for (int idx = tid; idx < 32 * D; idx += 256) {
+    const int k = idx / D, d = idx % D;
+    At[k * AROW + d] = f32_to_bf16(k < re ? Ah[d * A.rank + k] : 0.f);
+    Bt[d * BROW + k] = f32_to_bf16(k < re ? Bh[k * D + d] : 0.f);
+  }
+  for (int d = tid; d < D; d += 256) c0s[d] = A.fitc0[(int64_t)h * D + d];
+  __syncthreads();
+  // normalise and pack O (bf16) as the B operand over d
+  f32x16_t t;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) t[r] = 0.f;
+#pragma unroll
+  for (int db = 0; db < DBLK; ++db) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[db][r] *= inv;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      bf16x8_t ob;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ob[e] = (__bf16)o[db][8 * s2 + e];
+      const bf16_t* ar = At + l32 * AROW + 32 * db + 16 * s2 + 4 * hf;
+      const uint2 lo8 = *reinterpret_cast<const uint2*>(ar);
+      const uint2 hi8 = *reinterpret_cast<const uint2*>(ar + 8);
+      const uint4 av = make_uint4(lo8.x, lo8.y, hi8.x, hi8.y);
+      t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av), ob, t, 0, 0, 0);
+    }
+  }
+  // t^T[k][q] in the accumulator layout is the B operand over k of O^T += B^T t^T
+  bf16x8_t tb[2];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    tb[0][e] = (__bf16)t[e];
+    tb[1][e] = (__bf16)t[8 + e];
+  }
+  const int ksteps = re > 16 ? 2 : 1;
+#pragma unroll
+  for (int db = 0; db < DBLK; ++db) {
+    for (int s2 = 0; s2 < ksteps; ++s2) {
+      const bf16_t* br = Bt + (32 * db + l32) * BROW + 16 * s2 + 4 * hf;
+      const uint2 lo8 = *reinterpret_cast<const uint2*>(br);
+      const uint2 hi8 = *reinterpret_cast<const uint2*>(br + 8);
+      const uint4 bv = make_uint4(lo8.x, lo8.y, hi8.x, hi8.y);
+      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, bv), tb[s2], o[db], 0, 0, 0);
+    }
+  }
+  if (qvalid) {
+    const int64_t tok = A.qperm[(int64_t)kv * A.n + vrow];
+    bf16_t* orow = static_cast<bf16_t*>(A.out_tok) + ((int64_t)h * A.n + tok) * D;
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d0 = 32 * db + 8 * j + 4 * hf;
+        uint2 v2 = make_uint2((uint32_t)f32_to_bf16(o[db][4 * j] + c0s[d0]) |
+                                  ((uint32_t)f32_to_bf16(o[db][4 * j + 1] + c0s[d0 + 1]) << 16),
+                              (uint32_t)f32_to_bf16(o[db][4 * j + 2] + c0s[d0 + 2]) |
+                                  ((uint32_t)f32_to_bf16(o[db][4 * j + 3] + c0s[d0 + 3]) << 16));
+        *reinterpret_cast<uint2*>(orow + d0) = v2;
+      }
+  }
+}
+
 template <int D, int BN, typename OutT>
 __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs A) {
   using C = MfmaCfg<D, BN>;
@@ -258,10 +341,14 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs A) {
     ci = nci; k0 = nk0; k1 = nk1; kt = nkt; valid = nvalid;
   }
 
-  // epilogue: O / l, LSE; lane writes query l32's d = 32 db + 8 j + 4 hf + 0..3
   const float l_tot = l_i + __shfl_xor(l_i, 32);
+  const float inv = 1.f / l_tot;
+  if (A.fitA != nullptr) {
+    fused_writeback<D, C::STAGE * 2>(A, kv, vrow, qvalid, inv, o, &stages[0][0], tid, l32, hf);
+    return;
+  }
+  // epilogue: O / l, LSE; lane writes query l32's d = 32 db + 8 j + 4 hf + 0..3
   if (qvalid) {
-    const float inv = 1.f / l_tot;
     OutT* orow = static_cast<OutT*>(A.o) + (int64_t)kv * A.o_skv + (int64_t)(vrow / A.g) * A.o_sp +
                  (int64_t)(vrow % A.g) * A.o_sj;
 #pragma unroll

@@ -26,6 +26,15 @@ struct AttnArgs {
   float scale;
   int tiles_per_head;          // tiles scheduled per KV head
   int n_heads_kv;
+  // fused write-back (one query head per KV head): o_hat = o + c0 + (o A) B written to
+  // out_tok[h][qperm[p]] in the input dtype
+  const float* fitA;           // [Hq][d][rank] or NULL (no fused write-back)
+  const float* fitB;           // [Hq][rank][d]
+  const float* fitc0;          // [Hq][d]
+  const int32_t* r_eff;        // [Hq]
+  int rank;
+  const int32_t* qperm;        // [Hkv][n]
+  void* out_tok;               // [Hq][n][d]
 };
 
 struct TileInfo {

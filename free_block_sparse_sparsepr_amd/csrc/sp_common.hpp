@@ -85,6 +85,7 @@ struct Workspace {
   size_t maxbits, xk, xq, centroids, sums, usum, total_partition;
   size_t partials, fitbuf, probe_alloc, total_probe;
   size_t dense_meta, total_dense;
+  size_t fused_ogm, total_fused;
   size_t total;
   int fpk, fpq, nchunks;
 };

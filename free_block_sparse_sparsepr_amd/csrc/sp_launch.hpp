@@ -25,6 +25,7 @@ void launch_probe_attn_mfma(const Dims& dm, const void* q, const sparsepr_partit
                             float* partials, hipStream_t s);
 void launch_probe_fit(const Dims& dm, const Workspace& wp, const void* q, const sparsepr_partition_t& part,
                       const sparsepr_route_t& route, const sparsepr_fit_t& out, char* ws, hipStream_t s);
+void launch_probe_writeback(const Dims& dm, const sparsepr_fit_t& fit, void* o, hipStream_t s);
 void launch_apply(const Dims& dm, const float* o_gm, const sparsepr_partition_t& part, const sparsepr_fit_t& fit,
                   void* o, hipStream_t s);
 

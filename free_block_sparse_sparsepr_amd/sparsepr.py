@@ -142,12 +142,29 @@ class SparsePR:
                                         ctypes.byref(self._fit_t), _p(out), _stream()))
         return out
 
+    def attend_apply(self, out=None):
+        c = self.cfg
+        if out is None:
+            out = torch.empty((c.heads_q, c.n, c.d), dtype=c.torch_dtype, device=self.o_gm.device)
+        B.check(self.lib.sparsepr_attend_apply(ctypes.byref(self.prm), ctypes.byref(self._part_t),
+                                               ctypes.byref(self._route_t), ctypes.byref(self._fit_t), _p(out),
+                                               _p(self.ws), self.ws.numel(), _stream()))
+        return out
+
     def __call__(self, q, k, v, out=None):
+        """Unfused order: partition -> route -> attend -> probe_fit -> apply."""
         self.partition(q, k, v)
         self.route()
         self.attend()
         self.probe_fit(q)
         return self.apply(out)
+
+    def fused(self, q, k, v, out=None):
+        """Fused order: partition -> route -> probe_fit -> attend_apply."""
+        self.partition(q, k, v)
+        self.route()
+        self.probe_fit(q)
+        return self.attend_apply(out)
 
     def dense(self, q, k, v, out=None):
         self._check_qkv(q, k, v)

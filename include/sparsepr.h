@@ -37,6 +37,7 @@
  *    0 <= kmeans_iters <= 64, block == 64.
  *
  * Unfused call order: partition -> route -> attend -> probe_fit -> apply.
+ * Fused call order:   partition -> route -> probe_fit -> attend_apply.
  */
 #ifndef SPARSEPR_H
 #define SPARSEPR_H
@@ -178,6 +179,17 @@ sparsepr_status sparsepr_probe_fit(const sparsepr_params* params, const void* q,
 sparsepr_status sparsepr_apply(const sparsepr_params* params, const float* o_gm,
                                const sparsepr_partition_t* part, const sparsepr_fit_t* fit, void* o,
                                void* stream);
+
+/* Block-sparse attention with the write-back fused into its epilogue: the fused call order
+ * partition -> route -> probe_fit -> attend_apply produces the same output as the unfused
+ * order (up to the rounding of the correction, which is formed from bf16 operands with
+ * fp32 accumulation) without the fp32 group-major intermediate.  For bf16 with one query
+ * head per KV head the correction o + c0 + (o A) B runs on the matrix cores inside the
+ * attention kernel; otherwise O_gm is formed in the workspace and the write-back follows.
+ * Reads the partition, the route and the fit; o: [Hq, n, d] dtype, token order. */
+sparsepr_status sparsepr_attend_apply(const sparsepr_params* params, const sparsepr_partition_t* part,
+                                      const sparsepr_route_t* route, const sparsepr_fit_t* fit, void* o,
+                                      void* workspace, size_t workspace_bytes, void* stream);
 
 /* Dense softmax attention O = softmax(Q K^T * scale) V on the same tile machinery (the
  * baseline; dense formula as in the lmnt.cn SparsePR article, section 2.1).  V is first

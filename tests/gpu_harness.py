@@ -40,12 +40,14 @@ def run_gpu(cfg, Q, K, V):
     sp = S.SparsePR(S.config_from_workload(cfg))
     q, k, v = device_tensor(Q, cfg), device_tensor(K, cfg), device_tensor(V, cfg)
     out = sp(q, k, v)
+    out_fused = sp.fused(q, k, v).clone()
     dense = sp.dense(q, k, v)
     torch.cuda.synchronize()
     res = {k_: host(t) for k_, t in {**sp.part, **sp.route_buf, **sp.fit}.items()}
     res["o_gm"] = host(sp.o_gm)
     res["lse"] = host(sp.lse)
     res["out"] = host(out)
+    res["out_fused"] = host(out_fused)
     res["dense"] = host(dense)
     return res, sp, (q, k, v)
 

@@ -1,8 +1,8 @@
 """Full-size GPU parity at the workloads' real shapes, in the launch configuration bench.py
-times (the whole call, all heads).  The oracle checks a subset of heads: integer stages
-bit-exact given the GPU's S and U, float outputs on sampled rows (the probe rows, the
-first and last rows and seeded random rows) with the oracle fed the GPU's labels, cells
-and probes; bf16 bar max-abs <= 2e-2, mean-abs <= 2e-3."""
+times (the whole call, all heads, fused and unfused orders).  The oracle checks a subset
+of heads: integer stages bit-exact given the GPU's S and U, float outputs on sampled rows
+(the probe rows, the first and last rows and seeded random rows) with the oracle fed the
+GPU's labels, cells and probes; bf16 bar max-abs <= 2e-2, mean-abs <= 2e-3."""
 import numpy as np
 import pytest
 
@@ -74,6 +74,10 @@ def test_fullsize_sampled_rows_match_oracle(full):
             want = O.correct_rows(o_s, fit)
             ok, mx, mean = compare_float(gpu["out"][h][nonprobe], want, False)
             assert ok, (h, "corrected rows", mx, mean)
+            ok, mx, mean = compare_float(gpu["out_fused"][h][nonprobe], want, False)
+            assert ok, (h, "corrected rows, fused order", mx, mean)
+            ok, mx, mean = compare_float(gpu["out_fused"][h][probes.tokens], fit.o_dense, False)
+            assert ok, (h, "probe rows, fused order", mx, mean)
             ok, mx, mean = compare_float(gpu["out"][h][probes.tokens], fit.o_dense, False)
             assert ok, (h, "probe rows", mx, mean)
             od, _ = O.dense_attention(q, k, v, scale, rows=rows)

@@ -179,6 +179,21 @@ def test_final_output_matches_oracle(case):
             assert ok, ("probe rows", h, mx, mean)
 
 
+def test_fused_order_matches_oracle_and_unfused(case):
+    """partition -> route -> probe_fit -> attend_apply gives the unfused result (the fused
+    correction is formed from bf16 operands) and meets the same bar against the oracle."""
+    cfg, gpu = case["cfg"], case["gpu"]
+    fp32 = cfg.dtype == "fp32"
+    ok, mx, mean = compare_float(gpu["out_fused"], gpu["out"], fp32)
+    assert ok, ("fused vs unfused", mx, mean)
+    for kv in range(cfg.heads_kv):
+        for j in range(cfg.g):
+            h = kv * cfg.g + j
+            _, _, fit, final = _gpu_float_stages(case, kv, j)
+            ok, mx, mean = compare_float(gpu["out_fused"][h], final, fp32)
+            assert ok, (h, mx, mean)
+
+
 def test_dense_attention_matches_oracle(case):
     cfg, gpu = case["cfg"], case["gpu"]
     fp32 = cfg.dtype == "fp32"
