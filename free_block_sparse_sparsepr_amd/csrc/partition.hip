@@ -200,6 +200,189 @@ __global__ __launch_bounds__(256) void kmeans_assign_kernel(const int8_t* __rest
     if (cnt[gi]) atomicAdd(&sh[gi * (FP + 1) + FP], cnt[gi]);
 }
 
+typedef int32_t ki32x4_t __attribute__((ext_vector_type(4)));
+typedef int32_t ki32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int kAssignChunk = 256;       // points per chunk: 64 per wave
+
+// Matrix-core assignment with the same decisions and sums as kmeans_assign_kernel, on the
+// int8 matrix cores (exact int32 accumulation).  Every MFMA pairs byte e of the A lane
+// (i, l / 32) with byte e of the B lane (j, l / 32), so the two operands only have to agree
+// on which feature (or point) each byte stands for.
+//  * scores^T = C X^T: a lane owns one point and 16 of each 32-group block (its partner
+//    lane l ^ 32 the other 16).  key = 64 (||c_g||^2 - 2 <x, c_g>) + g orders by score,
+//    then by g; the minimum over the lane and its partner is the label (key mod 64).
+//    Groups beyond G carry a key above every real one.
+//  * transpose: the same X operand times an identity slice puts the features on the lanes
+//    and the points in the accumulator registers.
+//  * sums: S^T += X^T onehot(labels), byte e of both operands standing for the point in
+//    accumulator register e; the sums stay in registers across the block's chunks.
+//  * counts: runs of equal labels among each 32 consecutive points (ballot of run starts),
+//    one LDS add per run.
+// At the end the waves' sums meet in LDS and go to global memory with one integer atomic
+// per non-zero (group, feature).  FP must be a multiple of 16.
+// grid (blocks_per_head, H), block 256; block b of a head takes chunks [b chunks, (b+1) chunks).
+template <int FP>
+__global__ __launch_bounds__(256, 2) void kmeans_assign_mfma_kernel(const int8_t* __restrict__ X, int n, int G,
+                                                                    const int32_t* __restrict__ C, int chunks,
+                                                                    int32_t* __restrict__ labels,
+                                                                    int32_t* __restrict__ sums) {
+  constexpr int KB = (FP + 31) / 32;   // 32-feature blocks
+  constexpr int CROW = 32 * KB + 16;   // int8 row of C in LDS, padded
+  constexpr int SROW = FP + 1;         // int32 row of the LDS sums (last column = count)
+  __shared__ __attribute__((aligned(16))) int8_t cs[kMaxGroups * CROW];
+  __shared__ int32_t cnk[kMaxGroups];
+  __shared__ int32_t ssum[kMaxGroups * SROW];
+  __shared__ __attribute__((aligned(16))) uint8_t lab_s[4][2][32];
+  const int h = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, hf = lane >> 5;
+  for (int idx = tid; idx < kMaxGroups * 32 * KB; idx += 256) {
+    const int gi = idx / (32 * KB), f = idx % (32 * KB);
+    const int c = (gi < G && f < FP) ? C[((int64_t)h * kMaxGroups + gi) * FP + f] : 0;
+    cs[gi * CROW + f] = (int8_t)c;
+  }
+  for (int idx = tid; idx < kMaxGroups * SROW; idx += 256) ssum[idx] = 0;
+  __syncthreads();
+  {  // 64 ||c_g||^2 + g, four lanes per group
+    const int gi = tid >> 2, q = tid & 3;
+    int s2 = 0;
+#pragma unroll
+    for (int t = 0; t < FP / 4; ++t) {
+      const int c = cs[gi * CROW + q + 4 * t];
+      s2 += c * c;
+    }
+    s2 += __shfl_xor(s2, 1);
+    s2 += __shfl_xor(s2, 2);
+    if (q == 0) cnk[gi] = gi < G ? 64 * s2 + gi : (1 << 30) + gi;
+  }
+  __syncthreads();
+  // identity slice: byte e of lane (j, hf) is 1 where 16 hf + e == j
+  ki32x4_t ident;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e0 = l32 - 16 * hf - 4 * q;
+    ident[q] = (e0 >= 0 && e0 < 4) ? (1 << (8 * e0)) : 0;
+  }
+  ki32x16_t acc[KB][2];
+#pragma unroll
+  for (int fb = 0; fb < KB; ++fb)
+#pragma unroll
+    for (int gb = 0; gb < 2; ++gb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[fb][gb][r] = 0;
+
+  const int8_t* xh = X + (int64_t)h * n * FP;
+  const int pbeg = blockIdx.x * chunks * kAssignChunk;
+  const int pend = min(n, pbeg + chunks * kAssignChunk);
+  // operand bytes of 32 points: lane (p, hf) holds features 32 kb + 16 hf .. + 15 of point p;
+  // the next 32 points' bytes are in flight while the current 32 are processed
+  auto load32 = [&](int pt, ki32x4_t* raw) {
+    const bool pv = pt < pend;
+    const int8_t* xr = xh + (int64_t)(pv ? pt : 0) * FP + 16 * hf;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const bool in = pv && (32 * kb + 16 * hf < FP);
+      raw[kb] = in ? *reinterpret_cast<const ki32x4_t*>(xr + 32 * kb) : ki32x4_t{0, 0, 0, 0};
+    }
+  };
+  ki32x4_t nraw[KB];
+  load32(pbeg + w * 64 + l32, nraw);
+  for (int pbase = pbeg + w * 64; pbase < pend; pbase += kAssignChunk) {
+#pragma unroll 1
+    for (int pb = 0; pb < 2; ++pb) {
+      const int pt = pbase + pb * 32 + l32;
+      const bool pv = pt < pend;
+      ki32x4_t xo[KB];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) xo[kb] = nraw[kb];
+      load32(pb == 0 ? pt + 32 : pt - 32 + kAssignChunk, nraw);
+      // -- assignment
+      int best = 0x7fffffff;
+#pragma unroll
+      for (int gb = 0; gb < 2; ++gb) {
+        ki32x16_t sc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sc[r] = 0;
+        const int8_t* crow = cs + (32 * gb + l32) * CROW + 16 * hf;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+          sc = __builtin_amdgcn_mfma_i32_32x32x32_i8(*reinterpret_cast<const ki32x4_t*>(crow + 32 * kb), xo[kb], sc,
+                                                     0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int gi = 32 * gb + 8 * (r >> 2) + 4 * hf + (r & 3);
+          best = min(best, cnk[gi] - 128 * sc[r]);
+        }
+      }
+      best = min(best, __shfl_xor(best, 32));
+      const int bg = best & 63;
+      const int lab = pv ? bg : kMaxGroups;          // points past the end: no group
+      if (pv && hf == 0) labels[(int64_t)h * n + pt] = bg;
+      // -- counts: one add per run of equal labels among the 32 points
+      const int prev = __shfl(lab, lane - (l32 > 0 ? 1 : 0));
+      const int next = __shfl(lab, lane + (l32 < 31 ? 1 : 0));
+      const uint64_t startm = __ballot(l32 == 0 || prev != lab);
+      if (hf == 0) {
+        lab_s[w][pb][l32] = (uint8_t)lab;
+        if (lab < kMaxGroups && (l32 == 31 || next != lab)) {
+          const uint32_t m = (uint32_t)startm & (0xffffffffu >> (31 - l32));
+          const int first = 31 - __builtin_clz(m);
+          atomicAdd(&ssum[lab * SROW + FP], l32 - first + 1);
+        }
+      }
+      // -- onehot: byte e of lane (g, hf) is [label of point 8 (e / 4) + 4 hf + e % 4 == g]
+      const uint32_t* lw = reinterpret_cast<const uint32_t*>(lab_s[w][pb]);
+      uint32_t lq[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) lq[q] = lw[2 * q + hf];
+      ki32x4_t oh[2];
+#pragma unroll
+      for (int gb = 0; gb < 2; ++gb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          // label bytes are <= 64 and g < 64, so x + 0x7f per byte never carries
+          const uint32_t x = lq[q] ^ ((uint32_t)(32 * gb + l32) * 0x01010101u);
+          oh[gb][q] = (int32_t)((~(x + 0x7f7f7f7fu) >> 7) & 0x01010101u);
+        }
+      // -- transpose and sums: tx[r] = X[8 (r / 4) + 4 hf + r % 4][32 fb + l32]
+#pragma unroll
+      for (int fb = 0; fb < KB; ++fb) {
+        ki32x16_t tx;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) tx[r] = 0;
+        tx = __builtin_amdgcn_mfma_i32_32x32x32_i8(xo[fb], ident, tx, 0, 0, 0);
+        ki32x4_t xa;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t lo = __builtin_amdgcn_perm((uint32_t)tx[4 * q + 1], (uint32_t)tx[4 * q], 0x0c0c0400u);
+          const uint32_t hi = __builtin_amdgcn_perm((uint32_t)tx[4 * q + 3], (uint32_t)tx[4 * q + 2], 0x04000c0cu);
+          xa[q] = (int32_t)(lo | hi);
+        }
+#pragma unroll
+        for (int gb = 0; gb < 2; ++gb)
+          acc[fb][gb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(xa, oh[gb], acc[fb][gb], 0, 0, 0);
+      }
+    }
+  }
+  // acc[fb][gb][r] = sum of feature 32 fb + 8 (r / 4) + 4 hf + r % 4 over group 32 gb + l32
+#pragma unroll
+  for (int fb = 0; fb < KB; ++fb)
+#pragma unroll
+    for (int gb = 0; gb < 2; ++gb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int f = 32 * fb + 8 * (r >> 2) + 4 * hf + (r & 3), gi = 32 * gb + l32;
+        const int v = acc[fb][gb][r];
+        if (f < FP && gi < G && v) atomicAdd(&ssum[gi * SROW + f], v);
+      }
+  __syncthreads();
+  int32_t* sh = sums + (int64_t)h * kMaxGroups * SROW;
+  for (int idx = tid; idx < G * SROW; idx += 256) {
+    const int v = ssum[idx];
+    if (v) atomicAdd(&sh[idx], v);
+  }
+}
+
 // c_g = div_rhaz(sum_g, count_g); an empty group keeps its centroid.  Also clears the
 // other sums buffer for the next assignment.  grid H, block 256.
 __global__ void kmeans_update_kernel(const int32_t* __restrict__ sums, int G, int F, int fp,
@@ -467,8 +650,27 @@ static void launch_assign(const int8_t* X, int n, int H, int G, const int32_t* C
                      X, n, G, C, labels, sums);
 }
 
+template <int FP>
+static void launch_assign_mfma(const int8_t* X, int n, int H, int G, const int32_t* C, int32_t* labels,
+                               int32_t* sums, hipStream_t s) {
+  // at most 512 blocks in all (two 4-wave blocks per CU at two waves per SIMD): one pass
+  // over the chip, and few per-block atomic flushes of G * (FP + 1) sums
+  const int nchunks = (int)ceil_div(n, kAssignChunk);
+  const int per_head = std::max(1, std::min(nchunks, 512 / std::max(H, 1)));
+  const int chunks = (int)ceil_div(nchunks, per_head);
+  hipLaunchKernelGGL(kmeans_assign_mfma_kernel<FP>, dim3((unsigned)ceil_div(nchunks, chunks), H), dim3(256), 0, s,
+                     X, n, G, C, chunks, labels, sums);
+}
+
 static void assign_dispatch(int fp, const int8_t* X, int n, int H, int G, const int32_t* C,
                             int32_t* labels, int32_t* sums, hipStream_t s) {
+  switch (fp) {
+    case 16: launch_assign_mfma<16>(X, n, H, G, C, labels, sums, s); return;
+    case 32: launch_assign_mfma<32>(X, n, H, G, C, labels, sums, s); return;
+    case 48: launch_assign_mfma<48>(X, n, H, G, C, labels, sums, s); return;
+    case 64: launch_assign_mfma<64>(X, n, H, G, C, labels, sums, s); return;
+    default: break;
+  }
   switch (fp) {
 #define SP_FP_CASE(V) case V: launch_assign<V>(X, n, H, G, C, labels, sums, s); break;
     SP_FP_CASE(4) SP_FP_CASE(8) SP_FP_CASE(12) SP_FP_CASE(16) SP_FP_CASE(20) SP_FP_CASE(24)
