@@ -49,7 +49,7 @@ Workspace plan_workspace(const sparsepr_params& p) {
   w.fitbuf = o; o = align_up(o + hq * (3 * kMaxProbe * p.d + p.d * kMaxRank) * 8);
   w.total_probe = o;
   w.dense_meta = 0;
-  w.total_dense = align_up(hkv * (size_t)p.d * (size_t)pad8(p.n) * (p.dtype == SPARSEPR_BF16 ? 2 : 4));
+  w.total_dense = align_up(hkv * (size_t)p.d * (size_t)vt_pad(p.n) * (p.dtype == SPARSEPR_BF16 ? 2 : 4));
   // the fused write-back runs in the attention epilogue for bf16 with one query head per KV
   // head; otherwise attend writes O_gm into the workspace and apply follows
   w.fused_ogm = 0;
@@ -116,7 +116,7 @@ static AttnArgs sparse_args(const Dims& dm, const sparsepr_partition_t& part, co
   a.q_sp = (int64_t)dm.g * dm.d;
   a.q_sj = dm.d;
   a.kv_skv = (int64_t)dm.n * dm.d;
-  a.v_np = (int)pad8(dm.n);
+  a.v_np = (int)vt_pad(dm.n);
   a.v_skv = (int64_t)dm.d * a.v_np;
   a.qoff = part.query_offsets;
   a.koff = part.key_offsets;
@@ -297,7 +297,7 @@ sparsepr_status sparsepr_dense_attention(const sparsepr_params* params, const vo
   a.q = q;
   a.k = k;
   a.v = vt;
-  a.v_np = (int)pad8(dm.n);
+  a.v_np = (int)vt_pad(dm.n);
   a.v_skv = (int64_t)dm.d * a.v_np;
   a.q_skv = (int64_t)dm.g * dm.n * dm.d;
   a.q_sp = dm.d;

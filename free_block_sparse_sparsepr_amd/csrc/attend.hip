@@ -47,7 +47,7 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs A) {
         const int kk = idx / D, c = idx % D;
         const bool in = kk < nk;
         ks[kk][c] = in ? to_f32(kb[(int64_t)(kt + kk) * D + c]) : 0.f;
-        vs[kk][c] = in ? to_f32(vb[(int64_t)c * A.v_np + vt_pos(c, kt + kk)]) : 0.f;
+        vs[kk][c] = in ? to_f32(vb[(int64_t)c * A.v_np + vt_pos(kt + kk)]) : 0.f;
       }
       __syncthreads();
       float s[8];

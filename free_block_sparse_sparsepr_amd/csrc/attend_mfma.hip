@@ -46,13 +46,14 @@ struct MfmaCfg {
   static constexpr int VIPW = D * VCH / 256;
   static constexpr int KSTEPS = D / 16;
   static constexpr int DBLK = D / 32;
-  // chunk swizzle of V^T row d: together with the half swap of rows with bit 3 set (in
-  // the global layout) 16 consecutive rows read at one key offset hit distinct banks
-  __device__ static int vswz(int d) { return VCH == 8 ? (d & 7) : ((d >> 1) & 3); }
+  // chunk swizzle of V^T row d: rows that share a bank window (every second row for
+  // 128-byte rows, every fourth for 64-byte rows) see distinct chunk slots, so 16
+  // consecutive rows read at one chunk offset hit distinct banks
+  __device__ static int vswz(int d) { return VCH == 8 ? ((d >> 1) & 7) : ((d >> 2) & 3); }
 };
 
 // Key tiles walk the kept runs of a query tile (uniform across the block).  Tiles start
-// on 8-key boundaries so that 16-byte chunks of the transposed V are aligned; keys of a
+// on 16-key boundaries so that the transposed V's 16-key groups are aligned; keys of a
 // tile outside its run [k0, k1) are masked.  Advances (ci, k0, k1, kt) to the next tile;
 // returns false after the last one.
 __device__ __forceinline__ bool next_tile(const AttnArgs& A, int kv, const TileInfo& ti, int BN, int& ci, int& k0,
@@ -60,35 +61,75 @@ __device__ __forceinline__ bool next_tile(const AttnArgs& A, int kv, const TileI
   kt += BN;
   if (kt < k1) return true;
   if (!next_run(A, kv, ti, ci, k0, k1)) return false;
-  kt = k0 & ~7;
+  kt = k0 & ~15;
   return true;
 }
 
 // Global -> LDS copy of one tile (K rows kt.., V^T columns kt..) with the direct
 // global-to-LDS path: lane i of a copy instruction lands at the instruction's LDS base +
-// 16 i, so each lane fetches the global chunk that belongs at its LDS slot.  Rows beyond
-// the sequence are clamped (those keys are masked).
+// 16 i, so each lane fetches the global chunk that belongs at its LDS slot.  A lane's
+// source offsets relative to the tile (CopyPlan, fixed for the whole kernel) and a
+// wave-uniform tile base make an interior tile's copies address arithmetic-free; the
+// last tile of the sequence clamps rows beyond n (those keys are masked).
+__device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
 template <int D, int BN>
-__device__ __forceinline__ void stage_copy(const bf16_t* __restrict__ kb, const bf16_t* __restrict__ vtb, int n,
-                                           int np, int kt, char* stage, int w, int lane) {
+struct CopyPlan {
   using C = MfmaCfg<D, BN>;
+  uint32_t koff[C::KIPW];   // bytes from the tile's first K row
+  uint32_t voff[C::VIPW];   // bytes from the tile's first V^T column
+  int krow[C::KIPW];        // K row within the tile
+  int vcol[C::VIPW];        // V^T column (key) within the tile
+
+  __device__ CopyPlan(int w, int lane, int np) {
+#pragma unroll
+    for (int i = 0; i < C::KIPW; ++i) {
+      const int L = (w * C::KIPW + i) * 64 + lane;
+      const int r = L / C::KCH, slot = L % C::KCH, c = slot ^ (r & 7);
+      krow[i] = r;
+      koff[i] = (uint32_t)(r * D + 8 * c) * 2u;
+    }
+#pragma unroll
+    for (int i = 0; i < C::VIPW; ++i) {
+      const int L = (w * C::VIPW + i) * 64 + lane;
+      const int d = L / C::VCH, slot = L % C::VCH, c = slot ^ C::vswz(d);
+      vcol[i] = 8 * c;
+      voff[i] = (uint32_t)(d * np + 8 * c) * 2u;
+    }
+  }
+};
+
+template <int D, int BN>
+__device__ __forceinline__ void stage_copy(const CopyPlan<D, BN>& cp, const bf16_t* __restrict__ kb,
+                                           const bf16_t* __restrict__ vtb, int n, int np, int kt, char* stage,
+                                           int wu) {
+  using C = MfmaCfg<D, BN>;
+  char* vst = stage + C::KBYTES;
+  if (kt + BN <= n) {
+    const char* kbase = reinterpret_cast<const char*>(kb + (int64_t)kt * D);
+    const char* vbase = reinterpret_cast<const char*>(vtb + kt);
+#pragma unroll
+    for (int i = 0; i < C::KIPW; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(kbase + cp.koff[i]),
+                                       (lds_void_t*)(stage + (wu * C::KIPW + i) * 1024), 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < C::VIPW; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(vbase + cp.voff[i]),
+                                       (lds_void_t*)(vst + (wu * C::VIPW + i) * 1024), 16, 0, 0);
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < C::KIPW; ++i) {
-    const int L = (w * C::KIPW + i) * 64 + lane;
-    const int r = L / C::KCH, slot = L % C::KCH, c = slot ^ (r & 7);
-    const int row = min(kt + r, n - 1);
-    __builtin_amdgcn_global_load_lds(kb + (int64_t)row * D + 8 * c,
-                                     (lds_void_t*)(stage + (w * C::KIPW + i) * 1024), 16, 0, 0);
+    const int row = min(kt + cp.krow[i], n - 1);
+    const char* src = reinterpret_cast<const char*>(kb + (int64_t)(row - cp.krow[i]) * D) + cp.koff[i];
+    __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)(stage + (wu * C::KIPW + i) * 1024), 16, 0, 0);
   }
-  char* vst = stage + C::KBYTES;
 #pragma unroll
   for (int i = 0; i < C::VIPW; ++i) {
-    const int L = (w * C::VIPW + i) * 64 + lane;
-    const int d = L / C::VCH, slot = L % C::VCH, c = slot ^ C::vswz(d);
-    int pos = kt + 8 * c;
-    pos = pos + 8 <= np ? pos : 0;
-    __builtin_amdgcn_global_load_lds(vtb + (int64_t)d * np + pos, (lds_void_t*)(vst + (w * C::VIPW + i) * 1024), 16,
-                                     0, 0);
+    const int pos = kt + cp.vcol[i];
+    const int base = pos + 8 <= np ? kt : -cp.vcol[i];   // chunks past n_pad read the row's first chunk
+    const char* src = reinterpret_cast<const char*>(vtb + base) + cp.voff[i];
+    __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)(vst + (wu * C::VIPW + i) * 1024), 16, 0, 0);
   }
 }
 
@@ -173,9 +214,9 @@ __device__ __forceinline__ void mfma_tile_step(const char* __restrict__ stage, c
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
   }
-  // O^T += V^T P^T: key k-step (kb, s2) covers keys 32 kb + 16 s2 + {4 hf + 0..3, 8 + 4 hf + 0..3}
+  // O^T += V^T P^T: key k-step (kb, s2) covers keys 32 kb + 16 s2 + {4 hf + 0..3, 8 + 4 hf + 0..3},
+  // which the V^T layout keeps as chunk 2 (2 kb + s2) + hf of the row
   const char* vst = stage + C::KBYTES;
-  const int ph = (hf ^ ((l32 >> 3) & 1)) << 3;
 #pragma unroll
   for (int kb = 0; kb < C::NB; ++kb)
 #pragma unroll
@@ -183,13 +224,9 @@ __device__ __forceinline__ void mfma_tile_step(const char* __restrict__ stage, c
 #pragma unroll
       for (int db = 0; db < C::DBLK; ++db) {
         const int d = 32 * db + l32;
-        const int sw = C::vswz(d);
         const char* vr = vst + d * (C::BN * 2);
-        const uint2 lo8 = *reinterpret_cast<const uint2*>(vr + (((4 * kb + 2 * s2) ^ sw) << 4) + ph);
-        const uint2 hi8 = *reinterpret_cast<const uint2*>(vr + (((4 * kb + 2 * s2 + 1) ^ sw) << 4) + ph);
-        const uint4 av = make_uint4(lo8.x, lo8.y, hi8.x, hi8.y);
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av), p[kb][s2].v, o[db], 0, 0,
-                                                        0);
+        const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(vr + (((4 * kb + 2 * s2 + hf) ^ C::vswz(d)) << 4));
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, p[kb][s2].v, o[db], 0, 0, 0);
       }
     }
 }
@@ -295,6 +332,8 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs A) {
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
+  const int wu = wave_uniform(w);
+  const CopyPlan<D, BN> cp(wu, lane, A.v_np);
   const bf16_t* qb = static_cast<const bf16_t*>(A.q);
   const bf16_t* kb = static_cast<const bf16_t*>(A.k) + (int64_t)kv * A.kv_skv;
   const bf16_t* vtb = static_cast<const bf16_t*>(A.v) + (int64_t)kv * A.v_skv;
@@ -323,8 +362,8 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs A) {
   int ci = ti.kbeg < 0 ? 0 : ti.kbeg, k0 = 0, k1 = 0, kt = 0;
   bool valid = next_run(A, kv, ti, ci, k0, k1);
   if (valid) {
-    kt = k0 & ~7;
-    stage_copy<D, BN>(kb, vtb, A.n, A.v_np, kt, stages[0], w, lane);
+    kt = k0 & ~15;
+    stage_copy<D, BN>(cp, kb, vtb, A.n, A.v_np, kt, stages[0], wu);
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -332,7 +371,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs A) {
   while (valid) {
     int nci = ci, nk0 = k0, nk1 = k1, nkt = kt;
     const bool nvalid = next_tile(A, kv, ti, C::BN, nci, nk0, nk1, nkt);
-    if (nvalid) stage_copy<D, BN>(kb, vtb, A.n, A.v_np, nkt, stages[cur ^ 1], w, lane);
+    if (nvalid) stage_copy<D, BN>(cp, kb, vtb, A.n, A.v_np, nkt, stages[cur ^ 1], wu);
     const int lo = max(k0 - kt, 0), hi = min(k1 - kt, BN);
     mfma_tile_step<D, BN, false>(stages[cur], qreg, lo, hi, c2, nullptr, 0ull, m_i, l_i, o, l32, hf);
     __builtin_amdgcn_s_waitcnt(0);
@@ -401,7 +440,9 @@ __global__ __launch_bounds__(256, 2) void probe_attn_mfma_kernel(const bf16_t* _
   const int row = 32 * (w & 1) + l32;
   const bool sparse = (w >> 1) != 0;
   const int k0 = ch * chunk, k1 = min(n, k0 + chunk);
-  const int np = (int)pad8(n);
+  const int np = (int)vt_pad(n);
+  const int wu = wave_uniform(w);
+  const CopyPlan<D, 32> cp(wu, lane, np);
   for (int b = tid; b <= Gk; b += 256) ko[b] = koff[(int64_t)kv * (Gk + 1) + b];
   const bool rvalid = row < M;
   const uint64_t rowmask = rvalid ? kept_mask[(int64_t)kv * Gq + pgrp[kv * M + row]] : 0ull;
@@ -431,7 +472,7 @@ __global__ __launch_bounds__(256, 2) void probe_attn_mfma_kernel(const bf16_t* _
   };
   int kt = k0;
   if (kt < k1) {
-    stage_copy<D, 32>(kb, vtb, n, np, kt, stages[0], w, lane);
+    stage_copy<D, 32>(cp, kb, vtb, n, np, kt, stages[0], wu);
     if (tid < C::BN) klab[0][tid] = (uint8_t)(kt + tid < k1 ? label_of(kt + tid) : 0);
   }
   __builtin_amdgcn_s_waitcnt(0);
@@ -440,7 +481,7 @@ __global__ __launch_bounds__(256, 2) void probe_attn_mfma_kernel(const bf16_t* _
   while (kt < k1) {
     const int nt = kt + C::BN;
     if (nt < k1) {
-      stage_copy<D, 32>(kb, vtb, n, np, nt, stages[cur ^ 1], w, lane);
+      stage_copy<D, 32>(cp, kb, vtb, n, np, nt, stages[cur ^ 1], wu);
       if (tid < C::BN) klab[cur ^ 1][tid] = (uint8_t)(nt + tid < k1 ? label_of(nt + tid) : 0);
     }
     const int hi = min(k1 - kt, C::BN);

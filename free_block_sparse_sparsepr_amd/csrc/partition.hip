@@ -487,9 +487,10 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint4* __restric
 }
 
 // Transposing gather of V into group-major, d-major order: block = 64 positions; rows
-// perm[p] (or p when perm is NULL) are staged in LDS, then each thread writes 8-key
-// chunks of one d row (16 or 32 contiguous bytes) with the layout's half swap.  Positions
-// from n up to n_pad are zero.  grid (ceil(n_pad / 64), Hkv), block 256.
+// perm[p] (or p when perm is NULL) are staged in LDS, then each thread writes 8 positions
+// of one d row (16 or 32 contiguous bytes) in the layout's key order (vt_pos, an
+// involution within each 16-key group).  Positions from n up to n_pad are zero.
+// grid (ceil(n_pad / 64), Hkv), block 256.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void gather_vt_kernel(const T* __restrict__ v, const int32_t* __restrict__ perm,
                                                         int n, int np, T* __restrict__ vt) {
@@ -508,10 +509,9 @@ __global__ __launch_bounds__(256) void gather_vt_kernel(const T* __restrict__ v,
   for (int idx = threadIdx.x; idx < D * 8; idx += 256) {
     const int d = idx >> 3, pc = idx & 7;
     if (p0 + 8 * pc >= np) continue;
-    const int sw = ((d >> 3) & 1) << 2;
     T* dst = vt + ((int64_t)kv * D + d) * np + p0 + 8 * pc;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) dst[e] = tile[8 * pc + (e ^ sw)][d];
+    for (int e = 0; e < 8; ++e) dst[e] = tile[vt_pos(8 * pc + e)][d];
   }
 }
 
@@ -739,8 +739,8 @@ static void partition_typed(const Dims& dm, const Workspace& wp, const T* q, con
   run_kmeans(xk, n, hkv, dm.gk, dm.rk, wp.fpk, dm.iters, C, sums, out.key_labels, out.key_centroids_int, s);
   run_group_major(out.key_labels, n, hkv, dm.gk, out.key_perm, out.key_offsets, s);
   run_gather(k, out.key_perm, n, hkv, 1, D, dm.bf16, out.k_gm, s);
-  hipLaunchKernelGGL((gather_vt_kernel<T, D>), dim3((unsigned)ceil_div(pad8(n), 64), hkv), dim3(256), 0, s, v,
-                     out.key_perm, n, (int)pad8(n), static_cast<T*>(out.v_gm));
+  hipLaunchKernelGGL((gather_vt_kernel<T, D>), dim3((unsigned)ceil_div(vt_pad(n), 64), hkv), dim3(256), 0, s, v,
+                     out.key_perm, n, (int)vt_pad(n), static_cast<T*>(out.v_gm));
   hipLaunchKernelGGL((segment_mean_kernel<T, D>), dim3(dm.gk, hkv), dim3(256), 0, s,
                      static_cast<const T*>(out.k_gm), out.key_offsets, n, dm.gk, out.key_centroids);
   // queries
@@ -758,8 +758,8 @@ static void partition_typed(const Dims& dm, const Workspace& wp, const T* q, con
 }
 
 void launch_transpose_v(const Dims& dm, const void* v, void* vt, hipStream_t s) {
-  const dim3 grid((unsigned)ceil_div(pad8(dm.n), 64), dm.hkv);
-  const int np = (int)pad8(dm.n);
+  const dim3 grid((unsigned)ceil_div(vt_pad(dm.n), 64), dm.hkv);
+  const int np = (int)vt_pad(dm.n);
   if (dm.bf16) {
     if (dm.d == 128) hipLaunchKernelGGL((gather_vt_kernel<bf16_t, 128>), grid, dim3(256), 0, s, (const bf16_t*)v, nullptr, dm.n, np, (bf16_t*)vt);
     else hipLaunchKernelGGL((gather_vt_kernel<bf16_t, 64>), grid, dim3(256), 0, s, (const bf16_t*)v, nullptr, dm.n, np, (bf16_t*)vt);

@@ -191,7 +191,7 @@ __global__ __launch_bounds__(256) void probe_attn_kernel(const T* __restrict__ q
   if (tid < kMaxProbe) msk[tid] = tid < M ? kept_mask[(int64_t)kv * Gq + pgrp[kv * M + tid]] : 0ull;
   for (int b = tid; b <= Gk; b += 256) ko[b] = koff[(int64_t)kv * (Gk + 1) + b];
   const T* kb = kgm + (int64_t)kv * n * D;
-  const int np = (int)pad8(n);
+  const int np = (int)vt_pad(n);
   const T* vb = vgm + (int64_t)kv * D * np;
   float md = -INFINITY, ld = 0.f, ms = -INFINITY, ls = 0.f;
   float od[CPT], os[CPT];
@@ -204,7 +204,7 @@ __global__ __launch_bounds__(256) void probe_attn_kernel(const T* __restrict__ q
       const int kk = idx / D, c = idx % D;
       const bool in = kk < nk;
       ks[kk][c] = in ? to_f32(kb[(int64_t)(kt + kk) * D + c]) : 0.f;
-      vs[kk][c] = in ? to_f32(vb[(int64_t)c * np + vt_pos(c, kt + kk)]) : 0.f;
+      vs[kk][c] = in ? to_f32(vb[(int64_t)c * np + vt_pos(kt + kk)]) : 0.f;
     }
     if (tid < BN) {
       int lab = 0;

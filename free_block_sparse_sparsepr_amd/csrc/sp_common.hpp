@@ -21,11 +21,12 @@ constexpr int kProbeChunk = 1024;   // keys per probe-attention work item
 __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Group-major V is stored transposed (d-major) as [Hkv][d][n_pad], n_pad = n rounded up to
-// 8.  In rows d with bit 3 set the two 4-key halves of every 8-key chunk are swapped, so
-// the matrix cores' transposed V operand reads are free of LDS bank conflicts after a
-// straight 16-byte copy into LDS.  Element (d, p) lives at d * n_pad + vt_pos(d, p).
-__host__ __device__ inline int64_t pad8(int64_t n) { return (n + 7) & ~(int64_t)7; }
-__host__ __device__ inline int vt_pos(int d, int p) { return p ^ (((d >> 3) & 1) << 2); }
+// 16.  Within every 16-key group the keys are stored in the order 0-3, 8-11, 4-7, 12-15
+// (bits 2 and 3 of the position swapped), which is the order in which the matrix cores'
+// k-permuted P^T operand pairs them with V: a lane's 8 keys of one k-step are one
+// contiguous 16-byte chunk.  Element (d, p) lives at d * n_pad + vt_pos(p).
+__host__ __device__ inline int64_t vt_pad(int64_t n) { return (n + 15) & ~(int64_t)15; }
+__host__ __device__ inline int vt_pos(int p) { return (p & ~12) | ((p & 4) << 1) | ((p & 8) >> 1); }
 __host__ __device__ inline int round_up4(int x) { return (x + 3) & ~3; }
 
 __device__ __forceinline__ float bf16_to_f32(bf16_t x) { return __uint_as_float(((uint32_t)x) << 16); }

@@ -36,7 +36,7 @@ class Config:
 
     @property
     def n_pad(self):
-        return (self.n + 7) // 8 * 8
+        return (self.n + 15) // 16 * 16
 
     @property
     def torch_dtype(self):

@@ -102,10 +102,10 @@ typedef struct sparsepr_partition_t {
   int32_t* query_offsets;    /* [Hkv, G_Q + 1] */
   void* q_gm;                /* [Hkv, n, g, d] dtype: Q in group-major order */
   void* k_gm;                /* [Hkv, n, d] dtype: K in group-major order */
-  void* v_gm;                /* [Hkv, d, n_pad] dtype, n_pad = n rounded up to 8: V in group-major
+  void* v_gm;                /* [Hkv, d, n_pad] dtype, n_pad = n rounded up to 16: V in group-major
                                 order (follows K), stored transposed (d-major).  Element (d, p) is at
-                                d * n_pad + (p ^ 4) when bit 3 of d is set, else d * n_pad + p (the
-                                two 4-key halves of every 8-key chunk are swapped in those rows);
+                                d * n_pad + s(p), where s swaps bits 2 and 3 of p (within each
+                                16-key group the keys are stored as 0-3, 8-11, 4-7, 12-15);
                                 positions n .. n_pad - 1 are zero. */
 } sparsepr_partition_t;
 

@@ -53,16 +53,12 @@ def run_gpu(cfg, Q, K, V):
 
 
 def vgm_rows(vt, n):
-    """Group-major V rows [n, d] from the transposed layout [d, n_pad] (rows d with bit 3 set
-    hold each 8-key chunk with its 4-key halves swapped)."""
+    """Group-major V rows [n, d] from the transposed layout [d, n_pad] (key p of a row is
+    stored at p with bits 2 and 3 swapped)."""
     vt = np.asarray(vt)
-    d = vt.shape[0]
-    out = np.empty((n, d), vt.dtype)
     p = np.arange(n)
-    for dd in range(d):
-        pos = p ^ 4 if (dd >> 3) & 1 else p
-        out[:, dd] = vt[dd, pos]
-    return out
+    pos = (p & ~12) | ((p & 4) << 1) | ((p & 8) >> 1)
+    return np.ascontiguousarray(vt[:, pos].T)
 
 
 def kept_from_mask(mask, gq, gk):
