@@ -60,6 +60,19 @@ def cpu_baseline(cfg):
                       f"nproc {os.cpu_count()}"}
 
 
+def copy_probe(mib):
+    """A plain copy of `mib` MiB (torch's device copy kernel), three launches on a source larger
+    than the caches: each launch reads and writes exactly mib MiB."""
+    import torch
+    n = mib * (1 << 20)
+    src = torch.randint(0, 255, (n,), dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "launches": 3}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -71,7 +84,13 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--unfused", action="store_true",
                     help="time the unfused order (attend -> probe_fit -> apply) instead of the fused one")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (3 launches) and exit: the reference "
+                         "kernel of known traffic for scaling the FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
+    if args.copy_probe_mib:
+        copy_probe(args.copy_probe_mib)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for {args.gpus}); the SparsePR call "
               "shards by head with no exchange step, but no multi-GPU path is built.", file=sys.stderr)

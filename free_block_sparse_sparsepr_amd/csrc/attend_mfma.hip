@@ -39,13 +39,17 @@ struct MfmaCfg {
   static constexpr int NB = BN / 32;        // 32-key score blocks per tile
   static constexpr int KCH = D / 8;         // 16-byte chunks per K row
   static constexpr int VCH = BN / 8;        // 16-byte chunks per V^T row
-  static constexpr int KBYTES = BN * D * 2; // K stage: BN rows, chunk c of row r at slot c ^ (r & 7)
+  static constexpr int KBYTES = BN * D * 2; // K stage: BN rows, chunk c of row r at slot c ^ kswz(r)
   static constexpr int VBYTES = D * BN * 2; // V^T stage: D rows of BN keys, chunk c of row d at slot c ^ vswz(d)
   static constexpr int STAGE = KBYTES + VBYTES;
   static constexpr int KIPW = BN * KCH / 256;   // K copy instructions per wave
   static constexpr int VIPW = D * VCH / 256;
   static constexpr int KSTEPS = D / 16;
   static constexpr int DBLK = D / 32;
+  // chunk swizzle of K row r: 16 consecutive rows read at one chunk offset (the 16 lanes
+  // of one LDS cycle of a 16-byte read) hit distinct banks; 256-byte rows (d = 128) each
+  // fill the bank window, 128-byte rows (d = 64) share it in pairs
+  __device__ static int kswz(int r) { return KCH == 16 ? (r & 15) : ((r >> 1) & 7); }
   // chunk swizzle of V^T row d: rows that share a bank window (every second row for
   // 128-byte rows, every fourth for 64-byte rows) see distinct chunk slots, so 16
   // consecutive rows read at one chunk offset hit distinct banks
@@ -85,7 +89,7 @@ struct CopyPlan {
 #pragma unroll
     for (int i = 0; i < C::KIPW; ++i) {
       const int L = (w * C::KIPW + i) * 64 + lane;
-      const int r = L / C::KCH, slot = L % C::KCH, c = slot ^ (r & 7);
+      const int r = L / C::KCH, slot = L % C::KCH, c = slot ^ C::kswz(r);
       krow[i] = r;
       koff[i] = (uint32_t)(r * D + 8 * c) * 2u;
     }
@@ -159,7 +163,7 @@ __device__ __forceinline__ void mfma_tile_step(const char* __restrict__ stage, c
 #pragma unroll
     for (int kb = 0; kb < C::NB; ++kb) {
       const int row = 32 * kb + l32;
-      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(stage + row * (D * 2) + (((2 * kk + hf) ^ (row & 7)) << 4));
+      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(stage + row * (D * 2) + (((2 * kk + hf) ^ C::kswz(row)) << 4));
       sv[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[kk], sv[kb], 0, 0, 0);
     }
   }
