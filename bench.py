@@ -60,6 +60,35 @@ def cpu_baseline(cfg):
                       f"nproc {os.cpu_count()}"}
 
 
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "sparse_attention_720p_n118800_h24_hbm_traffic.md")
+KERNEL_SOURCES = ["free_block_sparse_sparsepr_amd/csrc/attend_mfma.hip", "free_block_sparse_sparsepr_amd/csrc/sp_attn.hpp",
+                  "free_block_sparse_sparsepr_amd/csrc/sp_common.hpp"]
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload_name):
+    """HBM bytes per launch of the attention kernel from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, each scaled against a plain copy of known size), or None when
+    the summary is missing, covers another workload, or the kernel sources have changed since."""
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+        block = text.split("```json", 1)[1].split("```", 1)[0]
+        rec = json.loads(block)
+    except (OSError, IndexError, ValueError):
+        return None
+    if rec.get("workload") != workload_name or rec.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
 def copy_probe(mib):
     """A plain copy of `mib` MiB (torch's device copy kernel), three launches on a source larger
     than the caches: each launch reads and writes exactly mib MiB."""
@@ -192,7 +221,7 @@ def main():
                      "sparsepr_attend_apply: attention with the fused write-back epilogue, plus the 64-row probe "
                      "write-back kernel") + ")",
                      "achieved": attend_tflops, "peak": peak, "unit": "TFLOP/s", "frac": attend_tflops / peak,
-                     "traffic": None},
+                     "traffic": None if args.unfused else measured_traffic(cfg.name)},
         "effective_tflops_call": call_tflops, "effective_frac_call": call_tflops / peak,
         "realised_rho_route": rho_route, "realised_rho_exec": rho_exec,
         "routed_pairs": routed, "stage_ms": stage_ms, "dense": dense, "cpu_baseline": cpu,
