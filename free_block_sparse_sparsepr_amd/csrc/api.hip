@@ -41,6 +41,7 @@ Workspace plan_workspace(const sparsepr_params& p) {
   w.centroids = o; o = align_up(o + hkv * kMaxGroups * fpmax * 4);
   w.sums = o; o = align_up(o + 2 * hkv * kMaxGroups * (fpmax + 1) * 4);
   w.usum = o; if (p.heads_q != p.heads_kv) o = align_up(o + hkv * n * p.groups_k * 4);
+  w.gm_hist = o; o = align_up(o + hkv * (size_t)ceil_div(p.n, kGmChunk) * kMaxGroups * 4);
   w.total_partition = o;
   w.nchunks = (int)ceil_div(p.n, kProbeChunk);
   o = 0;

@@ -409,58 +409,101 @@ __global__ void copy_centroids_kernel(const int32_t* __restrict__ C, int G, int 
 
 // ---------------------------------------------------------------------------------------
 // Stable counting sort of labels: offsets (exclusive scan of counts) and perm (token at
-// each group-major position, tokens ascending within a group).  One block per head.
-// Within a 1024-token chunk a token's rank among equal labels comes from wave ballots
-// plus the counts of earlier waves.
+// each group-major position, tokens ascending within a group), over 1024-token chunks in
+// three passes: per-chunk group counts, a scan over chunks (group offsets plus each
+// chunk's base per group), and the scatter.  Within a chunk a token's rank among equal
+// labels comes from wave ballots (one round per distinct label of the wave) plus the
+// counts of earlier waves.
 // ---------------------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void group_major_kernel(const int32_t* __restrict__ labels, int n,
-                                                           int G, int32_t* __restrict__ perm,
-                                                           int32_t* __restrict__ offsets) {
-  __shared__ int cnt[kMaxGroups];
-  __shared__ int base[kMaxGroups];
-  __shared__ int wcnt[16][kMaxGroups];
-  const int h = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int32_t* lh = labels + (int64_t)h * n;
-  for (int i = tid; i < kMaxGroups; i += 1024) cnt[i] = 0;
-  for (int i = tid; i < 16 * kMaxGroups; i += 1024) (&wcnt[0][0])[i] = 0;
-  __syncthreads();
-  for (int j = tid; j < n; j += 1024) atomicAdd(&cnt[lh[j]], 1);
-  __syncthreads();
-  if (tid == 0) {
-    int s = 0;
-    for (int b = 0; b < G; ++b) { base[b] = s; offsets[(int64_t)h * (G + 1) + b] = s; s += cnt[b]; }
-    offsets[(int64_t)h * (G + 1) + G] = s;
-  }
-  __syncthreads();
+// Per-wave counts of the chunk's labels into wcnt[w][.] (zeroed by the caller) and the
+// lane's rank among the equal labels of its wave.
+__device__ __forceinline__ int gm_wave_ranks(int lab, bool valid, int lane, int w, int (*wcnt)[kMaxGroups]) {
   const uint64_t lt = (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
-  for (int c0 = 0; c0 < n; c0 += 1024) {
-    const int j = c0 + tid;
-    const bool valid = j < n;
-    const int lab = valid ? lh[j] : -1;
-    uint64_t active = __ballot(valid);
-    int rank = 0;
-    while (active) {
-      int leader = __ffsll((long long)active) - 1;
-      int L = __shfl(lab, leader);
-      uint64_t m = __ballot(lab == L) & active;
-      if (valid && lab == L) rank = __popcll(m & lt);
-      if (lane == leader) wcnt[w][L] = __popcll(m);
-      active &= ~m;
+  uint64_t active = __ballot(valid);
+  int rank = 0;
+  while (active) {
+    const int leader = __ffsll((long long)active) - 1;
+    const int L = __shfl(lab, leader);
+    const uint64_t m = __ballot(lab == L) & active;
+    if (valid && lab == L) rank = __popcll(m & lt);
+    if (lane == leader) wcnt[w][L] = __popcll(m);
+    active &= ~m;
+  }
+  return rank;
+}
+
+// grid (nchunks, H), block 1024: hist[h][c][b] = count of label b in chunk c
+__global__ __launch_bounds__(1024) void gm_count_kernel(const int32_t* __restrict__ labels, int n, int G,
+                                                        int32_t* __restrict__ hist) {
+  __shared__ int wcnt[16][kMaxGroups];
+  const int c = blockIdx.x, h = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  (&wcnt[0][0])[tid] = 0;
+  __syncthreads();
+  const int j = c * kGmChunk + tid;
+  const bool valid = j < n;
+  gm_wave_ranks(valid ? labels[(int64_t)h * n + j] : -1, valid, lane, w, wcnt);
+  __syncthreads();
+  if (tid < kMaxGroups) {
+    int sum = 0;
+#pragma unroll
+    for (int ww = 0; ww < 16; ++ww) sum += wcnt[ww][tid];
+    hist[((int64_t)h * gridDim.x + c) * kMaxGroups + tid] = sum;
+  }
+}
+
+// grid (H), block 64 (lane = group): offsets and, in place, hist[h][c][b] = first
+// group-major position of chunk c's tokens of group b
+__global__ __launch_bounds__(64) void gm_scan_kernel(int32_t* __restrict__ hist, int nchunks, int G,
+                                                     int32_t* __restrict__ offsets) {
+  constexpr int U = 8;
+  const int h = blockIdx.x, b = threadIdx.x;
+  int32_t* hh = hist + (int64_t)h * nchunks * kMaxGroups + b;
+  int total = 0;
+  for (int c0 = 0; c0 < nchunks; c0 += U) {
+    int v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = c0 + u < nchunks ? hh[(int64_t)(c0 + u) * kMaxGroups] : 0;
+#pragma unroll
+    for (int u = 0; u < U; ++u) total += v[u];
+  }
+  int incl = total;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int x = __shfl_up(incl, o);
+    if (b >= o) incl += x;
+  }
+  int run = incl - total;
+  if (b < G) offsets[(int64_t)h * (G + 1) + b] = run;
+  if (b == G - 1) offsets[(int64_t)h * (G + 1) + G] = incl;
+  for (int c0 = 0; c0 < nchunks; c0 += U) {
+    int v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = c0 + u < nchunks ? hh[(int64_t)(c0 + u) * kMaxGroups] : 0;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (c0 + u < nchunks) hh[(int64_t)(c0 + u) * kMaxGroups] = run;
+      run += v[u];
     }
-    __syncthreads();
-    if (valid) {
-      int pre = 0;
-      for (int ww = 0; ww < w; ++ww) pre += wcnt[ww][lab];
-      perm[(int64_t)h * n + base[lab] + pre + rank] = j;
-    }
-    __syncthreads();
-    if (tid < G) {
-      int s = 0;
-      for (int ww = 0; ww < 16; ++ww) { s += wcnt[ww][tid]; wcnt[ww][tid] = 0; }
-      base[tid] += s;
-    }
-    __syncthreads();
+  }
+}
+
+// grid (nchunks, H), block 1024
+__global__ __launch_bounds__(1024) void gm_scatter_kernel(const int32_t* __restrict__ labels, int n,
+                                                          const int32_t* __restrict__ base,
+                                                          int32_t* __restrict__ perm) {
+  __shared__ int wcnt[16][kMaxGroups];
+  const int c = blockIdx.x, h = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  (&wcnt[0][0])[tid] = 0;
+  __syncthreads();
+  const int j = c * kGmChunk + tid;
+  const bool valid = j < n;
+  const int lab = valid ? labels[(int64_t)h * n + j] : -1;
+  const int rank = gm_wave_ranks(lab, valid, lane, w, wcnt);
+  __syncthreads();
+  if (valid) {
+    int pre = base[((int64_t)h * gridDim.x + c) * kMaxGroups + lab];
+    for (int ww = 0; ww < w; ++ww) pre += wcnt[ww][lab];
+    perm[(int64_t)h * n + pre + rank] = j;
   }
 }
 
@@ -487,31 +530,40 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint4* __restric
 }
 
 // Transposing gather of V into group-major, d-major order: block = 64 positions; rows
-// perm[p] (or p when perm is NULL) are staged in LDS, then each thread writes 8 positions
-// of one d row (16 or 32 contiguous bytes) in the layout's key order (vt_pos, an
-// involution within each 16-key group).  Positions from n up to n_pad are zero.
-// grid (ceil(n_pad / 64), Hkv), block 256.
+// perm[p] (or p when perm is NULL) are staged in LDS with 16-byte loads, then each thread
+// assembles one 16-byte chunk (8 positions of one d row, in the layout's key order
+// vt_pos, an involution within each 16-key group) and stores it whole.  Positions from n
+// up to n_pad are zero.  grid (ceil(n_pad / 64), Hkv), block 256.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void gather_vt_kernel(const T* __restrict__ v, const int32_t* __restrict__ perm,
                                                         int n, int np, T* __restrict__ vt) {
-  __shared__ T tile[64][D + 2];
+  constexpr int EPC = 16 / sizeof(T);       // elements per 16-byte chunk
+  constexpr int CPR = D / EPC;              // chunks per row
+  constexpr int ROW = D + 2;                // padded LDS row (elements)
+  __shared__ T tile[64 * ROW];
   const int kv = blockIdx.y, p0 = blockIdx.x * 64;
-  for (int idx = threadIdx.x; idx < 64 * D; idx += 256) {
-    const int r = idx / D, c = idx % D, p = p0 + r;
-    T x = from_f32<T>(0.f);
+  for (int idx = threadIdx.x; idx < 64 * CPR; idx += 256) {
+    const int r = idx / CPR, c = idx % CPR, p = p0 + r;
+    uint4 x = make_uint4(0, 0, 0, 0);
     if (p < n) {
       const int64_t tok = perm ? perm[(int64_t)kv * n + p] : p;
-      x = v[((int64_t)kv * n + tok) * D + c];
+      x = *reinterpret_cast<const uint4*>(v + ((int64_t)kv * n + tok) * D + c * EPC);
     }
-    tile[r][c] = x;
+    const T* xe = reinterpret_cast<const T*>(&x);
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) tile[r * ROW + c * EPC + e] = xe[e];
   }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < D * 8; idx += 256) {
-    const int d = idx >> 3, pc = idx & 7;
-    if (p0 + 8 * pc >= np) continue;
-    T* dst = vt + ((int64_t)kv * D + d) * np + p0 + 8 * pc;
+  // output chunk: row d, positions p0 + EPC q .. + EPC - 1
+  constexpr int QPR = 64 / EPC;             // chunks per d row in this block
+  for (int idx = threadIdx.x; idx < D * QPR; idx += 256) {
+    const int d = idx / QPR, q = idx % QPR;
+    if (p0 + EPC * q >= np) continue;
+    uint4 y;
+    T* ye = reinterpret_cast<T*>(&y);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) dst[e] = tile[vt_pos(8 * pc + e)][d];
+    for (int e = 0; e < EPC; ++e) ye[e] = tile[vt_pos(EPC * q + e) * ROW + d];
+    *reinterpret_cast<uint4*>(vt + ((int64_t)kv * D + d) * np + p0 + EPC * q) = y;
   }
 }
 
@@ -612,8 +664,8 @@ __global__ __launch_bounds__(256) void resp_u_kernel(const T* __restrict__ q, co
 // Response-direction features: u = rint(Usum 2^e_U) (e_U: largest e with
 // max|Usum| 2^e <= 2^14), c_b = G_K u_b - sum u, x_b = div_rhaz(127 c_b, max|c|).
 // Written to the caller's [Hkv][n][G_K] buffer and to a stride-fp copy for the k-means.
-// One wave per row (lanes over key groups, wave reductions); each wave walks 16 rows.
-// grid (ceil(n / 64), Hkv), block 256.
+// One wave per row (lanes over key groups, wave reductions); each wave walks 16 rows,
+// all 16 rows' loads issued before the first is used.  grid (ceil(n / 64), Hkv), block 256.
 __global__ __launch_bounds__(256) void query_features_kernel(const float* __restrict__ Usrc,
                                                              const uint32_t* maxbits, int n, int Gk,
                                                              int fp, int8_t* __restrict__ Xout,
@@ -622,11 +674,18 @@ __global__ __launch_bounds__(256) void query_features_kernel(const float* __rest
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int e = pow2_exponent(__uint_as_float(maxbits[kv]), 16384.f);
   if (blockIdx.x == 0 && threadIdx.x == 0) exps[kv * 2 + 1] = e;
+  const int i0 = blockIdx.x * 64 + w * 16;
+  float uv[16];
+#pragma unroll
   for (int rr = 0; rr < 16; ++rr) {
-    const int i = blockIdx.x * 64 + w * 16 + rr;
+    const int i = min(i0 + rr, n - 1);
+    uv[rr] = lane < Gk ? Usrc[((int64_t)kv * n + i) * Gk + lane] : 0.f;
+  }
+#pragma unroll
+  for (int rr = 0; rr < 16; ++rr) {
+    const int i = i0 + rr;
     if (i >= n) break;
-    const float* ur = Usrc + ((int64_t)kv * n + i) * Gk;
-    const int u = lane < Gk ? (int)rintf(ldexpf(ur[lane], e)) : 0;
+    const int u = lane < Gk ? (int)rintf(ldexpf(uv[rr], e)) : 0;
     int sum = u;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
@@ -697,8 +756,11 @@ void run_kmeans(const int8_t* X, int n, int H, int G, int F, int fp, int iters, 
 }
 
 void run_group_major(const int32_t* labels, int n, int H, int G, int32_t* perm, int32_t* offsets,
-                     hipStream_t s) {
-  hipLaunchKernelGGL(group_major_kernel, dim3(H), dim3(1024), 0, s, labels, n, G, perm, offsets);
+                     int32_t* hist, hipStream_t s) {
+  const int nchunks = (int)ceil_div(n, kGmChunk);
+  hipLaunchKernelGGL(gm_count_kernel, dim3(nchunks, H), dim3(1024), 0, s, labels, n, G, hist);
+  hipLaunchKernelGGL(gm_scan_kernel, dim3(H), dim3(64), 0, s, hist, nchunks, G, offsets);
+  hipLaunchKernelGGL(gm_scatter_kernel, dim3(nchunks, H), dim3(1024), 0, s, labels, n, hist, perm);
 }
 
 void run_gather(const void* src, const int32_t* perm, int n, int hkv, int g, int d, bool bf16,
@@ -726,6 +788,7 @@ static void partition_typed(const Dims& dm, const Workspace& wp, const T* q, con
   int32_t* C = reinterpret_cast<int32_t*>(ws + wp.centroids);
   int32_t* sums = reinterpret_cast<int32_t*>(ws + wp.sums);
   float* usum = dm.g > 1 ? reinterpret_cast<float*>(ws + wp.usum) : nullptr;
+  int32_t* gm_hist = reinterpret_cast<int32_t*>(ws + wp.gm_hist);
   const int n = dm.n, hkv = dm.hkv;
   fill_u32(maxbits, (size_t)hkv * 2, 0, s);
   // keys
@@ -737,7 +800,7 @@ static void partition_typed(const Dims& dm, const Workspace& wp, const T* q, con
   hipLaunchKernelGGL(key_features_kernel, dim3((unsigned)ceil_div(n, 256), hkv), dim3(256), 0, s,
                      out.responses_s, maxbits, n, dm.rk, wp.fpk, xk, out.exponents);
   run_kmeans(xk, n, hkv, dm.gk, dm.rk, wp.fpk, dm.iters, C, sums, out.key_labels, out.key_centroids_int, s);
-  run_group_major(out.key_labels, n, hkv, dm.gk, out.key_perm, out.key_offsets, s);
+  run_group_major(out.key_labels, n, hkv, dm.gk, out.key_perm, out.key_offsets, gm_hist, s);
   run_gather(k, out.key_perm, n, hkv, 1, D, dm.bf16, out.k_gm, s);
   hipLaunchKernelGGL((gather_vt_kernel<T, D>), dim3((unsigned)ceil_div(vt_pad(n), 64), hkv), dim3(256), 0, s, v,
                      out.key_perm, n, (int)vt_pad(n), static_cast<T*>(out.v_gm));
@@ -753,7 +816,7 @@ static void partition_typed(const Dims& dm, const Workspace& wp, const T* q, con
                      usum ? usum : out.responses_u, maxbits + hkv, n, dm.gk, wp.fpq, out.query_features,
                      xq, out.exponents);
   run_kmeans(xq, n, hkv, dm.gq, dm.gk, wp.fpq, dm.iters, C, sums, out.query_labels, out.query_centroids, s);
-  run_group_major(out.query_labels, n, hkv, dm.gq, out.query_perm, out.query_offsets, s);
+  run_group_major(out.query_labels, n, hkv, dm.gq, out.query_perm, out.query_offsets, gm_hist, s);
   run_gather(q, out.query_perm, n, hkv, dm.g, D, dm.bf16, out.q_gm, s);
 }
 

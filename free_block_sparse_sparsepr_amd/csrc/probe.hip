@@ -31,39 +31,46 @@ __global__ __launch_bounds__(256) void probe_select_kernel(const int8_t* __restr
                                                            double* __restrict__ pw,
                                                            int32_t* __restrict__ radius) {
   __shared__ int alloc[kMaxGroups], start[kMaxGroups], tgt[kMaxProbe];
+  __shared__ int sz[kMaxGroups];
   __shared__ int cent[kMaxFeat];
   __shared__ int lrad[1024];
   __shared__ uint64_t skey[kSortMax];
   const int a = blockIdx.x, kv = blockIdx.y, tid = threadIdx.x;
   const int32_t* qo = qoff + (int64_t)kv * (Gq + 1);
-  if (tid == 0) {
-    int ord[kMaxGroups], cnt = 0;
-    for (int b = 0; b < Gq; ++b) {
-      alloc[b] = 0;
-      if (qo[b + 1] > qo[b]) ord[cnt++] = b;
+  if (tid < kMaxGroups) sz[tid] = tid < Gq ? qo[tid + 1] - qo[tid] : 0;
+  __syncthreads();
+  if (tid < 64) {
+    // The one-at-a-time allocation in closed form: after p complete passes group b holds
+    // min(n_b, p) probes, T(p) = sum_b min(n_b, p); p* is the last p with T(p) <= M, and
+    // the R = M - T(p*) remaining probes go to the first R groups with n_b > p* in the
+    // order (larger group first, smaller index first).
+    const int b = tid, sb = sz[b];
+    int maxs = sb;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) maxs = max(maxs, __shfl_xor(maxs, o));
+    int pstar = 0, tp = 0;
+    for (int p = 1; p <= min(maxs, M); ++p) {
+      int t = min(sb, p);
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) t += __shfl_xor(t, o);
+      if (t > M) break;
+      pstar = p;
+      tp = t;
     }
-    for (int i = 1; i < cnt; ++i) {  // insertion sort by (size desc, index asc)
-      int x = ord[i], j = i - 1;
-      int sx = qo[x + 1] - qo[x];
-      while (j >= 0) {
-        int y = ord[j], sy = qo[y + 1] - qo[y];
-        if (sy > sx || (sy == sx && y < x)) break;
-        ord[j + 1] = y;
-        --j;
-      }
-      ord[j + 1] = x;
+    int rank = 0;
+    for (int c = 0; c < kMaxGroups; ++c) {
+      const int sc = sz[c];
+      rank += (sc > pstar) && (sc > sb || (sc == sb && c < b));
     }
-    int total = 0;
-    bool moved = true;
-    while (total < M && moved) {
-      moved = false;
-      for (int i = 0; i < cnt && total < M; ++i) {
-        int b = ord[i];
-        if (alloc[b] < qo[b + 1] - qo[b]) { ++alloc[b]; ++total; moved = true; }
-      }
+    const int al = min(sb, pstar) + ((sb > pstar && rank < M - tp) ? 1 : 0);
+    int incl = al;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(incl, o);
+      if (b >= o) incl += u;
     }
-    int s = 0;
-    for (int b = 0; b < Gq; ++b) { start[b] = s; s += alloc[b]; }
+    alloc[b] = al;
+    start[b] = incl - al;
   }
   __syncthreads();
   const int ma = alloc[a];

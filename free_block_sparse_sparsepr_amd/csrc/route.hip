@@ -42,38 +42,58 @@ hipError_t ensure_exp_table() {
 
 // One wave per query row (lanes over key groups): coalesced loads of the row's
 // responses, wave max / sum, per-lane fixed-point division, LDS accumulation per block,
-// then 64-bit integer atomics.  Each wave walks 16 rows.  grid (ceil(n / 64), Hq),
+// then 64-bit integer atomics.  Each wave walks kRouteRows rows, with the responses and
+// labels of the next kRoutePrefetch rows in flight and the exponential table staged in
+// LDS, so a row costs no dependent global load.  grid (ceil(n / (4 kRouteRows)), Hq),
 // block 256.  mass [Hkv][Gq][Gk] must be zero on entry.
+constexpr int kRouteRows = 64;
+constexpr int kRoutePrefetch = 8;
+
 __global__ __launch_bounds__(256) void route_mass_kernel(const float* __restrict__ U,
                                                          const int32_t* __restrict__ qlabels,
                                                          const int32_t* __restrict__ koff, int n,
                                                          int g, int Gq, int Gk,
                                                          unsigned long long* __restrict__ mass) {
   __shared__ unsigned long long acc[kMaxGroups * kMaxGroups];
+  __shared__ uint32_t etab[kExpTable];
   const int h = blockIdx.y, kv = h / g;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   for (int i = threadIdx.x; i < Gq * Gk; i += 256) acc[i] = 0ull;
+  for (int i = threadIdx.x; i < kExpTable; i += 256) etab[i] = c_exp_table[i];
   const int nb = lane < Gk ? koff[(int64_t)kv * (Gk + 1) + lane + 1] - koff[(int64_t)kv * (Gk + 1) + lane] : 0;
   __syncthreads();
-  for (int rr = 0; rr < 16; ++rr) {
-    const int i = blockIdx.x * 64 + w * 16 + rr;
-    if (i >= n) break;
-    const int a = qlabels[(int64_t)kv * n + i];
-    int z = INT_MIN;
-    if (lane < Gk) z = (int)fminf(fmaxf(rintf(64.f * U[((int64_t)h * n + i) * Gk + lane]), -1073741824.f), 1073741824.f);
-    int mu = (nb > 0) ? z : INT_MIN;
+  const int r0 = (blockIdx.x * 4 + w) * kRouteRows;
+  const int r1 = min(n, r0 + kRouteRows);
+  const float* Uh = U + (int64_t)h * n * Gk;
+  const int32_t* lab = qlabels + (int64_t)kv * n;
+  for (int i0 = r0; i0 < r1; i0 += kRoutePrefetch) {
+    float u[kRoutePrefetch];
+    int la[kRoutePrefetch];
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) mu = max(mu, __shfl_xor(mu, o));
-    uint64_t e = 0;
-    if (nb > 0) {
-      const int64_t dz = (int64_t)mu - (int64_t)z;
-      const int k = dz > kExpTable - 1 ? kExpTable - 1 : (int)dz;
-      e = (uint64_t)nb * (uint64_t)c_exp_table[k];
+    for (int j = 0; j < kRoutePrefetch; ++j) {
+      const int i = min(i0 + j, r1 - 1);
+      u[j] = lane < Gk ? Uh[(int64_t)i * Gk + lane] : 0.f;
+      la[j] = lab[i];
     }
-    uint64_t tot = e;
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) tot += __shfl_xor(tot, o);
-    if (e) atomicAdd(&acc[a * Gk + lane], (unsigned long long)udiv_exact(e << 20, tot));
+    for (int j = 0; j < kRoutePrefetch; ++j) {
+      if (i0 + j >= r1) break;
+      int z = INT_MIN;
+      if (lane < Gk) z = (int)fminf(fmaxf(rintf(64.f * u[j]), -1073741824.f), 1073741824.f);
+      int mu = (nb > 0) ? z : INT_MIN;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) mu = max(mu, __shfl_xor(mu, o));
+      uint64_t e = 0;
+      if (nb > 0) {
+        const int64_t dz = (int64_t)mu - (int64_t)z;
+        const int k = dz > kExpTable - 1 ? kExpTable - 1 : (int)dz;
+        e = (uint64_t)nb * (uint64_t)etab[k];
+      }
+      uint64_t tot = e;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) tot += __shfl_xor(tot, o);
+      if (e) atomicAdd(&acc[la[j] * Gk + lane], (unsigned long long)udiv_exact(e << 20, tot));
+    }
   }
   __syncthreads();
   for (int idx = threadIdx.x; idx < Gq * Gk; idx += 256) {
@@ -226,7 +246,7 @@ __global__ __launch_bounds__(1024) void route_select_kernel(const unsigned long 
 void launch_route(const Dims& dm, int64_t budget, const sparsepr_partition_t& part, const sparsepr_route_t& out,
                   hipStream_t s) {
   fill_u32(reinterpret_cast<uint32_t*>(out.cell_mass), (size_t)dm.hkv * dm.gq * dm.gk * 2, 0, s);
-  hipLaunchKernelGGL(route_mass_kernel, dim3((unsigned)ceil_div(dm.n, 64), dm.hq), dim3(256), 0, s,
+  hipLaunchKernelGGL(route_mass_kernel, dim3((unsigned)ceil_div(dm.n, 4 * kRouteRows), dm.hq), dim3(256), 0, s,
                      part.responses_u, part.query_labels, part.key_offsets, dm.n, dm.g, dm.gq, dm.gk,
                      reinterpret_cast<unsigned long long*>(out.cell_mass));
   hipLaunchKernelGGL(route_select_kernel, dim3(dm.hkv), dim3(1024), 0, s,

@@ -17,6 +17,7 @@ constexpr int kMaxProbe = 64;
 constexpr int kMaxRank = 32;
 constexpr int kExpTable = 1024;     // route exponential table entries
 constexpr int kProbeChunk = 1024;   // keys per probe-attention work item
+constexpr int kGmChunk = 1024;      // tokens per chunk of the group-major counting sort
 
 __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -83,7 +84,7 @@ void fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t s);
 // Workspace layout shared by the entry points (regions may overlap across entry
 // points because calls on one stream never run concurrently).
 struct Workspace {
-  size_t maxbits, xk, xq, centroids, sums, usum, total_partition;
+  size_t maxbits, xk, xq, centroids, sums, usum, gm_hist, total_partition;
   size_t partials, fitbuf, probe_alloc, total_probe;
   size_t dense_meta, total_dense;
   size_t fused_ogm, total_fused;
