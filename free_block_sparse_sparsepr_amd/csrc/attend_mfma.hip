@@ -32,9 +32,10 @@ constexpr int kXcds = 8;
 // probabilities stay below 2^8 and most tiles skip the rescale entirely.
 constexpr float kStaleMax = 8.f;
 
-template <int D, int BN_ = 32>
+template <int D, int BN_ = 32, int NW_ = 4>
 struct MfmaCfg {
-  static constexpr int BM = 128;            // virtual query rows per block (4 waves x 32)
+  static constexpr int NW = NW_;            // waves per block (32 query rows each)
+  static constexpr int BM = 32 * NW;        // virtual query rows per block
   static constexpr int BN = BN_;            // keys per tile (32 or 64)
   static constexpr int NB = BN / 32;        // 32-key score blocks per tile
   static constexpr int KCH = D / 8;         // 16-byte chunks per K row
@@ -42,8 +43,9 @@ struct MfmaCfg {
   static constexpr int KBYTES = BN * D * 2; // K stage: BN rows, chunk c of row r at slot c ^ kswz(r)
   static constexpr int VBYTES = D * BN * 2; // V^T stage: D rows of BN keys, chunk c of row d at slot c ^ vswz(d)
   static constexpr int STAGE = KBYTES + VBYTES;
-  static constexpr int KIPW = BN * KCH / 256;   // K copy instructions per wave
-  static constexpr int VIPW = D * VCH / 256;
+  static constexpr int KIPW = BN * KCH / (64 * NW);   // K copy instructions per wave
+  static constexpr int VIPW = D * VCH / (64 * NW);
+  static_assert(KIPW >= 1 && VIPW >= 1, "tile too small for the block's copy lanes");
   static constexpr int KSTEPS = D / 16;
   static constexpr int DBLK = D / 32;
   // chunk swizzle of K row r: 16 consecutive rows read at one chunk offset (the 16 lanes
@@ -77,9 +79,9 @@ __device__ __forceinline__ bool next_tile(const AttnArgs& A, int kv, const TileI
 // last tile of the sequence clamps rows beyond n (those keys are masked).
 __device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
-template <int D, int BN>
+template <int D, int BN, int NW>
 struct CopyPlan {
-  using C = MfmaCfg<D, BN>;
+  using C = MfmaCfg<D, BN, NW>;
   uint32_t koff[C::KIPW];   // bytes from the tile's first K row
   uint32_t voff[C::VIPW];   // bytes from the tile's first V^T column
   int krow[C::KIPW];        // K row within the tile
@@ -103,11 +105,11 @@ struct CopyPlan {
   }
 };
 
-template <int D, int BN>
-__device__ __forceinline__ void stage_copy(const CopyPlan<D, BN>& cp, const bf16_t* __restrict__ kb,
+template <int D, int BN, int NW>
+__device__ __forceinline__ void stage_copy(const CopyPlan<D, BN, NW>& cp, const bf16_t* __restrict__ kb,
                                            const bf16_t* __restrict__ vtb, int n, int np, int kt, char* stage,
                                            int wu) {
-  using C = MfmaCfg<D, BN>;
+  using C = MfmaCfg<D, BN, NW>;
   char* vst = stage + C::KBYTES;
   if (kt + BN <= n) {
     const char* kbase = reinterpret_cast<const char*>(kb + (int64_t)kt * D);
@@ -242,7 +244,7 @@ __device__ __forceinline__ void mfma_tile_step(const char* __restrict__ stage, c
 // is applied to both operands), so t^T = A^T O^T (k x q) and then O^T += B^T t^T need no
 // data movement; A^T, B^T (bf16) and c0 are staged in the free LDS stages.  Rows are
 // scattered to token order through the query permutation.
-template <int D, int LDS_BYTES>
+template <int D, int LDS_BYTES, int NT>
 __device__ __forceinline__ void fused_writeback(const AttnArgs& A, int kv, int vrow, bool qvalid, float inv,
                                                 f32x16_t* o, char* lds, int tid, int l32, int hf) {
   constexpr int DBLK = D / 32;
@@ -256,12 +258,12 @@ __device__ __forceinline__ void fused_writeback(const AttnArgs& A, int kv, int v
   const int re = A.r_eff[h];
   const float* Ah = A.fitA + (int64_t)h * D * A.rank;
   const float* Bh = A.fitB + (int64_t)h * A.rank * D;
-  for (int idx = tid; idx < 32 * D; idx += 256) {
+  for (int idx = tid; idx < 32 * D; idx += NT) {
     const int k = idx / D, d = idx % D;
     At[k * AROW + d] = f32_to_bf16(k < re ? Ah[d * A.rank + k] : 0.f);
     Bt[d * BROW + k] = f32_to_bf16(k < re ? Bh[k * D + d] : 0.f);
   }
-  for (int d = tid; d < D; d += 256) c0s[d] = A.fitc0[(int64_t)h * D + d];
+  for (int d = tid; d < D; d += NT) c0s[d] = A.fitc0[(int64_t)h * D + d];
   __syncthreads();
   // normalise and pack O (bf16) as the B operand over d
   f32x16_t t;
@@ -318,10 +320,26 @@ __device__ __forceinline__ void fused_writeback(const AttnArgs& A, int kv, int v
   }
 }
 
+constexpr int kAttnWaves = 8;    // waves per block of the main attention kernel
+constexpr int kAttnStages = 4;   // K/V tile stages in LDS; tile j + 3 is copied while tile j runs
+
+// Waits until at most `later` tiles' copies of this wave are still in flight (each tile is
+// C::KIPW + C::VIPW direct-to-LDS loads, which complete in order for the counter).
+template <int PER_TILE>
+__device__ __forceinline__ void wait_tiles_in_flight(int later) {
+  static_assert(2 * PER_TILE <= 15, "vmcnt immediate");
+  // s_waitcnt immediate: vmcnt in bits 3:0 (and 15:14), expcnt 6:4 and lgkmcnt 11:8 left at
+  // their maxima
+  if (later >= 2) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * PER_TILE));
+  else if (later == 1) __builtin_amdgcn_s_waitcnt(0x0F70 | PER_TILE);
+  else __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
 template <int D, int BN, typename OutT>
-__global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs A) {
-  using C = MfmaCfg<D, BN>;
-  __shared__ __attribute__((aligned(1024))) char stages[2][C::STAGE];
+__global__ __launch_bounds__(64 * kAttnWaves, 1) void attn_mfma_kernel(AttnArgs A) {
+  using C = MfmaCfg<D, BN, kAttnWaves>;
+  constexpr int PER_TILE = C::KIPW + C::VIPW;
+  __shared__ __attribute__((aligned(1024))) char stages[kAttnStages][C::STAGE];
 
   // XCD-aware remap of the linear block id (consecutive logical tiles on one XCD)
   const int total = gridDim.x;
@@ -337,7 +355,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs A) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
   const int wu = wave_uniform(w);
-  const CopyPlan<D, BN> cp(wu, lane, A.v_np);
+  const CopyPlan<D, BN, kAttnWaves> cp(wu, lane, A.v_np);
   const bf16_t* qb = static_cast<const bf16_t*>(A.q);
   const bf16_t* kb = static_cast<const bf16_t*>(A.k) + (int64_t)kv * A.kv_skv;
   const bf16_t* vtb = static_cast<const bf16_t*>(A.v) + (int64_t)kv * A.v_skv;
@@ -363,31 +381,45 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs A) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
 
+  // Tile iterators: (ci, k0, k1, kt) is the tile being computed; (fci, fk0, fk1, fkt) the
+  // copy frontier, kAttnStages - 1 tiles ahead.  Tile j lives in stage j % kAttnStages.
   int ci = ti.kbeg < 0 ? 0 : ti.kbeg, k0 = 0, k1 = 0, kt = 0;
   bool valid = next_run(A, kv, ti, ci, k0, k1);
-  if (valid) {
-    kt = k0 & ~15;
-    stage_copy<D, BN>(cp, kb, vtb, A.n, A.v_np, kt, stages[0], wu);
+  if (valid) kt = k0 & ~15;
+  int fci = ci, fk0 = k0, fk1 = k1, fkt = kt;
+  bool fvalid = valid;
+  int nfront = 0;           // copied tiles not yet computed
+  int fst = 0;              // stage of the frontier tile
+  for (int i = 0; i < kAttnStages - 1 && fvalid; ++i) {
+    stage_copy<D, BN, kAttnWaves>(cp, kb, vtb, A.n, A.v_np, fkt, stages[fst], wu);
+    ++nfront;
+    fst = fst == kAttnStages - 1 ? 0 : fst + 1;
+    fvalid = next_tile(A, kv, ti, C::BN, fci, fk0, fk1, fkt);
   }
-  __builtin_amdgcn_s_waitcnt(0);
+  wait_tiles_in_flight<PER_TILE>(nfront - 1);
   __syncthreads();
   int cur = 0;
   while (valid) {
-    int nci = ci, nk0 = k0, nk1 = k1, nkt = kt;
-    const bool nvalid = next_tile(A, kv, ti, C::BN, nci, nk0, nk1, nkt);
-    if (nvalid) stage_copy<D, BN>(cp, kb, vtb, A.n, A.v_np, nkt, stages[cur ^ 1], wu);
+    if (fvalid) {   // the stage of tile j + kAttnStages - 1 was last read in tile j - 1
+      stage_copy<D, BN, kAttnWaves>(cp, kb, vtb, A.n, A.v_np, fkt, stages[fst], wu);
+      ++nfront;
+      fst = fst == kAttnStages - 1 ? 0 : fst + 1;
+      fvalid = next_tile(A, kv, ti, C::BN, fci, fk0, fk1, fkt);
+    }
     const int lo = max(k0 - kt, 0), hi = min(k1 - kt, BN);
     mfma_tile_step<D, BN, false>(stages[cur], qreg, lo, hi, c2, nullptr, 0ull, m_i, l_i, o, l32, hf);
-    __builtin_amdgcn_s_waitcnt(0);
+    --nfront;
+    valid = next_tile(A, kv, ti, C::BN, ci, k0, k1, kt);
+    wait_tiles_in_flight<PER_TILE>(nfront - 1);   // tile j + 1 has landed
     __syncthreads();
-    cur ^= 1;
-    ci = nci; k0 = nk0; k1 = nk1; kt = nkt; valid = nvalid;
+    cur = cur == kAttnStages - 1 ? 0 : cur + 1;
   }
 
   const float l_tot = l_i + __shfl_xor(l_i, 32);
   const float inv = 1.f / l_tot;
   if (A.fitA != nullptr) {
-    fused_writeback<D, C::STAGE * 2>(A, kv, vrow, qvalid, inv, o, &stages[0][0], tid, l32, hf);
+    fused_writeback<D, C::STAGE * kAttnStages, 64 * kAttnWaves>(A, kv, vrow, qvalid, inv, o, &stages[0][0], tid,
+                                                                   l32, hf);
     return;
   }
   // epilogue: O / l, LSE; lane writes query l32's d = 32 db + 8 j + 4 hf + 0..3
@@ -446,7 +478,7 @@ __global__ __launch_bounds__(256, 2) void probe_attn_mfma_kernel(const bf16_t* _
   const int k0 = ch * chunk, k1 = min(n, k0 + chunk);
   const int np = (int)vt_pad(n);
   const int wu = wave_uniform(w);
-  const CopyPlan<D, 32> cp(wu, lane, np);
+  const CopyPlan<D, 32, 4> cp(wu, lane, np);
   for (int b = tid; b <= Gk; b += 256) ko[b] = koff[(int64_t)kv * (Gk + 1) + b];
   const bool rvalid = row < M;
   const uint64_t rowmask = rvalid ? kept_mask[(int64_t)kv * Gq + pgrp[kv * M + row]] : 0ull;
@@ -476,7 +508,7 @@ __global__ __launch_bounds__(256, 2) void probe_attn_mfma_kernel(const bf16_t* _
   };
   int kt = k0;
   if (kt < k1) {
-    stage_copy<D, 32>(cp, kb, vtb, n, np, kt, stages[0], wu);
+    stage_copy<D, 32, 4>(cp, kb, vtb, n, np, kt, stages[0], wu);
     if (tid < C::BN) klab[0][tid] = (uint8_t)(kt + tid < k1 ? label_of(kt + tid) : 0);
   }
   __builtin_amdgcn_s_waitcnt(0);
@@ -485,7 +517,7 @@ __global__ __launch_bounds__(256, 2) void probe_attn_mfma_kernel(const bf16_t* _
   while (kt < k1) {
     const int nt = kt + C::BN;
     if (nt < k1) {
-      stage_copy<D, 32>(cp, kb, vtb, n, np, nt, stages[cur ^ 1], wu);
+      stage_copy<D, 32, 4>(cp, kb, vtb, n, np, nt, stages[cur ^ 1], wu);
       if (tid < C::BN) klab[cur ^ 1][tid] = (uint8_t)(nt + tid < k1 ? label_of(nt + tid) : 0);
     }
     const int hi = min(k1 - kt, C::BN);
@@ -536,11 +568,11 @@ constexpr int kAttnBN = 64;   // keys per tile of the main attention kernel
 
 template <int D, typename OutT>
 void launch_mfma_typed(AttnArgs a, int hkv, hipStream_t s) {
-  a.tiles_per_head = (int)ceil_div((int64_t)a.n * a.g, MfmaCfg<D, kAttnBN>::BM) + (a.qoff ? a.gq : 0);
+  a.tiles_per_head = (int)ceil_div((int64_t)a.n * a.g, MfmaCfg<D, kAttnBN, kAttnWaves>::BM) + (a.qoff ? a.gq : 0);
   a.n_heads_kv = hkv;
   int64_t total = (int64_t)a.tiles_per_head * hkv;
   total = ceil_div(total, kXcds) * kXcds;
-  hipLaunchKernelGGL((attn_mfma_kernel<D, kAttnBN, OutT>), dim3((unsigned)total), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((attn_mfma_kernel<D, kAttnBN, OutT>), dim3((unsigned)total), dim3(64 * kAttnWaves), 0, s, a);
 }
 
 void launch_attention_mfma(const Dims& dm, AttnArgs a, bool out_is_input_dtype, hipStream_t s) {
