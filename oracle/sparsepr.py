@@ -564,6 +564,52 @@ def correct_rows(o_rows, fit: Fit):
 
 
 # --------------------------------------------------------------------------------------
+# ablations (PSRR, ablation paragraph): hard drop, ridge without the projection, and
+# probe rows drawn uniformly over space-time or by the caller instead of stratified
+# radially.  The page names the variants and reports their ordering; how each is built
+# is a reading.
+# --------------------------------------------------------------------------------------
+def hard_drop_rows(q, k, v, scale, q_labels, k_labels, kept, rows=None):
+    """Hard drop: the output is the renormalised sparse attention itself (no probes, no
+    fit, no correction)."""
+    o, _ = sparse_attention(q, k, v, scale, q_labels, k_labels, kept, rows=rows)
+    return o
+
+
+def uniform_probes(n, q_labels, n_probe):
+    """Uniform spatiotemporal probes.  Reading: the tokens floor((2k+1) N / (2M)), k < M,
+    of the raster (t, h, w) order, i.e. evenly spaced over the clip; each stands for N / M
+    tokens, so every mean-one weight is 1; a probe's group is its query label (it selects
+    the kept cells of the probe's sparse row)."""
+    k = np.arange(n_probe, dtype=np.int64)
+    toks = (2 * k + 1) * n // (2 * n_probe)
+    return given_probes(toks, q_labels)
+
+
+def given_probes(tokens, q_labels):
+    """Probe rows chosen by the caller (e.g. drawn uniformly at random with a seeded
+    generator): weight 1 each, group = query label."""
+    toks = np.asarray(tokens, dtype=np.int64)
+    grps = np.asarray(q_labels)[toks].astype(np.int64)
+    return Probes(toks, grps, np.ones(toks.size), None)
+
+
+def ridge_only_fit(q, k, v, scale, probes: Probes, q_labels, k_labels, kept, p: Params):
+    """Ridge without the rank-r projection: the correction of a row is
+    ybar + (o - xbar) W with the full weighted ridge map W = Xt^T Z,
+    Z = (Xt Xt^T + lambda I_M)^{-1} Yt.  Factored through the M probes as A = Xt^T [d, M],
+    B = Z [M, d] (so A B = W) and c0 = ybar - xbar A B, the same form the projected fit
+    is applied in."""
+    od, os_, R, _, _ = probe_rows(q, k, v, scale, probes.tokens, q_labels, k_labels, kept)
+    xbar, ybar, Xt, Yt = weighted_center(os_, R, probes.weights)
+    Z = np.linalg.solve(Xt @ Xt.T + p.lam * np.eye(Xt.shape[0]), Yt)
+    A = Xt.T
+    B = Z
+    c0 = ybar - xbar @ A @ B
+    return Fit(A, B, c0, A @ B, xbar, ybar, None, np.zeros(p.rank + 1), od, os_, R)
+
+
+# --------------------------------------------------------------------------------------
 # whole call
 # --------------------------------------------------------------------------------------
 @dataclass

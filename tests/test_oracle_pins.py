@@ -480,3 +480,67 @@ def test_fit_and_apply_recover_a_planted_affine_residual():
                 o_s[toks] + R_all[toks], o_s[toks], R_all[toks])
     out = O.apply_correction(o_s, fit, toks)
     np.testing.assert_allclose(out, o_s + R_all, atol=1e-5)
+
+
+# ----------------------------------------------------------------------------- ablations
+def test_hard_drop_is_the_renormalised_sparse_output_and_dense_on_full_route():
+    q, k, v = rand(40, 8), rand(40, 8), rand(40, 4)
+    ql, kl = _tiny_partition()
+    kept = np.array([[1, 0, 1, 0], [0, 1, 0, 0], [1, 1, 1, 0]], bool)
+    p = softmax(q @ k.T * 0.5, axis=1)
+    got = O.hard_drop_rows(q, k, v, 0.5, ql, kl, kept)
+    for i in range(40):
+        keep = kept[ql[i]][kl]
+        np.testing.assert_allclose(got[i], p[i, keep] @ v[keep] / p[i, keep].sum(), atol=1e-13)
+    full = O.hard_drop_rows(q, k, v, 0.5, ql, kl, np.ones((3, 4), bool))
+    np.testing.assert_allclose(full, softmax(q @ k.T * 0.5, axis=1) @ v, atol=1e-13)
+
+
+@pytest.mark.parametrize("n,m", [(118800, 64), (1000, 64), (64, 64), (100, 7)])
+def test_uniform_probes_are_evenly_spaced_and_unit_weight(n, m):
+    labels = RNG.integers(0, 5, n)
+    pr = O.uniform_probes(n, labels, m)
+    t = pr.tokens
+    assert t.size == m and np.all(np.diff(t) > 0) and t[0] >= 0 and t[-1] < n
+    gaps = np.diff(t)
+    assert gaps.min() >= n // m - 1 and gaps.max() <= -(-n // m) + 1
+    # symmetric about the middle of the clip: t_k + t_{M-1-k} is n - 1 or n - 2 ... n
+    s = t + t[::-1]
+    assert np.all(np.abs(s - (n - 1)) <= 1)
+    # the first probe sits half a spacing in
+    assert abs(t[0] - n / (2 * m)) <= 1
+    np.testing.assert_array_equal(pr.groups, labels[t])
+    np.testing.assert_array_equal(pr.weights, np.ones(m))
+
+
+def test_ridge_only_factors_the_weighted_ridge_map():
+    """A B of the ridge-only fit is the weighted ridge map that scikit-learn pins above;
+    the correction ybar + (o - xbar) W is written as o A B + c0."""
+    n, d, M = 120, 12, 16
+    q, k, v = rand(n, d), rand(n, d), rand(n, d)
+    ql, kl = RNG.integers(0, 3, n), RNG.integers(0, 4, n)
+    kept = np.array([[1, 0, 1, 0], [0, 1, 0, 1], [1, 1, 0, 0]], bool)
+    toks = np.sort(RNG.choice(n, M, replace=False))
+    pr = O.given_probes(toks, ql)
+    p = O.Params(groups_q=3, groups_k=4, rho_exec=0.5, n_probe=M, rank=4, lam=0.1)
+    fit = O.ridge_only_fit(q, k, v, 0.3, pr, ql, kl, kept, p)
+    W, xbar, ybar, _, _ = O.ridge_fit(fit.o_sparse, fit.R, pr.weights, 0.1)
+    np.testing.assert_allclose(fit.A @ fit.B, W, atol=1e-12)
+    o = rand(5, d)
+    np.testing.assert_allclose(O.correct_rows(o, fit), o + ybar + (o - xbar) @ W, atol=1e-12)
+
+
+def test_ridge_only_with_vanishing_lambda_interpolates_the_probe_residuals():
+    """With M < d and lambda -> 0 the unprojected ridge map interpolates: every probe row's
+    corrected sparse output equals its exact dense output (least squares with more unknowns
+    than equations); the rank-r projected fit does not when R has rank > r."""
+    n, d, M = 200, 24, 12
+    q, k, v = rand(n, d), rand(n, d), rand(n, d)
+    ql, kl = RNG.integers(0, 3, n), RNG.integers(0, 4, n)
+    kept = np.array([[1, 0, 0, 0], [0, 1, 0, 0], [0, 0, 1, 0]], bool)
+    pr = O.given_probes(np.sort(RNG.choice(n, M, replace=False)), ql)
+    p = O.Params(groups_q=3, groups_k=4, rho_exec=0.5, n_probe=M, rank=2, lam=1e-9)
+    fit = O.ridge_only_fit(q, k, v, 0.3, pr, ql, kl, kept, p)
+    np.testing.assert_allclose(O.correct_rows(fit.o_sparse, fit), fit.o_dense, atol=1e-6)
+    proj = O.probe_fit(q, k, v, 0.3, pr, ql, kl, kept, p)
+    assert np.abs(O.correct_rows(proj.o_sparse, proj) - proj.o_dense).max() > 1e-3
