@@ -11,6 +11,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libsparsepr.so")
 
 BF16, FP32 = 0, 1
+ABLATE_NONE, ABLATE_HARD_DROP, ABLATE_RIDGE_ONLY = 0, 1, 2
+PROBES_RADIAL, PROBES_UNIFORM, PROBES_GIVEN = 0, 1, 2
 STATUS = {0: "ok", -1: "null pointer", -2: "shape", -3: "dtype", -4: "alignment",
           -5: "workspace", -6: "parameter", -7: "HIP failure"}
 
@@ -21,7 +23,8 @@ class Params(ctypes.Structure):
                 ("groups_k", ctypes.c_int32), ("r_k", ctypes.c_int32), ("r_q", ctypes.c_int32),
                 ("n_probe", ctypes.c_int32), ("rank", ctypes.c_int32), ("lam", ctypes.c_float),
                 ("rho_exec", ctypes.c_float), ("block", ctypes.c_int32),
-                ("kmeans_iters", ctypes.c_int32), ("softmax_scale", ctypes.c_float)]
+                ("kmeans_iters", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+                ("ablation", ctypes.c_int32), ("probe_mode", ctypes.c_int32)]
 
 
 def _ptr_struct(name, names):

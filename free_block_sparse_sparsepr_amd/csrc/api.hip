@@ -20,6 +20,9 @@ Dims dims_of(const sparsepr_params& p) {
   d.m = p.n_probe;
   d.r = p.rank;
   d.iters = p.kmeans_iters;
+  d.ablation = p.ablation;
+  d.probe_mode = p.probe_mode;
+  d.rc = p.ablation == SPARSEPR_ABLATE_RIDGE_ONLY ? p.n_probe : p.rank;
   d.scale = p.softmax_scale > 0.f ? p.softmax_scale : (float)(1.0 / std::sqrt((double)p.d));
   d.lambda = p.lambda;
   d.bf16 = p.dtype == SPARSEPR_BF16;
@@ -82,6 +85,12 @@ static sparsepr_status check_params(const sparsepr_params* p) {
   if (p->kmeans_iters < 0 || p->kmeans_iters > 64) return SPARSEPR_ERR_PARAM;
   if (p->block != 64) return SPARSEPR_ERR_PARAM;
   if (!(p->softmax_scale >= 0.f) || !std::isfinite(p->softmax_scale)) return SPARSEPR_ERR_PARAM;
+  if (p->ablation != SPARSEPR_ABLATE_NONE && p->ablation != SPARSEPR_ABLATE_HARD_DROP &&
+      p->ablation != SPARSEPR_ABLATE_RIDGE_ONLY)
+    return SPARSEPR_ERR_PARAM;
+  if (p->probe_mode != SPARSEPR_PROBES_RADIAL && p->probe_mode != SPARSEPR_PROBES_UNIFORM &&
+      p->probe_mode != SPARSEPR_PROBES_GIVEN)
+    return SPARSEPR_ERR_PARAM;
   return SPARSEPR_OK;
 }
 
@@ -232,11 +241,11 @@ sparsepr_status sparsepr_attend_apply(const sparsepr_params* params, const spars
     a.fitB = fit->B;
     a.fitc0 = fit->c0;
     a.r_eff = fit->r_eff;
-    a.rank = dm.r;
+    a.rank = dm.rc;
     a.qperm = part->query_perm;
     a.out_tok = o;
     launch_attention(dm, a, false, (hipStream_t)stream);
-    launch_probe_writeback(dm, *fit, o, (hipStream_t)stream);
+    if (dm.ablation != SPARSEPR_ABLATE_HARD_DROP) launch_probe_writeback(dm, *fit, o, (hipStream_t)stream);
   } else {
     float* ogm = reinterpret_cast<float*>(static_cast<char*>(workspace) + wp.fused_ogm);
     a.o = ogm;
@@ -253,7 +262,7 @@ sparsepr_status sparsepr_probe_fit(const sparsepr_params* params, const void* q,
   if (st != SPARSEPR_OK) return st;
   if (!q || !part || !route || !out) return SPARSEPR_ERR_NULL;
   if (!part->query_features || !part->query_centroids || !part->query_perm || !part->query_offsets ||
-      !part->key_offsets || !part->k_gm || !part->v_gm || !route->kept_mask)
+      !part->query_labels || !part->key_offsets || !part->k_gm || !part->v_gm || !route->kept_mask)
     return SPARSEPR_ERR_NULL;
   if (!out->probe_tokens || !out->probe_groups || !out->probe_weights || !out->o_dense || !out->o_sparse ||
       !out->A || !out->B || !out->c0 || !out->r_eff || !out->eig)

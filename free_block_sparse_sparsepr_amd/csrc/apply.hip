@@ -11,24 +11,27 @@ namespace sp {
 
 // One block = 64 group-major rows of one query head.  The rows are staged in LDS, the
 // rank-r coordinates T = O A are a 64 x r product, then o + c0 + T B is written to the
-// token-order rows (4 threads per row, 16-byte stores).  grid (ceil(n / 64), Hq), block 256.
-template <typename OutT, int D>
+// token-order rows (4 threads per row, 16-byte stores).  RC bounds the correction rank
+// (32, or 64 for the unprojected ridge); `rank` is the leading dimension of A and B.
+// grid (ceil(n / 64), Hq), block 256.
+template <typename OutT, int D, int RC>
 __global__ __launch_bounds__(256) void apply_kernel(const float* __restrict__ o_gm, const int32_t* __restrict__ qperm,
                                                     const float* __restrict__ A, const float* __restrict__ B,
                                                     const float* __restrict__ c0, const int32_t* __restrict__ r_eff,
                                                     int n, int g, int rank, OutT* __restrict__ out) {
   constexpr int R = 64;
+  constexpr int TPT = RC / 4;   // rank coordinates per thread
   __shared__ float Os[R][D + 4];
-  __shared__ float As[D][kMaxRank];
-  __shared__ float Bs[kMaxRank][D];
-  __shared__ float Ts[R][kMaxRank + 1];
+  __shared__ float As[D][RC];
+  __shared__ float Bs[RC][D];
+  __shared__ float Ts[R][RC + 1];
   __shared__ float cs[D];
   const int h = blockIdx.y, kv = h / g, j = h % g;
   const int tid = threadIdx.x;
   const int p0 = blockIdx.x * R;
-  const int re = r_eff[h];
-  for (int idx = tid; idx < D * kMaxRank; idx += 256) {
-    const int c = idx / kMaxRank, k = idx % kMaxRank;
+  const int re = min(r_eff[h], min(rank, RC));
+  for (int idx = tid; idx < D * RC; idx += 256) {
+    const int c = idx / RC, k = idx % RC;
     As[c][k] = k < re ? A[((int64_t)h * D + c) * rank + k] : 0.f;
     const int kb = idx / D, cb = idx % D;
     Bs[kb][cb] = kb < re ? B[((int64_t)h * rank + kb) * D + cb] : 0.f;
@@ -44,16 +47,16 @@ __global__ __launch_bounds__(256) void apply_kernel(const float* __restrict__ o_
   __syncthreads();
   const int r = tid >> 2, q4 = tid & 3;
   {
-    float t[8];
+    float t[TPT];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) t[i] = 0.f;
+    for (int i = 0; i < TPT; ++i) t[i] = 0.f;
     for (int c = 0; c < D; ++c) {
       const float x = Os[r][c];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) t[i] = fmaf(x, As[c][8 * q4 + i], t[i]);
+      for (int i = 0; i < TPT; ++i) t[i] = fmaf(x, As[c][TPT * q4 + i], t[i]);
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) Ts[r][8 * q4 + i] = t[i];
+    for (int i = 0; i < TPT; ++i) Ts[r][TPT * q4 + i] = t[i];
   }
   __syncthreads();
   const int p = p0 + r;
@@ -100,10 +103,16 @@ __global__ void probe_writeback_kernel(const float* __restrict__ o_dense, const 
 template <typename OutT, int D>
 static void apply_typed(const Dims& dm, const float* o_gm, const sparsepr_partition_t& part, const sparsepr_fit_t& fit,
                         OutT* o, hipStream_t s) {
-  hipLaunchKernelGGL((apply_kernel<OutT, D>), dim3((unsigned)ceil_div(dm.n, 64), dm.hq), dim3(256), 0, s, o_gm,
-                     part.query_perm, fit.A, fit.B, fit.c0, fit.r_eff, dm.n, dm.g, dm.r, o);
-  hipLaunchKernelGGL(probe_writeback_kernel<OutT>, dim3(dm.hq), dim3(256), 0, s, fit.o_dense, fit.probe_tokens,
-                     dm.n, dm.g, dm.m, D, o);
+  const dim3 grid((unsigned)ceil_div(dm.n, 64), dm.hq);
+  if (dm.rc <= kMaxRank)
+    hipLaunchKernelGGL((apply_kernel<OutT, D, kMaxRank>), grid, dim3(256), 0, s, o_gm, part.query_perm, fit.A, fit.B,
+                       fit.c0, fit.r_eff, dm.n, dm.g, dm.rc, o);
+  else
+    hipLaunchKernelGGL((apply_kernel<OutT, D, kMaxCorrRank>), grid, dim3(256), 0, s, o_gm, part.query_perm, fit.A,
+                       fit.B, fit.c0, fit.r_eff, dm.n, dm.g, dm.rc, o);
+  if (dm.ablation != SPARSEPR_ABLATE_HARD_DROP)
+    hipLaunchKernelGGL(probe_writeback_kernel<OutT>, dim3(dm.hq), dim3(256), 0, s, fit.o_dense, fit.probe_tokens,
+                       dm.n, dm.g, dm.m, D, o);
 }
 
 void launch_probe_writeback(const Dims& dm, const sparsepr_fit_t& fit, void* o, hipStream_t s) {

@@ -248,27 +248,30 @@ template <int D, int LDS_BYTES, int NT>
 __device__ __forceinline__ void fused_writeback(const AttnArgs& A, int kv, int vrow, bool qvalid, float inv,
                                                 f32x16_t* o, char* lds, int tid, int l32, int hf) {
   constexpr int DBLK = D / 32;
-  constexpr int AROW = D + 8;      // At[k][d] bf16, padded rows (conflict-free 16-byte reads)
-  constexpr int BROW = 32 + 4;     // Bt[d][k] bf16, padded rows (conflict-free 8-byte reads)
-  static_assert((32 * AROW + D * BROW) * 2 + D * 4 <= LDS_BYTES, "fused write-back staging");
+  constexpr int RCM = kMaxCorrRank;  // up to 64 correction directions (two 32-row blocks of t)
+  constexpr int AROW = D + 8;        // At[k][d] bf16, padded rows (conflict-free 16-byte reads)
+  constexpr int BROW = RCM + 4;      // Bt[d][k] bf16, padded rows (conflict-free 8-byte reads)
+  static_assert((RCM * AROW + D * BROW) * 2 + D * 4 <= LDS_BYTES, "fused write-back staging");
   const int h = kv;   // one query head per KV head
   bf16_t* At = reinterpret_cast<bf16_t*>(lds);
-  bf16_t* Bt = At + 32 * AROW;
+  bf16_t* Bt = At + RCM * AROW;
   float* c0s = reinterpret_cast<float*>(Bt + D * BROW);
-  const int re = A.r_eff[h];
+  const int re = min(A.r_eff[h], min(A.rank, RCM));
   const float* Ah = A.fitA + (int64_t)h * D * A.rank;
   const float* Bh = A.fitB + (int64_t)h * A.rank * D;
-  for (int idx = tid; idx < 32 * D; idx += NT) {
+  for (int idx = tid; idx < RCM * D; idx += NT) {
     const int k = idx / D, d = idx % D;
     At[k * AROW + d] = f32_to_bf16(k < re ? Ah[d * A.rank + k] : 0.f);
     Bt[d * BROW + k] = f32_to_bf16(k < re ? Bh[k * D + d] : 0.f);
   }
   for (int d = tid; d < D; d += NT) c0s[d] = A.fitc0[(int64_t)h * D + d];
   __syncthreads();
-  // normalise and pack O (bf16) as the B operand over d
-  f32x16_t t;
+  // normalise and pack O (bf16) as the B operand over d; t^T = A^T O^T in one or two 32-row
+  // blocks of correction directions
+  const bool two = re > 32;
+  f32x16_t t[2];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) t[r] = 0.f;
+  for (int r = 0; r < 16; ++r) { t[0][r] = 0.f; t[1][r] = 0.f; }
 #pragma unroll
   for (int db = 0; db < DBLK; ++db) {
 #pragma unroll
@@ -278,24 +281,32 @@ __device__ __forceinline__ void fused_writeback(const AttnArgs& A, int kv, int v
       bf16x8_t ob;
 #pragma unroll
       for (int e = 0; e < 8; ++e) ob[e] = (__bf16)o[db][8 * s2 + e];
-      const bf16_t* ar = At + l32 * AROW + 32 * db + 16 * s2 + 4 * hf;
-      const uint2 lo8 = *reinterpret_cast<const uint2*>(ar);
-      const uint2 hi8 = *reinterpret_cast<const uint2*>(ar + 8);
-      const uint4 av = make_uint4(lo8.x, lo8.y, hi8.x, hi8.y);
-      t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av), ob, t, 0, 0, 0);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        if (kb == 1 && !two) break;
+        const bf16_t* ar = At + (32 * kb + l32) * AROW + 32 * db + 16 * s2 + 4 * hf;
+        const uint2 lo8 = *reinterpret_cast<const uint2*>(ar);
+        const uint2 hi8 = *reinterpret_cast<const uint2*>(ar + 8);
+        const uint4 av = make_uint4(lo8.x, lo8.y, hi8.x, hi8.y);
+        t[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av), ob, t[kb], 0, 0, 0);
+      }
     }
   }
   // t^T[k][q] in the accumulator layout is the B operand over k of O^T += B^T t^T
-  bf16x8_t tb[2];
+  bf16x8_t tb[4];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    tb[0][e] = (__bf16)t[e];
-    tb[1][e] = (__bf16)t[8 + e];
+    tb[0][e] = (__bf16)t[0][e];
+    tb[1][e] = (__bf16)t[0][8 + e];
+    tb[2][e] = (__bf16)t[1][e];
+    tb[3][e] = (__bf16)t[1][8 + e];
   }
-  const int ksteps = re > 16 ? 2 : 1;
+  const int ksteps = (re + 15) / 16;
 #pragma unroll
   for (int db = 0; db < DBLK; ++db) {
-    for (int s2 = 0; s2 < ksteps; ++s2) {
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2) {
+      if (s2 >= ksteps) break;
       const bf16_t* br = Bt + (32 * db + l32) * BROW + 16 * s2 + 4 * hf;
       const uint2 lo8 = *reinterpret_cast<const uint2*>(br);
       const uint2 hi8 = *reinterpret_cast<const uint2*>(br + 8);

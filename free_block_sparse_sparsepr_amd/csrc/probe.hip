@@ -16,6 +16,26 @@ namespace sp {
 constexpr int kSortMax = 8192;   // groups up to this size are sorted in LDS
 
 // ---------------------------------------------------------------------------------------
+// Probe rows for the ablations (PSRR, ablation paragraph): uniform over the raster order
+// (tokens floor((2k+1) n / (2M))) or the caller's tokens in ptok (clamped into [0, n));
+// weight 1, group = the token's query label.  grid Hkv, block 64.
+// ---------------------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void probe_select_plain_kernel(const int32_t* __restrict__ qlabels, int n, int M,
+                                                                int uniform, int32_t* __restrict__ ptok,
+                                                                int32_t* __restrict__ pgrp,
+                                                                double* __restrict__ pw) {
+  const int kv = blockIdx.x;
+  for (int k = threadIdx.x; k < M; k += 64) {
+    int tok;
+    if (uniform) tok = (int)(((int64_t)(2 * k + 1) * n) / (2 * M));
+    else tok = min(max(ptok[kv * M + k], 0), n - 1);
+    ptok[kv * M + k] = tok;
+    pgrp[kv * M + k] = qlabels[(int64_t)kv * n + tok];
+    pw[kv * M + k] = 1.0;
+  }
+}
+
+// ---------------------------------------------------------------------------------------
 // Probe selection.  grid (Gq, Hkv), block 256.
 // Allocation: one probe at a time over the non-empty groups in the order (larger group
 // first, smaller index first), skipping full groups.  Within group a the m_a probes are
@@ -335,10 +355,13 @@ __global__ __launch_bounds__(D) void probe_merge_kernel(const float* __restrict_
   X[kMaxProbe * D + r * D + c] = res[0] - res[1];
 }
 
+// ridge_only: write the unprojected ridge map as A = Xt^T [d, M], B = Z [M, d] (leading
+// dimension M) and skip the subspace (PSRR, ablation paragraph).
 template <int D>
 __global__ __launch_bounds__(256) void probe_fit_kernel(const float* __restrict__ partials, int nch,
                                                         const double* __restrict__ pw, int g, int M,
-                                                        int rank, double lam, double* __restrict__ fbuf,
+                                                        int rank, int ridge_only, double lam,
+                                                        double* __restrict__ fbuf,
                                                         float* __restrict__ o_dense,
                                                         float* __restrict__ o_sparse, float* __restrict__ Aout,
                                                         float* __restrict__ Bout, float* __restrict__ c0out,
@@ -410,6 +433,29 @@ __global__ __launch_bounds__(256) void probe_fit_kernel(const float* __restrict_
     }
   }
   __syncthreads();
+  if (ridge_only) {
+    // xa[k] = xbar . Xt[k]; c0 = ybar - xa Z; A = Xt^T, B = Z (leading dimension M)
+    double* xam = &Vm[0][0];
+    for (int k = tid; k < M; k += 256) {
+      double acc = 0.0;
+      for (int c = 0; c < D; ++c) acc += xbar[c] * X[k * D + c];
+      xam[k] = acc;
+    }
+    __syncthreads();
+    for (int idx = tid; idx < D * M; idx += 256) {
+      const int c = idx / M, k = idx % M;
+      Aout[(int64_t)h * D * M + idx] = (float)X[k * D + c];
+      Bout[(int64_t)h * M * D + (int64_t)k * D + c] = (float)Z[k * D + c];
+    }
+    for (int c = tid; c < D; c += 256) {
+      double acc = ybar[c];
+      for (int k = 0; k < M; ++k) acc -= xam[k] * Z[k * D + c];
+      c0out[(int64_t)h * D + c] = (float)acc;
+    }
+    for (int k = tid; k <= rank; k += 256) eig_out[(int64_t)h * (rank + 1) + k] = 0.f;
+    if (tid == 0) r_eff_out[h] = M;
+    return;
+  }
   // 6. G = Yt Yt^T (zero-padded to 64 x 64), V = I
   for (int idx = tid; idx < MM * MM; idx += 256) {
     const int i = idx / MM, j = idx % MM;
@@ -553,9 +599,29 @@ void launch_probe_fit(const Dims& dm, const Workspace& wp, const void* q, const 
   int32_t* radius = reinterpret_cast<int32_t*>(ws + wp.probe_alloc);
   float* partials = reinterpret_cast<float*>(ws + wp.partials);
   double* fbuf = reinterpret_cast<double*>(ws + wp.fitbuf);
-  hipLaunchKernelGGL(probe_select_kernel, dim3(dm.gq, dm.hkv), dim3(256), 0, s, part.query_features,
-                     part.query_centroids, part.query_perm, part.query_offsets, dm.n, dm.gq, dm.gk, dm.m,
-                     out.probe_tokens, out.probe_groups, out.probe_weights, radius);
+  if (dm.ablation == SPARSEPR_ABLATE_HARD_DROP) {
+    // empty fit: nothing is reconstructed and no probe row is written back
+    const size_t hq = (size_t)dm.hq, d = (size_t)dm.d;
+    fill_u32(reinterpret_cast<uint32_t*>(out.probe_tokens), (size_t)dm.hkv * dm.m, 0xffffffffu, s);
+    fill_u32(reinterpret_cast<uint32_t*>(out.probe_groups), (size_t)dm.hkv * dm.m, 0xffffffffu, s);
+    fill_u32(reinterpret_cast<uint32_t*>(out.probe_weights), (size_t)dm.hkv * dm.m * 2, 0, s);
+    fill_u32(reinterpret_cast<uint32_t*>(out.o_dense), hq * dm.m * d, 0, s);
+    fill_u32(reinterpret_cast<uint32_t*>(out.o_sparse), hq * dm.m * d, 0, s);
+    fill_u32(reinterpret_cast<uint32_t*>(out.A), hq * d * dm.rc, 0, s);
+    fill_u32(reinterpret_cast<uint32_t*>(out.B), hq * dm.rc * d, 0, s);
+    fill_u32(reinterpret_cast<uint32_t*>(out.c0), hq * d, 0, s);
+    fill_u32(reinterpret_cast<uint32_t*>(out.r_eff), hq, 0, s);
+    fill_u32(reinterpret_cast<uint32_t*>(out.eig), hq * (dm.r + 1), 0, s);
+    return;
+  }
+  if (dm.probe_mode == SPARSEPR_PROBES_RADIAL)
+    hipLaunchKernelGGL(probe_select_kernel, dim3(dm.gq, dm.hkv), dim3(256), 0, s, part.query_features,
+                       part.query_centroids, part.query_perm, part.query_offsets, dm.n, dm.gq, dm.gk, dm.m,
+                       out.probe_tokens, out.probe_groups, out.probe_weights, radius);
+  else
+    hipLaunchKernelGGL(probe_select_plain_kernel, dim3(dm.hkv), dim3(64), 0, s, part.query_labels, dm.n, dm.m,
+                       dm.probe_mode == SPARSEPR_PROBES_UNIFORM ? 1 : 0, out.probe_tokens, out.probe_groups,
+                       out.probe_weights);
   const dim3 pgrid(wp.nchunks, dm.hq);
   if (dm.bf16) {
     launch_probe_attn_mfma(dm, q, part, route, out, kProbeChunk, wp.nchunks, partials, s);
@@ -579,11 +645,13 @@ void launch_probe_fit(const Dims& dm, const Workspace& wp, const void* q, const 
                        fbuf, out.o_dense, out.o_sparse);
   if (dm.d == 128)
     hipLaunchKernelGGL(probe_fit_kernel<128>, dim3(dm.hq), dim3(256), 0, s, partials, wp.nchunks,
-                       out.probe_weights, dm.g, dm.m, dm.r, (double)dm.lambda, fbuf, out.o_dense, out.o_sparse,
+                       out.probe_weights, dm.g, dm.m, dm.r,
+                       dm.ablation == SPARSEPR_ABLATE_RIDGE_ONLY ? 1 : 0, (double)dm.lambda, fbuf, out.o_dense, out.o_sparse,
                        out.A, out.B, out.c0, out.r_eff, out.eig);
   else
     hipLaunchKernelGGL(probe_fit_kernel<64>, dim3(dm.hq), dim3(256), 0, s, partials, wp.nchunks,
-                       out.probe_weights, dm.g, dm.m, dm.r, (double)dm.lambda, fbuf, out.o_dense, out.o_sparse,
+                       out.probe_weights, dm.g, dm.m, dm.r,
+                       dm.ablation == SPARSEPR_ABLATE_RIDGE_ONLY ? 1 : 0, (double)dm.lambda, fbuf, out.o_dense, out.o_sparse,
                        out.A, out.B, out.c0, out.r_eff, out.eig);
 }
 

@@ -15,6 +15,7 @@ constexpr int kMaxGroups = 64;      // G_Q, G_K <= 64 (one 64-bit kept mask per 
 constexpr int kMaxFeat = 64;        // r_k and G_K feature widths <= 64
 constexpr int kMaxProbe = 64;
 constexpr int kMaxRank = 32;
+constexpr int kMaxCorrRank = 64;   // columns of A / rows of B: rank, or n_probe for the unprojected ridge
 constexpr int kExpTable = 1024;     // route exponential table entries
 constexpr int kProbeChunk = 1024;   // keys per probe-attention work item
 constexpr int kGmChunk = 1024;      // tokens per chunk of the group-major counting sort
@@ -95,6 +96,8 @@ Workspace plan_workspace(const sparsepr_params& p);
 
 struct Dims {
   int hq, hkv, g, n, d, gq, gk, rk, m, r, iters;
+  int ablation, probe_mode;
+  int rc;   // correction rank: columns of A / rows of B (rank, or m for the unprojected ridge)
   float scale, lambda;
   bool bf16;
 };

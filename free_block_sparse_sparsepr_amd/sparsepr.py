@@ -29,6 +29,13 @@ class Config:
     lam: float = 0.1
     kmeans_iters: int = 10
     softmax_scale: float = 0.0
+    ablation: int = 0           # _binding.ABLATE_*: 0 = the method
+    probe_mode: int = 0         # _binding.PROBES_*: 0 = stratified radial probes
+
+    @property
+    def corr_rank(self):
+        """Columns of A / rows of B: rank, or n_probe for the unprojected ridge."""
+        return self.n_probe if self.ablation == B.ABLATE_RIDGE_ONLY else self.rank
 
     @property
     def g(self):
@@ -46,7 +53,7 @@ class Config:
         return B.Params(self.heads_q, self.heads_kv, self.n, self.d,
                         B.BF16 if self.dtype == "bf16" else B.FP32, self.groups_q, self.groups_k,
                         self.r_k, self.r_q, self.n_probe, self.rank, self.lam, self.rho_exec, 64,
-                        self.kmeans_iters, self.softmax_scale)
+                        self.kmeans_iters, self.softmax_scale, self.ablation, self.probe_mode)
 
 
 def _p(t):
@@ -96,7 +103,8 @@ class SparsePR:
             probe_tokens=e(c.heads_kv, c.n_probe), probe_groups=e(c.heads_kv, c.n_probe),
             probe_weights=e(c.heads_kv, c.n_probe, dt=torch.float64),
             o_dense=e(c.heads_q, c.n_probe, c.d, dt=f32), o_sparse=e(c.heads_q, c.n_probe, c.d, dt=f32),
-            A=e(c.heads_q, c.d, c.rank, dt=f32), B=e(c.heads_q, c.rank, c.d, dt=f32), c0=e(c.heads_q, c.d, dt=f32),
+            A=e(c.heads_q, c.d, c.corr_rank, dt=f32), B=e(c.heads_q, c.corr_rank, c.d, dt=f32),
+            c0=e(c.heads_q, c.d, dt=f32),
             r_eff=e(c.heads_q), eig=e(c.heads_q, c.rank + 1, dt=f32))
         self.o_gm = e(c.heads_kv, c.n, c.g, c.d, dt=f32)
         self.lse = e(c.heads_kv, c.n, c.g, dt=f32)
@@ -176,8 +184,10 @@ class SparsePR:
         return out
 
 
-def config_from_workload(w) -> Config:
-    """Config of a sparsepr_workloads.Workload."""
-    return Config(heads_q=w.heads_q, heads_kv=w.heads_kv, n=w.n, d=w.d, dtype=w.dtype, groups_q=w.groups_q,
-                  groups_k=w.groups_k, rho_exec=w.rho_exec, r_k=w.r_k, r_q=w.r_q, n_probe=w.n_probe,
-                  rank=w.rank, lam=w.lam, kmeans_iters=w.kmeans_iters)
+def config_from_workload(w, **overrides) -> Config:
+    """Config of a sparsepr_workloads.Workload (keyword overrides, e.g. ablation=...)."""
+    kw = dict(heads_q=w.heads_q, heads_kv=w.heads_kv, n=w.n, d=w.d, dtype=w.dtype, groups_q=w.groups_q,
+              groups_k=w.groups_k, rho_exec=w.rho_exec, r_k=w.r_k, r_q=w.r_q, n_probe=w.n_probe,
+              rank=w.rank, lam=w.lam, kmeans_iters=w.kmeans_iters)
+    kw.update(overrides)
+    return Config(**kw)

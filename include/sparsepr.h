@@ -34,7 +34,8 @@
  *    heads_q / heads_kv <= 16, 1 <= groups_q, groups_k <= 64, groups <= n,
  *    groups_k <= r_q, 1 <= r_k <= 64, 1 <= n_probe <= min(64, n),
  *    1 <= rank <= min(32, n_probe, d), lambda > 0, n_probe / n < rho_exec <= 1,
- *    0 <= kmeans_iters <= 64, block == 64.
+ *    0 <= kmeans_iters <= 64, block == 64, ablation and probe_mode one of their
+ *    enumerators.
  *
  * Unfused call order: partition -> route -> attend -> probe_fit -> apply.
  * Fused call order:   partition -> route -> probe_fit -> attend_apply.
@@ -62,6 +63,35 @@ typedef enum {
 
 typedef enum { SPARSEPR_BF16 = 0, SPARSEPR_FP32 = 1 } sparsepr_dtype;
 
+/* Ablations of the residual reconstruction (PSRR, ablation paragraph, which compares the
+ * method with hard drop and with the ridge fit left unprojected).  Partition and route are
+ * unchanged in every variant, so a comparison isolates the reconstruction. */
+typedef enum {
+  SPARSEPR_ABLATE_NONE = 0,        /* the method as specified */
+  SPARSEPR_ABLATE_HARD_DROP = 1,   /* no reconstruction: the output is the renormalised sparse
+                                      attention.  probe_fit writes an empty fit (probe tokens
+                                      and groups -1, weights 0, r_eff 0, A, B, c0, eig, o_dense,
+                                      o_sparse zero) and launches nothing else; apply and
+                                      attend_apply write no probe rows. */
+  SPARSEPR_ABLATE_RIDGE_ONLY = 2   /* the weighted ridge correction without the rank-r
+                                      projection: ybar + (o - xbar) W with W = Xt^T Z, stored as
+                                      A = Xt^T [Hq, d, n_probe], B = Z [Hq, n_probe, d],
+                                      r_eff = n_probe, eig zero.  A and B then hold n_probe
+                                      columns / rows in place of rank. */
+} sparsepr_ablation;
+
+/* How the probe rows are chosen (PSRR, ablation paragraph: stratified probes against
+ * random and uniform spatiotemporal sampling). */
+typedef enum {
+  SPARSEPR_PROBES_RADIAL = 0,      /* the method: stratified over query groups, radial order */
+  SPARSEPR_PROBES_UNIFORM = 1,     /* tokens floor((2k+1) n / (2 n_probe)), k < n_probe, of the
+                                      raster order; weight 1; group = the token's query label */
+  SPARSEPR_PROBES_GIVEN = 2        /* the caller's tokens, read from fit->probe_tokens
+                                      [Hkv, n_probe] on entry to probe_fit (e.g. drawn at random
+                                      on the host); values outside [0, n) are clamped into it;
+                                      weight 1; group = the token's query label */
+} sparsepr_probe_mode;
+
 /* Problem and hyper-parameters.  Defaults on the page: r_k = 48, r_q = 64, n_probe = 64,
  * rank = 16, lambda = 0.1 (PSRR, partition and probe-fit paragraphs); rho_exec is the
  * target total execution density rho_route + n_probe / n (PSRR, execution paragraph). */
@@ -82,6 +112,8 @@ typedef struct sparsepr_params {
   int32_t block;         /* tile height in tokens; must be 64 */
   int32_t kmeans_iters;  /* Lloyd iterations before the final assignment */
   float softmax_scale;   /* 0 -> 1 / sqrt(d) */
+  int32_t ablation;      /* sparsepr_ablation (0 = the method) */
+  int32_t probe_mode;    /* sparsepr_probe_mode (0 = the method) */
 } sparsepr_params;
 
 /* Partition outputs (all caller-allocated device buffers).  g = heads_q / heads_kv.
@@ -126,8 +158,9 @@ typedef struct sparsepr_fit_t {
   double* probe_weights;     /* [Hkv, n_probe] group-coverage weights (sum n_probe) */
   float* o_dense;            /* [Hq, n_probe, d] exact probe rows over all keys */
   float* o_sparse;           /* [Hq, n_probe, d] probe rows over the kept cells */
-  float* A;                  /* [Hq, d, rank]  W V_r (zero beyond r_eff) */
-  float* B;                  /* [Hq, rank, d]  V_r^T (zero beyond r_eff) */
+  float* A;                  /* [Hq, d, R]  W V_r (zero beyond r_eff); R = rank, or n_probe
+                                with SPARSEPR_ABLATE_RIDGE_ONLY */
+  float* B;                  /* [Hq, R, d]  V_r^T (zero beyond r_eff) */
   float* c0;                 /* [Hq, d]        ybar - xbar A B */
   int32_t* r_eff;            /* [Hq] eigenpairs kept (lambda_k > 1e-8 lambda_1) */
   float* eig;                /* [Hq, rank + 1] leading eigenvalues of Yt Yt^T */

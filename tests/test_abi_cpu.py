@@ -66,11 +66,19 @@ def test_workspace_size_valid():
     (dict(n=60, groups_q=8, groups_k=8, n_probe=61, rank=4), -6), (dict(rank=33), -6),
     (dict(rank=17, n_probe=16), -6), (dict(lam=0.0), -6), (dict(lam=float("nan")), -6),
     (dict(rho_exec=1.5), -6), (dict(rho_exec=0.01, n=4096), -6), (dict(kmeans_iters=-1), -6),
-    (dict(block=32), -6), (dict(softmax_scale=-1.0), -6),
+    (dict(block=32), -6), (dict(softmax_scale=-1.0), -6), (dict(ablation=3), -6), (dict(ablation=-1), -6),
+    (dict(probe_mode=3), -6),
 ])
 def test_invalid_params_rejected(kw, code):
     st, _ = _ws(_params(**kw))
     assert st == code
+
+
+@pytest.mark.parametrize("ablation", [B.ABLATE_NONE, B.ABLATE_HARD_DROP, B.ABLATE_RIDGE_ONLY])
+@pytest.mark.parametrize("probe_mode", [B.PROBES_RADIAL, B.PROBES_UNIFORM, B.PROBES_GIVEN])
+def test_ablation_switches_accepted(ablation, probe_mode):
+    st, n = _ws(_params(ablation=ablation, probe_mode=probe_mode))
+    assert st == 0 and n > 0
 
 
 def test_entry_points_reject_before_any_launch():
