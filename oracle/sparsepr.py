@@ -576,6 +576,38 @@ def hard_drop_rows(q, k, v, scale, q_labels, k_labels, kept, rows=None):
     return o
 
 
+def semantic_features(x_heads):
+    """Integer features of raw activations for the semantic-partition ablation (the page
+    contrasts its response-coupled partition with clustering the activations
+    themselves).  Reading: keys use their own rows; queries under GQA use the rows summed
+    over the KV head's query heads in float32, ascending head order (as the query
+    coordinate is); one power of two per head scales the largest magnitude to at most
+    127, then round half-to-even, as for the key response features.  Width d."""
+    X = summed_response(x_heads)
+    e = pow2_exponent(np.abs(X).max() if X.size else 0.0, FEATURE_MAX)
+    return np.clip(np.rint(X * 2.0 ** e), -FEATURE_MAX, FEATURE_MAX).astype(np.int64), e
+
+
+def partition_semantic(q_heads, k, p: Params, U=None):
+    """Semantic partition: the same k-means, permutation and key centroids as the method,
+    but keys clustered on their raw vectors and queries on their raw vectors (not on
+    response curves and response directions).  The route still scores cells with the
+    query responses U to the key centroids.  S is not formed (None)."""
+    q_heads, k = f64(q_heads), f64(k)
+    scale = p.softmax_scale(k.shape[1])
+    xk, e_k = semantic_features(k[None])
+    k_labels, kc = kmeans(xk, p.groups_k, p.kmeans_iters)
+    k_perm, k_inv, k_off = group_major(k_labels, p.groups_k)
+    Ck = key_centroids(k, k_labels, p.groups_k)
+    if U is None:
+        U = query_responses(q_heads, Ck, scale)
+    xq, e_q = semantic_features(q_heads)
+    q_labels, qc = kmeans(xq, p.groups_q, p.kmeans_iters)
+    q_perm, q_inv, q_off = group_major(q_labels, p.groups_q)
+    return Partition(None, e_k, xk, k_labels, kc, k_perm, k_inv, k_off, Ck,
+                     np.asarray(U), e_q, xq, q_labels, qc, q_perm, q_inv, q_off)
+
+
 def uniform_probes(n, q_labels, n_probe):
     """Uniform spatiotemporal probes.  Reading: the tokens floor((2k+1) N / (2M)), k < M,
     of the raster (t, h, w) order, i.e. evenly spaced over the clip; each stands for N / M

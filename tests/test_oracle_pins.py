@@ -544,3 +544,29 @@ def test_ridge_only_with_vanishing_lambda_interpolates_the_probe_residuals():
     np.testing.assert_allclose(O.correct_rows(fit.o_sparse, fit), fit.o_dense, atol=1e-6)
     proj = O.probe_fit(q, k, v, 0.3, pr, ql, kl, kept, p)
     assert np.abs(O.correct_rows(proj.o_sparse, proj) - proj.o_dense).max() > 1e-3
+
+
+def test_semantic_features_quantise_raw_rows_and_recover_planted_clusters():
+    """Semantic partition: features are the raw rows on one power-of-two scale (invariant
+    to scaling the activations by a power of two); planted, well separated clusters of
+    raw keys and queries are recovered exactly."""
+    n, d, G = 256, 16, 4
+    centres = rand(G, d, scale=4.0)
+    truth = np.repeat(np.arange(G), n // G)
+    k = centres[truth] + 0.05 * rand(n, d)
+    x, e = O.semantic_features(k[None])
+    assert np.abs(x).max() <= 127 and np.abs(x).max() >= 64
+    x2, e2 = O.semantic_features(4.0 * k[None])
+    np.testing.assert_array_equal(x2, x)
+    assert e2 == e - 2
+    q = centres[truth[::-1]] + 0.05 * rand(n, d)
+    p = O.Params(groups_q=G, groups_k=G, rho_exec=0.5, n_probe=8, rank=2)
+    part = O.partition_semantic(np.stack([q, q]), k, p)
+    # every planted cluster is one group (labels are a relabelling of the truth)
+    for lab, tr in ((part.k_labels, truth), (part.q_labels, truth[::-1])):
+        pairs = set(zip(lab.tolist(), tr.tolist()))
+        assert len(pairs) == G and len({a for a, _ in pairs}) == G
+    # the GQA query coordinate is the float32 head sum
+    xq, _ = O.semantic_features(np.stack([q, 0.5 * q]))
+    xs, _ = O.semantic_features((q.astype(np.float32) + (0.5 * q).astype(np.float32))[None])
+    np.testing.assert_array_equal(xq, xs)
