@@ -22,6 +22,8 @@ Dims dims_of(const sparsepr_params& p) {
   d.iters = p.kmeans_iters;
   d.ablation = p.ablation;
   d.probe_mode = p.probe_mode;
+  d.semantic = p.partition_mode == SPARSEPR_PARTITION_SEMANTIC;
+  d.fq = d.semantic ? p.d : p.groups_k;
   d.rc = p.ablation == SPARSEPR_ABLATE_RIDGE_ONLY ? p.n_probe : p.rank;
   d.scale = p.softmax_scale > 0.f ? p.softmax_scale : (float)(1.0 / std::sqrt((double)p.d));
   d.lambda = p.lambda;
@@ -34,8 +36,9 @@ static size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 Workspace plan_workspace(const sparsepr_params& p) {
   Workspace w{};
   const size_t n = (size_t)p.n, hkv = (size_t)p.heads_kv, hq = (size_t)p.heads_q;
-  w.fpk = round_up4(p.r_k);
-  w.fpq = round_up4(p.groups_k);
+  const bool semantic = p.partition_mode == SPARSEPR_PARTITION_SEMANTIC;
+  w.fpk = semantic ? p.d : round_up4(p.r_k);
+  w.fpq = semantic ? p.d : round_up4(p.groups_k);
   const int fpmax = w.fpk > w.fpq ? w.fpk : w.fpq;
   size_t o = 0;
   w.maxbits = o; o = align_up(o + hkv * 2 * 4);
@@ -90,6 +93,8 @@ static sparsepr_status check_params(const sparsepr_params* p) {
     return SPARSEPR_ERR_PARAM;
   if (p->probe_mode != SPARSEPR_PROBES_RADIAL && p->probe_mode != SPARSEPR_PROBES_UNIFORM &&
       p->probe_mode != SPARSEPR_PROBES_GIVEN)
+    return SPARSEPR_ERR_PARAM;
+  if (p->partition_mode != SPARSEPR_PARTITION_RESPONSE && p->partition_mode != SPARSEPR_PARTITION_SEMANTIC)
     return SPARSEPR_ERR_PARAM;
   return SPARSEPR_OK;
 }

@@ -223,7 +223,7 @@ constexpr int kAssignChunk = 256;       // points per chunk: 64 per wave
 // per non-zero (group, feature).  FP must be a multiple of 16.
 // grid (blocks_per_head, H), block 256; block b of a head takes chunks [b chunks, (b+1) chunks).
 template <int FP>
-__global__ __launch_bounds__(256, 2) void kmeans_assign_mfma_kernel(const int8_t* __restrict__ X, int n, int G,
+__global__ __launch_bounds__(256, FP > 64 ? 1 : 2) void kmeans_assign_mfma_kernel(const int8_t* __restrict__ X, int n, int G,
                                                                     const int32_t* __restrict__ C, int chunks,
                                                                     int32_t* __restrict__ labels,
                                                                     int32_t* __restrict__ sums) {
@@ -700,6 +700,66 @@ __global__ __launch_bounds__(256) void query_features_kernel(const float* __rest
 }
 
 // ---------------------------------------------------------------------------------------
+// Semantic partition (ablation paragraph of the summary page of "Partition the Support,
+// Reconstruct the Residual": clustering the activations instead of their responses).
+// Row i of head kv is x = sum_j X[kv g + j][i] over the g heads of the group (fp32,
+// ascending j; g = 1 for keys), quantised as rint(x 2^e) clamped to [-127, 127] with e the
+// largest power of two such that max |x| 2^e <= 127 over the head.
+// ---------------------------------------------------------------------------------------
+template <typename T, int D>
+__device__ __forceinline__ float sem_value(const T* __restrict__ x, int n, int g, int kv, int i, int c) {
+  float acc = to_f32(x[((int64_t)(kv * g) * n + i) * D + c]);
+  for (int j = 1; j < g; ++j) acc = acc + to_f32(x[((int64_t)(kv * g + j) * n + i) * D + c]);
+  return acc;
+}
+
+// grid (ceil(n * D / 1024), Hkv), block 256: atomic max of |x| (float bits) per head
+template <typename T, int D>
+__global__ __launch_bounds__(256) void sem_maxabs_kernel(const T* __restrict__ x, int n, int g,
+                                                         uint32_t* __restrict__ maxbits) {
+  __shared__ float red[4];
+  const int kv = blockIdx.y;
+  float mx = 0.f;
+  for (int u = 0; u < 4; ++u) {
+    const int64_t idx = ((int64_t)blockIdx.x * 4 + u) * 256 + threadIdx.x;
+    if (idx < (int64_t)n * D) mx = fmaxf(mx, fabsf(sem_value<T, D>(x, n, g, kv, (int)(idx / D), (int)(idx % D))));
+  }
+  mx = wave_max(mx);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
+  __syncthreads();
+  if (threadIdx.x == 0) atomicMax(&maxbits[kv], __float_as_uint(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]))));
+}
+
+// grid (ceil(n * D / 256), Hkv), block 256: int8 features into Xpad [Hkv][n][D] (and Xout
+// when given), exponent into exps[kv * 2 + slot]
+template <typename T, int D>
+__global__ __launch_bounds__(256) void sem_quant_kernel(const T* __restrict__ x, int n, int g,
+                                                        const uint32_t* __restrict__ maxbits, int slot,
+                                                        int8_t* __restrict__ Xout, int8_t* __restrict__ Xpad,
+                                                        int32_t* __restrict__ exps) {
+  const int kv = blockIdx.y;
+  const int e = pow2_exponent(__uint_as_float(maxbits[kv]), 127.f);
+  if (blockIdx.x == 0 && threadIdx.x == 0) exps[kv * 2 + slot] = e;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)n * D) return;
+  const int i = (int)(idx / D), c = (int)(idx % D);
+  const float v = fminf(fmaxf(rintf(ldexpf(sem_value<T, D>(x, n, g, kv, i, c), e)), -127.f), 127.f);
+  const int8_t q = (int8_t)(int)v;
+  Xpad[((int64_t)kv * n + i) * D + c] = q;
+  if (Xout) Xout[((int64_t)kv * n + i) * D + c] = q;
+}
+
+template <typename T, int D>
+static void launch_semantic_features(const T* x, int n, int hkv, int g, uint32_t* maxbits, int slot, int8_t* Xout,
+                                     int8_t* Xpad, int32_t* exps, hipStream_t s) {
+  const int64_t total = (int64_t)n * D;
+  hipLaunchKernelGGL((sem_maxabs_kernel<T, D>), dim3((unsigned)ceil_div(total, 1024), hkv), dim3(256), 0, s, x, n, g,
+                     maxbits);
+  hipLaunchKernelGGL((sem_quant_kernel<T, D>), dim3((unsigned)ceil_div(total, 256), hkv), dim3(256), 0, s, x, n, g,
+                     maxbits, slot, Xout, Xpad, exps);
+}
+
+// ---------------------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------------------
 template <int FP>
@@ -728,6 +788,7 @@ static void assign_dispatch(int fp, const int8_t* X, int n, int H, int G, const 
     case 32: launch_assign_mfma<32>(X, n, H, G, C, labels, sums, s); return;
     case 48: launch_assign_mfma<48>(X, n, H, G, C, labels, sums, s); return;
     case 64: launch_assign_mfma<64>(X, n, H, G, C, labels, sums, s); return;
+    case 128: launch_assign_mfma<128>(X, n, H, G, C, labels, sums, s); return;
     default: break;
   }
   switch (fp) {
@@ -792,30 +853,39 @@ static void partition_typed(const Dims& dm, const Workspace& wp, const T* q, con
   const int n = dm.n, hkv = dm.hkv;
   fill_u32(maxbits, (size_t)hkv * 2, 0, s);
   // keys
-  if (dm.bf16)
-    launch_resp_s_mfma(dm, q, k, out.responses_s, maxbits, s);
-  else
-    hipLaunchKernelGGL((resp_s_kernel<T, D>), dim3((unsigned)ceil_div(n, 256), hkv), dim3(256), 0, s, q, k,
-                       n, dm.g, dm.rk, dm.scale, out.responses_s, maxbits);
-  hipLaunchKernelGGL(key_features_kernel, dim3((unsigned)ceil_div(n, 256), hkv), dim3(256), 0, s,
-                     out.responses_s, maxbits, n, dm.rk, wp.fpk, xk, out.exponents);
-  run_kmeans(xk, n, hkv, dm.gk, dm.rk, wp.fpk, dm.iters, C, sums, out.key_labels, out.key_centroids_int, s);
+  if (dm.semantic) {
+    launch_semantic_features<T, D>(k, n, hkv, 1, maxbits, 0, nullptr, xk, out.exponents, s);
+    run_kmeans(xk, n, hkv, dm.gk, D, D, dm.iters, C, sums, out.key_labels, out.key_centroids_int, s);
+  } else {
+    if (dm.bf16)
+      launch_resp_s_mfma(dm, q, k, out.responses_s, maxbits, s);
+    else
+      hipLaunchKernelGGL((resp_s_kernel<T, D>), dim3((unsigned)ceil_div(n, 256), hkv), dim3(256), 0, s, q, k,
+                         n, dm.g, dm.rk, dm.scale, out.responses_s, maxbits);
+    hipLaunchKernelGGL(key_features_kernel, dim3((unsigned)ceil_div(n, 256), hkv), dim3(256), 0, s,
+                       out.responses_s, maxbits, n, dm.rk, wp.fpk, xk, out.exponents);
+    run_kmeans(xk, n, hkv, dm.gk, dm.rk, wp.fpk, dm.iters, C, sums, out.key_labels, out.key_centroids_int, s);
+  }
   run_group_major(out.key_labels, n, hkv, dm.gk, out.key_perm, out.key_offsets, gm_hist, s);
   run_gather(k, out.key_perm, n, hkv, 1, D, dm.bf16, out.k_gm, s);
   hipLaunchKernelGGL((gather_vt_kernel<T, D>), dim3((unsigned)ceil_div(vt_pad(n), 64), hkv), dim3(256), 0, s, v,
                      out.key_perm, n, (int)vt_pad(n), static_cast<T*>(out.v_gm));
   hipLaunchKernelGGL((segment_mean_kernel<T, D>), dim3(dm.gk, hkv), dim3(256), 0, s,
                      static_cast<const T*>(out.k_gm), out.key_offsets, n, dm.gk, out.key_centroids);
-  // queries
+  // queries (the semantic features are formed first: the response kernels below reuse the
+  // second max slot)
+  if (dm.semantic)
+    launch_semantic_features<T, D>(q, n, hkv, dm.g, maxbits + hkv, 1, out.query_features, xq, out.exponents, s);
   if (dm.bf16)
     launch_resp_u_mfma(dm, q, out.key_centroids, out.responses_u, usum, maxbits + hkv, s);
   else
     hipLaunchKernelGGL((resp_u_kernel<T, D>), dim3((unsigned)ceil_div(n, 64), hkv), dim3(256), 0, s, q,
                        out.key_centroids, n, dm.g, dm.gk, dm.scale, out.responses_u, usum, maxbits + hkv);
-  hipLaunchKernelGGL(query_features_kernel, dim3((unsigned)ceil_div(n, 64), hkv), dim3(256), 0, s,
-                     usum ? usum : out.responses_u, maxbits + hkv, n, dm.gk, wp.fpq, out.query_features,
-                     xq, out.exponents);
-  run_kmeans(xq, n, hkv, dm.gq, dm.gk, wp.fpq, dm.iters, C, sums, out.query_labels, out.query_centroids, s);
+  if (!dm.semantic)
+    hipLaunchKernelGGL(query_features_kernel, dim3((unsigned)ceil_div(n, 64), hkv), dim3(256), 0, s,
+                       usum ? usum : out.responses_u, maxbits + hkv, n, dm.gk, wp.fpq, out.query_features,
+                       xq, out.exponents);
+  run_kmeans(xq, n, hkv, dm.gq, dm.fq, wp.fpq, dm.iters, C, sums, out.query_labels, out.query_centroids, s);
   run_group_major(out.query_labels, n, hkv, dm.gq, out.query_perm, out.query_offsets, gm_hist, s);
   run_gather(q, out.query_perm, n, hkv, dm.g, D, dm.bf16, out.q_gm, s);
 }

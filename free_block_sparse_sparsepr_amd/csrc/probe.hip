@@ -40,19 +40,19 @@ __global__ __launch_bounds__(64) void probe_select_plain_kernel(const int32_t* _
 // Allocation: one probe at a time over the non-empty groups in the order (larger group
 // first, smaller index first), skipping full groups.  Within group a the m_a probes are
 // the members of rank floor((2k+1) n_a / (2 m_a)) in the order (squared distance of the
-// integer direction features to the group centroid, token index).
+// integer query features (width F) to the group centroid, token index).
 // ---------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void probe_select_kernel(const int8_t* __restrict__ XQ,
                                                            const int32_t* __restrict__ qcent,
                                                            const int32_t* __restrict__ qperm,
                                                            const int32_t* __restrict__ qoff, int n,
-                                                           int Gq, int Gk, int M, int32_t* __restrict__ ptok,
+                                                           int Gq, int F, int M, int32_t* __restrict__ ptok,
                                                            int32_t* __restrict__ pgrp,
                                                            double* __restrict__ pw,
                                                            int32_t* __restrict__ radius) {
   __shared__ int alloc[kMaxGroups], start[kMaxGroups], tgt[kMaxProbe];
   __shared__ int sz[kMaxGroups];
-  __shared__ int cent[kMaxFeat];
+  __shared__ int cent[kMaxSemFeat];
   __shared__ int lrad[1024];
   __shared__ uint64_t skey[kSortMax];
   const int a = blockIdx.x, kv = blockIdx.y, tid = threadIdx.x;
@@ -96,16 +96,16 @@ __global__ __launch_bounds__(256) void probe_select_kernel(const int8_t* __restr
   const int ma = alloc[a];
   if (ma == 0) return;
   const int na = qo[a + 1] - qo[a], off = qo[a];
-  for (int f = tid; f < Gk; f += 256) cent[f] = qcent[((int64_t)kv * Gq + a) * Gk + f];
+  for (int f = tid; f < F; f += 256) cent[f] = qcent[((int64_t)kv * Gq + a) * F + f];
   for (int k = tid; k < ma; k += 256) tgt[k] = (int)(((int64_t)(2 * k + 1) * na) / (2 * ma));
   __syncthreads();
   int32_t* rad = radius + (int64_t)kv * n + off;
   for (int i = tid; i < na; i += 256) {
     const int tok = qperm[(int64_t)kv * n + off + i];
-    const int8_t* x = XQ + ((int64_t)kv * n + tok) * Gk;
+    const int8_t* x = XQ + ((int64_t)kv * n + tok) * F;
     int s = 0;
-    if ((Gk & 15) == 0) {
-      for (int f0 = 0; f0 < Gk; f0 += 16) {
+    if ((F & 15) == 0) {
+      for (int f0 = 0; f0 < F; f0 += 16) {
         const uint4 v = *reinterpret_cast<const uint4*>(x + f0);
         const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -115,7 +115,7 @@ __global__ __launch_bounds__(256) void probe_select_kernel(const int8_t* __restr
         }
       }
     } else {
-      for (int f = 0; f < Gk; ++f) { int dd = (int)x[f] - cent[f]; s += dd * dd; }
+      for (int f = 0; f < F; ++f) { int dd = (int)x[f] - cent[f]; s += dd * dd; }
     }
     rad[i] = s;
   }
@@ -616,7 +616,7 @@ void launch_probe_fit(const Dims& dm, const Workspace& wp, const void* q, const 
   }
   if (dm.probe_mode == SPARSEPR_PROBES_RADIAL)
     hipLaunchKernelGGL(probe_select_kernel, dim3(dm.gq, dm.hkv), dim3(256), 0, s, part.query_features,
-                       part.query_centroids, part.query_perm, part.query_offsets, dm.n, dm.gq, dm.gk, dm.m,
+                       part.query_centroids, part.query_perm, part.query_offsets, dm.n, dm.gq, dm.fq, dm.m,
                        out.probe_tokens, out.probe_groups, out.probe_weights, radius);
   else
     hipLaunchKernelGGL(probe_select_plain_kernel, dim3(dm.hkv), dim3(64), 0, s, part.query_labels, dm.n, dm.m,

@@ -13,6 +13,7 @@ typedef uint16_t bf16_t;
 constexpr int kWave = 64;
 constexpr int kMaxGroups = 64;      // G_Q, G_K <= 64 (one 64-bit kept mask per query group)
 constexpr int kMaxFeat = 64;        // r_k and G_K feature widths <= 64
+constexpr int kMaxSemFeat = 128;    // feature width of the semantic partition (d)
 constexpr int kMaxProbe = 64;
 constexpr int kMaxRank = 32;
 constexpr int kMaxCorrRank = 64;   // columns of A / rows of B: rank, or n_probe for the unprojected ridge
@@ -97,6 +98,8 @@ Workspace plan_workspace(const sparsepr_params& p);
 struct Dims {
   int hq, hkv, g, n, d, gq, gk, rk, m, r, iters;
   int ablation, probe_mode;
+  bool semantic;   // partition on raw activations (ablation)
+  int fq;          // query feature width: G_K, or d for the semantic partition
   int rc;   // correction rank: columns of A / rows of B (rank, or m for the unprojected ridge)
   float scale, lambda;
   bool bf16;

@@ -31,6 +31,17 @@ class Config:
     softmax_scale: float = 0.0
     ablation: int = 0           # _binding.ABLATE_*: 0 = the method
     probe_mode: int = 0         # _binding.PROBES_*: 0 = stratified radial probes
+    partition_mode: int = 0     # _binding.PARTITION_*: 0 = response-coupled
+
+    @property
+    def key_feat(self):
+        """Width of the key features (r_k, or d for the semantic partition)."""
+        return self.d if self.partition_mode == B.PARTITION_SEMANTIC else self.r_k
+
+    @property
+    def query_feat(self):
+        """Width of the query features (G_K, or d for the semantic partition)."""
+        return self.d if self.partition_mode == B.PARTITION_SEMANTIC else self.groups_k
 
     @property
     def corr_rank(self):
@@ -53,7 +64,8 @@ class Config:
         return B.Params(self.heads_q, self.heads_kv, self.n, self.d,
                         B.BF16 if self.dtype == "bf16" else B.FP32, self.groups_q, self.groups_k,
                         self.r_k, self.r_q, self.n_probe, self.rank, self.lam, self.rho_exec, 64,
-                        self.kmeans_iters, self.softmax_scale, self.ablation, self.probe_mode)
+                        self.kmeans_iters, self.softmax_scale, self.ablation, self.probe_mode,
+                        self.partition_mode)
 
 
 def _p(t):
@@ -88,10 +100,10 @@ class SparsePR:
         self.part = dict(
             responses_s=e(c.heads_kv, c.r_k, c.n, dt=f32), responses_u=e(c.heads_q, c.n, c.groups_k, dt=f32),
             exponents=e(c.heads_kv, 2), key_labels=e(c.heads_kv, c.n),
-            key_centroids_int=e(c.heads_kv, c.groups_k, c.r_k), key_perm=e(c.heads_kv, c.n),
+            key_centroids_int=e(c.heads_kv, c.groups_k, c.key_feat), key_perm=e(c.heads_kv, c.n),
             key_offsets=e(c.heads_kv, c.groups_k + 1), key_centroids=e(c.heads_kv, c.groups_k, c.d, dt=f32),
-            query_features=e(c.heads_kv, c.n, c.groups_k, dt=torch.int8), query_labels=e(c.heads_kv, c.n),
-            query_centroids=e(c.heads_kv, c.groups_q, c.groups_k), query_perm=e(c.heads_kv, c.n),
+            query_features=e(c.heads_kv, c.n, c.query_feat, dt=torch.int8), query_labels=e(c.heads_kv, c.n),
+            query_centroids=e(c.heads_kv, c.groups_q, c.query_feat), query_perm=e(c.heads_kv, c.n),
             query_offsets=e(c.heads_kv, c.groups_q + 1),
             q_gm=e(c.heads_kv, c.n, c.g, c.d, dt=c.torch_dtype), k_gm=e(c.heads_kv, c.n, c.d, dt=c.torch_dtype),
             v_gm=e(c.heads_kv, c.d, c.n_pad, dt=c.torch_dtype))

@@ -34,8 +34,8 @@
  *    heads_q / heads_kv <= 16, 1 <= groups_q, groups_k <= 64, groups <= n,
  *    groups_k <= r_q, 1 <= r_k <= 64, 1 <= n_probe <= min(64, n),
  *    1 <= rank <= min(32, n_probe, d), lambda > 0, n_probe / n < rho_exec <= 1,
- *    0 <= kmeans_iters <= 64, block == 64, ablation and probe_mode one of their
- *    enumerators.
+ *    0 <= kmeans_iters <= 64, block == 64, ablation, probe_mode and partition_mode one
+ *    of their enumerators.
  *
  * Unfused call order: partition -> route -> attend -> probe_fit -> apply.
  * Fused call order:   partition -> route -> probe_fit -> attend_apply.
@@ -80,6 +80,21 @@ typedef enum {
                                       columns / rows in place of rank. */
 } sparsepr_ablation;
 
+/* How queries and keys are grouped (PSRR, ablation paragraph: the response-coupled
+ * partition against a semantic partition that clusters the activations themselves). */
+typedef enum {
+  SPARSEPR_PARTITION_RESPONSE = 0, /* the method: keys by response curves, queries by response
+                                      directions */
+  SPARSEPR_PARTITION_SEMANTIC = 1  /* keys by their raw rows, queries by their raw rows (summed
+                                      in fp32 over the KV head's query heads under GQA), each
+                                      quantised to [-127, 127] on one power of two per head;
+                                      same k-means, permutation, centroids and route.
+                                      responses_s is not written; key_centroids_int is
+                                      [Hkv, G_K, d], query_features [Hkv, n, d] and
+                                      query_centroids [Hkv, G_Q, d]; exponents hold the two
+                                      quantisation exponents. */
+} sparsepr_partition_mode;
+
 /* How the probe rows are chosen (PSRR, ablation paragraph: stratified probes against
  * random and uniform spatiotemporal sampling). */
 typedef enum {
@@ -114,6 +129,7 @@ typedef struct sparsepr_params {
   float softmax_scale;   /* 0 -> 1 / sqrt(d) */
   int32_t ablation;      /* sparsepr_ablation (0 = the method) */
   int32_t probe_mode;    /* sparsepr_probe_mode (0 = the method) */
+  int32_t partition_mode;/* sparsepr_partition_mode (0 = the method) */
 } sparsepr_params;
 
 /* Partition outputs (all caller-allocated device buffers).  g = heads_q / heads_kv.

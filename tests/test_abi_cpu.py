@@ -67,7 +67,7 @@ def test_workspace_size_valid():
     (dict(rank=17, n_probe=16), -6), (dict(lam=0.0), -6), (dict(lam=float("nan")), -6),
     (dict(rho_exec=1.5), -6), (dict(rho_exec=0.01, n=4096), -6), (dict(kmeans_iters=-1), -6),
     (dict(block=32), -6), (dict(softmax_scale=-1.0), -6), (dict(ablation=3), -6), (dict(ablation=-1), -6),
-    (dict(probe_mode=3), -6),
+    (dict(probe_mode=3), -6), (dict(partition_mode=2), -6),
 ])
 def test_invalid_params_rejected(kw, code):
     st, _ = _ws(_params(**kw))
@@ -76,8 +76,9 @@ def test_invalid_params_rejected(kw, code):
 
 @pytest.mark.parametrize("ablation", [B.ABLATE_NONE, B.ABLATE_HARD_DROP, B.ABLATE_RIDGE_ONLY])
 @pytest.mark.parametrize("probe_mode", [B.PROBES_RADIAL, B.PROBES_UNIFORM, B.PROBES_GIVEN])
-def test_ablation_switches_accepted(ablation, probe_mode):
-    st, n = _ws(_params(ablation=ablation, probe_mode=probe_mode))
+@pytest.mark.parametrize("partition_mode", [B.PARTITION_RESPONSE, B.PARTITION_SEMANTIC])
+def test_ablation_switches_accepted(ablation, probe_mode, partition_mode):
+    st, n = _ws(_params(ablation=ablation, probe_mode=probe_mode, partition_mode=partition_mode))
     assert st == 0 and n > 0
 
 

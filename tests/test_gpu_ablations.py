@@ -25,6 +25,8 @@ VARIANTS = {
     "ridge_only": dict(ablation=2, probe_mode=0),
     "uniform_probes": dict(ablation=0, probe_mode=1),
     "random_probes": dict(ablation=0, probe_mode=2),
+    "semantic": dict(partition_mode=1),
+    "semantic_hard_drop": dict(partition_mode=1, ablation=1),
 }
 
 
@@ -76,7 +78,7 @@ def _expected(r, kv, j):
     kept = kept_from_mask(gpu["kept_mask"][kv], cfg.groups_q, cfg.groups_k)
     q, k, v = r["Q"][h], r["K"][kv], r["V"][kv]
     o_s, _ = O.sparse_attention(q, k, v, scale, ql, kl, kept)
-    if vname == "hard_drop":
+    if vname.endswith("hard_drop"):
         return O.hard_drop_rows(q, k, v, scale, ql, kl, kept), None, None
     if vname == "uniform_probes":
         probes = O.uniform_probes(cfg.n, ql, cfg.n_probe)
@@ -96,7 +98,7 @@ def test_probe_rows_of_the_variant(r):
     cfg, gpu, vname = r["cfg"], r["gpu"], r["variant"]
     for kv in range(cfg.heads_kv):
         ql = gpu["query_labels"][kv]
-        if vname == "hard_drop":
+        if vname.endswith("hard_drop"):
             assert (gpu["probe_tokens"][kv] == -1).all() and (gpu["r_eff"] == 0).all()
             assert not gpu["A"].any() and not gpu["B"].any() and not gpu["c0"].any()
             continue
@@ -126,3 +128,30 @@ def test_output_of_the_variant_matches_oracle(r):
                 assert int(gpu["r_eff"][h]) == cfg.n_probe
                 ok, mx, mean = compare_float(gpu["c0"][h], fit.c0, fp32)
                 assert ok, ("c0", h, mx, mean)
+
+
+def test_semantic_partition_bit_exact(r):
+    """Semantic partition: the oracle, fed the GPU's query responses U (which only the route
+    uses), reproduces the raw-activation features, both k-means, the permutations, the
+    route and (with probes) the radial probe choice bit for bit."""
+    cfg, gpu, p = r["cfg"], r["gpu"], r["p"]
+    if not r["variant"].startswith("semantic"):
+        pytest.skip("response-coupled partition (covered by test_gpu_parity)")
+    for kv in range(cfg.heads_kv):
+        qh = r["Q"][kv * cfg.g:(kv + 1) * cfg.g]
+        part = O.partition_semantic(qh, r["K"][kv], p, U=gpu["responses_u"][kv * cfg.g:(kv + 1) * cfg.g])
+        np.testing.assert_array_equal(gpu["key_labels"][kv], part.k_labels)
+        np.testing.assert_array_equal(gpu["key_centroids_int"][kv], part.k_centroids_int)
+        np.testing.assert_array_equal(gpu["key_perm"][kv], part.k_perm)
+        np.testing.assert_array_equal(gpu["key_offsets"][kv], part.k_offsets)
+        np.testing.assert_array_equal(gpu["query_features"][kv], part.xq)
+        np.testing.assert_array_equal(gpu["query_labels"][kv], part.q_labels)
+        np.testing.assert_array_equal(gpu["query_centroids"][kv], part.q_centroids)
+        np.testing.assert_array_equal(gpu["query_perm"][kv], part.q_perm)
+        np.testing.assert_array_equal(gpu["exponents"][kv], [part.e_s, part.e_u])
+        rt = O.route(part, p, cfg.n)
+        np.testing.assert_array_equal(gpu["cell_mass"][kv].astype(np.int64), rt.mass)
+        np.testing.assert_array_equal(kept_from_mask(gpu["kept_mask"][kv], cfg.groups_q, cfg.groups_k), rt.kept)
+        if r["variant"] == "semantic":
+            pr = O.select_probes(part.xq, part.q_labels, part.q_centroids, np.diff(part.q_offsets), cfg.n_probe)
+            np.testing.assert_array_equal(gpu["probe_tokens"][kv], pr.tokens)
