@@ -89,6 +89,64 @@ def measured_traffic(workload_name):
     return rec.get("hbm_bytes_per_launch")
 
 
+ABLATIONS = {   # summary page of "Partition the Support, Reconstruct the Residual", ablation paragraph
+    "sparsepr": dict(),
+    "hard_drop": dict(ablation=1),
+    "semantic_hard_drop": dict(partition_mode=1, ablation=1),
+    "semantic": dict(partition_mode=1),
+    "ridge_only": dict(ablation=2),
+    "uniform_probes": dict(probe_mode=1),
+    "random_probes": dict(probe_mode=2),
+}
+
+
+def ablation_report(workload):
+    """Mean and 99th-percentile absolute error of the whole call's output against the
+    same-GPU dense attention, for the method and each ablation switch, on one workload.
+    The p99 is taken over a fixed stride of 2^24 elements; random probes are drawn with
+    NumPy (seed 0) and passed in."""
+    import numpy as np
+    import torch
+
+    import free_block_sparse_sparsepr_amd as S
+    from sparsepr_workloads import CONFIGS, make_inputs
+
+    cfg = CONFIGS[workload]
+    dev = torch.device("cuda:0")
+    Q, K, V = make_inputs(cfg, threads=16)
+    tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    q, k, v = (torch.from_numpy(x).to(dev).to(tdt).contiguous() for x in (Q, K, V))
+    del Q, K, V
+    sp = S.SparsePR(S.config_from_workload(cfg), device=dev)
+    dense = sp.dense(q, k, v).float()
+    del sp
+    rng = np.random.default_rng(0)
+    given = np.stack([np.sort(rng.choice(cfg.n, cfg.n_probe, replace=False)) for _ in range(cfg.heads_kv)])
+    stride = max(1, dense.numel() // (1 << 24))
+    out = {}
+    for name, kw in ABLATIONS.items():
+        log(f"[ablations] {name}")
+        sp = S.SparsePR(S.config_from_workload(cfg, **kw), device=dev)
+        sp.partition(q, k, v)
+        sp.route()
+        if kw.get("probe_mode") == 2:
+            sp.fit["probe_tokens"].copy_(torch.from_numpy(given.astype(np.int32)))
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        sp.probe_fit(q)
+        o = sp.attend_apply()
+        torch.cuda.synchronize()
+        err = (o.float() - dense).abs_().flatten()
+        p99 = float(torch.quantile(err[::stride][: 1 << 24], 0.99))
+        out[name] = {"mean_abs_err": float(err.mean()), "p99_abs_err": p99,
+                     "probe_fit_plus_attend_ms": (time.perf_counter() - t0) * 1e3}
+        del sp, o, err
+        torch.cuda.empty_cache()
+    print(json.dumps({"ablation_report": cfg.name, "reference": "same-GPU dense attention",
+                      "data": "synthetic (seeded Fourier-feature Q/K, Gaussian V; no model weights)",
+                      "variants": out}), flush=True)
+
+
 def copy_probe(mib):
     """A plain copy of `mib` MiB (torch's device copy kernel), three launches on a source larger
     than the caches: each launch reads and writes exactly mib MiB."""
@@ -113,12 +171,19 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--unfused", action="store_true",
                     help="time the unfused order (attend -> probe_fit -> apply) instead of the fused one")
+    ap.add_argument("--ablations", action="store_true",
+                    help="instead of timing, print the output error against dense attention of the method and "
+                         "each ablation switch (hard drop, semantic partition, unprojected ridge, uniform and "
+                         "random probes) on the workload")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (3 launches) and exit: the reference "
                          "kernel of known traffic for scaling the FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
     if args.copy_probe_mib:
         copy_probe(args.copy_probe_mib)
+        return
+    if args.ablations:
+        ablation_report(args.workload)
         return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for {args.gpus}); the SparsePR call "
