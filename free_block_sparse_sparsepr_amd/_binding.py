@@ -46,7 +46,7 @@ FitT = _ptr_struct("FitT", FIT_FIELDS)
 
 EXPORTS = ["sparsepr_workspace_size", "sparsepr_partition", "sparsepr_route", "sparsepr_attend",
            "sparsepr_probe_fit", "sparsepr_apply", "sparsepr_attend_apply", "sparsepr_dense_attention",
-           "sparsepr_status_string"]
+           "sparsepr_diagnostics_workspace_size", "sparsepr_residual_diagnostics", "sparsepr_status_string"]
 
 _lib = None
 
@@ -73,6 +73,8 @@ def load():
         "sparsepr_apply": [P(Params), vp, P(PartitionT), P(FitT), vp, vp],
         "sparsepr_attend_apply": [P(Params), P(PartitionT), P(RouteT), P(FitT), vp, vp, sz, vp],
         "sparsepr_dense_attention": [P(Params), vp, vp, vp, vp, vp, sz, vp],
+        "sparsepr_diagnostics_workspace_size": [P(Params), P(ctypes.c_size_t)],
+        "sparsepr_residual_diagnostics": [P(Params), vp, vp, vp, P(PartitionT), P(RouteT), vp, vp, sz, vp],
     }
     for name, args in sigs.items():
         fn = getattr(lib, name)

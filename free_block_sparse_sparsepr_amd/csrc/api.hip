@@ -148,6 +148,29 @@ static AttnArgs sparse_args(const Dims& dm, const sparsepr_partition_t& part, co
   return a;
 }
 
+// Attention arguments of the dense path (token order, V already transposed into vt).
+static AttnArgs dense_args(const Dims& dm, const void* q, const void* k, const void* vt) {
+  AttnArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = vt;
+  a.v_np = (int)vt_pad(dm.n);
+  a.v_skv = (int64_t)dm.d * a.v_np;
+  a.q_skv = (int64_t)dm.g * dm.n * dm.d;
+  a.q_sp = dm.d;
+  a.q_sj = (int64_t)dm.n * dm.d;
+  a.kv_skv = (int64_t)dm.n * dm.d;
+  a.o_skv = a.q_skv;
+  a.o_sp = a.q_sp;
+  a.o_sj = a.q_sj;
+  a.n = dm.n;
+  a.g = dm.g;
+  a.gq = 1;
+  a.gk = 1;
+  a.scale = dm.scale;
+  return a;
+}
+
 }  // namespace sp
 
 using namespace sp;
@@ -308,27 +331,43 @@ sparsepr_status sparsepr_dense_attention(const sparsepr_params* params, const vo
   (void)hipGetLastError();
   void* vt = static_cast<char*>(workspace) + wp.dense_meta;
   launch_transpose_v(dm, v, vt, (hipStream_t)stream);
-  AttnArgs a{};
-  a.q = q;
-  a.k = k;
-  a.v = vt;
-  a.v_np = (int)vt_pad(dm.n);
-  a.v_skv = (int64_t)dm.d * a.v_np;
-  a.q_skv = (int64_t)dm.g * dm.n * dm.d;
-  a.q_sp = dm.d;
-  a.q_sj = (int64_t)dm.n * dm.d;
-  a.kv_skv = (int64_t)dm.n * dm.d;
+  AttnArgs a = dense_args(dm, q, k, vt);
   a.o = o;
-  a.o_skv = a.q_skv;
-  a.o_sp = a.q_sp;
-  a.o_sj = a.q_sj;
-  a.n = dm.n;
-  a.g = dm.g;
-  a.gq = 1;
-  a.gk = 1;
-  a.scale = dm.scale;
   (void)hipGetLastError();
   launch_attention(dm, a, true, (hipStream_t)stream);
+  return hip_status();
+}
+
+sparsepr_status sparsepr_diagnostics_workspace_size(const sparsepr_params* params, size_t* bytes) {
+  sparsepr_status st = check_params(params);
+  if (st != SPARSEPR_OK) return st;
+  if (!bytes) return SPARSEPR_ERR_NULL;
+  *bytes = plan_diagnostics(dims_of(*params)).total;
+  return SPARSEPR_OK;
+}
+
+sparsepr_status sparsepr_residual_diagnostics(const sparsepr_params* params, const void* q, const void* k,
+                                              const void* v, const sparsepr_partition_t* part,
+                                              const sparsepr_route_t* route, double* out, void* workspace,
+                                              size_t workspace_bytes, void* stream) {
+  sparsepr_status st = check_params(params);
+  if (st != SPARSEPR_OK) return st;
+  if (!q || !k || !v || !part || !route || !out) return SPARSEPR_ERR_NULL;
+  if (!part->q_gm || !part->k_gm || !part->v_gm || !part->query_offsets || !part->key_offsets ||
+      !part->query_perm || !route->row_ptr || !route->cols)
+    return SPARSEPR_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(part->q_gm) || !aligned16(part->k_gm) ||
+      !aligned16(part->v_gm) || ((uintptr_t)out & 7u) != 0)
+    return SPARSEPR_ERR_ALIGN;
+  const Dims dm = dims_of(*params);
+  const DiagWorkspace w = plan_diagnostics(dm);
+  st = check_ws(params, workspace, workspace_bytes, w.total);
+  if (st != SPARSEPR_OK) return st;
+  char* ws = static_cast<char*>(workspace);
+  (void)hipGetLastError();
+  launch_transpose_v(dm, v, ws + w.vt, (hipStream_t)stream);
+  launch_diagnostics(dm, w, dense_args(dm, q, k, ws + w.vt), sparse_args(dm, *part, *route), part->query_perm, out,
+                     ws, (hipStream_t)stream);
   return hip_status();
 }
 

@@ -29,4 +29,13 @@ void launch_probe_writeback(const Dims& dm, const sparsepr_fit_t& fit, void* o, 
 void launch_apply(const Dims& dm, const float* o_gm, const sparsepr_partition_t& part, const sparsepr_fit_t& fit,
                   void* o, hipStream_t s);
 
+// Residual diagnostics: workspace offsets and the launch (dense and sparse AttnArgs are
+// filled by the caller except for their outputs).
+struct DiagWorkspace {
+  size_t o_dense, o_gm, vt, part, scratch, total;
+};
+DiagWorkspace plan_diagnostics(const Dims& dm);
+void launch_diagnostics(const Dims& dm, const DiagWorkspace& w, AttnArgs dense, AttnArgs sparse,
+                        const int32_t* qperm, double* out, char* ws, hipStream_t s);
+
 }  // namespace sp

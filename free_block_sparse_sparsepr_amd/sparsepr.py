@@ -186,6 +186,21 @@ class SparsePR:
         self.probe_fit(q)
         return self.attend_apply(out)
 
+    def residual_diagnostics(self, q, k, v):
+        """[Hq, 4] float64: ||R||^2, ||R - mean R||^2, affine-orthogonal energy, explainable
+        fraction of R = O_dense - O_sparse over every row (needs partition and route first;
+        allocates its own large workspace for the call)."""
+        c = self.cfg
+        self._check_qkv(q, k, v)
+        nbytes = ctypes.c_size_t(0)
+        B.check(self.lib.sparsepr_diagnostics_workspace_size(ctypes.byref(self.prm), ctypes.byref(nbytes)))
+        ws = torch.empty(max(nbytes.value, 256), dtype=torch.uint8, device=q.device)
+        out = torch.empty((c.heads_q, 4), dtype=torch.float64, device=q.device)
+        B.check(self.lib.sparsepr_residual_diagnostics(ctypes.byref(self.prm), _p(q), _p(k), _p(v),
+                                                       ctypes.byref(self._part_t), ctypes.byref(self._route_t),
+                                                       _p(out), _p(ws), ws.numel(), _stream()))
+        return out
+
     def dense(self, q, k, v, out=None):
         self._check_qkv(q, k, v)
         c = self.cfg

@@ -250,6 +250,24 @@ sparsepr_status sparsepr_dense_attention(const sparsepr_params* params, const vo
                                          void* stream);
 
 /* Static description of a status code. */
+/* Residual diagnostics (PSRR, partition paragraph: how much of the hard-drop residual is
+ * an affine function of the sparse output, and the energy orthogonal to it; the page
+ * compares these between its partition and a semantic one).  For every query head, over
+ * all n rows: R = O_dense - O_sparse (O_sparse = the renormalised sparse attention of this
+ * partition and route, before any correction) and the ordinary least-squares fit
+ * R ~ c + O_sparse W (a 1e-9 relative guard on the normal equations' diagonal).
+ *   out: [Hq, 4] float64 device buffer (8-byte aligned): ||R||_F^2, ||R - mean R||_F^2,
+ *        ||R - (c + O_sparse W)||_F^2 (affine-orthogonal energy) and the explainable
+ *        fraction 1 - orthogonal / centred.
+ * Needs Q, K, V of the call and the partition and route outputs; the workspace
+ * (sparsepr_diagnostics_workspace_size) holds fp32 dense and sparse outputs of every row,
+ * so it is large (about 8 n d Hq bytes).  Not part of the timed call. */
+sparsepr_status sparsepr_diagnostics_workspace_size(const sparsepr_params* params, size_t* bytes);
+sparsepr_status sparsepr_residual_diagnostics(const sparsepr_params* params, const void* q, const void* k,
+                                              const void* v, const sparsepr_partition_t* part,
+                                              const sparsepr_route_t* route, double* out, void* workspace,
+                                              size_t workspace_bytes, void* stream);
+
 const char* sparsepr_status_string(sparsepr_status status);
 
 #ifdef __cplusplus

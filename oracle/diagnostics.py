@@ -32,3 +32,22 @@ def support_fraction(q, k, scale, rows, mass=0.9):
 
 def median_support(q, k, scale, count=256, mass=0.9):
     return float(np.median(support_fraction(q, k, scale, support_rows(k.shape[0], count), mass)))
+
+
+def affine_residual_stats(o_sparse, o_dense):
+    """How much of the hard-drop residual R = O_dense - O_sparse is an affine function of
+    the sparse output, over every row of one query head (the page's partition paragraph
+    reports this share, and the energy orthogonal to it, for its oracle diagnostic).
+
+    Reading: ordinary least squares R ~ c + O_sparse W over all n rows (unweighted, no
+    penalty).  Returns (||R||_F^2, ||R - mean R||_F^2, ||R - (c + O_sparse W)||_F^2,
+    explainable fraction = 1 - third / second)."""
+    X = f64(o_sparse)
+    R = f64(o_dense) - X
+    Xa = np.hstack([X, np.ones((X.shape[0], 1))])
+    coef = np.linalg.lstsq(Xa, R, rcond=None)[0]
+    res = R - Xa @ coef
+    tot = float((R * R).sum())
+    cen = float(((R - R.mean(axis=0)) ** 2).sum())
+    orth = float((res * res).sum())
+    return tot, cen, orth, 1.0 - orth / cen if cen > 0 else 0.0

@@ -570,3 +570,23 @@ def test_semantic_features_quantise_raw_rows_and_recover_planted_clusters():
     xq, _ = O.semantic_features(np.stack([q, 0.5 * q]))
     xs, _ = O.semantic_features((q.astype(np.float32) + (0.5 * q).astype(np.float32))[None])
     np.testing.assert_array_equal(xq, xs)
+
+
+def test_affine_residual_stats_pins():
+    """Explainable fraction = scikit-learn's variance-weighted R^2 of a linear regression of
+    R on the sparse output; 1 for an exactly affine residual; orthogonal energy = the
+    least-squares residual energy."""
+    from sklearn.linear_model import LinearRegression
+    from sklearn.metrics import r2_score
+    from oracle import diagnostics as D
+    n, d = 500, 8
+    o_s = rand(n, d)
+    R = 0.3 * o_s @ rand(d, d) + 0.1 * rand(n, d) + 0.2
+    tot, cen, orth, frac = D.affine_residual_stats(o_s, o_s + R)
+    lr = LinearRegression().fit(o_s, R)
+    assert abs(frac - r2_score(R, lr.predict(o_s), multioutput="variance_weighted")) < 1e-12
+    assert abs(orth - ((R - lr.predict(o_s)) ** 2).sum()) < 1e-9 * orth
+    assert abs(tot - (R * R).sum()) < 1e-9 * tot and cen <= tot
+    W0, c0 = rand(d, d), rand(d)
+    _, _, orth1, frac1 = D.affine_residual_stats(o_s, o_s + (o_s @ W0 + c0))
+    assert frac1 > 1 - 1e-12 and orth1 < 1e-18 * n * d
