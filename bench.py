@@ -147,6 +147,49 @@ def ablation_report(workload):
                       "variants": out}), flush=True)
 
 
+def diagnostics_report(workload):
+    """Per-head statistics of the hard-drop residual R = O_dense - O_sparse over every row, for
+    the response-coupled and the semantic partition on one workload: the fraction of R's
+    centred energy that is an affine function of the sparse output, and the energy left
+    orthogonal to it (summary page of "Partition the Support, Reconstruct the Residual",
+    partition paragraph)."""
+    import numpy as np
+    import torch
+
+    import free_block_sparse_sparsepr_amd as S
+    from sparsepr_workloads import CONFIGS, make_inputs
+
+    cfg = CONFIGS[workload]
+    dev = torch.device("cuda:0")
+    Q, K, V = make_inputs(cfg, threads=16)
+    tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    q, k, v = (torch.from_numpy(x).to(dev).to(tdt).contiguous() for x in (Q, K, V))
+    del Q, K, V
+    out = {}
+    for name, mode in (("response", 0), ("semantic", 1)):
+        log(f"[diagnostics] {name} partition")
+        sp = S.SparsePR(S.config_from_workload(cfg, partition_mode=mode), device=dev)
+        sp.partition(q, k, v)
+        sp.route()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        st = sp.residual_diagnostics(q, k, v).cpu().numpy()
+        ms = (time.perf_counter() - t0) * 1e3
+        rows = cfg.n * cfg.d
+        out[name] = {"explainable_frac_mean": float(st[:, 3].mean()),
+                     "explainable_frac_min": float(st[:, 3].min()),
+                     "explainable_frac_max": float(st[:, 3].max()),
+                     "residual_energy_per_elem": float(st[:, 0].sum() / (rows * cfg.heads_q)),
+                     "orthogonal_energy_per_elem": float(st[:, 2].sum() / (rows * cfg.heads_q)),
+                     "per_head_frac": [round(float(x), 4) for x in st[:, 3]],
+                     "call_ms": ms}
+        del sp
+        torch.cuda.empty_cache()
+    print(json.dumps({"diagnostics_report": cfg.name,
+                      "data": "synthetic (seeded Fourier-feature Q/K, Gaussian V; no model weights)",
+                      "partitions": out}), flush=True)
+
+
 def copy_probe(mib):
     """A plain copy of `mib` MiB (torch's device copy kernel), three launches on a source larger
     than the caches: each launch reads and writes exactly mib MiB."""
@@ -175,6 +218,9 @@ def main():
                     help="instead of timing, print the output error against dense attention of the method and "
                          "each ablation switch (hard drop, semantic partition, unprojected ridge, uniform and "
                          "random probes) on the workload")
+    ap.add_argument("--diagnostics", action="store_true",
+                    help="instead of timing, print the affine-explainable fraction and orthogonal energy of "
+                         "the hard-drop residual for the response-coupled and semantic partitions")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (3 launches) and exit: the reference "
                          "kernel of known traffic for scaling the FETCH_SIZE / WRITE_SIZE counters")
@@ -184,6 +230,9 @@ def main():
         return
     if args.ablations:
         ablation_report(args.workload)
+        return
+    if args.diagnostics:
+        diagnostics_report(args.workload)
         return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for {args.gpus}); the SparsePR call "
