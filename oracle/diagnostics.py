@@ -1,9 +1,11 @@
-"""Attention-support statistics (test infrastructure only; see oracle/sparsepr.py).
+"""Attention-support and residual statistics (test infrastructure only; see
+oracle/sparsepr.py).
 
-The PSRR support paragraph measures how many keys a single query row needs to keep
-90 % of its attention mass (median 6.2 % on Wan2.2, 56.5 % on Cosmos-Predict2.5) and how
-that grows when queries share a route.  The synthetic workloads are calibrated to those
-single-row medians with ``support_fraction``.
+The support paragraph of the summary page of "Partition the Support, Reconstruct the
+Residual" measures how many keys a single query row needs to keep 90 % of its attention
+mass and how much that grows when several queries share one route; its partition
+paragraph measures how much of the hard-drop residual is an affine function of the sparse
+output.  Each function here writes out one of those definitions in float64.
 """
 import numpy as np
 
@@ -16,18 +18,44 @@ def support_rows(n, count=256):
     return (2 * r + 1) * n // (2 * r.size)
 
 
-def support_fraction(q, k, scale, rows, mass=0.9):
-    """Per row: the smallest number of keys whose softmax mass reaches ``mass``,
-    as a fraction of N (float64)."""
+def row_supports(q, k, scale, rows, mass=0.9):
+    """The 90 %-mass support of single query rows (summary page of "Partition the Support,
+    Reconstruct the Residual", support paragraph): for each row, the fewest keys whose
+    softmax probabilities sum to at least ``mass``, taken in order of decreasing probability
+    with ties broken by the smaller key index.  Returns (count per row [R] int64, member mask
+    [R, N] bool); float64 throughout."""
     q, k = f64(q)[np.asarray(rows)], f64(k)
     s = (q @ k.T) * scale
     s -= s.max(axis=1, keepdims=True)
     p = np.exp(s)
     p /= p.sum(axis=1, keepdims=True)
-    p = -np.sort(-p, axis=1)
-    c = np.cumsum(p, axis=1)
-    need = (c < mass).sum(axis=1) + 1
-    return need / k.shape[0]
+    n = k.shape[0]
+    count = np.empty(p.shape[0], dtype=np.int64)
+    member = np.zeros(p.shape, dtype=bool)
+    for r in range(p.shape[0]):
+        order = np.lexsort((np.arange(n), -p[r]))
+        c = np.cumsum(p[r][order])
+        need = int((c < mass).sum()) + 1
+        count[r] = min(need, n)
+        member[r, order[:count[r]]] = True
+    return count, member
+
+
+def shared_supports(q, k, scale, sets, mass=0.9):
+    """Queries that share one route must keep the union of their single-row supports (same
+    paragraph: eight queries per route).  ``sets`` [S, s] holds token indices; returns
+    (count per row [S, s], union size per set [S]) as int64."""
+    sets = np.asarray(sets)
+    count, member = row_supports(q, k, scale, sets.reshape(-1), mass)
+    union = member.reshape(sets.shape[0], sets.shape[1], -1).any(axis=1).sum(axis=1)
+    return count.reshape(sets.shape), union.astype(np.int64)
+
+
+def support_fraction(q, k, scale, rows, mass=0.9):
+    """Per row: the single-row support as a fraction of N (float64).  The page reports
+    medians of 6.2 % (Wan2.2) and 56.5 % (Cosmos-Predict2.5); the synthetic workloads are
+    shaped to span that range."""
+    return row_supports(q, k, scale, rows, mass)[0] / f64(k).shape[0]
 
 
 def median_support(q, k, scale, count=256, mass=0.9):

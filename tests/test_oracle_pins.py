@@ -590,3 +590,66 @@ def test_affine_residual_stats_pins():
     W0, c0 = rand(d, d), rand(d)
     _, _, orth1, frac1 = D.affine_residual_stats(o_s, o_s + (o_s @ W0 + c0))
     assert frac1 > 1 - 1e-12 and orth1 < 1e-18 * n * d
+
+
+# ----------------------------------------------------------------------------- support diagnostics
+def test_row_support_brute_force_over_subsets():
+    """The single-row support count is the size of the smallest key subset reaching the mass
+    (every subset enumerated), and the chosen members form such a subset."""
+    from oracle import diagnostics as D
+    n = 10
+    for trial in range(6):
+        q, k = rand(3, 4), rand(n, 4, scale=1.5)
+        for mass in (0.5, 0.9, 0.99):
+            count, member = D.row_supports(q, k, 0.8, np.arange(3), mass)
+            p = softmax(q @ k.T * 0.8, axis=1)
+            for r in range(3):
+                best = min(len(c) for m in range(1, n + 1) for c in itertools.combinations(range(n), m)
+                           if p[r, list(c)].sum() >= mass)
+                assert count[r] == best == member[r].sum()
+                assert p[r, member[r]].sum() >= mass
+
+
+def test_row_support_closed_forms():
+    """Identical keys: every probability is 1/N, the count is ceil(mass N) and the ties go to
+    the lowest key indices.  Two levels (a keys e^delta times likelier than the other b):
+    the count follows from the mass arithmetic by hand."""
+    from oracle import diagnostics as D
+    n = 1001
+    k = np.repeat(rand(1, 6), n, axis=0)
+    count, member = D.row_supports(rand(5, 6), k, 1.0, np.arange(5), 0.9)
+    assert (count == math.ceil(0.9 * n)).all()
+    assert member[:, :901].all() and not member[:, 901:].any()
+    _, union = D.shared_supports(rand(8, 6), k, 1.0, np.arange(8).reshape(2, 4), 0.9)
+    assert (union == 901).all()
+    a, b, delta = 7, 300, 4.0
+    k = np.zeros((a + b, 2))
+    k[RNG.choice(a + b, a, replace=False), 0] = delta
+    q = np.array([[1.0, 0.0]])
+    w = math.exp(delta)
+    total = a * w + b
+    count, _ = D.row_supports(q, k, 1.0, [0], 0.9)
+    want = math.ceil(0.9 * total / w) if a * w >= 0.9 * total else a + math.ceil(0.9 * total - a * w)
+    assert count[0] == want
+
+
+def test_shared_support_dominant_keys_and_bounds():
+    """A row whose key j scores far above the rest needs that one key; a route shared by rows
+    with distinct dominant keys keeps one key per distinct dominant key.  For any set the
+    union lies between the largest single-row count and the sum of them, and a set of one
+    repeated row keeps exactly that row's support."""
+    from oracle import diagnostics as D
+    n, d = 64, 16
+    k = rand(n, d) * 0.1
+    k[:d] += 40 * np.eye(d)
+    q = np.eye(d)
+    sets = np.array([[0, 1, 2, 3, 4, 5, 6, 7], [3, 3, 3, 9, 9, 11, 3, 9]])
+    count, union = D.shared_supports(q, k, 1.0, sets, 0.9)
+    assert (count == 1).all()
+    assert list(union) == [8, 3]
+    q, k = rand(40, 8), rand(300, 8)
+    sets = RNG.integers(0, 40, (12, 8))
+    count, union = D.shared_supports(q, k, 0.5, sets, 0.9)
+    assert (union >= count.max(axis=1)).all() and (union <= count.sum(axis=1)).all()
+    c1, u1 = D.shared_supports(q, k, 0.5, np.full((1, 8), 5), 0.9)
+    assert u1[0] == c1[0, 0]
