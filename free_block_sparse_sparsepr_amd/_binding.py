@@ -46,7 +46,8 @@ FitT = _ptr_struct("FitT", FIT_FIELDS)
 
 EXPORTS = ["sparsepr_workspace_size", "sparsepr_partition", "sparsepr_route", "sparsepr_attend",
            "sparsepr_probe_fit", "sparsepr_apply", "sparsepr_attend_apply", "sparsepr_dense_attention",
-           "sparsepr_diagnostics_workspace_size", "sparsepr_residual_diagnostics", "sparsepr_status_string"]
+           "sparsepr_diagnostics_workspace_size", "sparsepr_residual_diagnostics",
+           "sparsepr_support_workspace_size", "sparsepr_support_diagnostics", "sparsepr_status_string"]
 
 _lib = None
 
@@ -75,6 +76,9 @@ def load():
         "sparsepr_dense_attention": [P(Params), vp, vp, vp, vp, vp, sz, vp],
         "sparsepr_diagnostics_workspace_size": [P(Params), P(ctypes.c_size_t)],
         "sparsepr_residual_diagnostics": [P(Params), vp, vp, vp, P(PartitionT), P(RouteT), vp, vp, sz, vp],
+        "sparsepr_support_workspace_size": [P(Params), ctypes.c_int, ctypes.c_int, P(ctypes.c_size_t)],
+        "sparsepr_support_diagnostics": [P(Params), vp, vp, vp, ctypes.c_int, ctypes.c_int, ctypes.c_double,
+                                         vp, vp, vp, sz, vp],
     }
     for name, args in sigs.items():
         fn = getattr(lib, name)

@@ -371,6 +371,38 @@ sparsepr_status sparsepr_residual_diagnostics(const sparsepr_params* params, con
   return hip_status();
 }
 
+sparsepr_status sparsepr_support_workspace_size(const sparsepr_params* params, int n_sets, int set_size,
+                                                size_t* bytes) {
+  sparsepr_status st = check_params(params);
+  if (st != SPARSEPR_OK) return st;
+  if (!bytes) return SPARSEPR_ERR_NULL;
+  if (n_sets < 0 || set_size < 1 || set_size > kSupportMaxSet) return SPARSEPR_ERR_PARAM;
+  *bytes = support_workspace_bytes(dims_of(*params), n_sets, set_size);
+  return SPARSEPR_OK;
+}
+
+sparsepr_status sparsepr_support_diagnostics(const sparsepr_params* params, const void* q, const void* k,
+                                             const int32_t* sets, int n_sets, int set_size, double mass,
+                                             int32_t* row_support, int32_t* shared_support, void* workspace,
+                                             size_t workspace_bytes, void* stream) {
+  sparsepr_status st = check_params(params);
+  if (st != SPARSEPR_OK) return st;
+  if (n_sets < 0 || set_size < 1 || set_size > kSupportMaxSet || !(mass > 0.0 && mass <= 1.0))
+    return SPARSEPR_ERR_PARAM;
+  if (n_sets == 0) return SPARSEPR_OK;
+  if (!q || !k || !sets || !row_support || !shared_support) return SPARSEPR_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || ((uintptr_t)sets & 3u) || ((uintptr_t)row_support & 3u) ||
+      ((uintptr_t)shared_support & 3u))
+    return SPARSEPR_ERR_ALIGN;
+  const Dims dm = dims_of(*params);
+  st = check_ws(params, workspace, workspace_bytes, support_workspace_bytes(dm, n_sets, set_size));
+  if (st != SPARSEPR_OK) return st;
+  (void)hipGetLastError();
+  launch_support(dm, q, k, sets, n_sets, set_size, mass, row_support, shared_support, workspace,
+                 (hipStream_t)stream);
+  return hip_status();
+}
+
 const char* sparsepr_status_string(sparsepr_status status) {
   switch (status) {
     case SPARSEPR_OK: return "ok";

@@ -38,4 +38,12 @@ DiagWorkspace plan_diagnostics(const Dims& dm);
 void launch_diagnostics(const Dims& dm, const DiagWorkspace& w, AttnArgs dense, AttnArgs sparse,
                         const int32_t* qperm, double* out, char* ws, hipStream_t s);
 
+// Support diagnostics: at most kSupportMaxSet queries per set, kSupportSlots concurrent
+// (head, set) items, each with its own score slot in the workspace.
+constexpr int kSupportMaxSet = 16;
+constexpr int kSupportSlots = 512;
+size_t support_workspace_bytes(const Dims& dm, int n_sets, int set_size);
+void launch_support(const Dims& dm, const void* q, const void* k, const int32_t* sets, int n_sets, int set_size,
+                    double mass, int32_t* row_out, int32_t* union_out, void* ws, hipStream_t s);
+
 }  // namespace sp

@@ -201,6 +201,26 @@ class SparsePR:
                                                        _p(out), _p(ws), ws.numel(), _stream()))
         return out
 
+    def support_diagnostics(self, q, k, sets, mass=0.9):
+        """90 %-mass supports: ``sets`` [Hq, n_sets, s] int32 query tokens (device).  Returns
+        (row_support [Hq, n_sets, s], shared_support [Hq, n_sets]) int32 key counts; needs
+        only Q and K (allocates its own workspace for the call)."""
+        c = self.cfg
+        if sets.dtype != torch.int32 or sets.dim() != 3 or sets.shape[0] != c.heads_q or not sets.is_contiguous():
+            raise ValueError("sets must be a contiguous int32 tensor [heads_q, n_sets, set_size]")
+        if sets.device != q.device or k.device != q.device:
+            raise ValueError("q, k and sets must be on one device")
+        n_sets, s = int(sets.shape[1]), int(sets.shape[2])
+        nbytes = ctypes.c_size_t(0)
+        B.check(self.lib.sparsepr_support_workspace_size(ctypes.byref(self.prm), n_sets, s, ctypes.byref(nbytes)))
+        ws = torch.empty(max(nbytes.value, 256), dtype=torch.uint8, device=q.device)
+        rows = torch.empty((c.heads_q, n_sets, s), dtype=torch.int32, device=q.device)
+        union = torch.empty((c.heads_q, n_sets), dtype=torch.int32, device=q.device)
+        B.check(self.lib.sparsepr_support_diagnostics(ctypes.byref(self.prm), _p(q), _p(k), _p(sets), n_sets, s,
+                                                      float(mass), _p(rows), _p(union), _p(ws), ws.numel(),
+                                                      _stream()))
+        return rows, union
+
     def dense(self, q, k, v, out=None):
         self._check_qkv(q, k, v)
         c = self.cfg

@@ -249,7 +249,6 @@ sparsepr_status sparsepr_dense_attention(const sparsepr_params* params, const vo
                                          void* workspace, size_t workspace_bytes,
                                          void* stream);
 
-/* Static description of a status code. */
 /* Residual diagnostics (PSRR, partition paragraph: how much of the hard-drop residual is
  * an affine function of the sparse output, and the energy orthogonal to it; the page
  * compares these between its partition and a semantic one).  For every query head, over
@@ -268,6 +267,29 @@ sparsepr_status sparsepr_residual_diagnostics(const sparsepr_params* params, con
                                               const sparsepr_route_t* route, double* out, void* workspace,
                                               size_t workspace_bytes, void* stream);
 
+/* Support diagnostics (PSRR, support paragraph: a single query row keeps 90 % of its
+ * attention mass on few keys, while queries that share one route must keep the union of
+ * their supports).  For each query head h and each set of set_size query tokens:
+ *   support of a row = the fewest keys whose softmax probabilities (scale from params)
+ *   reach `mass` of the row's total, taken by decreasing score, ties by lower key index;
+ *   row_support[h][s][i] = its size, shared_support[h][s] = size of the union over the set.
+ *   sets:  [Hq, n_sets, set_size] int32 token indices (device); an index outside [0, n)
+ *          marks that row invalid: its row_support is -1 and it is left out of the union.
+ *   row_support [Hq, n_sets, set_size], shared_support [Hq, n_sets]: int32 (device).
+ *   1 <= set_size <= 16, n_sets >= 0 (0: nothing to do), 0 < mass <= 1.
+ * Scores are fp32 dot products of the stored Q and K values; probabilities enter the
+ * decision as floor(2^40 p / p_max) in 64-bit integers, so keys below 2^-40 of the row's
+ * largest probability carry no mass.  The workspace (sparsepr_support_workspace_size)
+ * holds set_size * n fp32 scores for each of up to 512 concurrent (head, set) items.
+ * Needs only params, Q and K (no partition).  Not part of the timed call. */
+sparsepr_status sparsepr_support_workspace_size(const sparsepr_params* params, int n_sets, int set_size,
+                                                size_t* bytes);
+sparsepr_status sparsepr_support_diagnostics(const sparsepr_params* params, const void* q, const void* k,
+                                             const int32_t* sets, int n_sets, int set_size, double mass,
+                                             int32_t* row_support, int32_t* shared_support, void* workspace,
+                                             size_t workspace_bytes, void* stream);
+
+/* Static description of a status code. */
 const char* sparsepr_status_string(sparsepr_status status);
 
 #ifdef __cplusplus

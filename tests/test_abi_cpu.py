@@ -110,3 +110,26 @@ def test_entry_points_reject_before_any_launch():
     assert lib.sparsepr_partition(ctypes.byref(good), fake, fake, fake, ctypes.byref(full), fake, 16,
                                   nul) == -5
     assert lib.sparsepr_status_string(-5) == b"workspace too small"
+
+
+def test_support_diagnostics_validation():
+    """Set sizes 1..16, n_sets >= 0 and 0 < mass <= 1 are checked on the host; zero sets is a
+    no-op that touches no pointer."""
+    lib = lib_or_skip()
+    p = _params()
+    out = ctypes.c_size_t(0)
+    assert lib.sparsepr_support_workspace_size(ctypes.byref(p), 8, 8, ctypes.byref(out)) == 0
+    assert out.value == 4 * 8 * 8 * p.n * 4          # 32 items, each 8 rows of n fp32 scores
+    assert lib.sparsepr_support_workspace_size(ctypes.byref(p), 1000, 8, ctypes.byref(out)) == 0
+    assert out.value == 512 * 8 * p.n * 4            # at most 512 concurrent items
+    for n_sets, s in [(-1, 8), (4, 0), (4, 17)]:
+        assert lib.sparsepr_support_workspace_size(ctypes.byref(p), n_sets, s, ctypes.byref(out)) == -6
+    nul = ctypes.c_void_p(0)
+    assert lib.sparsepr_support_diagnostics(ctypes.byref(p), nul, nul, nul, 0, 8, 0.9, nul, nul, nul, 0, nul) == 0
+    assert lib.sparsepr_support_diagnostics(ctypes.byref(p), nul, nul, nul, 4, 8, 0.9, nul, nul, nul, 0, nul) == -1
+    for mass in (0.0, 1.5, float("nan")):
+        assert lib.sparsepr_support_diagnostics(ctypes.byref(p), nul, nul, nul, 4, 8, mass, nul, nul, nul, 0,
+                                                nul) == -6
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.sparsepr_support_diagnostics(ctypes.byref(p), fake, fake, fake, 4, 8, 0.9, fake, fake, fake, 16,
+                                            nul) == -5
