@@ -190,6 +190,56 @@ def diagnostics_report(workload):
                       "partitions": out}), flush=True)
 
 
+def support_report(workload, n_sets=64, set_size=8):
+    """Single-row and shared-route 90 %-mass supports on one workload (summary page of
+    "Partition the Support, Reconstruct the Residual", support paragraph): per query head,
+    n_sets sets of set_size queries, either consecutive raster tokens at seeded random
+    starts or seeded random members of one query group of the response partition (group
+    drawn in proportion to its size).  Reports medians as fractions of N."""
+    import numpy as np
+    import torch
+
+    import free_block_sparse_sparsepr_amd as S
+    from sparsepr_workloads import CONFIGS, make_inputs
+
+    cfg = CONFIGS[workload]
+    dev = torch.device("cuda:0")
+    Q, K, V = make_inputs(cfg, threads=16)
+    tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    q, k, v = (torch.from_numpy(x).to(dev).to(tdt).contiguous() for x in (Q, K, V))
+    del Q, K, V
+    sp = S.SparsePR(S.config_from_workload(cfg), device=dev)
+    sp.partition(q, k, v)
+    labels = sp.part["query_labels"].cpu().numpy()
+    rng = np.random.default_rng(11)
+    starts = rng.integers(0, cfg.n - set_size + 1, (cfg.heads_q, n_sets))
+    kinds = {"consecutive_tokens": starts[..., None] + np.arange(set_size)}
+    grp = np.empty((cfg.heads_q, n_sets, set_size), np.int64)
+    for h in range(cfg.heads_q):
+        lab = labels[h // cfg.g]
+        for si in range(n_sets):
+            members = np.flatnonzero(lab == lab[rng.integers(0, cfg.n)])
+            grp[h, si] = rng.choice(members, set_size, replace=members.size < set_size)
+    kinds["one_query_group"] = grp
+    out = {}
+    for name, sets in kinds.items():
+        log(f"[support] {name}")
+        st = torch.from_numpy(sets.astype(np.int32)).to(dev)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        rows, union = sp.support_diagnostics(q, k, st, 0.9)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3
+        rows, union = rows.cpu().numpy() / cfg.n, union.cpu().numpy() / cfg.n
+        out[name] = {"single_row_median": float(np.median(rows)), "shared_median": float(np.median(union)),
+                     "single_row_median_per_head": [round(float(x), 4) for x in np.median(rows, axis=(1, 2))],
+                     "shared_median_per_head": [round(float(x), 4) for x in np.median(union, axis=1)],
+                     "call_ms": ms}
+    print(json.dumps({"support_report": cfg.name, "mass": 0.9, "sets_per_head": n_sets, "set_size": set_size,
+                      "data": "synthetic (seeded Fourier-feature Q/K, Gaussian V; no model weights)",
+                      "sets": out}), flush=True)
+
+
 def copy_probe(mib):
     """A plain copy of `mib` MiB (torch's device copy kernel), three launches on a source larger
     than the caches: each launch reads and writes exactly mib MiB."""
@@ -221,6 +271,9 @@ def main():
     ap.add_argument("--diagnostics", action="store_true",
                     help="instead of timing, print the affine-explainable fraction and orthogonal energy of "
                          "the hard-drop residual for the response-coupled and semantic partitions")
+    ap.add_argument("--support", action="store_true",
+                    help="instead of timing, print the median single-row and shared-route 90%%-mass supports "
+                         "for sets of 8 consecutive tokens and of 8 members of one query group")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (3 launches) and exit: the reference "
                          "kernel of known traffic for scaling the FETCH_SIZE / WRITE_SIZE counters")
@@ -233,6 +286,9 @@ def main():
         return
     if args.diagnostics:
         diagnostics_report(args.workload)
+        return
+    if args.support:
+        support_report(args.workload)
         return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for {args.gpus}); the SparsePR call "
