@@ -29,6 +29,7 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3
 STAGES_FUSED = ["partition", "route", "probe_fit", "attend_apply"]
 STAGES_UNFUSED = ["partition", "route", "attend", "probe_fit", "apply"]
+STAGES_OVERLAPPED = ["partition", "route", "probe_fit (second stream)", "attend", "apply"]
 
 
 def log(*a):
@@ -264,6 +265,13 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--unfused", action="store_true",
                     help="time the unfused order (attend -> probe_fit -> apply) instead of the fused one")
+    ap.add_argument("--order", choices=["fused", "unfused", "overlapped"], default=None,
+                    help="call order to time: fused (probe_fit -> attend_apply), unfused (attend -> probe_fit "
+                         "-> apply) or overlapped (probe_fit on a second stream beside attend, then apply); "
+                         "default fused")
+    ap.add_argument("--graph", action="store_true",
+                    help="after the eager timed region, capture one call of the same order in a HIP graph and "
+                         "time the same number of replays (reported under \"graph\")")
     ap.add_argument("--ablations", action="store_true",
                     help="instead of timing, print the output error against dense attention of the method and "
                          "each ablation switch (hard drop, semantic partition, unprojected ridge, uniform and "
@@ -314,21 +322,35 @@ def main():
     out = torch.empty((cfg.heads_q, cfg.n, cfg.d), dtype=tdt, device=dev)
     stream = torch.cuda.current_stream()
 
-    if args.unfused:
+    order = args.order or ("unfused" if args.unfused else "fused")
+    side = sp.side_stream() if order == "overlapped" else None
+    if order == "unfused":
         stages = STAGES_UNFUSED
         fns = [lambda: sp.partition(q, k, v), sp.route, sp.attend, lambda: sp.probe_fit(q), lambda: sp.apply(out)]
+        streams = [stream] * 5
+    elif order == "overlapped":
+        stages = STAGES_OVERLAPPED
+        fns = [lambda: sp.partition(q, k, v), sp.route, lambda: sp.probe_fit(q), sp.attend, lambda: sp.apply(out)]
+        streams = [stream, stream, side, stream, stream]
     else:
         stages = STAGES_FUSED
         fns = [lambda: sp.partition(q, k, v), sp.route, lambda: sp.probe_fit(q), lambda: sp.attend_apply(out)]
-    attn_stage = "attend" if args.unfused else "attend_apply"
+        streams = [stream] * 4
+    attn_stage = "attend_apply" if order == "fused" else "attend"
 
     def step(ev=None):
         for i, fn in enumerate(fns):
-            if ev is not None:
-                ev[i][0].record(stream)
-            fn()
-            if ev is not None:
-                ev[i][1].record(stream)
+            st = streams[i]
+            if st is not stream:
+                st.wait_stream(stream)      # the side branch starts after route
+            with torch.cuda.stream(st):
+                if ev is not None:
+                    ev[i][0].record(st)
+                fn()
+                if ev is not None:
+                    ev[i][1].record(st)
+            if i == len(fns) - 2 and side is not None:
+                stream.wait_stream(side)    # apply waits for the fit
 
     for i in range(args.warmup):
         step()
@@ -346,6 +368,21 @@ def main():
     stage_ms = {name: float(np.mean([events[s][i][0].elapsed_time(events[s][i][1]) for s in range(args.steps)]))
                 for i, name in enumerate(stages)}
     ms_per_step = wall * 1e3 / args.steps
+
+    graph = None
+    if args.graph:
+        g = sp.capture(q, k, v, out, order)
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            g.replay()
+        torch.cuda.synchronize()
+        gwall = time.perf_counter() - t0
+        graph = {"ms_per_call": gwall * 1e3 / args.steps, "calls_per_s": args.steps / gwall}
+        log(f"[bench] graph replays: {graph['ms_per_call']:.2f} ms/call")
+        del g
 
     pairs_kv = sp.route_buf["pairs"].cpu().numpy().astype(np.int64)
     routed = int(pairs_kv.sum()) * cfg.g                     # summed over query heads
@@ -386,12 +423,13 @@ def main():
                    "heads_kv": cfg.heads_kv, "d": cfg.d, "rho_exec_target": cfg.rho_exec,
                    "groups_q": cfg.groups_q, "groups_k": cfg.groups_k, "n_probe": cfg.n_probe,
                    "rank": cfg.rank, "r_k": cfg.r_k, "r_q": cfg.r_q, "lambda": cfg.lam},
-        "call_order": "unfused" if args.unfused else "fused",
-        "roofline": {"bound": "mfma", "kernel": "sparse attention (" + ("sparsepr_attend" if args.unfused else
+        "call_order": order,
+        "roofline": {"bound": "mfma", "kernel": "sparse attention (" + ("sparsepr_attend" if order != "fused" else
                      "sparsepr_attend_apply: attention with the fused write-back epilogue, plus the 64-row probe "
                      "write-back kernel") + ")",
                      "achieved": attend_tflops, "peak": peak, "unit": "TFLOP/s", "frac": attend_tflops / peak,
-                     "traffic": None if args.unfused else measured_traffic(cfg.name)},
+                     "traffic": None if order != "fused" else measured_traffic(cfg.name)},
+        "graph": graph,
         "effective_tflops_call": call_tflops, "effective_frac_call": call_tflops / peak,
         "realised_rho_route": rho_route, "realised_rho_exec": rho_exec,
         "routed_pairs": routed, "stage_ms": stage_ms, "dense": dense, "cpu_baseline": cpu,

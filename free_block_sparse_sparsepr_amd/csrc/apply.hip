@@ -89,6 +89,71 @@ __global__ __launch_bounds__(256) void apply_kernel(const float* __restrict__ o_
   }
 }
 
+// Fast path for correction rank 16 (the method's default): one lane = one group-major row
+// of one query head, held in registers; a wave covers 64 consecutive rows.  T = o A and
+// o + c0 + T B are computed with A, B and c0 read at wave-uniform addresses (scalar
+// loads, no LDS) and the row is written to its token-order position with 16-byte stores.
+// Coordinates beyond r_eff are zeroed once T is formed (A and B hold zeros there too).
+// Same accumulation order as apply_kernel.  grid (ceil(n / 256), Hq), block 256.
+constexpr int kApplyFastRank = 16;
+template <typename OutT, int D>
+__global__ __launch_bounds__(256) void apply_rows_kernel(const float* __restrict__ o_gm,
+                                                         const int32_t* __restrict__ qperm,
+                                                         const float* __restrict__ A, const float* __restrict__ B,
+                                                         const float* __restrict__ c0,
+                                                         const int32_t* __restrict__ r_eff, int n, int g,
+                                                         OutT* __restrict__ out) {
+  constexpr int RC = kApplyFastRank;
+  const int h = blockIdx.y, kv = h / g, j = h % g;
+  const int p = blockIdx.x * 256 + threadIdx.x;
+  const int re = min(r_eff[h], RC);
+  const float* Ah = A + (int64_t)h * D * RC;
+  const float* Bh = B + (int64_t)h * RC * D;
+  const float* ch = c0 + (int64_t)h * D;
+  const bool valid = p < n;
+  const float* orow = o_gm + (((int64_t)kv * n + (valid ? p : 0)) * g + j) * D;
+  float o[D];
+#pragma clang loop unroll(full)
+  for (int c = 0; c < D; c += 4) {
+    const float4 v = *reinterpret_cast<const float4*>(orow + c);
+    o[c] = v.x; o[c + 1] = v.y; o[c + 2] = v.z; o[c + 3] = v.w;
+  }
+  float t[RC];
+#pragma clang loop unroll(full)
+  for (int k = 0; k < RC; ++k) t[k] = 0.f;
+#pragma clang loop unroll(full)
+  for (int c = 0; c < D; ++c) {
+#pragma clang loop unroll(full)
+    for (int k = 0; k < RC; ++k) t[k] = fmaf(o[c], Ah[c * RC + k], t[k]);
+  }
+#pragma clang loop unroll(full)
+  for (int k = 0; k < RC; ++k) t[k] = k < re ? t[k] : 0.f;
+  if (!valid) return;
+  OutT* dst = out + ((int64_t)h * n + qperm[(int64_t)kv * n + p]) * D;
+#pragma clang loop unroll(full)
+  for (int c8 = 0; c8 < D; c8 += 8) {
+    float v[8];
+#pragma clang loop unroll(full)
+    for (int e = 0; e < 8; ++e) v[e] = o[c8 + e] + ch[c8 + e];
+#pragma clang loop unroll(full)
+    for (int k = 0; k < RC; ++k) {
+#pragma clang loop unroll(full)
+      for (int e = 0; e < 8; ++e) v[e] = fmaf(t[k], Bh[k * D + c8 + e], v[e]);
+    }
+    if constexpr (sizeof(OutT) == 4) {
+      *reinterpret_cast<float4*>(reinterpret_cast<float*>(dst) + c8) = make_float4(v[0], v[1], v[2], v[3]);
+      *reinterpret_cast<float4*>(reinterpret_cast<float*>(dst) + c8 + 4) = make_float4(v[4], v[5], v[6], v[7]);
+    } else {
+      uint4 pk;
+      pk.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+      pk.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+      pk.z = (uint32_t)f32_to_bf16(v[4]) | ((uint32_t)f32_to_bf16(v[5]) << 16);
+      pk.w = (uint32_t)f32_to_bf16(v[6]) | ((uint32_t)f32_to_bf16(v[7]) << 16);
+      *reinterpret_cast<uint4*>(reinterpret_cast<bf16_t*>(dst) + c8) = pk;
+    }
+  }
+}
+
 // Probe rows take their exact dense output.  grid Hq, block 256.
 template <typename OutT>
 __global__ void probe_writeback_kernel(const float* __restrict__ o_dense, const int32_t* __restrict__ ptok, int n,
@@ -104,7 +169,10 @@ template <typename OutT, int D>
 static void apply_typed(const Dims& dm, const float* o_gm, const sparsepr_partition_t& part, const sparsepr_fit_t& fit,
                         OutT* o, hipStream_t s) {
   const dim3 grid((unsigned)ceil_div(dm.n, 64), dm.hq);
-  if (dm.rc <= kMaxRank)
+  if (dm.rc == kApplyFastRank)
+    hipLaunchKernelGGL((apply_rows_kernel<OutT, D>), dim3((unsigned)ceil_div(dm.n, 256), dm.hq), dim3(256), 0, s,
+                       o_gm, part.query_perm, fit.A, fit.B, fit.c0, fit.r_eff, dm.n, dm.g, o);
+  else if (dm.rc <= kMaxRank)
     hipLaunchKernelGGL((apply_kernel<OutT, D, kMaxRank>), grid, dim3(256), 0, s, o_gm, part.query_perm, fit.A, fit.B,
                        fit.c0, fit.r_eff, dm.n, dm.g, dm.rc, o);
   else

@@ -186,6 +186,45 @@ class SparsePR:
         self.probe_fit(q)
         return self.attend_apply(out)
 
+    def side_stream(self):
+        """The second stream of the overlapped order (default priority), created on first use."""
+        if getattr(self, "_side", None) is None:
+            self._side = torch.cuda.Stream(device=self.o_gm.device)
+        return self._side
+
+    def overlapped(self, q, k, v, out=None):
+        """Unfused order with the probe stage on a second stream: partition -> route, then
+        probe_fit (second stream) concurrently with attend (current stream), then apply once
+        both are done.  The two branches share only read-only partition and route buffers:
+        attend writes o_gm and lse, probe_fit writes the fit buffers and the workspace."""
+        main = torch.cuda.current_stream()
+        side = self.side_stream()
+        self.partition(q, k, v)
+        self.route()
+        side.wait_stream(main)
+        with torch.cuda.stream(side):
+            self.probe_fit(q)
+        self.attend()
+        main.wait_stream(side)
+        return self.apply(out)
+
+    def capture(self, q, k, v, out, order="fused"):
+        """Records one whole call of the given order ("fused", "unfused" or "overlapped") into
+        a HIP graph and returns it (``graph.replay()`` reruns the call on the same buffers).
+        One eager call runs first, on a side stream, so that one-time set-up (the route's
+        exponential table upload) happens outside the capture."""
+        fn = {"fused": self.fused, "unfused": self.__call__, "overlapped": self.overlapped}[order]
+        warm = torch.cuda.Stream(device=out.device)
+        warm.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(warm):
+            fn(q, k, v, out)
+        torch.cuda.current_stream().wait_stream(warm)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            fn(q, k, v, out)
+        return graph
+
     def residual_diagnostics(self, q, k, v):
         """[Hq, 4] float64: ||R||^2, ||R - mean R||^2, affine-orthogonal energy, explainable
         fraction of R = O_dense - O_sparse over every row (needs partition and route first;
