@@ -61,7 +61,10 @@ def cpu_baseline(cfg):
                       f"nproc {os.cpu_count()}"}
 
 
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "sparse_attention_720p_n118800_h24_hbm_traffic.md")
+TRAFFIC_PROFILES = {   # call order -> counter summary of that order's attention kernel
+    "fused": os.path.join(ROOT, "profiles", "sparse_attention_720p_n118800_h24_hbm_traffic.md"),
+    "overlapped": os.path.join(ROOT, "profiles", "sparse_attention_overlapped_720p_n118800_h24_hbm_traffic.md"),
+}
 KERNEL_SOURCES = ["free_block_sparse_sparsepr_amd/csrc/attend_mfma.hip", "free_block_sparse_sparsepr_amd/csrc/sp_attn.hpp",
                   "free_block_sparse_sparsepr_amd/csrc/sp_common.hpp"]
 
@@ -75,17 +78,22 @@ def kernel_source_hash():
     return h.hexdigest()
 
 
-def measured_traffic(workload_name):
-    """HBM bytes per launch of the attention kernel from the committed counter summary
-    (FETCH_SIZE + WRITE_SIZE, each scaled against a plain copy of known size), or None when
-    the summary is missing, covers another workload, or the kernel sources have changed since."""
+def measured_traffic(workload_name, order):
+    """HBM bytes per launch of the attention kernel from the committed counter summary of
+    this call order (FETCH_SIZE + WRITE_SIZE, each scaled against a plain copy of known
+    size), or None when the summary is missing, covers another workload or order, or the
+    kernel sources have changed since."""
+    if order not in TRAFFIC_PROFILES:
+        return None
     try:
-        text = open(TRAFFIC_PROFILE).read()
+        text = open(TRAFFIC_PROFILES[order]).read()
         block = text.split("```json", 1)[1].split("```", 1)[0]
         rec = json.loads(block)
     except (OSError, IndexError, ValueError):
         return None
     if rec.get("workload") != workload_name or rec.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    if rec.get("call_order", "fused") != order:
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -267,8 +275,8 @@ def main():
                     help="time the unfused order (attend -> probe_fit -> apply) instead of the fused one")
     ap.add_argument("--order", choices=["fused", "unfused", "overlapped"], default=None,
                     help="call order to time: fused (probe_fit -> attend_apply), unfused (attend -> probe_fit "
-                         "-> apply) or overlapped (probe_fit on a second stream beside attend, then apply); "
-                         "default fused")
+                         "-> apply) or overlapped (probe_fit on a second stream beside attend, then apply; the "
+                         "default, measured fastest)")
     ap.add_argument("--graph", action="store_true",
                     help="after the eager timed region, capture one call of the same order in a HIP graph and "
                          "time the same number of replays (reported under \"graph\")")
@@ -322,7 +330,7 @@ def main():
     out = torch.empty((cfg.heads_q, cfg.n, cfg.d), dtype=tdt, device=dev)
     stream = torch.cuda.current_stream()
 
-    order = args.order or ("unfused" if args.unfused else "fused")
+    order = args.order or ("unfused" if args.unfused else "overlapped")
     side = sp.side_stream() if order == "overlapped" else None
     if order == "unfused":
         stages = STAGES_UNFUSED
@@ -428,7 +436,7 @@ def main():
                      "sparsepr_attend_apply: attention with the fused write-back epilogue, plus the 64-row probe "
                      "write-back kernel") + ")",
                      "achieved": attend_tflops, "peak": peak, "unit": "TFLOP/s", "frac": attend_tflops / peak,
-                     "traffic": None if order != "fused" else measured_traffic(cfg.name)},
+                     "traffic": measured_traffic(cfg.name, order)},
         "graph": graph,
         "effective_tflops_call": call_tflops, "effective_frac_call": call_tflops / peak,
         "realised_rho_route": rho_route, "realised_rho_exec": rho_exec,
