@@ -51,6 +51,8 @@ class Params:
     lam: float = 0.1
     kmeans_iters: int = 10
     scale: float = 0.0       # 0 -> 1/sqrt(d)
+    tile_cost: int = 0       # 0: cell cost n_a n_b; 64: tile-padded cost (budget variant)
+    global_budget: bool = False   # one budget shared by all KV heads (budget variant)
 
     def softmax_scale(self, d):
         return self.scale if self.scale > 0 else 1.0 / np.sqrt(d)
@@ -339,31 +341,58 @@ class Route:
     mass: np.ndarray         # [G_Q, G_K]
 
 
-def select_cells(m, q_counts, k_counts, rho, n, n_probe):
+def cell_costs(q_counts, k_counts, tile=0):
+    """Cost of every cell (a, b) in query-key pairs: n_a n_b, or with ``tile`` > 0 the
+    pairs of the tiles it occupies, ceil(n_a / tile) tile x ceil(n_b / tile) tile (a cell is
+    an indivisible routing unit and the kernel executes whole tiles; execution paragraph).
+    Empty groups cost 0."""
+    qc = np.asarray(q_counts, dtype=np.int64)
+    kc = np.asarray(k_counts, dtype=np.int64)
+    if tile > 0:
+        qc = (qc + tile - 1) // tile * tile
+        kc = (kc + tile - 1) // tile * tile
+    return qc[:, None] * kc[None, :]
+
+
+def _mandatory(m, q_counts, k_counts):
+    """Every non-empty query group keeps its heaviest non-empty key group (ties: smaller b),
+    so the renormalised set is never empty."""
+    qc, kc = np.asarray(q_counts), np.asarray(k_counts)
+    mand = np.zeros(m.shape, dtype=bool)
+    for a in range(m.shape[0]):
+        if qc[a] == 0 or not np.any(kc > 0):
+            continue
+        mand[a, int(np.argmax(np.where(kc > 0, m[a], -1)))] = True
+    return mand
+
+
+def _route_of(kept, mand, m, q_counts, k_counts, budget):
+    Gq = kept.shape[0]
+    row_ptr = np.concatenate([[0], np.cumsum(kept.sum(axis=1))]).astype(np.int64)
+    cols = np.concatenate([np.nonzero(kept[a])[0] for a in range(Gq)]).astype(np.int64) \
+        if kept.any() else np.zeros(0, np.int64)
+    pairs = int(cell_costs(q_counts, k_counts)[kept].sum())
+    return Route(kept, mand, row_ptr, cols, pairs, budget, m)
+
+
+def select_cells(m, q_counts, k_counts, rho, n, n_probe, tile=0):
     """Top-cell selection to the target execution density.
 
     Reading (the order and the overshoot rule are not on the page; cells are
     indivisible so the realised density deviates from the target, and the page reports
     realised values): every non-empty query group keeps its heaviest non-empty key
     group (ties: smaller b) so the renormalised set is never empty; the remaining
-    non-empty cells are ranked by mass per pair m_ab / (n_a n_b) (exact rational
+    non-empty cells are ranked by mass per unit cost m_ab / c_ab (exact rational
     comparison), larger first, ties to smaller a*G_K + b, and the longest prefix whose
     cost fits the budget left after the mandatory cells is kept (a fractional-knapsack
-    order for retained mass)."""
+    order for retained mass).  c_ab = n_a n_b, or tile-padded with ``tile`` > 0; the
+    reported pairs are always the unpadded n_a n_b of the kept cells."""
     m = np.asarray(m, dtype=np.int64)
     Gq, Gk = m.shape
-    qc = np.asarray(q_counts, dtype=np.int64)
-    kc = np.asarray(k_counts, dtype=np.int64)
-    cost = qc[:, None] * kc[None, :]
+    cost = cell_costs(q_counts, k_counts, tile)
     B = route_budget(rho, n, n_probe)
-    kept = np.zeros((Gq, Gk), dtype=bool)
-    mand = np.zeros((Gq, Gk), dtype=bool)
-    for a in range(Gq):
-        if qc[a] == 0 or not np.any(kc > 0):
-            continue
-        cand = np.where(kc > 0, m[a], -1)
-        b = int(np.argmax(cand))
-        mand[a, b] = kept[a, b] = True
+    mand = _mandatory(m, q_counts, k_counts)
+    kept = mand.copy()
     left = B - int(cost[mand].sum())
     ranked = []
     for a in range(Gq):
@@ -378,18 +407,60 @@ def select_cells(m, q_counts, k_counts, rho, n, n_probe):
             break
         kept[a, b] = True
         used += c
-    row_ptr = np.concatenate([[0], np.cumsum(kept.sum(axis=1))]).astype(np.int64)
-    cols = np.concatenate([np.nonzero(kept[a])[0] for a in range(Gq)]).astype(np.int64) \
-        if kept.any() else np.zeros(0, np.int64)
-    pairs = int(cost[kept].sum())
-    return Route(kept, mand, row_ptr, cols, pairs, B, m)
+    return _route_of(kept, mand, m, q_counts, k_counts, B)
+
+
+def select_cells_global(ms, q_counts, k_counts, rho, n, n_probe, tile=0):
+    """Budget shared by all KV heads of the call (a variant the page leaves open: heads
+    whose mass is concentrated can take budget from diffuse ones).  The mandatory cells
+    stay per head; the budget is H_kv times the per-head budget; the remaining cells of
+    all heads are ranked together by m_ab / c_ab, larger first, ties to the smaller
+    (head, a*G_K + b), and the longest prefix that fits is kept.  Returns one Route per
+    head (each reports the shared budget)."""
+    H = len(ms)
+    B = route_budget(rho, n, n_probe) * H
+    costs = [cell_costs(q_counts[h], k_counts[h], tile) for h in range(H)]
+    mands = [_mandatory(np.asarray(ms[h], np.int64), q_counts[h], k_counts[h]) for h in range(H)]
+    kepts = [mk.copy() for mk in mands]
+    left = B - sum(int(costs[h][mands[h]].sum()) for h in range(H))
+    ranked = []
+    for h in range(H):
+        m = np.asarray(ms[h], np.int64)
+        Gq, Gk = m.shape
+        for a in range(Gq):
+            for b in range(Gk):
+                if costs[h][a, b] > 0 and not mands[h][a, b]:
+                    ranked.append((-Fraction(int(m[a, b]), int(costs[h][a, b])), h, a * Gk + b, a, b))
+    ranked.sort()
+    used = 0
+    for _, h, _, a, b in ranked:
+        c = int(costs[h][a, b])
+        if used + c > left:
+            break
+        kepts[h][a, b] = True
+        used += c
+    return [_route_of(kepts[h], mands[h], np.asarray(ms[h], np.int64), q_counts[h], k_counts[h], B)
+            for h in range(H)]
 
 
 def route(part: Partition, p: Params, n):
+    """Route of one KV head with its own budget (the global budget needs every head: see
+    route_heads)."""
     qc = np.diff(part.q_offsets)
     kc = np.diff(part.k_offsets)
     m = block_mass(part.U, part.q_labels, kc, p.groups_q)
-    return select_cells(m, qc, kc, p.rho_exec, n, p.n_probe)
+    return select_cells(m, qc, kc, p.rho_exec, n, p.n_probe, p.tile_cost)
+
+
+def route_heads(parts, p: Params, n):
+    """Routes of all KV heads of a call: per head, or with p.global_budget one shared
+    budget."""
+    if not p.global_budget:
+        return [route(part, p, n) for part in parts]
+    qcs = [np.diff(part.q_offsets) for part in parts]
+    kcs = [np.diff(part.k_offsets) for part in parts]
+    ms = [block_mass(part.U, part.q_labels, kc, p.groups_q) for part, kc in zip(parts, kcs)]
+    return select_cells_global(ms, qcs, kcs, p.rho_exec, n, p.n_probe, p.tile_cost)
 
 
 # --------------------------------------------------------------------------------------

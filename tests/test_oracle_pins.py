@@ -3,6 +3,7 @@ invariants stated on the pages, and brute force on tiny inputs.  CPU only."""
 import decimal
 import itertools
 import math
+from fractions import Fraction
 
 import numpy as np
 import pytest
@@ -653,3 +654,88 @@ def test_shared_support_dominant_keys_and_bounds():
     assert (union >= count.max(axis=1)).all() and (union <= count.sum(axis=1)).all()
     c1, u1 = D.shared_supports(q, k, 0.5, np.full((1, 8), 5), 0.9)
     assert u1[0] == c1[0, 0]
+
+
+# ----------------------------------------------------------------------------- budget variants
+def test_tile_padded_costs_and_ranking_by_hand():
+    """Tile-padded cost: ceil(n/64)*64 per side, empty groups free.  Worked by hand: one
+    query group of 64 rows, key groups of 10, 64 and 70 keys with masses 100, 500, 600 and a
+    budget of 9000 pairs.  Unpadded: the mandatory cell is b=2 (4480 pairs), then b=0
+    (ratio 100/640) fits and b=1 (4096) does not.  Padded: b=2 costs 8192, b=1 now ranks
+    first (500/4096 > 100/4096) and does not fit in the 808 left, so the prefix stops."""
+    np.testing.assert_array_equal(O.cell_costs([65, 64, 0], [1, 128], tile=64),
+                                  [[128 * 64, 128 * 128], [64 * 64, 64 * 128], [0, 0]])
+    np.testing.assert_array_equal(O.cell_costs([65, 3], [7], tile=0), [[455], [21]])
+    m = np.array([[100, 500, 600]])
+    assert O.route_budget(0.009, 1000, 0) == 9000
+    r0 = O.select_cells(m, [64], [10, 64, 70], 0.009, 1000, 0)
+    r1 = O.select_cells(m, [64], [10, 64, 70], 0.009, 1000, 0, tile=64)
+    assert list(r0.kept[0]) == [True, False, True] and r0.pairs == 640 + 4480
+    assert list(r1.kept[0]) == [False, False, True] and r1.pairs == 4480
+
+
+def test_tile_padded_equals_unpadded_on_whole_tiles():
+    """Group sizes that are multiples of 64 make the two cost models identical."""
+    qc = 64 * RNG.integers(0, 4, 6)
+    kc = 64 * RNG.integers(0, 4, 5)
+    n = int(qc.sum())
+    m = RNG.integers(0, 10 ** 9, (6, 5))
+    for rho in (0.1, 0.3, 0.6):
+        a = O.select_cells(m, qc, kc, rho, n, 4)
+        b = O.select_cells(m, qc, kc, rho, n, 4, tile=64)
+        np.testing.assert_array_equal(a.kept, b.kept)
+
+
+def test_global_budget_single_head_is_the_per_head_route():
+    n = 400
+    qc = np.bincount(RNG.integers(0, 6, n), minlength=6)
+    kc = np.bincount(RNG.integers(0, 5, n), minlength=5)
+    m = RNG.integers(0, 10 ** 9, (6, 5))
+    for rho in (0.05, 0.3):
+        for tile in (0, 64):
+            a = O.select_cells(m, qc, kc, rho, n, 8, tile)
+            (b,) = O.select_cells_global([m], [qc], [kc], rho, n, 8, tile)
+            np.testing.assert_array_equal(a.kept, b.kept)
+
+
+def test_global_budget_moves_budget_to_the_concentrated_head():
+    """Two heads, one query group, four key groups of 50 keys and 100 queries (cells of
+    5000 pairs), per-head budget 3 cells.  Head 0's masses all beat head 1's: per head each
+    keeps its mandatory cell plus two; with the shared budget of 6 cells head 0 keeps all
+    four and head 1 its mandatory cell plus one (the best of its remaining three)."""
+    n = 1000
+    qc, kc = np.array([100]), np.array([50, 50, 50, 50])
+    m0, m1 = np.array([[900, 800, 700, 600]]), np.array([[40, 10, 30, 20]])
+    rho = 0.015          # 15000 pairs per head with no probes
+    assert O.route_budget(rho, n, 0) == 15000
+    per = [O.select_cells(m, qc, kc, rho, n, 0) for m in (m0, m1)]
+    assert [list(r.kept[0]) for r in per] == [[True, True, True, False], [True, False, True, True]]
+    glob = O.select_cells_global([m0, m1], [qc, qc], [kc, kc], rho, n, 0)
+    assert [list(r.kept[0]) for r in glob] == [[True, True, True, True], [True, False, True, False]]
+    assert sum(r.pairs for r in glob) == 6 * 5000
+
+
+@pytest.mark.parametrize("tile", [0, 64])
+def test_global_budget_is_a_feasible_maximal_prefix(tile):
+    """Over random heads: the kept cost fits the shared budget, every kept optional cell
+    precedes every dropped one in the shared order (ratio, then head, then cell), and the
+    first dropped cell would not fit."""
+    H, n = 3, 600
+    qcs = [np.bincount(RNG.integers(0, 5, n), minlength=5) for _ in range(H)]
+    kcs = [np.bincount(RNG.integers(0, 6, n), minlength=6) for _ in range(H)]
+    ms = [RNG.integers(0, 10 ** 8, (5, 6)) for _ in range(H)]
+    rs = O.select_cells_global(ms, qcs, kcs, 0.2, n, 4, tile)
+    costs = [O.cell_costs(qcs[h], kcs[h], tile) for h in range(H)]
+    total = sum(int(costs[h][rs[h].kept].sum()) for h in range(H))
+    assert total <= 3 * O.route_budget(0.2, n, 4) or all(
+        (rs[h].kept == rs[h].mandatory).all() for h in range(H))
+    opt = [(Fraction(int(ms[h][a, b]), int(costs[h][a, b])), h, a * 6 + b, bool(rs[h].kept[a, b]))
+           for h in range(H) for a in range(5) for b in range(6)
+           if costs[h][a, b] > 0 and not rs[h].mandatory[a, b]]
+    opt.sort(key=lambda t: (-t[0], t[1], t[2]))
+    flags = [t[3] for t in opt]
+    first_drop = flags.index(False) if False in flags else len(flags)
+    assert all(flags[:first_drop]) and not any(flags[first_drop:])
+    if first_drop < len(opt):
+        _, h, c, _ = opt[first_drop]
+        assert total + int(costs[h][c // 6, c % 6]) > 3 * O.route_budget(0.2, n, 4)
