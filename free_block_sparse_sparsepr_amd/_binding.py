@@ -14,6 +14,8 @@ BF16, FP32 = 0, 1
 ABLATE_NONE, ABLATE_HARD_DROP, ABLATE_RIDGE_ONLY = 0, 1, 2
 PROBES_RADIAL, PROBES_UNIFORM, PROBES_GIVEN = 0, 1, 2
 PARTITION_RESPONSE, PARTITION_SEMANTIC = 0, 1
+BUDGET_PER_HEAD, BUDGET_GLOBAL = 0, 1
+COST_PAIRS, COST_TILES = 0, 1
 STATUS = {0: "ok", -1: "null pointer", -2: "shape", -3: "dtype", -4: "alignment",
           -5: "workspace", -6: "parameter", -7: "HIP failure"}
 
@@ -26,7 +28,8 @@ class Params(ctypes.Structure):
                 ("rho_exec", ctypes.c_float), ("block", ctypes.c_int32),
                 ("kmeans_iters", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
                 ("ablation", ctypes.c_int32), ("probe_mode", ctypes.c_int32),
-                ("partition_mode", ctypes.c_int32)]
+                ("partition_mode", ctypes.c_int32), ("budget_mode", ctypes.c_int32),
+                ("cost_mode", ctypes.c_int32)]
 
 
 def _ptr_struct(name, names):

@@ -25,6 +25,8 @@ Dims dims_of(const sparsepr_params& p) {
   d.semantic = p.partition_mode == SPARSEPR_PARTITION_SEMANTIC;
   d.fq = d.semantic ? p.d : p.groups_k;
   d.rc = p.ablation == SPARSEPR_ABLATE_RIDGE_ONLY ? p.n_probe : p.rank;
+  d.global_budget = p.budget_mode == SPARSEPR_BUDGET_GLOBAL;
+  d.tile = p.cost_mode == SPARSEPR_COST_TILES ? p.block : 0;
   d.scale = p.softmax_scale > 0.f ? p.softmax_scale : (float)(1.0 / std::sqrt((double)p.d));
   d.lambda = p.lambda;
   d.bf16 = p.dtype == SPARSEPR_BF16;
@@ -62,7 +64,19 @@ Workspace plan_workspace(const sparsepr_params& p) {
   w.fused_ogm = 0;
   w.total_fused = (p.dtype == SPARSEPR_BF16 && p.heads_q == p.heads_kv)
                       ? 0 : align_up(hkv * n * (size_t)(p.heads_q / p.heads_kv) * p.d * 4);
+  {
+    const size_t cells = hkv * (size_t)p.groups_q * (size_t)p.groups_k;
+    size_t r = 0;
+    w.rt_order = r; r = align_up(r + cells * 4);
+    w.rt_pos = r; r = align_up(r + cells * 4);
+    w.rt_prefix = r; r = align_up(r + cells * 8);
+    w.rt_cost = r; r = align_up(r + cells * 8);
+    w.rt_kept = r; r = align_up(r + cells);
+    w.rt_head = r; r = align_up(r + hkv * 16);
+    w.total_route = p.budget_mode == SPARSEPR_BUDGET_GLOBAL ? r : 0;
+  }
   w.total = w.total_partition;
+  if (w.total_route > w.total) w.total = w.total_route;
   if (w.total_fused > w.total) w.total = w.total_fused;
   if (w.total_probe > w.total) w.total = w.total_probe;
   if (w.total_dense > w.total) w.total = w.total_dense;
@@ -88,6 +102,9 @@ static sparsepr_status check_params(const sparsepr_params* p) {
   if (p->kmeans_iters < 0 || p->kmeans_iters > 64) return SPARSEPR_ERR_PARAM;
   if (p->block != 64) return SPARSEPR_ERR_PARAM;
   if (!(p->softmax_scale >= 0.f) || !std::isfinite(p->softmax_scale)) return SPARSEPR_ERR_PARAM;
+  if (p->budget_mode != SPARSEPR_BUDGET_PER_HEAD && p->budget_mode != SPARSEPR_BUDGET_GLOBAL)
+    return SPARSEPR_ERR_PARAM;
+  if (p->cost_mode != SPARSEPR_COST_PAIRS && p->cost_mode != SPARSEPR_COST_TILES) return SPARSEPR_ERR_PARAM;
   if (p->ablation != SPARSEPR_ABLATE_NONE && p->ablation != SPARSEPR_ABLATE_HARD_DROP &&
       p->ablation != SPARSEPR_ABLATE_RIDGE_ONLY)
     return SPARSEPR_ERR_PARAM;
@@ -209,8 +226,6 @@ sparsepr_status sparsepr_partition(const sparsepr_params* params, const void* q,
 
 sparsepr_status sparsepr_route(const sparsepr_params* params, const sparsepr_partition_t* part,
                                const sparsepr_route_t* out, void* workspace, size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   sparsepr_status st = check_params(params);
   if (st != SPARSEPR_OK) return st;
   if (!part || !out) return SPARSEPR_ERR_NULL;
@@ -218,9 +233,13 @@ sparsepr_status sparsepr_route(const sparsepr_params* params, const sparsepr_par
     return SPARSEPR_ERR_NULL;
   if (!out->row_ptr || !out->cols || !out->kept_mask || !out->pairs || !out->cell_mass) return SPARSEPR_ERR_NULL;
   if (((uintptr_t)out->cell_mass & 7u) != 0) return SPARSEPR_ERR_ALIGN;
+  const Workspace wp = plan_workspace(*params);
+  st = check_ws(params, workspace, workspace_bytes, wp.total_route);
+  if (st != SPARSEPR_OK) return st;
   (void)hipGetLastError();
   if (ensure_exp_table() != hipSuccess) return SPARSEPR_ERR_HIP;
-  launch_route(dims_of(*params), route_budget(*params), *part, *out, (hipStream_t)stream);
+  launch_route(dims_of(*params), route_budget(*params), *part, *out, wp, static_cast<char*>(workspace),
+               (hipStream_t)stream);
   return hip_status();
 }
 

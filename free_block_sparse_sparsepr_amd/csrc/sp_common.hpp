@@ -90,6 +90,7 @@ struct Workspace {
   size_t partials, fitbuf, probe_alloc, total_probe;
   size_t dense_meta, total_dense;
   size_t fused_ogm, total_fused;
+  size_t rt_order, rt_pos, rt_prefix, rt_cost, rt_kept, rt_head, total_route;   // global route budget
   size_t total;
   int fpk, fpq, nchunks;
 };
@@ -101,6 +102,8 @@ struct Dims {
   bool semantic;   // partition on raw activations (ablation)
   int fq;          // query feature width: G_K, or d for the semantic partition
   int rc;   // correction rank: columns of A / rows of B (rank, or m for the unprojected ridge)
+  bool global_budget;   // one route budget shared by all KV heads
+  int tile;             // cell cost padded to tile x tile blocks (0: unpadded pairs)
   float scale, lambda;
   bool bf16;
 };

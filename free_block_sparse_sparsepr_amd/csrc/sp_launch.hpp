@@ -16,7 +16,7 @@ void launch_transpose_v(const Dims& dm, const void* v, void* vt, hipStream_t s);
 void launch_partition(const Dims& dm, const Workspace& wp, const void* q, const void* k, const void* v,
                       const sparsepr_partition_t& out, char* ws, hipStream_t s);
 void launch_route(const Dims& dm, int64_t budget, const sparsepr_partition_t& part, const sparsepr_route_t& out,
-                  hipStream_t s);
+                  const Workspace& wp, char* ws, hipStream_t s);
 // out_is_input_dtype: output element type equals Q's (dense baseline); otherwise fp32.
 void launch_attention(const Dims& dm, AttnArgs a, bool out_is_input_dtype, hipStream_t s);
 void launch_attention_mfma(const Dims& dm, AttnArgs a, bool out_is_input_dtype, hipStream_t s);

@@ -32,6 +32,8 @@ class Config:
     ablation: int = 0           # _binding.ABLATE_*: 0 = the method
     probe_mode: int = 0         # _binding.PROBES_*: 0 = stratified radial probes
     partition_mode: int = 0     # _binding.PARTITION_*: 0 = response-coupled
+    budget_mode: int = 0        # _binding.BUDGET_*: 0 = per KV head, 1 = shared by all KV heads
+    cost_mode: int = 0          # _binding.COST_*: 0 = pairs, 1 = tile-padded pairs
 
     @property
     def key_feat(self):
@@ -65,7 +67,7 @@ class Config:
                         B.BF16 if self.dtype == "bf16" else B.FP32, self.groups_q, self.groups_k,
                         self.r_k, self.r_q, self.n_probe, self.rank, self.lam, self.rho_exec, 64,
                         self.kmeans_iters, self.softmax_scale, self.ablation, self.probe_mode,
-                        self.partition_mode)
+                        self.partition_mode, self.budget_mode, self.cost_mode)
 
 
 def _p(t):

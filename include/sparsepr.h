@@ -34,11 +34,14 @@
  *    heads_q / heads_kv <= 16, 1 <= groups_q, groups_k <= 64, groups <= n,
  *    groups_k <= r_q, 1 <= r_k <= 64, 1 <= n_probe <= min(64, n),
  *    1 <= rank <= min(32, n_probe, d), lambda > 0, n_probe / n < rho_exec <= 1,
- *    0 <= kmeans_iters <= 64, block == 64, ablation, probe_mode and partition_mode one
- *    of their enumerators.
+ *    0 <= kmeans_iters <= 64, block == 64, ablation, probe_mode, partition_mode, budget_mode
+ *    and cost_mode one of their enumerators.
  *
  * Unfused call order: partition -> route -> attend -> probe_fit -> apply.
  * Fused call order:   partition -> route -> probe_fit -> attend_apply.
+ * Overlapped order:   partition -> route -> (probe_fit on a second stream, attend) -> apply,
+ *                     with a separate workspace for probe_fit or none for attend (attend
+ *                     uses none) and apply ordered after both.
  */
 #ifndef SPARSEPR_H
 #define SPARSEPR_H
@@ -107,6 +110,29 @@ typedef enum {
                                       weight 1; group = the token's query label */
 } sparsepr_probe_mode;
 
+/* How the route's budget is shared (PSRR, execution paragraph: the router spends a
+ * budget of pairs after subtracting the probe cost; how it is split across heads is not
+ * stated). */
+typedef enum {
+  SPARSEPR_BUDGET_PER_HEAD = 0,    /* the method as read here: every KV head gets
+                                      floor(rho_ppm n^2 / 10^6) - n_probe n pairs */
+  SPARSEPR_BUDGET_GLOBAL = 1       /* one budget of H_kv times that, shared by all KV heads of
+                                      the call: mandatory cells stay per head, the other cells
+                                      of all heads are ranked together by mass per unit cost
+                                      (ties: smaller head, then smaller a G_K + b) and the
+                                      longest prefix that fits is kept.  Needs
+                                      sparsepr_workspace_size's workspace in sparsepr_route. */
+} sparsepr_budget_mode;
+
+/* What a cell costs the router (PSRR, execution paragraph: cells are indivisible units). */
+typedef enum {
+  SPARSEPR_COST_PAIRS = 0,         /* the method as read here: n_a n_b query-key pairs */
+  SPARSEPR_COST_TILES = 1          /* the pairs of the block x block tiles the cell occupies,
+                                      ceil(n_a / block) block x ceil(n_b / block) block, in the
+                                      ranking and in the budget; route.pairs still reports the
+                                      unpadded pairs */
+} sparsepr_cost_mode;
+
 /* Problem and hyper-parameters.  Defaults on the page: r_k = 48, r_q = 64, n_probe = 64,
  * rank = 16, lambda = 0.1 (PSRR, partition and probe-fit paragraphs); rho_exec is the
  * target total execution density rho_route + n_probe / n (PSRR, execution paragraph). */
@@ -130,6 +156,8 @@ typedef struct sparsepr_params {
   int32_t ablation;      /* sparsepr_ablation (0 = the method) */
   int32_t probe_mode;    /* sparsepr_probe_mode (0 = the method) */
   int32_t partition_mode;/* sparsepr_partition_mode (0 = the method) */
+  int32_t budget_mode;   /* sparsepr_budget_mode (0 = per KV head) */
+  int32_t cost_mode;     /* sparsepr_cost_mode (0 = pairs) */
 } sparsepr_params;
 
 /* Partition outputs (all caller-allocated device buffers).  g = heads_q / heads_kv.
@@ -199,8 +227,10 @@ sparsepr_status sparsepr_partition(const sparsepr_params* params, const void* q,
 /* Routing to the target execution density (PSRR, execution paragraph): fixed-point cell
  * masses from the size-weighted centroid softmax of every query row (summed over the
  * KV head's query heads), budget rho_exec n^2 - n_probe n pairs per head, one mandatory
- * heaviest cell per non-empty query group, the rest by mass per pair until the budget
- * is spent.  Reads responses_u, query_labels, query_offsets, key_offsets. */
+ * heaviest cell per non-empty query group, the rest by mass per unit cost until the
+ * budget is spent (budget_mode and cost_mode select the variants).  Reads responses_u,
+ * query_labels, query_offsets, key_offsets; the workspace is used by the global budget
+ * only (it may be NULL otherwise). */
 sparsepr_status sparsepr_route(const sparsepr_params* params, const sparsepr_partition_t* part,
                                const sparsepr_route_t* out, void* workspace,
                                size_t workspace_bytes, void* stream);

@@ -613,7 +613,15 @@ def probe_fit(q, k, v, scale, probes: Probes, q_labels, k_labels, kept, p: Param
     ybar + (o - xbar) W V_r V_r^T = o A B + c0 with A = W V_r, B = V_r^T,
     c0 = ybar - xbar A B."""
     od, os_, R, _, _ = probe_rows(q, k, v, scale, probes.tokens, q_labels, k_labels, kept)
-    W, xbar, ybar, Xt, Yt = ridge_fit(os_, R, probes.weights, p.lam)
+    return fit_from_probe_rows(od, os_, probes.weights, p)
+
+
+def fit_from_probe_rows(o_dense, o_sparse, weights, p: Params):
+    """The weighted ridge and rank-r projection given the probe rows' dense and sparse
+    outputs (R = O_dense - O_sparse)."""
+    od, os_ = f64(o_dense), f64(o_sparse)
+    R = od - os_
+    W, xbar, ybar, Xt, Yt = ridge_fit(os_, R, weights, p.lam)
     V, eig = output_subspace(Yt, p.rank)
     A = W @ V
     B = V.T

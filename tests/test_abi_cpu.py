@@ -67,7 +67,7 @@ def test_workspace_size_valid():
     (dict(rank=17, n_probe=16), -6), (dict(lam=0.0), -6), (dict(lam=float("nan")), -6),
     (dict(rho_exec=1.5), -6), (dict(rho_exec=0.01, n=4096), -6), (dict(kmeans_iters=-1), -6),
     (dict(block=32), -6), (dict(softmax_scale=-1.0), -6), (dict(ablation=3), -6), (dict(ablation=-1), -6),
-    (dict(probe_mode=3), -6), (dict(partition_mode=2), -6),
+    (dict(probe_mode=3), -6), (dict(partition_mode=2), -6), (dict(budget_mode=2), -6), (dict(cost_mode=-1), -6),
 ])
 def test_invalid_params_rejected(kw, code):
     st, _ = _ws(_params(**kw))
@@ -133,3 +133,20 @@ def test_support_diagnostics_validation():
     fake = ctypes.c_void_p(0x1000)
     assert lib.sparsepr_support_diagnostics(ctypes.byref(p), fake, fake, fake, 4, 8, 0.9, fake, fake, fake, 16,
                                             nul) == -5
+
+
+def test_global_budget_route_needs_its_workspace():
+    """The shared budget keeps per-head sorted cells in the workspace; the per-head route
+    needs none."""
+    lib = lib_or_skip()
+    _, n0 = _ws(_params(groups_q=64, groups_k=64, n=1 << 20))
+    st, n1 = _ws(_params(groups_q=64, groups_k=64, n=1 << 20, budget_mode=B.BUDGET_GLOBAL))
+    assert st == 0 and n1 >= n0
+    nul = ctypes.c_void_p(0)
+    fields = {f: 0x2000 for f in B.PARTITION_FIELDS}
+    part = B.PartitionT(**fields)
+    route = B.RouteT(**{f: 0x3000 for f in B.ROUTE_FIELDS})
+    g = _params(budget_mode=B.BUDGET_GLOBAL, cost_mode=B.COST_TILES)
+    assert lib.sparsepr_route(ctypes.byref(g), ctypes.byref(part), ctypes.byref(route), nul, 0, nul) == -1
+    assert lib.sparsepr_route(ctypes.byref(g), ctypes.byref(part), ctypes.byref(route), ctypes.c_void_p(0x1000), 16,
+                              nul) == -5
