@@ -106,6 +106,10 @@ ABLATIONS = {   # summary page of "Partition the Support, Reconstruct the Residu
     "ridge_only": dict(ablation=2),
     "uniform_probes": dict(probe_mode=1),
     "random_probes": dict(probe_mode=2),
+    # budget variants (execution paragraph: the router spends a pair budget over cells)
+    "tile_padded_costs": dict(cost_mode=1),
+    "global_budget": dict(budget_mode=1),
+    "global_budget_tile_padded": dict(budget_mode=1, cost_mode=1),
 }
 
 
@@ -147,7 +151,11 @@ def ablation_report(workload):
         torch.cuda.synchronize()
         err = (o.float() - dense).abs_().flatten()
         p99 = float(torch.quantile(err[::stride][: 1 << 24], 0.99))
+        pairs = sp.route_buf["pairs"].cpu().numpy().astype(np.int64)
         out[name] = {"mean_abs_err": float(err.mean()), "p99_abs_err": p99,
+                     "realised_rho_exec": float(pairs.mean()) / cfg.n ** 2 + cfg.n_probe / cfg.n,
+                     "rho_exec_min_max_over_heads": [float(pairs.min()) / cfg.n ** 2 + cfg.n_probe / cfg.n,
+                                                     float(pairs.max()) / cfg.n ** 2 + cfg.n_probe / cfg.n],
                      "probe_fit_plus_attend_ms": (time.perf_counter() - t0) * 1e3}
         del sp, o, err
         torch.cuda.empty_cache()
@@ -277,13 +285,17 @@ def main():
                     help="call order to time: fused (probe_fit -> attend_apply), unfused (attend -> probe_fit "
                          "-> apply) or overlapped (probe_fit on a second stream beside attend, then apply; the "
                          "default, measured fastest)")
+    ap.add_argument("--budget-mode", type=int, default=0, choices=[0, 1],
+                    help="route budget: 0 per KV head (the method), 1 one budget shared by all KV heads")
+    ap.add_argument("--cost-mode", type=int, default=0, choices=[0, 1],
+                    help="cell cost: 0 query-key pairs (the method), 1 tile-padded pairs")
     ap.add_argument("--graph", action="store_true",
                     help="after the eager timed region, capture one call of the same order in a HIP graph and "
                          "time the same number of replays (reported under \"graph\")")
     ap.add_argument("--ablations", action="store_true",
                     help="instead of timing, print the output error against dense attention of the method and "
                          "each ablation switch (hard drop, semantic partition, unprojected ridge, uniform and "
-                         "random probes) on the workload")
+                         "random probes) and budget variant (tile-padded costs, global budget) on the workload")
     ap.add_argument("--diagnostics", action="store_true",
                     help="instead of timing, print the affine-explainable fraction and orthogonal energy of "
                          "the hard-drop residual for the response-coupled and semantic partitions")
@@ -326,7 +338,7 @@ def main():
     q, k, v = (torch.from_numpy(x).to(dev).to(tdt).contiguous() for x in (Q, K, V))
     del Q, K, V
     log(f"[bench] inputs ready in {time.perf_counter() - t0:.1f} s")
-    sp = S.SparsePR(S.config_from_workload(cfg), device=dev)
+    sp = S.SparsePR(S.config_from_workload(cfg, budget_mode=args.budget_mode, cost_mode=args.cost_mode), device=dev)
     out = torch.empty((cfg.heads_q, cfg.n, cfg.d), dtype=tdt, device=dev)
     stream = torch.cuda.current_stream()
 
@@ -432,6 +444,8 @@ def main():
                    "groups_q": cfg.groups_q, "groups_k": cfg.groups_k, "n_probe": cfg.n_probe,
                    "rank": cfg.rank, "r_k": cfg.r_k, "r_q": cfg.r_q, "lambda": cfg.lam},
         "call_order": order,
+        "route_variant": {"budget_mode": ["per_kv_head", "global"][args.budget_mode],
+                          "cost_mode": ["pairs", "tile_padded"][args.cost_mode]},
         "roofline": {"bound": "mfma", "kernel": "sparse attention (" + ("sparsepr_attend" if order != "fused" else
                      "sparsepr_attend_apply: attention with the fused write-back epilogue, plus the 64-row probe "
                      "write-back kernel") + ")",
