@@ -281,10 +281,13 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--unfused", action="store_true",
                     help="time the unfused order (attend -> probe_fit -> apply) instead of the fused one")
-    ap.add_argument("--order", choices=["fused", "unfused", "overlapped"], default=None,
+    ap.add_argument("--chunks", type=int, default=4,
+                    help="KV-head chunks of the pipelined order")
+    ap.add_argument("--order", choices=["fused", "unfused", "overlapped", "pipelined"], default=None,
                     help="call order to time: fused (probe_fit -> attend_apply), unfused (attend -> probe_fit "
-                         "-> apply) or overlapped (probe_fit on a second stream beside attend, then apply; the "
-                         "default, measured fastest)")
+                         "-> apply), overlapped (probe_fit on a second stream beside attend, then apply) or "
+                         "pipelined (the fused order over --chunks chunks of KV heads on three streams, each "
+                         "chunk's partition, route and probe stage beside the previous chunk's attention)")
     ap.add_argument("--budget-mode", type=int, default=0, choices=[0, 1],
                     help="route budget: 0 per KV head (the method), 1 one budget shared by all KV heads")
     ap.add_argument("--cost-mode", type=int, default=0, choices=[0, 1],
@@ -344,7 +347,16 @@ def main():
 
     order = args.order or ("unfused" if args.unfused else "overlapped")
     side = sp.side_stream() if order == "overlapped" else None
-    if order == "unfused":
+    pipe = None
+    if order == "pipelined":
+        pipe = S.PipelinedSparsePR(S.config_from_workload(cfg, budget_mode=args.budget_mode,
+                                                          cost_mode=args.cost_mode),
+                                   chunks=args.chunks, device=dev, fused=True)
+        stages = STAGES_FUSED
+        nch = len(pipe.parts)
+    if order == "pipelined":
+        pass
+    elif order == "unfused":
         stages = STAGES_UNFUSED
         fns = [lambda: sp.partition(q, k, v), sp.route, sp.attend, lambda: sp.probe_fit(q), lambda: sp.apply(out)]
         streams = [stream] * 5
@@ -356,9 +368,12 @@ def main():
         stages = STAGES_FUSED
         fns = [lambda: sp.partition(q, k, v), sp.route, lambda: sp.probe_fit(q), lambda: sp.attend_apply(out)]
         streams = [stream] * 4
-    attn_stage = "attend_apply" if order == "fused" else "attend"
+    attn_stage = "attend_apply" if order in ("fused", "pipelined") else "attend"
 
     def step(ev=None):
+        if pipe is not None:
+            pipe(q, k, v, out, events=None if ev is None else {name: ev[i] for i, name in enumerate(stages)})
+            return
         for i, fn in enumerate(fns):
             st = streams[i]
             if st is not stream:
@@ -376,7 +391,9 @@ def main():
         step()
         log(f"[bench] warmup {i + 1}/{args.warmup}")
     torch.cuda.synchronize()
-    events = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+    per = nch if pipe is not None else 1
+    events = [[[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in range(per)]
+               if pipe is not None else [torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
                for _ in stages] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -385,13 +402,17 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     log(f"[bench] timed {args.steps} calls in {wall:.3f} s")
-    stage_ms = {name: float(np.mean([events[s][i][0].elapsed_time(events[s][i][1]) for s in range(args.steps)]))
-                for i, name in enumerate(stages)}
+    if pipe is not None:    # stage time summed over the chunks (each on its own stream)
+        stage_ms = {name: float(np.mean([sum(e0.elapsed_time(e1) for e0, e1 in events[s][i])
+                                          for s in range(args.steps)])) for i, name in enumerate(stages)}
+    else:
+        stage_ms = {name: float(np.mean([events[s][i][0].elapsed_time(events[s][i][1]) for s in range(args.steps)]))
+                    for i, name in enumerate(stages)}
     ms_per_step = wall * 1e3 / args.steps
 
     graph = None
     if args.graph:
-        g = sp.capture(q, k, v, out, order)
+        g = (pipe or sp).capture(q, k, v, out, order)
         for _ in range(args.warmup):
             g.replay()
         torch.cuda.synchronize()
@@ -404,7 +425,10 @@ def main():
         log(f"[bench] graph replays: {graph['ms_per_call']:.2f} ms/call")
         del g
 
-    pairs_kv = sp.route_buf["pairs"].cpu().numpy().astype(np.int64)
+    if pipe is not None:
+        pairs_kv = np.concatenate([p.route_buf["pairs"].cpu().numpy() for _, _, p in pipe.parts]).astype(np.int64)
+    else:
+        pairs_kv = sp.route_buf["pairs"].cpu().numpy().astype(np.int64)
     routed = int(pairs_kv.sum()) * cfg.g                     # summed over query heads
     executed = routed + cfg.heads_q * cfg.n_probe * cfg.n
     flop_attend = 4.0 * cfg.d * routed
@@ -443,7 +467,7 @@ def main():
                    "heads_kv": cfg.heads_kv, "d": cfg.d, "rho_exec_target": cfg.rho_exec,
                    "groups_q": cfg.groups_q, "groups_k": cfg.groups_k, "n_probe": cfg.n_probe,
                    "rank": cfg.rank, "r_k": cfg.r_k, "r_q": cfg.r_q, "lambda": cfg.lam},
-        "call_order": order,
+        "call_order": order if pipe is None else f"pipelined over {nch} chunks of KV heads (fused order per chunk)",
         "route_variant": {"budget_mode": ["per_kv_head", "global"][args.budget_mode],
                           "cost_mode": ["pairs", "tile_padded"][args.cost_mode]},
         "roofline": {"bound": "mfma", "kernel": "sparse attention (" + ("sparsepr_attend" if order != "fused" else

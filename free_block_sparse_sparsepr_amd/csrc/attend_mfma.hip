@@ -245,9 +245,7 @@ __device__ __forceinline__ void mfma_tile_step(const char* __restrict__ stage, c
 // data movement; A^T, B^T (bf16) and c0 are staged in the free LDS stages.  Rows are
 // scattered to token order through the query permutation.
 template <int D, int LDS_BYTES, int NT>
-__device__ __forceinline__ void fused_writeback(const AttnArgs& A, int kv, int vrow, bool qvalid, float inv,
-                                                f32x16_t* o, char* lds, int tid, int l32, int hf) {
-  constexpr int DBLK = D / 32;
+__device__ __forceinline__ void fused_stage(const AttnArgs& A, int kv, char* lds, int tid) {
   constexpr int RCM = kMaxCorrRank;  // up to 64 correction directions (two 32-row blocks of t)
   constexpr int AROW = D + 8;        // At[k][d] bf16, padded rows (conflict-free 16-byte reads)
   constexpr int BROW = RCM + 4;      // Bt[d][k] bf16, padded rows (conflict-free 8-byte reads)
@@ -266,6 +264,22 @@ __device__ __forceinline__ void fused_writeback(const AttnArgs& A, int kv, int v
   }
   for (int d = tid; d < D; d += NT) c0s[d] = A.fitc0[(int64_t)h * D + d];
   __syncthreads();
+}
+
+// The correction and scatter of one wave's 32 rows from A^T, B^T and c0 staged by
+// fused_stage.
+template <int D>
+__device__ __forceinline__ void fused_apply(const AttnArgs& A, int kv, int vrow, bool qvalid, float inv,
+                                            f32x16_t* o, const char* lds, int l32, int hf) {
+  constexpr int DBLK = D / 32;
+  constexpr int RCM = kMaxCorrRank;
+  constexpr int AROW = D + 8;
+  constexpr int BROW = RCM + 4;
+  const int h = kv;
+  const bf16_t* At = reinterpret_cast<const bf16_t*>(lds);
+  const bf16_t* Bt = At + RCM * AROW;
+  const float* c0s = reinterpret_cast<const float*>(Bt + D * BROW);
+  const int re = min(A.r_eff[h], min(A.rank, RCM));
   // normalise and pack O (bf16) as the B operand over d; t^T = A^T O^T in one or two 32-row
   // blocks of correction directions
   const bool two = re > 32;
@@ -331,6 +345,13 @@ __device__ __forceinline__ void fused_writeback(const AttnArgs& A, int kv, int v
   }
 }
 
+template <int D, int LDS_BYTES, int NT>
+__device__ __forceinline__ void fused_writeback(const AttnArgs& A, int kv, int vrow, bool qvalid, float inv,
+                                                f32x16_t* o, char* lds, int tid, int l32, int hf) {
+  fused_stage<D, LDS_BYTES, NT>(A, kv, lds, tid);
+  fused_apply<D>(A, kv, vrow, qvalid, inv, o, lds, l32, hf);
+}
+
 constexpr int kAttnWaves = 8;    // waves per block of the main attention kernel
 constexpr int kAttnStages = 4;   // K/V tile stages in LDS; tile j + 3 is copied while tile j runs
 
@@ -338,11 +359,12 @@ constexpr int kAttnStages = 4;   // K/V tile stages in LDS; tile j + 3 is copied
 // C::KIPW + C::VIPW direct-to-LDS loads, which complete in order for the counter).
 template <int PER_TILE>
 __device__ __forceinline__ void wait_tiles_in_flight(int later) {
-  static_assert(2 * PER_TILE <= 15, "vmcnt immediate");
-  // s_waitcnt immediate: vmcnt in bits 3:0 (and 15:14), expcnt 6:4 and lgkmcnt 11:8 left at
+  static_assert(2 * PER_TILE <= 63, "vmcnt immediate");
+  // s_waitcnt immediate: vmcnt bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at
   // their maxima
-  if (later >= 2) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * PER_TILE));
-  else if (later == 1) __builtin_amdgcn_s_waitcnt(0x0F70 | PER_TILE);
+  constexpr int V2 = 2 * PER_TILE, V1 = PER_TILE;
+  if (later >= 2) __builtin_amdgcn_s_waitcnt(0x0F70 | (V2 & 15) | ((V2 >> 4) << 14));
+  else if (later == 1) __builtin_amdgcn_s_waitcnt(0x0F70 | (V1 & 15) | ((V1 >> 4) << 14));
   else __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 

@@ -5,6 +5,7 @@ points (partition, route, attend, probe_fit, apply) and the dense baseline all r
 libsparsepr.so.  There is no fallback: without the library every call raises.
 """
 import ctypes
+import dataclasses
 from dataclasses import dataclass
 
 import torch
@@ -279,3 +280,79 @@ def config_from_workload(w, **overrides) -> Config:
               rank=w.rank, lam=w.lam, kmeans_iters=w.kmeans_iters)
     kw.update(overrides)
     return Config(**kw)
+
+
+class PipelinedSparsePR:
+    """The SparsePR call over chunks of KV heads, pipelined on three streams (default
+    priority): chunk i's partition and route run beside chunk i-1's attention, so only the
+    first chunk's partition, route and probe stage are exposed.  Every head's arithmetic is
+    that of one SparsePR call (each chunk is a SparsePR instance on its slice of the
+    heads), so the output is identical.  The budget must be per KV head (a shared budget
+    couples the heads).
+
+    fused=True:  partition, route (stream P) -> probe_fit (stream F) -> attend_apply (stream A).
+    fused=False: partition, route (P) -> attend (A) beside probe_fit (F) -> apply (A)."""
+
+    def __init__(self, cfg: Config, chunks=4, device="cuda", fused=True):
+        if cfg.budget_mode != B.BUDGET_PER_HEAD:
+            raise ValueError("a budget shared across heads cannot be split into head chunks")
+        chunks = max(1, min(chunks, cfg.heads_kv))
+        base, extra = divmod(cfg.heads_kv, chunks)
+        self.cfg, self.fused = cfg, fused
+        self.parts = []      # (kv0, kv1, SparsePR)
+        kv0 = 0
+        for i in range(chunks):
+            nkv = base + (1 if i < extra else 0)
+            sub = dataclasses.replace(cfg, heads_kv=nkv, heads_q=nkv * cfg.g)
+            self.parts.append((kv0, kv0 + nkv, SparsePR(sub, device=device)))
+            kv0 += nkv
+        dev = torch.device(device)
+        self.streams = [torch.cuda.Stream(device=dev) for _ in range(3)]   # P, F, A
+
+    def __call__(self, q, k, v, out=None, events=None):
+        """``events``: optional dict stage -> list of (start, end) torch events per chunk,
+        recorded on the stream that runs the stage (for timing)."""
+        c = self.cfg
+        if out is None:
+            out = torch.empty((c.heads_q, c.n, c.d), dtype=c.torch_dtype, device=q.device)
+        main = torch.cuda.current_stream()
+        sp_, sf, sa = self.streams
+        for s in self.streams:
+            s.wait_stream(main)
+
+        def run(stage, i, stream, fn):
+            with torch.cuda.stream(stream):
+                if events is not None:
+                    events[stage][i][0].record(stream)
+                fn()
+                if events is not None:
+                    events[stage][i][1].record(stream)
+
+        for i, (kv0, kv1, sp) in enumerate(self.parts):
+            h0, h1 = kv0 * c.g, kv1 * c.g
+            qc, kc, vc, oc = q[h0:h1], k[kv0:kv1], v[kv0:kv1], out[h0:h1]
+            run("partition", i, sp_, lambda: sp.partition(qc, kc, vc))
+            run("route", i, sp_, sp.route)
+            sf.wait_stream(sp_)
+            run("probe_fit", i, sf, lambda: sp.probe_fit(qc))
+            if self.fused:
+                sa.wait_stream(sf)
+                run("attend_apply", i, sa, lambda: sp.attend_apply(oc))
+            else:
+                sa.wait_stream(sp_)
+                run("attend", i, sa, sp.attend)
+                sa.wait_stream(sf)
+                run("apply", i, sa, lambda: sp.apply(oc))
+        for s in self.streams:
+            main.wait_stream(s)
+        return out
+
+    def capture(self, q, k, v, out, order=None):
+        """Records one pipelined call into a HIP graph (the three streams join the capture);
+        one eager call runs first so one-time set-up stays outside it."""
+        self(q, k, v, out)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            self(q, k, v, out)
+        return graph
