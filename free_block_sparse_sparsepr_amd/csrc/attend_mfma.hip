@@ -407,6 +407,7 @@ __global__ __launch_bounds__(64 * kAttnWaves, 1) void attn_mfma_kernel(AttnArgs 
   }
 
   const float c2 = A.scale * 1.4426950408889634f;   // scale * log2(e)
+  const bool wave_rows = ti.v0 + 32 * wu < ti.v1;
   float m_i = -INFINITY, l_i = 0.f;
   f32x16_t o[C::DBLK];
 #pragma unroll
@@ -440,7 +441,8 @@ __global__ __launch_bounds__(64 * kAttnWaves, 1) void attn_mfma_kernel(AttnArgs 
       fvalid = next_tile(A, kv, ti, C::BN, fci, fk0, fk1, fkt);
     }
     const int lo = max(k0 - kt, 0), hi = min(k1 - kt, BN);
-    mfma_tile_step<D, BN, false>(stages[cur], qreg, lo, hi, c2, nullptr, 0ull, m_i, l_i, o, l32, hf);
+    if (wave_rows)   // a wave whose rows all lie past the tile's end only keeps the copies and barriers
+      mfma_tile_step<D, BN, false>(stages[cur], qreg, lo, hi, c2, nullptr, 0ull, m_i, l_i, o, l32, hf);
     --nfront;
     valid = next_tile(A, kv, ti, C::BN, ci, k0, k1, kt);
     wait_tiles_in_flight<PER_TILE>(nfront - 1);   // tile j + 1 has landed

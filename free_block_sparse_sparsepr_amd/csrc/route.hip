@@ -82,18 +82,16 @@ __global__ __launch_bounds__(256) void route_mass_kernel(const float* __restrict
       if (i0 + j >= r1) break;
       int z = INT_MIN;
       if (lane < Gk) z = (int)fminf(fmaxf(rintf(64.f * u[j]), -1073741824.f), 1073741824.f);
-      int mu = (nb > 0) ? z : INT_MIN;
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) mu = max(mu, __shfl_xor(mu, o));
+      const int mu = wave_max_i32((nb > 0) ? z : INT_MIN);
       uint64_t e = 0;
       if (nb > 0) {
         const int64_t dz = (int64_t)mu - (int64_t)z;
         const int k = dz > kExpTable - 1 ? kExpTable - 1 : (int)dz;
         e = (uint64_t)nb * (uint64_t)etab[k];
       }
-      uint64_t tot = e;
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) tot += __shfl_xor(tot, o);
+      // e <= 2^22 * 2^20 per lane, so every partial sum of the 64 lanes stays below 2^48
+      // and the float64 sum is exact
+      const uint64_t tot = (uint64_t)wave_sum_f64((double)e);
       if (e) atomicAdd(&acc[la[j] * Gk + lane], (unsigned long long)udiv_exact(e << 20, tot));
     }
   }

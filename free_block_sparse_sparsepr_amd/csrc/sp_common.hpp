@@ -74,6 +74,53 @@ __device__ __forceinline__ uint64_t udiv_exact(uint64_t num, uint64_t den) {
   return q;
 }
 
+// Butterfly reductions over the 64 lanes of a wave (every lane receives the result) with DPP
+// row permutes (quad pairs, quads, half-row and row mirrors) and the gfx950 lane-swap
+// instructions across 16- and 32-lane halves: no LDS traffic.  All lanes must be active.
+template <int CTRL>
+__device__ __forceinline__ int dpp_i32(int v) {
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ int wave_max_i32(int v) {
+  v = max(v, dpp_i32<0xB1>(v));    // quad_perm [1,0,3,2]
+  v = max(v, dpp_i32<0x4E>(v));    // quad_perm [2,3,0,1]
+  v = max(v, dpp_i32<0x141>(v));   // row_half_mirror
+  v = max(v, dpp_i32<0x140>(v));   // row_mirror
+  const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = max((int)a[0], (int)a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return max((int)b[0], (int)b[1]);
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double x) {
+  const int lo = dpp_i32<CTRL>(__double2loint(x)), hi = dpp_i32<CTRL>(__double2hiint(x));
+  return __hiloint2double(hi, lo);
+}
+__device__ __forceinline__ double swap16_f64(double x, double& other) {
+  const auto lo = __builtin_amdgcn_permlane16_swap(__double2loint(x), __double2loint(x), false, false);
+  const auto hi = __builtin_amdgcn_permlane16_swap(__double2hiint(x), __double2hiint(x), false, false);
+  other = __hiloint2double((int)hi[1], (int)lo[1]);
+  return __hiloint2double((int)hi[0], (int)lo[0]);
+}
+__device__ __forceinline__ double swap32_f64(double x, double& other) {
+  const auto lo = __builtin_amdgcn_permlane32_swap(__double2loint(x), __double2loint(x), false, false);
+  const auto hi = __builtin_amdgcn_permlane32_swap(__double2hiint(x), __double2hiint(x), false, false);
+  other = __hiloint2double((int)hi[1], (int)lo[1]);
+  return __hiloint2double((int)hi[0], (int)lo[0]);
+}
+// Sum over the wave in float64: exact whenever every partial sum is an integer below 2^53.
+__device__ __forceinline__ double wave_sum_f64(double x) {
+  x += dpp_f64<0xB1>(x);
+  x += dpp_f64<0x4E>(x);
+  x += dpp_f64<0x141>(x);
+  x += dpp_f64<0x140>(x);
+  double o;
+  double s = swap16_f64(x, o);
+  x = s + o;
+  s = swap32_f64(x, o);
+  return s + o;
+}
+
 __device__ __forceinline__ float wave_max(float v) {
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
   return v;
