@@ -185,7 +185,7 @@ __device__ __forceinline__ void mfma_tile_step(const char* __restrict__ stage, c
   for (int kb = 0; kb < C::NB; ++kb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sv[kb][r]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32)) * c2;
+  mx = max_xor32(mx) * c2;
   const float m_use = (mx > m_i + kStaleMax) ? mx : m_i;
   float alpha;
   if constexpr (MASK) alpha = (m_use == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_i - m_use);
@@ -450,7 +450,7 @@ __global__ __launch_bounds__(64 * kAttnWaves, 1) void attn_mfma_kernel(AttnArgs 
     cur = cur == kAttnStages - 1 ? 0 : cur + 1;
   }
 
-  const float l_tot = l_i + __shfl_xor(l_i, 32);
+  const float l_tot = add_xor32(l_i);
   const float inv = 1.f / l_tot;
   if (A.fitA != nullptr) {
     fused_writeback<D, C::STAGE * kAttnStages, 64 * kAttnWaves>(A, kv, vrow, qvalid, inv, o, &stages[0][0], tid,
@@ -565,7 +565,7 @@ __global__ __launch_bounds__(256, 2) void probe_attn_mfma_kernel(const bf16_t* _
     cur ^= 1;
     kt = nt;
   }
-  const float l_tot = l_i + __shfl_xor(l_i, 32);
+  const float l_tot = add_xor32(l_i);
   if (rvalid) {
     float* pb = partials + (((int64_t)h * nch + ch) * M + row) * 2 * (D + 2) + (sparse ? D + 2 : 0);
 #pragma unroll

@@ -686,13 +686,9 @@ __global__ __launch_bounds__(256) void query_features_kernel(const float* __rest
     const int i = i0 + rr;
     if (i >= n) break;
     const int u = lane < Gk ? (int)rintf(ldexpf(uv[rr], e)) : 0;
-    int sum = u;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
+    const int sum = wave_sum_i32(u);
     const int c = Gk * u - sum;
-    int mx = lane < Gk ? (c < 0 ? -c : c) : 0;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) mx = max(mx, __shfl_xor(mx, o));
+    const int mx = wave_max_i32(lane < Gk ? (c < 0 ? -c : c) : 0);
     const int x = (lane < Gk && mx > 0) ? div_rhaz(127 * c, mx) : 0;
     if (lane < Gk) Xout[((int64_t)kv * n + i) * Gk + lane] = (int8_t)x;
     if (lane < fp) Xpad[((int64_t)kv * n + i) * fp + lane] = (int8_t)x;

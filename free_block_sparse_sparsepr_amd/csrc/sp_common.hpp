@@ -91,6 +91,25 @@ __device__ __forceinline__ int wave_max_i32(int v) {
   const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
   return max((int)b[0], (int)b[1]);
 }
+__device__ __forceinline__ int wave_sum_i32(int v) {
+  v += dpp_i32<0xB1>(v);
+  v += dpp_i32<0x4E>(v);
+  v += dpp_i32<0x141>(v);
+  v += dpp_i32<0x140>(v);
+  const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = (int)a[0] + (int)a[1];
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return (int)b[0] + (int)b[1];
+}
+// A lane's value combined with that of lane l ^ 32 (both lanes get the same result).
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
+  return fmaxf(__int_as_float((int)b[0]), __int_as_float((int)b[1]));
+}
+__device__ __forceinline__ float add_xor32(float v) {
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
+  return __int_as_float((int)b[0]) + __int_as_float((int)b[1]);
+}
 template <int CTRL>
 __device__ __forceinline__ double dpp_f64(double x) {
   const int lo = dpp_i32<CTRL>(__double2loint(x)), hi = dpp_i32<CTRL>(__double2hiint(x));
