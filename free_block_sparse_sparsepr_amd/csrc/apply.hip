@@ -194,7 +194,14 @@ void launch_probe_writeback(const Dims& dm, const sparsepr_fit_t& fit, void* o, 
 
 void launch_apply(const Dims& dm, const float* o_gm, const sparsepr_partition_t& part, const sparsepr_fit_t& fit,
                   void* o, hipStream_t s) {
-  if (dm.bf16) {
+  if (dm.bf16 && dm.rc <= kMaxRank && dm.g == 1) {
+    // bf16 output, one query head per KV head and the projected correction (rank <= 32): the
+    // matrix-core write-back (the fused epilogue's arithmetic, bf16 operands), then the exact
+    // probe rows.  Elsewhere the fp32 path: under GQA and for the unprojected ridge the fitted
+    // corrections extrapolate further, and bf16 operand rounding would exceed the output's own.
+    launch_apply_mfma(dm, o_gm, part, fit, o, s);
+    if (dm.ablation != SPARSEPR_ABLATE_HARD_DROP) launch_probe_writeback(dm, fit, o, s);
+  } else if (dm.bf16) {
     if (dm.d == 128) apply_typed<bf16_t, 128>(dm, o_gm, part, fit, (bf16_t*)o, s);
     else apply_typed<bf16_t, 64>(dm, o_gm, part, fit, (bf16_t*)o, s);
   } else {

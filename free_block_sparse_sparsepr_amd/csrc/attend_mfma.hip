@@ -245,12 +245,11 @@ __device__ __forceinline__ void mfma_tile_step(const char* __restrict__ stage, c
 // data movement; A^T, B^T (bf16) and c0 are staged in the free LDS stages.  Rows are
 // scattered to token order through the query permutation.
 template <int D, int LDS_BYTES, int NT>
-__device__ __forceinline__ void fused_stage(const AttnArgs& A, int kv, char* lds, int tid) {
+__device__ __forceinline__ void fused_stage(const AttnArgs& A, int h, char* lds, int tid) {
   constexpr int RCM = kMaxCorrRank;  // up to 64 correction directions (two 32-row blocks of t)
   constexpr int AROW = D + 8;        // At[k][d] bf16, padded rows (conflict-free 16-byte reads)
   constexpr int BROW = RCM + 4;      // Bt[d][k] bf16, padded rows (conflict-free 8-byte reads)
   static_assert((RCM * AROW + D * BROW) * 2 + D * 4 <= LDS_BYTES, "fused write-back staging");
-  const int h = kv;   // one query head per KV head
   bf16_t* At = reinterpret_cast<bf16_t*>(lds);
   bf16_t* Bt = At + RCM * AROW;
   float* c0s = reinterpret_cast<float*>(Bt + D * BROW);
@@ -266,16 +265,15 @@ __device__ __forceinline__ void fused_stage(const AttnArgs& A, int kv, char* lds
   __syncthreads();
 }
 
-// The correction and scatter of one wave's 32 rows from A^T, B^T and c0 staged by
-// fused_stage.
+// The correction and scatter of one wave's 32 rows of query head h (group-major position
+// p of KV head kv) from A^T, B^T and c0 staged by fused_stage.
 template <int D>
-__device__ __forceinline__ void fused_apply(const AttnArgs& A, int kv, int vrow, bool qvalid, float inv,
+__device__ __forceinline__ void fused_apply(const AttnArgs& A, int h, int kv, int p, bool qvalid, float inv,
                                             f32x16_t* o, const char* lds, int l32, int hf) {
   constexpr int DBLK = D / 32;
   constexpr int RCM = kMaxCorrRank;
   constexpr int AROW = D + 8;
   constexpr int BROW = RCM + 4;
-  const int h = kv;
   const bf16_t* At = reinterpret_cast<const bf16_t*>(lds);
   const bf16_t* Bt = At + RCM * AROW;
   const float* c0s = reinterpret_cast<const float*>(Bt + D * BROW);
@@ -329,7 +327,7 @@ __device__ __forceinline__ void fused_apply(const AttnArgs& A, int kv, int vrow,
     }
   }
   if (qvalid) {
-    const int64_t tok = A.qperm[(int64_t)kv * A.n + vrow];
+    const int64_t tok = A.qperm[(int64_t)kv * A.n + p];
     bf16_t* orow = static_cast<bf16_t*>(A.out_tok) + ((int64_t)h * A.n + tok) * D;
 #pragma unroll
     for (int db = 0; db < DBLK; ++db)
@@ -348,8 +346,8 @@ __device__ __forceinline__ void fused_apply(const AttnArgs& A, int kv, int vrow,
 template <int D, int LDS_BYTES, int NT>
 __device__ __forceinline__ void fused_writeback(const AttnArgs& A, int kv, int vrow, bool qvalid, float inv,
                                                 f32x16_t* o, char* lds, int tid, int l32, int hf) {
-  fused_stage<D, LDS_BYTES, NT>(A, kv, lds, tid);
-  fused_apply<D>(A, kv, vrow, qvalid, inv, o, lds, l32, hf);
+  fused_stage<D, LDS_BYTES, NT>(A, kv, lds, tid);   // one query head per KV head
+  fused_apply<D>(A, kv, kv, vrow, qvalid, inv, o, lds, l32, hf);
 }
 
 constexpr int kAttnWaves = 8;    // waves per block of the main attention kernel
@@ -481,6 +479,53 @@ __global__ __launch_bounds__(64 * kAttnWaves, 1) void attn_mfma_kernel(AttnArgs 
     if (A.lse && hf == 0)
       A.lse[((int64_t)kv * A.n + vrow / A.g) * A.g + vrow % A.g] = (m_i + log2f(l_tot)) * 0.6931471805599453f;
   }
+}
+
+// Write-back of the unfused order on the matrix cores (bf16 output): the fp32 group-major
+// rows of one query head are loaded in the accumulator layout of O^T and corrected and
+// scattered exactly as in the fused epilogue.  grid (ceil(n / 128), Hq), block 256 (4 waves x
+// 32 rows).
+template <int D>
+__global__ __launch_bounds__(256) void apply_mfma_kernel(AttnArgs A, const float* __restrict__ o_gm) {
+  constexpr int LDS = (kMaxCorrRank * (D + 8) + D * (kMaxCorrRank + 4)) * 2 + D * 4;
+  __shared__ __attribute__((aligned(16))) char lds[LDS];
+  const int h = blockIdx.y, kv = h / A.g, j = h % A.g;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, hf = lane >> 5;
+  fused_stage<D, LDS, 256>(A, h, lds, tid);
+  const int p = blockIdx.x * 128 + 32 * w + l32;
+  const bool valid = p < A.n;
+  const float* row = o_gm + (((int64_t)kv * A.n + (valid ? p : 0)) * A.g + j) * D;
+  f32x16_t o[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const float4 v = valid ? *reinterpret_cast<const float4*>(row + 32 * db + 8 * jj + 4 * hf)
+                             : make_float4(0.f, 0.f, 0.f, 0.f);
+      o[db][4 * jj] = v.x;
+      o[db][4 * jj + 1] = v.y;
+      o[db][4 * jj + 2] = v.z;
+      o[db][4 * jj + 3] = v.w;
+    }
+  fused_apply<D>(A, h, kv, p, valid, 1.f, o, lds, l32, hf);
+}
+
+void launch_apply_mfma(const Dims& dm, const float* o_gm, const sparsepr_partition_t& part,
+                       const sparsepr_fit_t& fit, void* o, hipStream_t s) {
+  AttnArgs a{};
+  a.n = dm.n;
+  a.g = dm.g;
+  a.fitA = fit.A;
+  a.fitB = fit.B;
+  a.fitc0 = fit.c0;
+  a.r_eff = fit.r_eff;
+  a.rank = dm.rc;
+  a.qperm = part.query_perm;
+  a.out_tok = o;
+  const dim3 grid((unsigned)ceil_div(dm.n, 128), dm.hq);
+  if (dm.d == 128) hipLaunchKernelGGL(apply_mfma_kernel<128>, grid, dim3(256), 0, s, a, o_gm);
+  else hipLaunchKernelGGL(apply_mfma_kernel<64>, grid, dim3(256), 0, s, a, o_gm);
 }
 
 // ---------------------------------------------------------------------------------------

@@ -28,6 +28,9 @@ void launch_probe_fit(const Dims& dm, const Workspace& wp, const void* q, const 
 void launch_probe_writeback(const Dims& dm, const sparsepr_fit_t& fit, void* o, hipStream_t s);
 void launch_apply(const Dims& dm, const float* o_gm, const sparsepr_partition_t& part, const sparsepr_fit_t& fit,
                   void* o, hipStream_t s);
+// bf16 write-back on the matrix cores (the fused epilogue's arithmetic on stored rows)
+void launch_apply_mfma(const Dims& dm, const float* o_gm, const sparsepr_partition_t& part,
+                       const sparsepr_fit_t& fit, void* o, hipStream_t s);
 
 // Residual diagnostics: workspace offsets and the launch (dense and sparse AttnArgs are
 // filled by the caller except for their outputs).
