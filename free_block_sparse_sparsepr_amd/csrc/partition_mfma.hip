@@ -18,8 +18,12 @@ namespace sp {
 typedef __bf16 pbf16x8_t __attribute__((ext_vector_type(8)));
 typedef float pf32x16_t __attribute__((ext_vector_type(16)));
 
+// Row tiles of 128 per block of the two response kernels (the staged operand is shared by
+// all of them).
+constexpr int kRespTiles = 8;
+
 // S: one wave = 32 keys; D[sample][key] so lanes run over consecutive keys.
-// grid (ceil(n / 128), Hkv), block 256.
+// grid (ceil(n / (128 kRespTiles)), Hkv), block 256.
 template <int D>
 __global__ __launch_bounds__(256) void resp_s_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                                                           int n, int g, int rk, float scale, float* __restrict__ S,
@@ -40,35 +44,39 @@ __global__ __launch_bounds__(256) void resp_s_mfma_kernel(const bf16_t* __restri
   }
   __syncthreads();
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, l32 = lane & 31, hf = lane >> 5;
-  const int key = blockIdx.x * 128 + 32 * w + l32;
-  const bool kval = key < n;
-  pbf16x8_t kreg[D / 16];
-  const bf16_t* kr = k + ((int64_t)kv * n + (kval ? key : 0)) * D;
-#pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) {
-    uint4 x = kval ? *reinterpret_cast<const uint4*>(kr + 16 * kk + 8 * hf) : make_uint4(0, 0, 0, 0);
-    kreg[kk] = __builtin_bit_cast(pbf16x8_t, x);
-  }
   float mx = 0.f;
-  const int nsb = (rk + 31) / 32;
-  for (int sb = 0; sb < nsb; ++sb) {
-    pf32x16_t acc;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-    const bf16_t* qrow = qs + (32 * sb + l32) * QROW + 8 * hf;
+  for (int t = 0; t < kRespTiles; ++t) {
+    const int tile = blockIdx.x * kRespTiles + t;
+    if (tile * 128 >= n) break;
+    const int key = tile * 128 + 32 * w + l32;
+    const bool kval = key < n;
+    pbf16x8_t kreg[D / 16];
+    const bf16_t* kr = k + ((int64_t)kv * n + (kval ? key : 0)) * D;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
-      pbf16x8_t a = *reinterpret_cast<const pbf16x8_t*>(qrow + 16 * kk);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kreg[kk], acc, 0, 0, 0);
+      uint4 x = kval ? *reinterpret_cast<const uint4*>(kr + 16 * kk + 8 * hf) : make_uint4(0, 0, 0, 0);
+      kreg[kk] = __builtin_bit_cast(pbf16x8_t, x);
     }
-    if (kval) {
+    const int nsb = (rk + 31) / 32;
+    for (int sb = 0; sb < nsb; ++sb) {
+      pf32x16_t acc;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int s = 32 * sb + 8 * (r >> 2) + 4 * hf + (r & 3);
-        if (s < rk) {
-          const float v = acc[r] * scale;
-          S[((int64_t)kv * rk + s) * n + key] = v;
-          mx = fmaxf(mx, fabsf(v));
+      for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+      const bf16_t* qrow = qs + (32 * sb + l32) * QROW + 8 * hf;
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        pbf16x8_t a = *reinterpret_cast<const pbf16x8_t*>(qrow + 16 * kk);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kreg[kk], acc, 0, 0, 0);
+      }
+      if (kval) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int s = 32 * sb + 8 * (r >> 2) + 4 * hf + (r & 3);
+          if (s < rk) {
+            const float v = acc[r] * scale;
+            S[((int64_t)kv * rk + s) * n + key] = v;
+            mx = fmaxf(mx, fabsf(v));
+          }
         }
       }
     }
@@ -81,7 +89,7 @@ __global__ __launch_bounds__(256) void resp_s_mfma_kernel(const bf16_t* __restri
 
 // U: one wave = 32 query rows (A = Q rows from global), B = C^T split in hi / lo bf16
 // parts from LDS, groups padded to multiples of 32 with zero centroids.
-// grid (ceil(n / 128), Hkv), block 256.
+// grid (ceil(n / (128 kRespTiles)), Hkv), block 256.
 template <int D>
 __global__ __launch_bounds__(256) void resp_u_mfma_kernel(const bf16_t* __restrict__ q, const float* __restrict__ Ck,
                                                           int n, int g, int Gk, float scale, float* __restrict__ U,
@@ -101,46 +109,50 @@ __global__ __launch_bounds__(256) void resp_u_mfma_kernel(const bf16_t* __restri
   }
   __syncthreads();
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, l32 = lane & 31, hf = lane >> 5;
-  const int row0 = blockIdx.x * 128 + 32 * w;
-  pf32x16_t usum[2];
   float mx = 0.f;
-  for (int jh = 0; jh < g; ++jh) {
-    const int h = kv * g + jh;
-    const int qrow = row0 + l32;
-    const bool qv = qrow < n;
-    pbf16x8_t qa[D / 16];
-    const bf16_t* qr = q + ((int64_t)h * n + (qv ? qrow : 0)) * D;
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      uint4 x = qv ? *reinterpret_cast<const uint4*>(qr + 16 * kk + 8 * hf) : make_uint4(0, 0, 0, 0);
-      qa[kk] = __builtin_bit_cast(pbf16x8_t, x);
-    }
-    for (int gb = 0; gb < ngb; ++gb) {
-      pf32x16_t acc;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-      const bf16_t* ch = chi + (32 * gb + l32) * CROW + 8 * hf;
-      const bf16_t* cl = clo + (32 * gb + l32) * CROW + 8 * hf;
+  for (int t = 0; t < kRespTiles; ++t) {
+    const int tile = blockIdx.x * kRespTiles + t;
+    if (tile * 128 >= n) break;
+    const int row0 = tile * 128 + 32 * w;
+    pf32x16_t usum[2];
+    for (int jh = 0; jh < g; ++jh) {
+      const int h = kv * g + jh;
+      const int qrow = row0 + l32;
+      const bool qv = qrow < n;
+      pbf16x8_t qa[D / 16];
+      const bf16_t* qr = q + ((int64_t)h * n + (qv ? qrow : 0)) * D;
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) {
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[kk], *reinterpret_cast<const pbf16x8_t*>(ch + 16 * kk), acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[kk], *reinterpret_cast<const pbf16x8_t*>(cl + 16 * kk), acc, 0, 0, 0);
+        uint4 x = qv ? *reinterpret_cast<const uint4*>(qr + 16 * kk + 8 * hf) : make_uint4(0, 0, 0, 0);
+        qa[kk] = __builtin_bit_cast(pbf16x8_t, x);
       }
-      const int b = 32 * gb + l32;
+      for (int gb = 0; gb < ngb; ++gb) {
+        pf32x16_t acc;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = row0 + 8 * (r >> 2) + 4 * hf + (r & 3);
-        const float u = acc[r] * scale;
-        usum[gb & 1][r] = (jh == 0) ? u : usum[gb & 1][r] + u;
-        if (row < n && b < Gk) U[((int64_t)h * n + row) * Gk + b] = u;
-      }
-      if (jh == g - 1) {
+        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+        const bf16_t* ch = chi + (32 * gb + l32) * CROW + 8 * hf;
+        const bf16_t* cl = clo + (32 * gb + l32) * CROW + 8 * hf;
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[kk], *reinterpret_cast<const pbf16x8_t*>(ch + 16 * kk), acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[kk], *reinterpret_cast<const pbf16x8_t*>(cl + 16 * kk), acc, 0, 0, 0);
+        }
+        const int b = 32 * gb + l32;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = row0 + 8 * (r >> 2) + 4 * hf + (r & 3);
-          if (row < n && b < Gk) {
-            mx = fmaxf(mx, fabsf(usum[gb & 1][r]));
-            if (Usum) Usum[((int64_t)kv * n + row) * Gk + b] = usum[gb & 1][r];
+          const float u = acc[r] * scale;
+          usum[gb & 1][r] = (jh == 0) ? u : usum[gb & 1][r] + u;
+          if (row < n && b < Gk) U[((int64_t)h * n + row) * Gk + b] = u;
+        }
+        if (jh == g - 1) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = row0 + 8 * (r >> 2) + 4 * hf + (r & 3);
+            if (row < n && b < Gk) {
+              mx = fmaxf(mx, fabsf(usum[gb & 1][r]));
+              if (Usum) Usum[((int64_t)kv * n + row) * Gk + b] = usum[gb & 1][r];
+            }
           }
         }
       }
@@ -153,7 +165,7 @@ __global__ __launch_bounds__(256) void resp_u_mfma_kernel(const bf16_t* __restri
 }
 
 void launch_resp_s_mfma(const Dims& dm, const void* q, const void* k, float* S, uint32_t* maxbits, hipStream_t s) {
-  const dim3 grid((unsigned)ceil_div(dm.n, 128), dm.hkv);
+  const dim3 grid((unsigned)ceil_div(dm.n, 128 * kRespTiles), dm.hkv);
   if (dm.d == 128)
     hipLaunchKernelGGL(resp_s_mfma_kernel<128>, grid, dim3(256), 0, s, (const bf16_t*)q, (const bf16_t*)k, dm.n, dm.g,
                        dm.rk, dm.scale, S, maxbits);
@@ -164,7 +176,7 @@ void launch_resp_s_mfma(const Dims& dm, const void* q, const void* k, float* S, 
 
 void launch_resp_u_mfma(const Dims& dm, const void* q, const float* Ck, float* U, float* Usum, uint32_t* maxbits,
                         hipStream_t s) {
-  const dim3 grid((unsigned)ceil_div(dm.n, 128), dm.hkv);
+  const dim3 grid((unsigned)ceil_div(dm.n, 128 * kRespTiles), dm.hkv);
   if (dm.d == 128)
     hipLaunchKernelGGL(resp_u_mfma_kernel<128>, grid, dim3(256), 0, s, (const bf16_t*)q, Ck, dm.n, dm.g, dm.gk,
                        dm.scale, U, Usum, maxbits);
