@@ -568,25 +568,46 @@ __global__ __launch_bounds__(256) void gather_vt_kernel(const T* __restrict__ v,
 }
 
 // C^K_b = mean of the group-major key rows of group b in fixed order (fp32).  Thread t
-// sums 4 columns (4 * (t % (D / 4)) ..) over rows start + ph, ph + P, ... with P = 256 /
-// (D / 4) row phases, then the phases are combined in ascending order.  grid (G, Hkv),
-// block 256.
+// sums 8 columns (8 * (t % (D / 8)) ..) over rows start + ph, ph + P, ... with P = 256 /
+// (D / 8) row phases (16-byte loads), then the phases are combined in ascending order.
+// grid (G, Hkv), block 256.
+template <typename T>
+__device__ __forceinline__ void load8f(const T* p, float* x);
+template <>
+__device__ __forceinline__ void load8f<bf16_t>(const bf16_t* p, float* x) {
+  const uint4 v = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    x[2 * e] = __uint_as_float(w[e] << 16);
+    x[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+  }
+}
+template <>
+__device__ __forceinline__ void load8f<float>(const float* p, float* x) {
+  const float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(256) void segment_mean_kernel(const T* __restrict__ kgm,
                                                            const int32_t* __restrict__ offsets, int n,
                                                            int G, float* __restrict__ C) {
-  constexpr int CQ = D / 4;
+  constexpr int CQ = D / 8;
   constexpr int P = 256 / CQ;
   __shared__ float red[P][D];
   const int b = blockIdx.x, h = blockIdx.y;
   const int cq = threadIdx.x % CQ, ph = threadIdx.x / CQ;
   const int start = offsets[(int64_t)h * (G + 1) + b], end = offsets[(int64_t)h * (G + 1) + b + 1];
-  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int r = start + ph; r < end; r += P) {
-    const T* src = kgm + ((int64_t)h * n + r) * D + 4 * cq;
-    s0 += to_f32(src[0]); s1 += to_f32(src[1]); s2 += to_f32(src[2]); s3 += to_f32(src[3]);
+    float x[8];
+    load8f<T>(kgm + ((int64_t)h * n + r) * D + 8 * cq, x);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += x[e];
   }
-  red[ph][4 * cq] = s0; red[ph][4 * cq + 1] = s1; red[ph][4 * cq + 2] = s2; red[ph][4 * cq + 3] = s3;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) red[ph][8 * cq + e] = acc[e];
   __syncthreads();
   for (int col = threadIdx.x; col < D; col += 256) {
     float tot = 0.f;
