@@ -129,10 +129,13 @@ __device__ __forceinline__ uint64_t cell_cost(int na, int nb, int tile) {
 }
 
 // CSR (columns ascending), kept masks and routed (unpadded) pairs of one KV head from its
-// kept flags (LDS or global).  Called by the whole block.
+// kept flags (LDS or global).  Called by the whole block: thread a < G_Q counts, then
+// writes, row a; one thread forms the row offsets and the pair total.
 __device__ void emit_route(const uint8_t* kept, const int* na, const int* nbk, int kv, int Gq, int Gk,
                            int* rcount, int32_t* __restrict__ row_ptr, int32_t* __restrict__ cols,
                            uint64_t* __restrict__ kept_mask, int64_t* __restrict__ pairs) {
+  __shared__ int rstart[kMaxGroups];
+  __shared__ int64_t rpairs[kMaxGroups];
   const int tid = threadIdx.x, ncell = Gq * Gk;
   if (tid < Gq) {
     int cnt = 0;
@@ -145,15 +148,25 @@ __device__ void emit_route(const uint8_t* kept, const int* na, const int* nbk, i
   __syncthreads();
   if (tid == 0) {
     int s = 0;
-    int64_t pr = 0;
     for (int a = 0; a < Gq; ++a) {
+      rstart[a] = s;
       row_ptr[(int64_t)kv * (Gq + 1) + a] = s;
-      int w = s;
-      for (int b = 0; b < Gk; ++b)
-        if (kept[a * Gk + b]) { cols[(int64_t)kv * ncell + w++] = b; pr += (int64_t)na[a] * nbk[b]; }
       s += rcount[a];
     }
     row_ptr[(int64_t)kv * (Gq + 1) + Gq] = s;
+  }
+  __syncthreads();
+  if (tid < Gq) {
+    int w = rstart[tid];
+    int64_t pr = 0;
+    for (int b = 0; b < Gk; ++b)
+      if (kept[tid * Gk + b]) { cols[(int64_t)kv * ncell + w++] = b; pr += (int64_t)na[tid] * nbk[b]; }
+    rpairs[tid] = pr;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int64_t pr = 0;
+    for (int a = 0; a < Gq; ++a) pr += rpairs[a];
     pairs[kv] = pr;
   }
 }
