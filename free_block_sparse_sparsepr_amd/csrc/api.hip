@@ -46,8 +46,8 @@ Workspace plan_workspace(const sparsepr_params& p) {
   w.maxbits = o; o = align_up(o + hkv * 2 * 4);
   w.xk = o; o = align_up(o + hkv * n * w.fpk);
   w.xq = o; o = align_up(o + hkv * n * w.fpq);
-  w.centroids = o; o = align_up(o + hkv * kMaxGroups * fpmax * 4);
-  w.sums = o; o = align_up(o + 2 * hkv * kMaxGroups * (fpmax + 1) * 4);
+  w.centroids = o; o = align_up(o + 2 * hkv * kMaxGroups * fpmax * 4);
+  w.sums = o; o = align_up(o + 3 * hkv * kMaxGroups * (fpmax + 1) * 4);
   w.usum = o; if (p.heads_q != p.heads_kv) o = align_up(o + hkv * n * p.groups_k * 4);
   w.gm_hist = o; o = align_up(o + hkv * (size_t)ceil_div(p.n, kGmChunk) * kMaxGroups * 4);
   w.total_partition = o;

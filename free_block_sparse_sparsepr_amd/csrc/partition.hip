@@ -221,12 +221,17 @@ constexpr int kAssignChunk = 256;       // points per chunk: 64 per wave
 //    one LDS add per run.
 // At the end the waves' sums meet in LDS and go to global memory with one integer atomic
 // per non-zero (group, feature).  FP must be a multiple of 16.
+// The centroid update of the previous iteration runs in every block's prologue: with
+// prev_sums, c_g = div_rhaz(sum_g, count_g) for features below F and groups with members,
+// otherwise c_g keeps its value in Cprev; block 0 of a head stores the result in Cout.
+// The blocks of a head also clear that head's slice of zero_sums (the buffer the next
+// iteration accumulates into).  Without SUMS only the labels are produced.
 // grid (blocks_per_head, H), block 256; block b of a head takes chunks [b chunks, (b+1) chunks).
-template <int FP>
-__global__ __launch_bounds__(256, FP > 64 ? 1 : 2) void kmeans_assign_mfma_kernel(const int8_t* __restrict__ X, int n, int G,
-                                                                    const int32_t* __restrict__ C, int chunks,
-                                                                    int32_t* __restrict__ labels,
-                                                                    int32_t* __restrict__ sums) {
+template <int FP, bool SUMS>
+__global__ __launch_bounds__(256, FP > 64 ? 1 : 2) void kmeans_assign_mfma_kernel(
+    const int8_t* __restrict__ X, int n, int G, int F, const int32_t* __restrict__ Cprev,
+    const int32_t* __restrict__ prev_sums, int32_t* __restrict__ Cout, int chunks, int32_t* __restrict__ labels,
+    int32_t* __restrict__ sums, int32_t* __restrict__ zero_sums) {
   constexpr int KB = (FP + 31) / 32;   // 32-feature blocks
   constexpr int CROW = 32 * KB + 16;   // int8 row of C in LDS, padded
   constexpr int SROW = FP + 1;         // int32 row of the LDS sums (last column = count)
@@ -236,10 +241,24 @@ __global__ __launch_bounds__(256, FP > 64 ? 1 : 2) void kmeans_assign_mfma_kerne
   __shared__ __attribute__((aligned(16))) uint8_t lab_s[4][2][32];
   const int h = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, hf = lane >> 5;
+  const int32_t* ps = prev_sums ? prev_sums + (int64_t)h * kMaxGroups * SROW : nullptr;
   for (int idx = tid; idx < kMaxGroups * 32 * KB; idx += 256) {
     const int gi = idx / (32 * KB), f = idx % (32 * KB);
-    const int c = (gi < G && f < FP) ? C[((int64_t)h * kMaxGroups + gi) * FP + f] : 0;
+    int c = 0;
+    if (gi < G && f < FP) {
+      const int64_t ci = ((int64_t)h * kMaxGroups + gi) * FP + f;
+      c = Cprev[ci];
+      if (ps != nullptr) {
+        const int cnt = ps[gi * SROW + FP];
+        if (cnt > 0 && f < F) c = div_rhaz(ps[gi * SROW + f], cnt);
+        if (Cout != nullptr && blockIdx.x == 0) Cout[ci] = c;
+      }
+    }
     cs[gi * CROW + f] = (int8_t)c;
+  }
+  if (zero_sums != nullptr) {
+    int32_t* zh = zero_sums + (int64_t)h * kMaxGroups * SROW;
+    for (int idx = blockIdx.x * 256 + tid; idx < kMaxGroups * SROW; idx += gridDim.x * 256) zh[idx] = 0;
   }
   for (int idx = tid; idx < kMaxGroups * SROW; idx += 256) ssum[idx] = 0;
   __syncthreads();
@@ -318,6 +337,7 @@ __global__ __launch_bounds__(256, FP > 64 ? 1 : 2) void kmeans_assign_mfma_kerne
       const int bg = best & 63;
       const int lab = pv ? bg : kMaxGroups;          // points past the end: no group
       if (pv && hf == 0) labels[(int64_t)h * n + pt] = bg;
+      if constexpr (!SUMS) continue;
       // -- counts: one add per run of equal labels among the 32 points
       const int prev = __shfl(lab, lane - (l32 > 0 ? 1 : 0));
       const int next = __shfl(lab, lane + (l32 < 31 ? 1 : 0));
@@ -364,6 +384,7 @@ __global__ __launch_bounds__(256, FP > 64 ? 1 : 2) void kmeans_assign_mfma_kerne
       }
     }
   }
+  if constexpr (!SUMS) return;
   // acc[fb][gb][r] = sum of feature 32 fb + 8 (r / 4) + 4 hf + r % 4 over group 32 gb + l32
 #pragma unroll
   for (int fb = 0; fb < KB; ++fb)
@@ -786,28 +807,49 @@ static void launch_assign(const int8_t* X, int n, int H, int G, const int32_t* C
                      X, n, G, C, labels, sums);
 }
 
+// One k-means iteration on the matrix cores (see kmeans_assign_mfma_kernel): the update
+// from prev_sums (or none), the assignment, and the sums into `sums` (none: labels only).
+struct AssignStep {
+  const int32_t* cprev;
+  const int32_t* prev_sums;
+  int32_t* cout;
+  int32_t* sums;
+  int32_t* zero_sums;
+};
+
 template <int FP>
-static void launch_assign_mfma(const int8_t* X, int n, int H, int G, const int32_t* C, int32_t* labels,
-                               int32_t* sums, hipStream_t s) {
+static void launch_assign_mfma(const int8_t* X, int n, int H, int G, int F, const AssignStep& st, int32_t* labels,
+                               hipStream_t s) {
   // at most 512 blocks in all (two 4-wave blocks per CU at two waves per SIMD): one pass
   // over the chip, and few per-block atomic flushes of G * (FP + 1) sums
   const int nchunks = (int)ceil_div(n, kAssignChunk);
   const int per_head = std::max(1, std::min(nchunks, 512 / std::max(H, 1)));
   const int chunks = (int)ceil_div(nchunks, per_head);
-  hipLaunchKernelGGL(kmeans_assign_mfma_kernel<FP>, dim3((unsigned)ceil_div(nchunks, chunks), H), dim3(256), 0, s,
-                     X, n, G, C, chunks, labels, sums);
+  const dim3 grid((unsigned)ceil_div(nchunks, chunks), H);
+  if (st.sums != nullptr)
+    hipLaunchKernelGGL((kmeans_assign_mfma_kernel<FP, true>), grid, dim3(256), 0, s, X, n, G, F, st.cprev,
+                       st.prev_sums, st.cout, chunks, labels, st.sums, st.zero_sums);
+  else
+    hipLaunchKernelGGL((kmeans_assign_mfma_kernel<FP, false>), grid, dim3(256), 0, s, X, n, G, F, st.cprev,
+                       st.prev_sums, st.cout, chunks, labels, st.sums, st.zero_sums);
 }
+
+static bool assign_mfma_dispatch(int fp, const int8_t* X, int n, int H, int G, int F, const AssignStep& st,
+                                 int32_t* labels, hipStream_t s) {
+  switch (fp) {
+    case 16: launch_assign_mfma<16>(X, n, H, G, F, st, labels, s); return true;
+    case 32: launch_assign_mfma<32>(X, n, H, G, F, st, labels, s); return true;
+    case 48: launch_assign_mfma<48>(X, n, H, G, F, st, labels, s); return true;
+    case 64: launch_assign_mfma<64>(X, n, H, G, F, st, labels, s); return true;
+    case 128: launch_assign_mfma<128>(X, n, H, G, F, st, labels, s); return true;
+    default: return false;
+  }
+}
+
+static bool has_assign_mfma(int fp) { return fp == 16 || fp == 32 || fp == 48 || fp == 64 || fp == 128; }
 
 static void assign_dispatch(int fp, const int8_t* X, int n, int H, int G, const int32_t* C,
                             int32_t* labels, int32_t* sums, hipStream_t s) {
-  switch (fp) {
-    case 16: launch_assign_mfma<16>(X, n, H, G, C, labels, sums, s); return;
-    case 32: launch_assign_mfma<32>(X, n, H, G, C, labels, sums, s); return;
-    case 48: launch_assign_mfma<48>(X, n, H, G, C, labels, sums, s); return;
-    case 64: launch_assign_mfma<64>(X, n, H, G, C, labels, sums, s); return;
-    case 128: launch_assign_mfma<128>(X, n, H, G, C, labels, sums, s); return;
-    default: break;
-  }
   switch (fp) {
 #define SP_FP_CASE(V) case V: launch_assign<V>(X, n, H, G, C, labels, sums, s); break;
     SP_FP_CASE(4) SP_FP_CASE(8) SP_FP_CASE(12) SP_FP_CASE(16) SP_FP_CASE(20) SP_FP_CASE(24)
@@ -818,12 +860,33 @@ static void assign_dispatch(int fp, const int8_t* X, int n, int H, int G, const 
   }
 }
 
-void run_kmeans(const int8_t* X, int n, int H, int G, int F, int fp, int iters, int32_t* C,
-                int32_t* sums2, int32_t* labels, int32_t* centroids_out, hipStream_t s) {
+// C2: two centroid buffers [H][kMaxGroups][fp]; sums3: three sums buffers [H][kMaxGroups][fp + 1].
+void run_kmeans(const int8_t* X, int n, int H, int G, int F, int fp, int iters, int32_t* C2,
+                int32_t* sums3, int32_t* labels, int32_t* centroids_out, hipStream_t s) {
   const size_t sums_elems = (size_t)H * kMaxGroups * (fp + 1);
-  int32_t* sums[2] = {sums2, sums2 + sums_elems};
-  hipLaunchKernelGGL(kmeans_init_kernel, dim3(H), dim3(256), 0, s, X, n, G, fp, C);
-  fill_u32(reinterpret_cast<uint32_t*>(sums[0]), sums_elems, 0, s);
+  const size_t c_elems = (size_t)H * kMaxGroups * fp;
+  hipLaunchKernelGGL(kmeans_init_kernel, dim3(H), dim3(256), 0, s, X, n, G, fp, C2);
+  fill_u32(reinterpret_cast<uint32_t*>(sums3), sums_elems, 0, s);
+  if (has_assign_mfma(fp)) {
+    // iteration t assigns with C_t (kept in buffer t % 2), forming C_t from the sums of
+    // iteration t - 1 (buffer (t - 1) % 3); it accumulates into buffer t % 3 and clears
+    // buffer (t + 1) % 3, which iteration t - 1 read and iteration t + 1 fills
+    int32_t* Cb[2] = {C2, C2 + c_elems};
+    int32_t* Sb[3] = {sums3, sums3 + sums_elems, sums3 + 2 * sums_elems};
+    for (int t = 0; t <= iters; ++t) {
+      AssignStep st;
+      st.cprev = t > 0 ? Cb[(t - 1) & 1] : Cb[0];
+      st.prev_sums = t > 0 ? Sb[(t - 1) % 3] : nullptr;
+      st.cout = t > 0 ? Cb[t & 1] : nullptr;
+      st.sums = t < iters ? Sb[t % 3] : nullptr;
+      st.zero_sums = t + 1 < iters ? Sb[(t + 1) % 3] : nullptr;
+      assign_mfma_dispatch(fp, X, n, H, G, F, st, labels, s);
+    }
+    hipLaunchKernelGGL(copy_centroids_kernel, dim3(H), dim3(256), 0, s, Cb[iters & 1], G, F, fp, centroids_out);
+    return;
+  }
+  int32_t* C = C2;
+  int32_t* sums[2] = {sums3, sums3 + sums_elems};
   for (int t = 0; t < iters; ++t) {
     assign_dispatch(fp, X, n, H, G, C, labels, sums[t & 1], s);
     hipLaunchKernelGGL(kmeans_update_kernel, dim3(H), dim3(256), 0, s, sums[t & 1], G, F, fp, C,
