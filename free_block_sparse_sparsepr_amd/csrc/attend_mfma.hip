@@ -351,7 +351,7 @@ __device__ __forceinline__ void fused_writeback(const AttnArgs& A, int kv, int v
 }
 
 constexpr int kAttnWaves = 8;    // waves per block of the main attention kernel
-constexpr int kAttnStages = 4;   // K/V tile stages in LDS; tile j + 3 is copied while tile j runs
+constexpr int kAttnStages = 4;   // K/V tile stages in LDS; tile j + 2 is copied while tile j runs
 
 // Waits until at most `later` tiles' copies of this wave are still in flight (each tile is
 // C::KIPW + C::VIPW direct-to-LDS loads, which complete in order for the counter).
@@ -414,7 +414,14 @@ __global__ __launch_bounds__(64 * kAttnWaves, 1) void attn_mfma_kernel(AttnArgs 
     for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
 
   // Tile iterators: (ci, k0, k1, kt) is the tile being computed; (fci, fk0, fk1, fkt) the
-  // copy frontier, kAttnStages - 1 tiles ahead.  Tile j lives in stage j % kAttnStages.
+  // copy frontier, kAttnStages - 2 tiles ahead.  Tile j lives in stage j % kAttnStages.
+  // The block meets at a barrier after every second tile (odd j) and after the last one:
+  // a wave working on tile j has then passed the barrier after tile j - 1 or j - 2, so
+  // every wave is done with tile j - 2, whose stage the copy of tile j + 2 reuses; and
+  // before the barrier after an odd tile j each wave waits for its copies of tiles j + 1
+  // and j + 2, the two tiles computed before the next barrier.  The barrier is a bare
+  // s_barrier after the counted waits: the workgroup fence of __syncthreads() would also
+  // drain the copies still in flight.
   int ci = ti.kbeg < 0 ? 0 : ti.kbeg, k0 = 0, k1 = 0, kt = 0;
   bool valid = next_run(A, kv, ti, ci, k0, k1);
   if (valid) kt = k0 & ~15;
@@ -422,17 +429,17 @@ __global__ __launch_bounds__(64 * kAttnWaves, 1) void attn_mfma_kernel(AttnArgs 
   bool fvalid = valid;
   int nfront = 0;           // copied tiles not yet computed
   int fst = 0;              // stage of the frontier tile
-  for (int i = 0; i < kAttnStages - 1 && fvalid; ++i) {
+  for (int i = 0; i < kAttnStages - 2 && fvalid; ++i) {
     stage_copy<D, BN, kAttnWaves>(cp, kb, vtb, A.n, A.v_np, fkt, stages[fst], wu);
     ++nfront;
     fst = fst == kAttnStages - 1 ? 0 : fst + 1;
     fvalid = next_tile(A, kv, ti, C::BN, fci, fk0, fk1, fkt);
   }
-  wait_tiles_in_flight<PER_TILE>(nfront - 1);
+  wait_tiles_in_flight<PER_TILE>(nfront - 2);   // tiles 0 and 1 have landed
   __syncthreads();
-  int cur = 0;
+  int cur = 0, j = 0;
   while (valid) {
-    if (fvalid) {   // the stage of tile j + kAttnStages - 1 was last read in tile j - 1
+    if (fvalid) {
       stage_copy<D, BN, kAttnWaves>(cp, kb, vtb, A.n, A.v_np, fkt, stages[fst], wu);
       ++nfront;
       fst = fst == kAttnStages - 1 ? 0 : fst + 1;
@@ -443,8 +450,11 @@ __global__ __launch_bounds__(64 * kAttnWaves, 1) void attn_mfma_kernel(AttnArgs 
       mfma_tile_step<D, BN, false>(stages[cur], qreg, lo, hi, c2, nullptr, 0ull, m_i, l_i, o, l32, hf);
     --nfront;
     valid = next_tile(A, kv, ti, C::BN, ci, k0, k1, kt);
-    wait_tiles_in_flight<PER_TILE>(nfront - 1);   // tile j + 1 has landed
-    __syncthreads();
+    if ((j & 1) || !valid) {
+      wait_tiles_in_flight<PER_TILE>(nfront - 2);   // tiles j + 1 and j + 2 have landed
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
+    ++j;
     cur = cur == kAttnStages - 1 ? 0 : cur + 1;
   }
 
