@@ -493,8 +493,10 @@ __global__ __launch_bounds__(64 * kAttnWaves, 1) void attn_mfma_kernel(AttnArgs 
 
 // Write-back of the unfused order on the matrix cores (bf16 output): the fp32 group-major
 // rows of one query head are loaded in the accumulator layout of O^T and corrected and
-// scattered exactly as in the fused epilogue.  grid (ceil(n / 128), Hq), block 256 (4 waves x
-// 32 rows).
+// scattered exactly as in the fused epilogue.  grid (ceil(n / (128 kApplyTiles)), Hq), block
+// 256 (4 waves x 32 rows per tile); one staging of the correction per block.
+constexpr int kApplyTiles = 4;
+
 template <int D>
 __global__ __launch_bounds__(256) void apply_mfma_kernel(AttnArgs A, const float* __restrict__ o_gm) {
   constexpr int LDS = (kMaxCorrRank * (D + 8) + D * (kMaxCorrRank + 4)) * 2 + D * 4;
@@ -503,22 +505,27 @@ __global__ __launch_bounds__(256) void apply_mfma_kernel(AttnArgs A, const float
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
   fused_stage<D, LDS, 256>(A, h, lds, tid);
-  const int p = blockIdx.x * 128 + 32 * w + l32;
-  const bool valid = p < A.n;
-  const float* row = o_gm + (((int64_t)kv * A.n + (valid ? p : 0)) * A.g + j) * D;
-  f32x16_t o[D / 32];
+  // the staged A^T, B^T and c0 serve kApplyTiles tiles of 128 rows
+  for (int it = 0; it < kApplyTiles; ++it) {
+    const int p0 = (blockIdx.x * kApplyTiles + it) * 128;
+    if (p0 >= A.n) break;
+    const int p = p0 + 32 * w + l32;
+    const bool valid = p < A.n;
+    const float* row = o_gm + (((int64_t)kv * A.n + (valid ? p : 0)) * A.g + j) * D;
+    f32x16_t o[D / 32];
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db)
+    for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const float4 v = valid ? *reinterpret_cast<const float4*>(row + 32 * db + 8 * jj + 4 * hf)
-                             : make_float4(0.f, 0.f, 0.f, 0.f);
-      o[db][4 * jj] = v.x;
-      o[db][4 * jj + 1] = v.y;
-      o[db][4 * jj + 2] = v.z;
-      o[db][4 * jj + 3] = v.w;
-    }
-  fused_apply<D>(A, h, kv, p, valid, 1.f, o, lds, l32, hf);
+      for (int jj = 0; jj < 4; ++jj) {
+        const float4 v = valid ? *reinterpret_cast<const float4*>(row + 32 * db + 8 * jj + 4 * hf)
+                               : make_float4(0.f, 0.f, 0.f, 0.f);
+        o[db][4 * jj] = v.x;
+        o[db][4 * jj + 1] = v.y;
+        o[db][4 * jj + 2] = v.z;
+        o[db][4 * jj + 3] = v.w;
+      }
+    fused_apply<D>(A, h, kv, p, valid, 1.f, o, lds, l32, hf);
+  }
 }
 
 void launch_apply_mfma(const Dims& dm, const float* o_gm, const sparsepr_partition_t& part,
@@ -533,7 +540,7 @@ void launch_apply_mfma(const Dims& dm, const float* o_gm, const sparsepr_partiti
   a.rank = dm.rc;
   a.qperm = part.query_perm;
   a.out_tok = o;
-  const dim3 grid((unsigned)ceil_div(dm.n, 128), dm.hq);
+  const dim3 grid((unsigned)ceil_div(dm.n, 128 * kApplyTiles), dm.hq);
   if (dm.d == 128) hipLaunchKernelGGL(apply_mfma_kernel<128>, grid, dim3(256), 0, s, a, o_gm);
   else hipLaunchKernelGGL(apply_mfma_kernel<64>, grid, dim3(256), 0, s, a, o_gm);
 }
