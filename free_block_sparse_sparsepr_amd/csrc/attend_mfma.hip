@@ -3,10 +3,9 @@
 // Support, Reconstruct the Residual", execution paragraph: exact on the selected cells,
 // renormalised over the kept K/V groups) and for the dense baseline.
 //
-// Work decomposition: one block = 128 virtual query rows of one query group (4 waves x
+// Work decomposition: one block = 256 virtual query rows of one query group (8 waves x
 // 32 rows); the block walks the group's kept key runs in 64-key tiles staged through LDS
-// (double-buffered: the next tile's global loads are in flight while the current one is
-// consumed).  Each wave computes S^T = K Q^T so that a lane owns one query and 32 of the
+// (four stages, direct global-to-LDS copies two tiles ahead of the tile being consumed).  Each wave computes S^T = K Q^T so that a lane owns one query and 32 of the
 // tile's keys: the row max and sum are in-register plus one exchange with the partner
 // lane (l ^ 32), and the probabilities are already laid out as the B operand of
 // O^T += V^T P^T, so P never leaves registers.  V is stored transposed in LDS for that
