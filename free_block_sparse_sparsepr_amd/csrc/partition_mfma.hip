@@ -126,23 +126,44 @@ __global__ __launch_bounds__(256) void resp_u_mfma_kernel(const bf16_t* __restri
         uint4 x = qv ? *reinterpret_cast<const uint4*>(qr + 16 * kk + 8 * hf) : make_uint4(0, 0, 0, 0);
         qa[kk] = __builtin_bit_cast(pbf16x8_t, x);
       }
-      for (int gb = 0; gb < ngb; ++gb) {
-        pf32x16_t acc;
+      // the 32-group blocks' accumulation chains run side by side (same order within each)
+      pf32x16_t acc[2];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-        const bf16_t* ch = chi + (32 * gb + l32) * CROW + 8 * hf;
-        const bf16_t* cl = clo + (32 * gb + l32) * CROW + 8 * hf;
+      for (int gb = 0; gb < 2; ++gb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[gb][r] = 0.f;
+      if (ngb == 2) {
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+          for (int gb = 0; gb < 2; ++gb) {
+            const bf16_t* ch = chi + (32 * gb + l32) * CROW + 8 * hf;
+            const bf16_t* cl = clo + (32 * gb + l32) * CROW + 8 * hf;
+            acc[gb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[kk], *reinterpret_cast<const pbf16x8_t*>(ch + 16 * kk),
+                                                              acc[gb], 0, 0, 0);
+            acc[gb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[kk], *reinterpret_cast<const pbf16x8_t*>(cl + 16 * kk),
+                                                              acc[gb], 0, 0, 0);
+          }
+      } else {
+        const bf16_t* ch = chi + l32 * CROW + 8 * hf;
+        const bf16_t* cl = clo + l32 * CROW + 8 * hf;
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) {
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[kk], *reinterpret_cast<const pbf16x8_t*>(ch + 16 * kk), acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[kk], *reinterpret_cast<const pbf16x8_t*>(cl + 16 * kk), acc, 0, 0, 0);
+          acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[kk], *reinterpret_cast<const pbf16x8_t*>(ch + 16 * kk),
+                                                           acc[0], 0, 0, 0);
+          acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[kk], *reinterpret_cast<const pbf16x8_t*>(cl + 16 * kk),
+                                                           acc[0], 0, 0, 0);
         }
+      }
+#pragma unroll
+      for (int gb = 0; gb < 2; ++gb) {
+        if (gb >= ngb) break;
         const int b = 32 * gb + l32;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = row0 + 8 * (r >> 2) + 4 * hf + (r & 3);
-          const float u = acc[r] * scale;
-          usum[gb & 1][r] = (jh == 0) ? u : usum[gb & 1][r] + u;
+          const float u = acc[gb][r] * scale;
+          usum[gb][r] = (jh == 0) ? u : usum[gb][r] + u;
           if (row < n && b < Gk) U[((int64_t)h * n + row) * Gk + b] = u;
         }
         if (jh == g - 1) {
@@ -150,8 +171,8 @@ __global__ __launch_bounds__(256) void resp_u_mfma_kernel(const bf16_t* __restri
           for (int r = 0; r < 16; ++r) {
             const int row = row0 + 8 * (r >> 2) + 4 * hf + (r & 3);
             if (row < n && b < Gk) {
-              mx = fmaxf(mx, fabsf(usum[gb & 1][r]));
-              if (Usum) Usum[((int64_t)kv * n + row) * Gk + b] = usum[gb & 1][r];
+              mx = fmaxf(mx, fabsf(usum[gb][r]));
+              if (Usum) Usum[((int64_t)kv * n + row) * Gk + b] = usum[gb][r];
             }
           }
         }
