@@ -49,6 +49,7 @@ hipError_t ensure_exp_table() {
 // LDS, so a row costs no dependent global load.  grid (ceil(n / (4 kRouteRows)), Hq),
 // block 256.  mass [Hkv][Gq][Gk] must be zero on entry.
 constexpr int kRouteRows = 64;
+static_assert(4 * kRouteRows <= 4096, "a block's cell sums must stay below 2^32");
 constexpr int kRoutePrefetch = 8;
 
 __global__ __launch_bounds__(256) void route_mass_kernel(const float* __restrict__ U,
@@ -56,11 +57,13 @@ __global__ __launch_bounds__(256) void route_mass_kernel(const float* __restrict
                                                          const int32_t* __restrict__ koff, int n,
                                                          int g, int Gq, int Gk,
                                                          unsigned long long* __restrict__ mass) {
-  __shared__ unsigned long long acc[kMaxGroups * kMaxGroups];
+  // a block's rows (at most 4 kRouteRows = 256, each adding at most 2^20 to a cell) keep a
+  // cell's partial sum below 2^28: 32-bit LDS accumulators (16 KB), 64-bit global atomics
+  __shared__ uint32_t acc[kMaxGroups * kMaxGroups];
   __shared__ uint32_t etab[kExpTable];
   const int h = blockIdx.y, kv = h / g;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  for (int i = threadIdx.x; i < Gq * Gk; i += 256) acc[i] = 0ull;
+  for (int i = threadIdx.x; i < Gq * Gk; i += 256) acc[i] = 0u;
   for (int i = threadIdx.x; i < kExpTable; i += 256) etab[i] = c_exp_table[i];
   const int nb = lane < Gk ? koff[(int64_t)kv * (Gk + 1) + lane + 1] - koff[(int64_t)kv * (Gk + 1) + lane] : 0;
   __syncthreads();
@@ -92,12 +95,12 @@ __global__ __launch_bounds__(256) void route_mass_kernel(const float* __restrict
       // e <= 2^22 * 2^20 per lane, so every partial sum of the 64 lanes stays below 2^48
       // and the float64 sum is exact
       const uint64_t tot = (uint64_t)wave_sum_f64((double)e);
-      if (e) atomicAdd(&acc[la[j] * Gk + lane], (unsigned long long)udiv_exact(e << 20, tot));
+      if (e) atomicAdd(&acc[la[j] * Gk + lane], (uint32_t)udiv_exact(e << 20, tot));
     }
   }
   __syncthreads();
   for (int idx = threadIdx.x; idx < Gq * Gk; idx += 256) {
-    unsigned long long v = acc[idx];
+    const unsigned long long v = acc[idx];
     if (v) atomicAdd(&mass[(int64_t)kv * Gq * Gk + idx], v);
   }
 }
