@@ -621,7 +621,18 @@ __global__ __launch_bounds__(256) void segment_mean_kernel(const T* __restrict__
   const int cq = threadIdx.x % CQ, ph = threadIdx.x / CQ;
   const int start = offsets[(int64_t)h * (G + 1) + b], end = offsets[(int64_t)h * (G + 1) + b + 1];
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int r = start + ph; r < end; r += P) {
+  // eight rows' loads in flight per thread, added in row order (the sum order is unchanged)
+  int r = start + ph;
+  for (; r + 7 * P < end; r += 8 * P) {
+    float x[8][8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) load8f<T>(kgm + ((int64_t)h * n + r + u * P) * D + 8 * cq, x[u]);
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += x[u][e];
+  }
+  for (; r < end; r += P) {
     float x[8];
     load8f<T>(kgm + ((int64_t)h * n + r) * D + 8 * cq, x);
 #pragma unroll
