@@ -80,6 +80,8 @@ Workspace plan_workspace(const sparsepr_params& p) {
   if (w.total_fused > w.total) w.total = w.total_fused;
   if (w.total_probe > w.total) w.total = w.total_probe;
   if (w.total_dense > w.total) w.total = w.total_dense;
+  w.attn_order = align_up(w.total);
+  w.total = align_up(w.attn_order + attn_order_bytes(p.n, p.heads_q / p.heads_kv, p.heads_kv, p.groups_q));
   return w;
 }
 
@@ -246,8 +248,6 @@ sparsepr_status sparsepr_route(const sparsepr_params* params, const sparsepr_par
 sparsepr_status sparsepr_attend(const sparsepr_params* params, const sparsepr_partition_t* part,
                                 const sparsepr_route_t* route, float* o_gm, float* lse, void* workspace,
                                 size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   sparsepr_status st = check_params(params);
   if (st != SPARSEPR_OK) return st;
   if (!part || !route || !o_gm) return SPARSEPR_ERR_NULL;
@@ -256,11 +256,15 @@ sparsepr_status sparsepr_attend(const sparsepr_params* params, const sparsepr_pa
     return SPARSEPR_ERR_NULL;
   if (!aligned16(part->q_gm) || !aligned16(part->k_gm) || !aligned16(part->v_gm) || !aligned16(o_gm))
     return SPARSEPR_ERR_ALIGN;
+  const Workspace wp = plan_workspace(*params);
+  st = check_ws(params, workspace, workspace_bytes, wp.total);
+  if (st != SPARSEPR_OK) return st;
   const Dims dm = dims_of(*params);
   AttnArgs a = sparse_args(dm, *part, *route);
   a.o = o_gm;
   a.lse = lse;
   (void)hipGetLastError();
+  if (dm.bf16) launch_tile_order(dm, a, static_cast<char*>(workspace) + wp.attn_order, (hipStream_t)stream);
   launch_attention(dm, a, false, (hipStream_t)stream);
   return hip_status();
 }
@@ -278,11 +282,12 @@ sparsepr_status sparsepr_attend_apply(const sparsepr_params* params, const spars
   if (!aligned16(part->q_gm) || !aligned16(part->k_gm) || !aligned16(part->v_gm) || !aligned16(o))
     return SPARSEPR_ERR_ALIGN;
   const Workspace wp = plan_workspace(*params);
-  st = check_ws(params, workspace, workspace_bytes, wp.total_fused);
+  st = check_ws(params, workspace, workspace_bytes, wp.total);
   if (st != SPARSEPR_OK) return st;
   const Dims dm = dims_of(*params);
   AttnArgs a = sparse_args(dm, *part, *route);
   (void)hipGetLastError();
+  if (dm.bf16) launch_tile_order(dm, a, static_cast<char*>(workspace) + wp.attn_order, (hipStream_t)stream);
   if (wp.total_fused == 0) {
     a.fitA = fit->A;
     a.fitB = fit->B;

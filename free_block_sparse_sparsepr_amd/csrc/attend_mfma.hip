@@ -376,11 +376,20 @@ __global__ __launch_bounds__(64 * kAttnWaves, 1) void attn_mfma_kernel(AttnArgs 
   const int per_xcd = total / kXcds;
   const int b = blockIdx.x;
   const int logical = (b % kXcds) * per_xcd + b / kXcds;
-  const int kv = logical / A.tiles_per_head;
-  const int t = logical % A.tiles_per_head;
-  if (kv >= A.n_heads_kv) return;
+  int kv;
   TileInfo ti;
-  if (!find_tile(A, kv, t, C::BM, ti)) return;
+  if (A.order != nullptr) {   // the head's groups longest first
+    kv = logical / A.tiles_per_head;
+    if (kv >= A.n_heads_kv) return;
+    const int idx = logical % A.tiles_per_head;
+    if (idx >= A.order_count[kv]) return;
+    const int32_t* e = A.order + 2 * ((int64_t)kv * A.tiles_per_head + idx);
+    if (!group_tile(A, kv, e[0], e[1], C::BM, ti)) return;
+  } else {
+    kv = logical / A.tiles_per_head;
+    if (kv >= A.n_heads_kv) return;
+    if (!find_tile(A, kv, logical % A.tiles_per_head, C::BM, ti)) return;
+  }
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
@@ -661,6 +670,76 @@ void launch_probe_attn_mfma(const Dims& dm, const void* q, const sparsepr_partit
 }
 
 constexpr int kAttnBN = 64;   // keys per tile of the main attention kernel
+
+// Longest-first schedule of the block-sparse attention within each KV head: a head's query
+// groups are ranked by the number of key tiles each of their query tiles walks (descending,
+// ties to the smaller group) and their query tiles laid out in that order.  Heads keep their
+// place in the grid (a head's tiles stay together on one XCD, where its K/V runs are shared
+// in L2); only the order of its groups changes, so the last blocks of a head are its
+// shortest.  The order changes the schedule, never a result.  grid Hkv, block 64.
+__global__ __launch_bounds__(64) void tile_order_kernel(const int32_t* __restrict__ qoff,
+                                                        const int32_t* __restrict__ koff,
+                                                        const int32_t* __restrict__ row_ptr,
+                                                        const int32_t* __restrict__ cols, int gq, int gk, int g,
+                                                        int BM, int BN, int tiles_per_head,
+                                                        int32_t* __restrict__ order, int32_t* __restrict__ count) {
+  __shared__ int nkt[kMaxGroups], nqt[kMaxGroups], start[kMaxGroups];
+  const int kv = blockIdx.x, a = threadIdx.x;
+  if (a < gq) {
+    const int32_t* qo = qoff + (int64_t)kv * (gq + 1);
+    nqt[a] = (int)ceil_div((int64_t)(qo[a + 1] - qo[a]) * g, BM);
+    const int32_t* cl = cols + (int64_t)kv * gq * gk;
+    const int32_t* ko = koff + (int64_t)kv * (gk + 1);
+    const int32_t* rp = row_ptr + (int64_t)kv * (gq + 1);
+    int t = 0;
+    for (int ci = rp[a], ce = rp[a + 1]; ci < ce;) {   // runs of adjacent kept key groups, as next_run
+      const int b = cl[ci++];
+      int e = b;
+      while (ci < ce && cl[ci] == e + 1) { ++e; ++ci; }
+      const int k0 = ko[b], k1 = ko[e + 1];
+      if (k1 > k0) t += (k1 - (k0 & ~15) + BN - 1) / BN;
+    }
+    nkt[a] = t;
+  }
+  __syncthreads();
+  if (a < gq) {   // tiles of the groups ranked before this one
+    int before = 0;
+    for (int b = 0; b < gq; ++b)
+      if (nkt[b] > nkt[a] || (nkt[b] == nkt[a] && b < a)) before += nqt[b];
+    start[a] = before;
+  }
+  __syncthreads();
+  if (a < gq) {
+    int32_t* oh = order + 2 * (int64_t)kv * tiles_per_head;
+    for (int t = 0; t < nqt[a]; ++t) {
+      oh[2 * (start[a] + t)] = a;
+      oh[2 * (start[a] + t) + 1] = t;
+    }
+  }
+  if (a == 0) {
+    int tot = 0;
+    for (int b = 0; b < gq; ++b) tot += nqt[b];
+    count[kv] = tot;
+  }
+}
+
+static int attn_tiles_per_head(int n, int g, int gq) {
+  return (int)ceil_div((int64_t)n * g, MfmaCfg<128, kAttnBN, kAttnWaves>::BM) + gq;
+}
+
+size_t attn_order_bytes(int n, int g, int hkv, int gq) {
+  return (size_t)(2 * (int64_t)attn_tiles_per_head(n, g, gq) * hkv + 64 + hkv) * 4;
+}
+
+void launch_tile_order(const Dims& dm, AttnArgs& a, char* region, hipStream_t s) {
+  const int tph = attn_tiles_per_head(dm.n, dm.g, dm.gq);
+  int32_t* order = reinterpret_cast<int32_t*>(region);
+  int32_t* count = order + 2 * (int64_t)tph * dm.hkv;
+  hipLaunchKernelGGL(tile_order_kernel, dim3(dm.hkv), dim3(64), 0, s, a.qoff, a.koff, a.row_ptr, a.cols, dm.gq, dm.gk,
+                     dm.g, MfmaCfg<128, kAttnBN, kAttnWaves>::BM, kAttnBN, tph, order, count);
+  a.order = order;
+  a.order_count = count;
+}
 
 template <int D, typename OutT>
 void launch_mfma_typed(AttnArgs a, int hkv, hipStream_t s) {

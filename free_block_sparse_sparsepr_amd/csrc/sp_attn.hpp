@@ -26,6 +26,8 @@ struct AttnArgs {
   float scale;
   int tiles_per_head;          // tiles scheduled per KV head
   int n_heads_kv;
+  const int32_t* order;        // NULL, or [Hkv][tiles_per_head][2]: (query group, tile of the group)
+  const int32_t* order_count;  // [Hkv] tiles of each head in order
   // fused write-back (one query head per KV head): o_hat = o + c0 + (o A) B written to
   // out_tok[h][qperm[p]] in the input dtype
   const float* fitA;           // [Hq][d][rank] or NULL (no fused write-back)
@@ -42,6 +44,20 @@ struct TileInfo {
   int v0, v1;     // virtual row range of this tile
   int kbeg, kend; // CSR range in cols (routed) or -1 (dense)
 };
+
+// Tile t of query group a of KV head kv (false past the group's last tile).
+__device__ __forceinline__ bool group_tile(const AttnArgs& A, int kv, int a, int t, int BM, TileInfo& ti) {
+  const int32_t* qo = A.qoff + (int64_t)kv * (A.gq + 1);
+  const int r0 = qo[a] * A.g, r1 = qo[a + 1] * A.g;
+  ti.a = a;
+  ti.v0 = r0 + t * BM;
+  if (ti.v0 >= r1) return false;
+  ti.v1 = min(r1, ti.v0 + BM);
+  const int32_t* rp = A.row_ptr + (int64_t)kv * (A.gq + 1);
+  ti.kbeg = rp[a];
+  ti.kend = rp[a + 1];
+  return true;
+}
 
 // Number of tiles of a head is bounded by ceil(n g / BM) + Gq; blocks beyond the head's
 // real tile count return early.

@@ -157,6 +157,7 @@ struct Workspace {
   size_t dense_meta, total_dense;
   size_t fused_ogm, total_fused;
   size_t rt_order, rt_pos, rt_prefix, rt_cost, rt_kept, rt_head, total_route;   // global route budget
+  size_t attn_order;   // attention tile order, past every other region (attend may run beside probe_fit)
   size_t total;
   int fpk, fpq, nchunks;
 };

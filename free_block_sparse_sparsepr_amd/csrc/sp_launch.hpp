@@ -20,6 +20,10 @@ void launch_route(const Dims& dm, int64_t budget, const sparsepr_partition_t& pa
 // out_is_input_dtype: output element type equals Q's (dense baseline); otherwise fp32.
 void launch_attention(const Dims& dm, AttnArgs a, bool out_is_input_dtype, hipStream_t s);
 void launch_attention_mfma(const Dims& dm, AttnArgs a, bool out_is_input_dtype, hipStream_t s);
+// Longest-first order of the block-sparse attention's query tiles (matrix-core path): bytes of
+// its workspace region, and the kernel that fills it and points `a` at it.
+size_t attn_order_bytes(int n, int g, int hkv, int gq);
+void launch_tile_order(const Dims& dm, AttnArgs& a, char* region, hipStream_t s);
 void launch_probe_attn_mfma(const Dims& dm, const void* q, const sparsepr_partition_t& part,
                             const sparsepr_route_t& route, const sparsepr_fit_t& fit, int chunk, int nchunks,
                             float* partials, hipStream_t s);

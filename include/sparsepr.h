@@ -237,7 +237,10 @@ sparsepr_status sparsepr_route(const sparsepr_params* params, const sparsepr_par
 
 /* Block-sparse attention over the kept cells, renormalised over the kept K/V groups
  * (PSRR, execution paragraph).  Reads q_gm, k_gm, v_gm, offsets and the CSR.
- * o_gm: [Hkv, n, g, d] fp32, group-major rows; lse: [Hkv, n, g] fp32 (natural log). */
+ * o_gm: [Hkv, n, g, d] fp32, group-major rows; lse: [Hkv, n, g] fp32 (natural log).
+ * The workspace (sparsepr_workspace_size bytes, 256-byte aligned) holds the tile schedule
+ * (each head's query groups longest first) in a region disjoint from the one
+ * sparsepr_probe_fit uses, so the two may run concurrently on one workspace. */
 sparsepr_status sparsepr_attend(const sparsepr_params* params, const sparsepr_partition_t* part,
                                 const sparsepr_route_t* route, float* o_gm, float* lse,
                                 void* workspace, size_t workspace_bytes, void* stream);
