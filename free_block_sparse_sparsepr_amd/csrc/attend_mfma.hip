@@ -14,7 +14,7 @@
 //
 // Blocks are remapped so that consecutive tiles of one query group run on the same XCD
 // (the hardware deals blocks round-robin over the 8 XCDs), keeping a group's key runs
-// hot in that XCD's L2.
+// hot in that XCD's L2; a head's tiles stay together, its query groups longest first.
 #include "sp_attn.hpp"
 #include "sp_common.hpp"
 #include "sp_launch.hpp"
@@ -684,13 +684,17 @@ __global__ __launch_bounds__(64) void tile_order_kernel(const int32_t* __restric
                                                         int BM, int BN, int tiles_per_head,
                                                         int32_t* __restrict__ order, int32_t* __restrict__ count) {
   __shared__ int nkt[kMaxGroups], nqt[kMaxGroups], start[kMaxGroups];
+  __shared__ int cl[kMaxGroups * kMaxGroups], ko[kMaxGroups + 1], rp[kMaxGroups + 1];
   const int kv = blockIdx.x, a = threadIdx.x;
+  // the head's CSR and key offsets, staged with coalesced loads
+  for (int i = a; i <= gk; i += 64) ko[i] = koff[(int64_t)kv * (gk + 1) + i];
+  for (int i = a; i <= gq; i += 64) rp[i] = row_ptr[(int64_t)kv * (gq + 1) + i];
+  __syncthreads();
+  for (int i = a; i < rp[gq]; i += 64) cl[i] = cols[(int64_t)kv * gq * gk + i];
+  __syncthreads();
   if (a < gq) {
     const int32_t* qo = qoff + (int64_t)kv * (gq + 1);
     nqt[a] = (int)ceil_div((int64_t)(qo[a + 1] - qo[a]) * g, BM);
-    const int32_t* cl = cols + (int64_t)kv * gq * gk;
-    const int32_t* ko = koff + (int64_t)kv * (gk + 1);
-    const int32_t* rp = row_ptr + (int64_t)kv * (gq + 1);
     int t = 0;
     for (int ci = rp[a], ce = rp[a + 1]; ci < ce;) {   // runs of adjacent kept key groups, as next_run
       const int b = cl[ci++];
