@@ -110,6 +110,21 @@ def test_entry_points_reject_before_any_launch():
     assert lib.sparsepr_partition(ctypes.byref(good), fake, fake, fake, ctypes.byref(full), fake, 16,
                                   nul) == -5
     assert lib.sparsepr_status_string(-5) == b"workspace too small"
+    # attend and attend_apply keep their tile schedule in the workspace: a missing or short
+    # one is rejected before anything is launched
+    rfields = {f: 0x2000 for f in B.ROUTE_FIELDS}
+    froute = B.RouteT(**rfields)
+    ffit = B.FitT(**{f: 0x2000 for f in B.FIT_FIELDS})
+    assert lib.sparsepr_attend(ctypes.byref(good), ctypes.byref(full), ctypes.byref(froute), fake, fake, nul, 0,
+                               nul) == -1
+    assert lib.sparsepr_attend(ctypes.byref(good), ctypes.byref(full), ctypes.byref(froute), fake, fake, fake, 16,
+                               nul) == -5
+    assert lib.sparsepr_attend_apply(ctypes.byref(good), ctypes.byref(full), ctypes.byref(froute),
+                                     ctypes.byref(ffit), fake, fake, 16, nul) == -5
+    need = ctypes.c_size_t(0)
+    assert lib.sparsepr_workspace_size(ctypes.byref(good), ctypes.byref(need)) == 0
+    assert lib.sparsepr_attend(ctypes.byref(good), ctypes.byref(full), ctypes.byref(froute), fake, fake, odd,
+                               need.value, nul) == -4
 
 
 def test_support_diagnostics_validation():
