@@ -550,20 +550,25 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint4* __restric
   dst[r * VPR + c] = src[srow * VPR + c];
 }
 
-// Transposing gather of V into group-major, d-major order: block = 64 positions; rows
+// Transposing gather of V into group-major, d-major order: block = kVtBlock positions; rows
 // perm[p] (or p when perm is NULL) are staged in LDS with 16-byte loads, then each thread
 // assembles one 16-byte chunk (8 positions of one d row, in the layout's key order
 // vt_pos, an involution within each 16-key group) and stores it whole.  Positions from n
-// up to n_pad are zero.  grid (ceil(n_pad / 64), Hkv), block 256.
+// up to n_pad are zero.  grid (ceil(n_pad / kVtBlock), Hkv), block 256.  128 positions make
+// each d row's store 256 contiguous bytes (bf16) at four blocks per CU.
+constexpr int kVtBlock = 128;
+
+static_assert(kVtBlock % 16 == 0, "vt_pos permutes within 16-key groups");
+
 template <typename T, int D>
 __global__ __launch_bounds__(256) void gather_vt_kernel(const T* __restrict__ v, const int32_t* __restrict__ perm,
                                                         int n, int np, T* __restrict__ vt) {
   constexpr int EPC = 16 / sizeof(T);       // elements per 16-byte chunk
   constexpr int CPR = D / EPC;              // chunks per row
   constexpr int ROW = D + 2;                // padded LDS row (elements)
-  __shared__ T tile[64 * ROW];
-  const int kv = blockIdx.y, p0 = blockIdx.x * 64;
-  for (int idx = threadIdx.x; idx < 64 * CPR; idx += 256) {
+  __shared__ T tile[kVtBlock * ROW];
+  const int kv = blockIdx.y, p0 = blockIdx.x * kVtBlock;
+  for (int idx = threadIdx.x; idx < kVtBlock * CPR; idx += 256) {
     const int r = idx / CPR, c = idx % CPR, p = p0 + r;
     uint4 x = make_uint4(0, 0, 0, 0);
     if (p < n) {
@@ -576,7 +581,7 @@ __global__ __launch_bounds__(256) void gather_vt_kernel(const T* __restrict__ v,
   }
   __syncthreads();
   // output chunk: row d, positions p0 + EPC q .. + EPC - 1
-  constexpr int QPR = 64 / EPC;             // chunks per d row in this block
+  constexpr int QPR = kVtBlock / EPC;       // chunks per d row in this block
   for (int idx = threadIdx.x; idx < D * QPR; idx += 256) {
     const int d = idx / QPR, q = idx % QPR;
     if (p0 + EPC * q >= np) continue;
@@ -959,7 +964,7 @@ static void partition_typed(const Dims& dm, const Workspace& wp, const T* q, con
   }
   run_group_major(out.key_labels, n, hkv, dm.gk, out.key_perm, out.key_offsets, gm_hist, s);
   run_gather(k, out.key_perm, n, hkv, 1, D, dm.bf16, out.k_gm, s);
-  hipLaunchKernelGGL((gather_vt_kernel<T, D>), dim3((unsigned)ceil_div(vt_pad(n), 64), hkv), dim3(256), 0, s, v,
+  hipLaunchKernelGGL((gather_vt_kernel<T, D>), dim3((unsigned)ceil_div(vt_pad(n), kVtBlock), hkv), dim3(256), 0, s, v,
                      out.key_perm, n, (int)vt_pad(n), static_cast<T*>(out.v_gm));
   hipLaunchKernelGGL((segment_mean_kernel<T, D>), dim3(dm.gk, hkv), dim3(256), 0, s,
                      static_cast<const T*>(out.k_gm), out.key_offsets, n, dm.gk, out.key_centroids);
@@ -982,7 +987,7 @@ static void partition_typed(const Dims& dm, const Workspace& wp, const T* q, con
 }
 
 void launch_transpose_v(const Dims& dm, const void* v, void* vt, hipStream_t s) {
-  const dim3 grid((unsigned)ceil_div(vt_pad(dm.n), 64), dm.hkv);
+  const dim3 grid((unsigned)ceil_div(vt_pad(dm.n), kVtBlock), dm.hkv);
   const int np = (int)vt_pad(dm.n);
   if (dm.bf16) {
     if (dm.d == 128) hipLaunchKernelGGL((gather_vt_kernel<bf16_t, 128>), grid, dim3(256), 0, s, (const bf16_t*)v, nullptr, dm.n, np, (bf16_t*)vt);
