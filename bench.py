@@ -144,6 +144,8 @@ def ablation_report(workload):
         sp.route()
         if kw.get("probe_mode") == 2:
             sp.fit["probe_tokens"].copy_(torch.from_numpy(given.astype(np.int32)))
+        sp.probe_fit(q)            # untimed first pass: the first launches load their kernels
+        sp.attend_apply()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         sp.probe_fit(q)
