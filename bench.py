@@ -29,7 +29,7 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3
 STAGES_FUSED = ["partition", "route", "probe_fit", "attend_apply"]
 STAGES_UNFUSED = ["partition", "route", "attend", "probe_fit", "apply"]
-STAGES_OVERLAPPED = ["partition", "route", "probe_fit (second stream)", "attend", "apply"]
+STAGES_OVERLAPPED = ["partition", "gather_kv (second stream)", "route", "probe_fit (second stream)", "attend", "apply"]
 
 
 def log(*a):
@@ -362,10 +362,12 @@ def main():
         stages = STAGES_UNFUSED
         fns = [lambda: sp.partition(q, k, v), sp.route, sp.attend, lambda: sp.probe_fit(q), lambda: sp.apply(out)]
         streams = [stream] * 5
-    elif order == "overlapped":
+    elif order == "overlapped":   # as SparsePR.overlapped, stage by stage
         stages = STAGES_OVERLAPPED
-        fns = [lambda: sp.partition(q, k, v), sp.route, lambda: sp.probe_fit(q), sp.attend, lambda: sp.apply(out)]
-        streams = [stream, stream, side, stream, stream]
+        kv_ready = torch.cuda.Event()
+        fns = [lambda: sp.partition(q, k, v, defer_kv=True), lambda: sp.gather_kv(k, v), sp.route,
+               lambda: sp.probe_fit(q), sp.attend, lambda: sp.apply(out)]
+        streams = [stream, side, stream, side, stream, stream]
     else:
         stages = STAGES_FUSED
         fns = [lambda: sp.partition(q, k, v), sp.route, lambda: sp.probe_fit(q), lambda: sp.attend_apply(out)]
@@ -379,13 +381,17 @@ def main():
         for i, fn in enumerate(fns):
             st = streams[i]
             if st is not stream:
-                st.wait_stream(stream)      # the side branch starts after route
+                st.wait_stream(stream)      # a side stage starts after the main stream's work so far
+            if side is not None and stages[i] == "attend":
+                stream.wait_event(kv_ready)  # attend reads the gathered K and V
             with torch.cuda.stream(st):
                 if ev is not None:
                     ev[i][0].record(st)
                 fn()
                 if ev is not None:
                     ev[i][1].record(st)
+                if side is not None and stages[i].startswith("gather_kv"):
+                    kv_ready.record(st)
             if i == len(fns) - 2 and side is not None:
                 stream.wait_stream(side)    # apply waits for the fit
 

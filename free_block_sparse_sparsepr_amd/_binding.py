@@ -29,7 +29,7 @@ class Params(ctypes.Structure):
                 ("kmeans_iters", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
                 ("ablation", ctypes.c_int32), ("probe_mode", ctypes.c_int32),
                 ("partition_mode", ctypes.c_int32), ("budget_mode", ctypes.c_int32),
-                ("cost_mode", ctypes.c_int32)]
+                ("cost_mode", ctypes.c_int32), ("defer_kv_gather", ctypes.c_int32)]
 
 
 def _ptr_struct(name, names):
@@ -47,7 +47,7 @@ PartitionT = _ptr_struct("PartitionT", PARTITION_FIELDS)
 RouteT = _ptr_struct("RouteT", ROUTE_FIELDS)
 FitT = _ptr_struct("FitT", FIT_FIELDS)
 
-EXPORTS = ["sparsepr_workspace_size", "sparsepr_partition", "sparsepr_route", "sparsepr_attend",
+EXPORTS = ["sparsepr_workspace_size", "sparsepr_partition", "sparsepr_gather_kv", "sparsepr_route", "sparsepr_attend",
            "sparsepr_probe_fit", "sparsepr_apply", "sparsepr_attend_apply", "sparsepr_dense_attention",
            "sparsepr_diagnostics_workspace_size", "sparsepr_residual_diagnostics",
            "sparsepr_support_workspace_size", "sparsepr_support_diagnostics", "sparsepr_status_string"]
@@ -71,6 +71,7 @@ def load():
     sigs = {
         "sparsepr_workspace_size": [P(Params), P(ctypes.c_size_t)],
         "sparsepr_partition": [P(Params), vp, vp, vp, P(PartitionT), vp, sz, vp],
+        "sparsepr_gather_kv": [P(Params), vp, vp, P(PartitionT), vp],
         "sparsepr_route": [P(Params), P(PartitionT), P(RouteT), vp, sz, vp],
         "sparsepr_attend": [P(Params), P(PartitionT), P(RouteT), vp, vp, vp, sz, vp],
         "sparsepr_probe_fit": [P(Params), vp, P(PartitionT), P(RouteT), P(FitT), vp, sz, vp],

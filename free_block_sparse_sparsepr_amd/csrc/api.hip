@@ -102,6 +102,7 @@ static sparsepr_status check_params(const sparsepr_params* p) {
   if (!(p->lambda > 0.f) || !std::isfinite(p->lambda)) return SPARSEPR_ERR_PARAM;
   if (!(p->rho_exec <= 1.f) || !((double)p->rho_exec > (double)p->n_probe / (double)p->n)) return SPARSEPR_ERR_PARAM;
   if (p->kmeans_iters < 0 || p->kmeans_iters > 64) return SPARSEPR_ERR_PARAM;
+  if (p->defer_kv_gather != 0 && p->defer_kv_gather != 1) return SPARSEPR_ERR_PARAM;
   if (p->block != 64) return SPARSEPR_ERR_PARAM;
   if (!(p->softmax_scale >= 0.f) || !std::isfinite(p->softmax_scale)) return SPARSEPR_ERR_PARAM;
   if (p->budget_mode != SPARSEPR_BUDGET_PER_HEAD && p->budget_mode != SPARSEPR_BUDGET_GLOBAL)
@@ -222,7 +223,20 @@ sparsepr_status sparsepr_partition(const sparsepr_params* params, const void* q,
   st = check_ws(params, workspace, workspace_bytes, wp.total_partition);
   if (st != SPARSEPR_OK) return st;
   (void)hipGetLastError();
-  launch_partition(dims_of(*params), wp, q, k, v, o, static_cast<char*>(workspace), (hipStream_t)stream);
+  launch_partition(dims_of(*params), wp, q, k, v, o, static_cast<char*>(workspace), params->defer_kv_gather != 0,
+                   (hipStream_t)stream);
+  return hip_status();
+}
+
+sparsepr_status sparsepr_gather_kv(const sparsepr_params* params, const void* k, const void* v,
+                                   const sparsepr_partition_t* part, void* stream) {
+  sparsepr_status st = check_params(params);
+  if (st != SPARSEPR_OK) return st;
+  if (!k || !v || !part) return SPARSEPR_ERR_NULL;
+  if (!part->key_perm || !part->k_gm || !part->v_gm) return SPARSEPR_ERR_NULL;
+  if (!aligned16(k) || !aligned16(v) || !aligned16(part->k_gm) || !aligned16(part->v_gm)) return SPARSEPR_ERR_ALIGN;
+  (void)hipGetLastError();
+  launch_gather_kv(dims_of(*params), k, v, *part, (hipStream_t)stream);
   return hip_status();
 }
 

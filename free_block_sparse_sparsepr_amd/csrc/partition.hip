@@ -593,7 +593,13 @@ __global__ __launch_bounds__(256) void gather_vt_kernel(const T* __restrict__ v,
   }
 }
 
-// C^K_b = mean of the group-major key rows of group b in fixed order (fp32).  Thread t
+// Row of K holding group-major position r: K itself is group-major when perm is NULL.
+__device__ __forceinline__ int row_of(const int32_t* __restrict__ perm, int h, int n, int r) {
+  return perm ? perm[(int64_t)h * n + r] : r;
+}
+
+// C^K_b = mean of the group-major key rows of group b in fixed order (fp32), read from K_gm,
+// or from K through the key permutation (perm non-NULL) when K_gm is formed later.  Thread t
 // sums 8 columns (8 * (t % (D / 8)) ..) over rows start + ph, ph + P, ... with P = 256 /
 // (D / 8) row phases (16-byte loads), then the phases are combined in ascending order.
 // grid (G, Hkv), block 256.
@@ -616,7 +622,7 @@ __device__ __forceinline__ void load8f<float>(const float* p, float* x) {
 }
 
 template <typename T, int D>
-__global__ __launch_bounds__(256) void segment_mean_kernel(const T* __restrict__ kgm,
+__global__ __launch_bounds__(256) void segment_mean_kernel(const T* __restrict__ kgm, const int32_t* __restrict__ perm,
                                                            const int32_t* __restrict__ offsets, int n,
                                                            int G, float* __restrict__ C) {
   constexpr int CQ = D / 8;
@@ -631,7 +637,7 @@ __global__ __launch_bounds__(256) void segment_mean_kernel(const T* __restrict__
   for (; r + 7 * P < end; r += 8 * P) {
     float x[8][8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) load8f<T>(kgm + ((int64_t)h * n + r + u * P) * D + 8 * cq, x[u]);
+    for (int u = 0; u < 8; ++u) load8f<T>(kgm + ((int64_t)h * n + row_of(perm, h, n, r + u * P)) * D + 8 * cq, x[u]);
 #pragma unroll
     for (int u = 0; u < 8; ++u)
 #pragma unroll
@@ -639,7 +645,7 @@ __global__ __launch_bounds__(256) void segment_mean_kernel(const T* __restrict__
   }
   for (; r < end; r += P) {
     float x[8];
-    load8f<T>(kgm + ((int64_t)h * n + r) * D + 8 * cq, x);
+    load8f<T>(kgm + ((int64_t)h * n + row_of(perm, h, n, r)) * D + 8 * cq, x);
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] += x[e];
   }
@@ -937,8 +943,15 @@ void run_gather(const void* src, const int32_t* perm, int n, int hkv, int g, int
 }
 
 template <typename T, int D>
+static void gather_kv_typed(const Dims& dm, const T* k, const T* v, const sparsepr_partition_t& out, hipStream_t s) {
+  run_gather(k, out.key_perm, dm.n, dm.hkv, 1, D, dm.bf16, out.k_gm, s);
+  hipLaunchKernelGGL((gather_vt_kernel<T, D>), dim3((unsigned)ceil_div(vt_pad(dm.n), kVtBlock), dm.hkv), dim3(256), 0,
+                     s, v, out.key_perm, dm.n, (int)vt_pad(dm.n), static_cast<T*>(out.v_gm));
+}
+
+template <typename T, int D>
 static void partition_typed(const Dims& dm, const Workspace& wp, const T* q, const T* k, const T* v,
-                            const sparsepr_partition_t& out, char* ws, hipStream_t s) {
+                            const sparsepr_partition_t& out, char* ws, bool defer_kv, hipStream_t s) {
   uint32_t* maxbits = reinterpret_cast<uint32_t*>(ws + wp.maxbits);
   int8_t* xk = reinterpret_cast<int8_t*>(ws + wp.xk);
   int8_t* xq = reinterpret_cast<int8_t*>(ws + wp.xq);
@@ -963,11 +976,14 @@ static void partition_typed(const Dims& dm, const Workspace& wp, const T* q, con
     run_kmeans(xk, n, hkv, dm.gk, dm.rk, wp.fpk, dm.iters, C, sums, out.key_labels, out.key_centroids_int, s);
   }
   run_group_major(out.key_labels, n, hkv, dm.gk, out.key_perm, out.key_offsets, gm_hist, s);
-  run_gather(k, out.key_perm, n, hkv, 1, D, dm.bf16, out.k_gm, s);
-  hipLaunchKernelGGL((gather_vt_kernel<T, D>), dim3((unsigned)ceil_div(vt_pad(n), kVtBlock), hkv), dim3(256), 0, s, v,
-                     out.key_perm, n, (int)vt_pad(n), static_cast<T*>(out.v_gm));
-  hipLaunchKernelGGL((segment_mean_kernel<T, D>), dim3(dm.gk, hkv), dim3(256), 0, s,
-                     static_cast<const T*>(out.k_gm), out.key_offsets, n, dm.gk, out.key_centroids);
+  if (defer_kv) {
+    hipLaunchKernelGGL((segment_mean_kernel<T, D>), dim3(dm.gk, hkv), dim3(256), 0, s, k, out.key_perm,
+                       out.key_offsets, n, dm.gk, out.key_centroids);
+  } else {
+    gather_kv_typed<T, D>(dm, k, v, out, s);
+    hipLaunchKernelGGL((segment_mean_kernel<T, D>), dim3(dm.gk, hkv), dim3(256), 0, s,
+                       static_cast<const T*>(out.k_gm), nullptr, out.key_offsets, n, dm.gk, out.key_centroids);
+  }
   // queries (the semantic features are formed first: the response kernels below reuse the
   // second max slot)
   if (dm.semantic)
@@ -999,17 +1015,28 @@ void launch_transpose_v(const Dims& dm, const void* v, void* vt, hipStream_t s) 
 }
 
 void launch_partition(const Dims& dm, const Workspace& wp, const void* q, const void* k, const void* v,
-                      const sparsepr_partition_t& out, char* ws, hipStream_t s) {
+                      const sparsepr_partition_t& out, char* ws, bool defer_kv, hipStream_t s) {
   if (dm.bf16) {
     if (dm.d == 128)
-      partition_typed<bf16_t, 128>(dm, wp, (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, out, ws, s);
+      partition_typed<bf16_t, 128>(dm, wp, (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, out, ws, defer_kv, s);
     else
-      partition_typed<bf16_t, 64>(dm, wp, (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, out, ws, s);
+      partition_typed<bf16_t, 64>(dm, wp, (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, out, ws, defer_kv, s);
   } else {
     if (dm.d == 128)
-      partition_typed<float, 128>(dm, wp, (const float*)q, (const float*)k, (const float*)v, out, ws, s);
+      partition_typed<float, 128>(dm, wp, (const float*)q, (const float*)k, (const float*)v, out, ws, defer_kv, s);
     else
-      partition_typed<float, 64>(dm, wp, (const float*)q, (const float*)k, (const float*)v, out, ws, s);
+      partition_typed<float, 64>(dm, wp, (const float*)q, (const float*)k, (const float*)v, out, ws, defer_kv, s);
+  }
+}
+
+void launch_gather_kv(const Dims& dm, const void* k, const void* v, const sparsepr_partition_t& part,
+                      hipStream_t s) {
+  if (dm.bf16) {
+    if (dm.d == 128) gather_kv_typed<bf16_t, 128>(dm, (const bf16_t*)k, (const bf16_t*)v, part, s);
+    else gather_kv_typed<bf16_t, 64>(dm, (const bf16_t*)k, (const bf16_t*)v, part, s);
+  } else {
+    if (dm.d == 128) gather_kv_typed<float, 128>(dm, (const float*)k, (const float*)v, part, s);
+    else gather_kv_typed<float, 64>(dm, (const float*)k, (const float*)v, part, s);
   }
 }
 

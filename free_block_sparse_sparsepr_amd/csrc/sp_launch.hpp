@@ -13,8 +13,10 @@ void launch_resp_u_mfma(const Dims& dm, const void* q, const float* Ck, float* U
 
 // V [Hkv][n][d] (token order) -> transposed layout [Hkv][d][n_pad] (see vt_pos).
 void launch_transpose_v(const Dims& dm, const void* v, void* vt, hipStream_t s);
+// defer_kv: leave the K and V gathers (k_gm, v_gm) to launch_gather_kv.
 void launch_partition(const Dims& dm, const Workspace& wp, const void* q, const void* k, const void* v,
-                      const sparsepr_partition_t& out, char* ws, hipStream_t s);
+                      const sparsepr_partition_t& out, char* ws, bool defer_kv, hipStream_t s);
+void launch_gather_kv(const Dims& dm, const void* k, const void* v, const sparsepr_partition_t& part, hipStream_t s);
 void launch_route(const Dims& dm, int64_t budget, const sparsepr_partition_t& part, const sparsepr_route_t& out,
                   const Workspace& wp, char* ws, hipStream_t s);
 // out_is_input_dtype: output element type equals Q's (dense baseline); otherwise fp32.

@@ -95,6 +95,8 @@ class SparsePR:
         self.cfg = cfg
         self.lib = B.load()
         self.prm = cfg.params()
+        self.prm_defer = cfg.params()      # the same call with the K/V gathers left to gather_kv
+        self.prm_defer.defer_kv_gather = 1
         dev = torch.device(device)
         c = cfg
         i32, f32 = torch.int32, torch.float32
@@ -137,10 +139,17 @@ class SparsePR:
                 raise ValueError(f"expected contiguous {c.torch_dtype} cuda tensor of shape {(h, c.n, c.d)}, "
                                  f"got {tuple(t.shape)} {t.dtype} {t.device}")
 
-    def partition(self, q, k, v):
+    def partition(self, q, k, v, defer_kv=False):
+        """defer_kv: leave k_gm and v_gm to gather_kv (which may then run on another stream)."""
         self._check_qkv(q, k, v)
-        B.check(self.lib.sparsepr_partition(ctypes.byref(self.prm), _p(q), _p(k), _p(v),
+        prm = self.prm_defer if defer_kv else self.prm
+        B.check(self.lib.sparsepr_partition(ctypes.byref(prm), _p(q), _p(k), _p(v),
                                             ctypes.byref(self._part_t), _p(self.ws), self.ws.numel(), _stream()))
+
+    def gather_kv(self, k, v):
+        self._check_qkv(None, k, v)
+        B.check(self.lib.sparsepr_gather_kv(ctypes.byref(self.prm), _p(k), _p(v), ctypes.byref(self._part_t),
+                                            _stream()))
 
     def route(self):
         B.check(self.lib.sparsepr_route(ctypes.byref(self.prm), ctypes.byref(self._part_t),
@@ -196,17 +205,24 @@ class SparsePR:
         return self._side
 
     def overlapped(self, q, k, v, out=None):
-        """Unfused order with the probe stage on a second stream: partition -> route, then
-        probe_fit (second stream) concurrently with attend (current stream), then apply once
-        both are done.  The two branches share only read-only partition and route buffers:
-        attend writes o_gm and lse, probe_fit writes the fit buffers and the workspace."""
+        """Unfused order on two streams: the partition leaves the K/V gathers to the second
+        stream, where they run beside the route; then probe_fit (second stream) runs beside
+        attend (current stream, after the gathers), and apply once both are done.  The
+        branches share only read-only partition and route buffers: the gathers write k_gm
+        and v_gm, attend o_gm and lse, probe_fit the fit buffers and its workspace region."""
         main = torch.cuda.current_stream()
         side = self.side_stream()
-        self.partition(q, k, v)
+        self.partition(q, k, v, defer_kv=True)
+        side.wait_stream(main)
+        with torch.cuda.stream(side):
+            self.gather_kv(k, v)
+            kv_ready = torch.cuda.Event()
+            kv_ready.record(side)
         self.route()
         side.wait_stream(main)
         with torch.cuda.stream(side):
             self.probe_fit(q)
+        main.wait_event(kv_ready)
         self.attend()
         main.wait_stream(side)
         return self.apply(out)

@@ -158,6 +158,7 @@ typedef struct sparsepr_params {
   int32_t partition_mode;/* sparsepr_partition_mode (0 = the method) */
   int32_t budget_mode;   /* sparsepr_budget_mode (0 = per KV head) */
   int32_t cost_mode;     /* sparsepr_cost_mode (0 = pairs) */
+  int32_t defer_kv_gather;/* 1: sparsepr_partition leaves k_gm and v_gm to sparsepr_gather_kv */
 } sparsepr_params;
 
 /* Partition outputs (all caller-allocated device buffers).  g = heads_q / heads_kv.
@@ -223,6 +224,13 @@ sparsepr_status sparsepr_workspace_size(const sparsepr_params* params, size_t* b
 sparsepr_status sparsepr_partition(const sparsepr_params* params, const void* q, const void* k,
                                    const void* v, const sparsepr_partition_t* out, void* workspace,
                                    size_t workspace_bytes, void* stream);
+
+/* The gathers of K and V into group-major order (k_gm, and v_gm transposed) from key_perm,
+ * for a partition made with defer_kv_gather = 1, which leaves them out so that they can run
+ * on another stream beside the route (only the attention and the probe stage read them).
+ * k, v: [Hkv, n, d] (dtype, token order); writes part->k_gm and part->v_gm. */
+sparsepr_status sparsepr_gather_kv(const sparsepr_params* params, const void* k, const void* v,
+                                   const sparsepr_partition_t* part, void* stream);
 
 /* Routing to the target execution density (PSRR, execution paragraph): fixed-point cell
  * masses from the size-weighted centroid softmax of every query row (summed over the

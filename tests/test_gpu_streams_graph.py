@@ -1,5 +1,6 @@
-"""Overlapped and graph-captured execution of the whole call (the probe stage on a second
-stream beside the sparse attention; one HIP graph per call).  Every kernel of the call is
+"""Overlapped and graph-captured execution of the whole call (the K/V gathers on a second
+stream beside the route, the probe stage there beside the sparse attention; one HIP graph
+per call).  Every kernel of the call is
 deterministic (integer atomics only, fixed reduction orders), so both must reproduce the
 eager unfused / fused outputs bit for bit.  Graph replays are interleaved with eager work
 and synchronisations, each replay is checked, and a replay after the inputs are overwritten
@@ -33,6 +34,27 @@ def _setup(cname, seed_shift=0):
         K = K[:, rng.permutation(cfg.n)]
     sp = S.SparsePR(S.config_from_workload(cfg))
     return cfg, sp, device_tensor(Q, cfg), device_tensor(K, cfg), device_tensor(V, cfg)
+
+
+@pytest.mark.parametrize("cname", sorted(CASES))
+def test_deferred_kv_gather_is_bit_identical(cname):
+    """A partition that leaves the K/V gathers to gather_kv (the key centroids then read K
+    through the permutation, in the same order) gives the same buffers bit for bit."""
+    import torch
+    print(f"\n[deferred gathers {cname}]", flush=True)
+    cfg, sp, q, k, v = _setup(cname)
+    sp.partition(q, k, v)
+    torch.cuda.synchronize()
+    want = {n: host(t.clone()) for n, t in sp.part.items()}
+    for n in ("k_gm", "v_gm", "key_centroids"):
+        sp.part[n].zero_()
+    sp.partition(q, k, v, defer_kv=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(sp.part["key_centroids"]), want["key_centroids"])
+    sp.gather_kv(k, v)
+    torch.cuda.synchronize()
+    for n, t in sp.part.items():
+        np.testing.assert_array_equal(host(t), want[n], err_msg=n)
 
 
 @pytest.mark.parametrize("cname", sorted(CASES))
