@@ -725,37 +725,96 @@ __global__ __launch_bounds__(256) void resp_u_kernel(const T* __restrict__ q, co
   }
 }
 
+// All-reduce over the 16 lanes of a DPP row (every lane of the row gets the result).
+__device__ __forceinline__ int row16_sum_i32(int v) {
+  v += dpp_i32<0xB1>(v);    // quad_perm [1,0,3,2]
+  v += dpp_i32<0x4E>(v);    // quad_perm [2,3,0,1]
+  v += dpp_i32<0x141>(v);   // row_half_mirror
+  return v + dpp_i32<0x140>(v);   // row_mirror
+}
+__device__ __forceinline__ int row16_max_i32(int v) {
+  v = max(v, dpp_i32<0xB1>(v));
+  v = max(v, dpp_i32<0x4E>(v));
+  v = max(v, dpp_i32<0x141>(v));
+  return max(v, dpp_i32<0x140>(v));
+}
+
+// div_rhaz(127 c, m) for |c| <= m < 2^22: the quotient (254 |c| + m) / (2 m) is at most 127.5;
+// its fp32 estimate (operand rounding, a 1-ulp reciprocal and the product: relative error
+// below 2^-21) truncates to the floor or one off it, and the exact integer remainder
+// corrects that step.
+__device__ __forceinline__ int div127_rhaz(int c, int m) {
+  const int a = 254 * (c < 0 ? -c : c) + m, b = 2 * m;
+  int q = (int)((float)a * __builtin_amdgcn_rcpf((float)b));
+  const int r = a - q * b;
+  q += (r >= b) ? 1 : (r < 0 ? -1 : 0);
+  return c < 0 ? -q : q;
+}
+
 // Response-direction features: u = rint(Usum 2^e_U) (e_U: largest e with
 // max|Usum| 2^e <= 2^14), c_b = G_K u_b - sum u, x_b = div_rhaz(127 c_b, max|c|).
 // Written to the caller's [Hkv][n][G_K] buffer and to a stride-fp copy for the k-means.
-// One wave per row (lanes over key groups, wave reductions); each wave walks 16 rows,
-// all 16 rows' loads issued before the first is used.  grid (ceil(n / 64), Hkv), block 256.
+// One row per 16 lanes (a DPP row: sum and max without cross-row traffic), each lane
+// holding key groups 4 l .. 4 l + 3 (G_K <= 64); every 16 lanes walk four rows, all four
+// rows' loads issued before the first is used.  |u| <= 2^14 keeps |c| <= 2^21.
+// grid (ceil(n / 64), Hkv), block 256.
 __global__ __launch_bounds__(256) void query_features_kernel(const float* __restrict__ Usrc,
                                                              const uint32_t* maxbits, int n, int Gk,
                                                              int fp, int8_t* __restrict__ Xout,
                                                              int8_t* __restrict__ Xpad, int32_t* exps) {
   const int kv = blockIdx.y;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int l16 = threadIdx.x & 15, rw = threadIdx.x >> 4, f0 = 4 * l16;
   const int e = pow2_exponent(__uint_as_float(maxbits[kv]), 16384.f);
   if (blockIdx.x == 0 && threadIdx.x == 0) exps[kv * 2 + 1] = e;
-  const int i0 = blockIdx.x * 64 + w * 16;
-  float uv[16];
+  const bool vin = (Gk & 3) == 0 && ((uintptr_t)Usrc & 15) == 0;
+  const bool vout = (Gk & 3) == 0 && ((uintptr_t)Xout & 3) == 0;
+  float uv[4][4];
 #pragma unroll
-  for (int rr = 0; rr < 16; ++rr) {
-    const int i = min(i0 + rr, n - 1);
-    uv[rr] = lane < Gk ? Usrc[((int64_t)kv * n + i) * Gk + lane] : 0.f;
+  for (int rr = 0; rr < 4; ++rr) {
+    const int i = min(blockIdx.x * 64 + 16 * rr + rw, n - 1);
+    const float* src = Usrc + ((int64_t)kv * n + i) * Gk;
+    if (vin) {
+      const float4 t = f0 < Gk ? *reinterpret_cast<const float4*>(src + f0) : make_float4(0.f, 0.f, 0.f, 0.f);
+      uv[rr][0] = t.x; uv[rr][1] = t.y; uv[rr][2] = t.z; uv[rr][3] = t.w;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) uv[rr][j] = f0 + j < Gk ? src[f0 + j] : 0.f;
+    }
   }
 #pragma unroll
-  for (int rr = 0; rr < 16; ++rr) {
-    const int i = i0 + rr;
-    if (i >= n) break;
-    const int u = lane < Gk ? (int)rintf(ldexpf(uv[rr], e)) : 0;
-    const int sum = wave_sum_i32(u);
-    const int c = Gk * u - sum;
-    const int mx = wave_max_i32(lane < Gk ? (c < 0 ? -c : c) : 0);
-    const int x = (lane < Gk && mx > 0) ? div_rhaz(127 * c, mx) : 0;
-    if (lane < Gk) Xout[((int64_t)kv * n + i) * Gk + lane] = (int8_t)x;
-    if (lane < fp) Xpad[((int64_t)kv * n + i) * fp + lane] = (int8_t)x;
+  for (int rr = 0; rr < 4; ++rr) {
+    const int i = blockIdx.x * 64 + 16 * rr + rw;
+    int u[4], s = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      u[j] = f0 + j < Gk ? (int)rintf(ldexpf(uv[rr][j], e)) : 0;
+      s += u[j];
+    }
+    s = row16_sum_i32(s);
+    int c[4], m = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      c[j] = Gk * u[j] - s;
+      if (f0 + j < Gk) m = max(m, c[j] < 0 ? -c[j] : c[j]);
+    }
+    m = row16_max_i32(m);
+    uint32_t word = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int x = (f0 + j < Gk && m > 0) ? div127_rhaz(c[j], m) : 0;
+      word |= (uint32_t)(uint8_t)(int8_t)x << (8 * j);
+    }
+    if (i >= n) continue;
+    int8_t* xo = Xout + ((int64_t)kv * n + i) * Gk;
+    if (vout) {
+      if (f0 < Gk) *reinterpret_cast<uint32_t*>(xo + f0) = word;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (f0 + j < Gk) xo[f0 + j] = (int8_t)(word >> (8 * j));
+    }
+    // fp is a multiple of four: lanes past G_K store the zero padding
+    if (f0 < fp) *reinterpret_cast<uint32_t*>(Xpad + ((int64_t)kv * n + i) * fp + f0) = word;
   }
 }
 
