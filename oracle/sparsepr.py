@@ -203,20 +203,18 @@ def query_responses(q_heads, Ck, scale):
 
 
 def summed_response(U_heads):
-    """Reading: under GQA the route is shared (PSRR, execution paragraph), so the query
-    coordinate is the response summed over the KV head's query heads.  For g > 1 the
-    sum is formed in float32 in ascending head order (the kernel's precision: it
-    decides integer features); for g = 1 the single response is used as given."""
+    """Reading: under GQA the route is shared by the KV head's query heads (PSRR,
+    execution paragraph), so the query coordinate is the response summed over those heads:
+    sum_h U^(h), formed in float64 in ascending head order (for g = 1 the single response
+    as given)."""
     U_heads = np.asarray(U_heads)
-    if U_heads.shape[0] == 1:
-        return f64(U_heads[0])
-    acc = U_heads[0].astype(np.float32)
+    acc = f64(U_heads[0]).copy()
     for j in range(1, U_heads.shape[0]):
-        acc = (acc + U_heads[j].astype(np.float32)).astype(np.float32)
-    return f64(acc)
+        acc = acc + f64(U_heads[j])
+    return acc
 
 
-def query_features(U_heads):
+def query_features(U_heads, U_sum=None):
     """Integer response-direction features X^Q [N, G_K].
 
     Reading: queries "whose response directions are alike" share a route.  A direction
@@ -224,8 +222,12 @@ def query_features(U_heads):
     per-row scale: quantise the summed response at 2**14 levels of the head maximum,
     centre each row (G_K u - sum u), and divide by the row's largest magnitude onto
     [-127, 127] with round-half-away integer division.  The feature width is
-    min(r_Q, G_K) = G_K (G_K > r_Q is rejected)."""
-    U = summed_response(U_heads)
+    min(r_Q, G_K) = G_K (G_K > r_Q is rejected).
+
+    ``U_sum`` [N, G_K], when given, is the head-summed coordinate to quantise in place of
+    summed_response(U_heads): the float values another implementation formed, so that the
+    integer decisions below are taken on identical inputs."""
+    U = summed_response(U_heads) if U_sum is None else f64(U_sum)
     e = pow2_exponent(np.abs(U).max() if U.size else 0.0, QUERY_RESP_LIMIT)
     u = np.rint(U * 2.0 ** e).astype(np.int64)
     c = U.shape[1] * u - u.sum(axis=1, keepdims=True)
@@ -255,10 +257,11 @@ class Partition:
     q_offsets: np.ndarray
 
 
-def partition(q_heads, k, p: Params, S=None, U=None):
+def partition(q_heads, k, p: Params, S=None, U=None, U_sum=None):
     """Response-coupled partition of one KV head (PSRR, response-coupled partition
-    paragraph): keys first, then queries, one asymmetric pass.  S and U may be supplied
-    (e.g. the GPU's) to take every integer decision on identical responses."""
+    paragraph): keys first, then queries, one asymmetric pass.  S, U and the head-summed
+    U_sum may be supplied (e.g. the GPU's) to take every integer decision on identical
+    responses."""
     q_heads, k = f64(q_heads), f64(k)
     n, d = k.shape
     scale = p.softmax_scale(d)
@@ -272,7 +275,7 @@ def partition(q_heads, k, p: Params, S=None, U=None):
     Ck = key_centroids(k, k_labels, p.groups_k)
     if U is None:
         U = query_responses(q_heads, Ck, scale)
-    xq, e_u = query_features(U)
+    xq, e_u = query_features(U, U_sum)
     q_labels, qc = kmeans(xq, p.groups_q, p.kmeans_iters)
     q_perm, q_inv, q_off = group_major(q_labels, p.groups_q)
     return Partition(np.asarray(S), e_s, xk, k_labels, kc, k_perm, k_inv, k_off, Ck,
@@ -655,19 +658,21 @@ def hard_drop_rows(q, k, v, scale, q_labels, k_labels, kept, rows=None):
     return o
 
 
-def semantic_features(x_heads):
+def semantic_features(x_heads, x_sum=None):
     """Integer features of raw activations for the semantic-partition ablation (the page
     contrasts its response-coupled partition with clustering the activations
     themselves).  Reading: keys use their own rows; queries under GQA use the rows summed
-    over the KV head's query heads in float32, ascending head order (as the query
-    coordinate is); one power of two per head scales the largest magnitude to at most
-    127, then round half-to-even, as for the key response features.  Width d."""
-    X = summed_response(x_heads)
+    over the KV head's query heads (as the query coordinate is: float64, ascending head
+    order); one power of two per head scales the largest magnitude to at most 127, then
+    round half-to-even, as for the key response features.  Width d.  ``x_sum`` [N, d],
+    when given, replaces the head sum (another implementation's float values, so the
+    integer decisions are taken on identical inputs)."""
+    X = summed_response(x_heads) if x_sum is None else f64(x_sum)
     e = pow2_exponent(np.abs(X).max() if X.size else 0.0, FEATURE_MAX)
     return np.clip(np.rint(X * 2.0 ** e), -FEATURE_MAX, FEATURE_MAX).astype(np.int64), e
 
 
-def partition_semantic(q_heads, k, p: Params, U=None):
+def partition_semantic(q_heads, k, p: Params, U=None, x_sum=None):
     """Semantic partition: the same k-means, permutation and key centroids as the method,
     but keys clustered on their raw vectors and queries on their raw vectors (not on
     response curves and response directions).  The route still scores cells with the
@@ -680,7 +685,7 @@ def partition_semantic(q_heads, k, p: Params, U=None):
     Ck = key_centroids(k, k_labels, p.groups_k)
     if U is None:
         U = query_responses(q_heads, Ck, scale)
-    xq, e_q = semantic_features(q_heads)
+    xq, e_q = semantic_features(q_heads, x_sum)
     q_labels, qc = kmeans(xq, p.groups_q, p.kmeans_iters)
     q_perm, q_inv, q_off = group_major(q_labels, p.groups_q)
     return Partition(None, e_k, xk, k_labels, kc, k_perm, k_inv, k_off, Ck,

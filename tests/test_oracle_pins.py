@@ -134,12 +134,92 @@ def test_query_features_shift_and_scale_invariance():
 
 
 def test_query_features_head_sum_for_gqa():
-    U = RNG.uniform(-1, 1, (3, 20, 8)).astype(np.float32)
+    """Under GQA the coordinate is the float64 head sum: values whose float32 sum loses
+    the small term keep it, and a supplied U_sum replaces the sum."""
+    U = RNG.uniform(-1, 1, (3, 20, 8))
     x, _ = O.query_features(U)
-    s = (U[0] + U[1]) .astype(np.float32)
-    s = (s + U[2]).astype(np.float32)
-    x1, _ = O.query_features(s[None].astype(np.float64))
+    x1, _ = O.query_features((U[0] + U[1] + U[2])[None])
     np.testing.assert_array_equal(x, x1)
+    tiny = np.zeros((3, 1, 4))
+    tiny[0, 0] = [1.0, 1.0, 0.0, 0.0]
+    tiny[1, 0] = [2.0 ** -30, 0.0, 0.0, 0.0]
+    tiny[2, 0] = [-1.0, -1.0, 0.0, 0.0]
+    np.testing.assert_array_equal(O.summed_response(tiny)[0], [2.0 ** -30, 0.0, 0.0, 0.0])
+    assert np.float32(np.float32(1.0) + np.float32(2.0 ** -30)) - np.float32(1.0) == 0.0
+    np.testing.assert_array_equal(O.summed_response(U[:1]), U[0])
+    # the supplied sum is what gets quantised
+    other = U[0] - U[1]
+    np.testing.assert_array_equal(O.query_features(U, U_sum=other)[0], O.query_features(other[None])[0])
+
+
+# ----------------------------------------------------------------- sampled responses
+def test_sample_queries_hand_values():
+    """r_K evenly strided sampled rows, token floor((2s+1) N / (2 r_K)), head s mod g
+    (values worked by hand for N = 100, r_K = 4, g = 3)."""
+    tok, hd = O.sample_queries(100, 4, 3)
+    np.testing.assert_array_equal(tok, [12, 37, 62, 87])
+    np.testing.assert_array_equal(hd, [0, 1, 2, 0])
+    tok, hd = O.sample_queries(7, 3, 1)
+    np.testing.assert_array_equal(tok, [1, 3, 5])
+    np.testing.assert_array_equal(hd, [0, 0, 0])
+
+
+def test_key_responses_decode_the_sampled_rows():
+    """A planted one-hot code: query (h, t) is the unit vector e_{h N + t}, and key j answers
+    head 0's token j with 1 and head 1's token j with 2, so row s of S is non-zero only at
+    the sampled token, with a value that names the sampled head, times scale.  A wrong
+    head cycle, stride or scale changes the decoded rows or the value."""
+    scale = 1 / np.sqrt(7.0)
+    g, n, r_k = 2, 12, 4
+    d = g * n
+    q = np.zeros((g, n, d))
+    for h in range(g):
+        for t in range(n):
+            q[h, t, h * n + t] = 1.0
+    k = np.zeros((n, d))
+    for j in range(n):              # key j answers to both heads' token j
+        k[j, j] = 1.0
+        k[j, n + j] = 2.0
+    S = O.key_responses(q, k, scale, r_k)
+    # sampled tokens floor((2s+1) 12 / 8) = 1, 4, 7, 10; heads 0, 1, 0, 1
+    want = np.zeros((r_k, n))
+    for s, (t, h) in enumerate([(1, 0), (4, 1), (7, 0), (10, 1)]):
+        want[s, t] = scale * (1.0 if h == 0 else 2.0)
+    np.testing.assert_array_equal(S, want)
+
+
+def test_key_responses_explicit_dot_products():
+    """S[s, j] = scale * sum_c Q[h_s, t_s, c] K[j, c], written as plain loops over the
+    hand-computed sampled rows of N = 9, r_K = 3, g = 2 (tokens 1, 4, 7; heads 0, 1, 0)."""
+    g, n, d = 2, 9, 5
+    q, k = rand(g, n, d), rand(n, d)
+    scale = 0.3141
+    S = O.key_responses(q, k, scale, 3)
+    for s, (t, h) in enumerate([(1, 0), (4, 1), (7, 0)]):
+        for j in range(n):
+            acc = 0.0
+            for c in range(d):
+                acc += q[h, t, c] * k[j, c]
+            assert abs(S[s, j] - scale * acc) < 1e-12
+
+
+def test_query_responses_explicit_dot_products_and_unit_centroids():
+    """U^(h)[i, b] = scale * <q^(h)_i, C^K_b>: plain loops, and unit-vector centroids pick
+    the query's coordinates."""
+    g, n, d, G = 2, 6, 4, 3
+    q, C = rand(g, n, d), rand(G, d)
+    scale = 0.777
+    U = O.query_responses(q, C, scale)
+    assert U.shape == (g, n, G)
+    for h in range(g):
+        for i in range(n):
+            for b in range(G):
+                acc = 0.0
+                for c in range(d):
+                    acc += q[h, i, c] * C[b, c]
+                assert abs(U[h, i, b] - scale * acc) < 1e-12
+    E = np.eye(d)[[2, 0, 3]]
+    np.testing.assert_array_equal(O.query_responses(q, E, 1.0), q[:, :, [2, 0, 3]])
 
 
 # ----------------------------------------------------------------------------- k-means
@@ -567,10 +647,12 @@ def test_semantic_features_quantise_raw_rows_and_recover_planted_clusters():
     for lab, tr in ((part.k_labels, truth), (part.q_labels, truth[::-1])):
         pairs = set(zip(lab.tolist(), tr.tolist()))
         assert len(pairs) == G and len({a for a, _ in pairs}) == G
-    # the GQA query coordinate is the float32 head sum
+    # the GQA query coordinate is the float64 head sum; a supplied sum replaces it
     xq, _ = O.semantic_features(np.stack([q, 0.5 * q]))
-    xs, _ = O.semantic_features((q.astype(np.float32) + (0.5 * q).astype(np.float32))[None])
+    xs, _ = O.semantic_features((1.5 * q)[None])
     np.testing.assert_array_equal(xq, xs)
+    np.testing.assert_array_equal(O.semantic_features(np.stack([q, 0.5 * q]), x_sum=-q)[0],
+                                  O.semantic_features(-q[None])[0])
 
 
 def test_affine_residual_stats_pins():
