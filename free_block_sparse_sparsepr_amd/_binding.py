@@ -38,7 +38,8 @@ def _ptr_struct(name, names):
 
 PARTITION_FIELDS = ["responses_s", "responses_u", "exponents", "key_labels", "key_centroids_int",
                     "key_perm", "key_offsets", "key_centroids", "query_features", "query_labels",
-                    "query_centroids", "query_perm", "query_offsets", "q_gm", "k_gm", "v_gm"]
+                    "query_centroids", "query_perm", "query_offsets", "q_gm", "k_gm", "v_gm",
+                    "query_coord_sum"]
 ROUTE_FIELDS = ["row_ptr", "cols", "kept_mask", "pairs", "cell_mass"]
 FIT_FIELDS = ["probe_tokens", "probe_groups", "probe_weights", "o_dense", "o_sparse", "A", "B", "c0",
               "r_eff", "eig"]

@@ -138,7 +138,9 @@ static sparsepr_status hip_status() {
 static int64_t route_budget(const sparsepr_params& p) {
   const int64_t ppm = (int64_t)std::floor((double)p.rho_exec * 1e6 + 0.5);
   const int64_t n = p.n;
-  return (ppm * n * n) / 1000000 - (int64_t)p.n_probe * n;
+  // ppm n^2 reaches 10^6 2^44 at the largest accepted n: formed in 128 bits
+  const unsigned __int128 prod = (unsigned __int128)(uint64_t)ppm * (uint64_t)n * (uint64_t)n;
+  return (int64_t)(prod / 1000000u) - (int64_t)p.n_probe * n;
 }
 
 // Attention arguments of the block-sparse path (group-major Q, K, transposed V, CSR).
@@ -253,7 +255,6 @@ sparsepr_status sparsepr_route(const sparsepr_params* params, const sparsepr_par
   st = check_ws(params, workspace, workspace_bytes, wp.total_route);
   if (st != SPARSEPR_OK) return st;
   (void)hipGetLastError();
-  if (ensure_exp_table() != hipSuccess) return SPARSEPR_ERR_HIP;
   launch_route(dims_of(*params), route_budget(*params), *part, *out, wp, static_cast<char*>(workspace),
                (hipStream_t)stream);
   return hip_status();

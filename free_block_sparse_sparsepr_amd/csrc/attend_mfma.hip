@@ -78,29 +78,36 @@ __device__ __forceinline__ bool next_tile(const AttnArgs& A, int kv, const TileI
 // last tile of the sequence clamps rows beyond n (those keys are masked).
 __device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// 32-bit LDS byte address of a pointer into a __shared__ array
+__device__ __forceinline__ uint32_t lds_addr(const char* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
 template <int D, int BN, int NW>
 struct CopyPlan {
   using C = MfmaCfg<D, BN, NW>;
   uint32_t koff[C::KIPW];   // bytes from the tile's first K row
   uint32_t voff[C::VIPW];   // bytes from the tile's first V^T column
-  int krow[C::KIPW];        // K row within the tile
-  int vcol[C::VIPW];        // V^T column (key) within the tile
+  int w, lane;
 
-  __device__ CopyPlan(int w, int lane, int np) {
+  __device__ CopyPlan(int w_, int lane_, int np) : w(w_), lane(lane_) {
 #pragma unroll
-    for (int i = 0; i < C::KIPW; ++i) {
-      const int L = (w * C::KIPW + i) * 64 + lane;
-      const int r = L / C::KCH, slot = L % C::KCH, c = slot ^ C::kswz(r);
-      krow[i] = r;
-      koff[i] = (uint32_t)(r * D + 8 * c) * 2u;
-    }
+    for (int i = 0; i < C::KIPW; ++i) koff[i] = (uint32_t)(krow(i) * D + 8 * kchunk(i)) * 2u;
 #pragma unroll
-    for (int i = 0; i < C::VIPW; ++i) {
-      const int L = (w * C::VIPW + i) * 64 + lane;
-      const int d = L / C::VCH, slot = L % C::VCH, c = slot ^ C::vswz(d);
-      vcol[i] = 8 * c;
-      voff[i] = (uint32_t)(d * np + 8 * c) * 2u;
-    }
+    for (int i = 0; i < C::VIPW; ++i) voff[i] = (uint32_t)(vrow(i) * np + vcol(i)) * 2u;
+  }
+  // K row within the tile and its chunk for copy instruction i (recomputed where needed,
+  // so that only the byte offsets stay in registers)
+  __device__ int krow(int i) const { return ((w * C::KIPW + i) * 64 + lane) / C::KCH; }
+  __device__ int kchunk(int i) const {
+    const int L = (w * C::KIPW + i) * 64 + lane;
+    return (L % C::KCH) ^ C::kswz(L / C::KCH);
+  }
+  // V^T row (d) and column (key within the tile) for copy instruction i
+  __device__ int vrow(int i) const { return ((w * C::VIPW + i) * 64 + lane) / C::VCH; }
+  __device__ int vcol(int i) const {
+    const int L = (w * C::VIPW + i) * 64 + lane;
+    return 8 * ((L % C::VCH) ^ C::vswz(L / C::VCH));
   }
 };
 
@@ -125,14 +132,16 @@ __device__ __forceinline__ void stage_copy(const CopyPlan<D, BN, NW>& cp, const 
   }
 #pragma unroll
   for (int i = 0; i < C::KIPW; ++i) {
-    const int row = min(kt + cp.krow[i], n - 1);
-    const char* src = reinterpret_cast<const char*>(kb + (int64_t)(row - cp.krow[i]) * D) + cp.koff[i];
+    const int kr = cp.krow(i);
+    const int row = min(kt + kr, n - 1);
+    const char* src = reinterpret_cast<const char*>(kb + (int64_t)(row - kr) * D) + cp.koff[i];
     __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)(stage + (wu * C::KIPW + i) * 1024), 16, 0, 0);
   }
 #pragma unroll
   for (int i = 0; i < C::VIPW; ++i) {
-    const int pos = kt + cp.vcol[i];
-    const int base = pos + 8 <= np ? kt : -cp.vcol[i];   // chunks past n_pad read the row's first chunk
+    const int vc = cp.vcol(i);
+    const int pos = kt + vc;
+    const int base = pos + 8 <= np ? kt : -vc;   // chunks past n_pad read the row's first chunk
     const char* src = reinterpret_cast<const char*>(vtb + base) + cp.voff[i];
     __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)(vst + (wu * C::VIPW + i) * 1024), 16, 0, 0);
   }
@@ -143,18 +152,12 @@ union PackP {
   bf16x2_t h[4];
 };
 
-// One tile (BN keys) of the online softmax for a wave's 32 queries: S^T = K Q^T on the
-// matrix cores (one accumulation chain per 32-key block), masking (keys outside [lo, hi)
-// of the tile; with MASK also keys whose group bit is clear in rowmask), the row max
-// (in-register plus the partner lane l ^ 32), p = exp2(s c2 - m) with one FMA and the
-// hardware exp2, bf16 packing, the row sum as bf16 dot products of the packed p (the
-// values the second product consumes), a lazy rescale, and O^T += V^T P^T.
-template <int D, int BN, bool MASK>
-__device__ __forceinline__ void mfma_tile_step(const char* __restrict__ stage, const bf16x8_t* qreg, int lo, int hi,
-                                               float c2, const uint8_t* __restrict__ klab, uint64_t rowmask,
-                                               float& m_i, float& l_i, f32x16_t* o, int l32, int hf) {
+// The three parts of one tile (BN keys) of the online softmax for a wave's 32 queries.
+// scores_mfma: S^T = K Q^T on the matrix cores (one accumulation chain per 32-key block).
+template <int D, int BN>
+__device__ __forceinline__ void scores_mfma(const char* __restrict__ stage, const bf16x8_t* qreg, f32x16_t* sv,
+                                            int l32, int hf) {
   using C = MfmaCfg<D, BN>;
-  f32x16_t sv[C::NB];
 #pragma unroll
   for (int kb = 0; kb < C::NB; ++kb)
 #pragma unroll
@@ -168,6 +171,18 @@ __device__ __forceinline__ void mfma_tile_step(const char* __restrict__ stage, c
       sv[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[kk], sv[kb], 0, 0, 0);
     }
   }
+}
+
+// softmax_step: masking (keys outside [lo, hi) of the tile; with MASK also keys whose
+// group bit is clear in rowmask), the row max (in-register plus the partner lane l ^ 32),
+// p = exp2(s c2 - m) with one FMA and the hardware exp2, bf16 packing into the B-operand
+// layout of the second product, the row sum as bf16 dot products of the packed p (the
+// values the second product consumes) and a lazy rescale of O.
+template <int D, int BN, bool MASK>
+__device__ __forceinline__ void softmax_step(f32x16_t* sv, int lo, int hi, float c2, const uint8_t* __restrict__ klab,
+                                             uint64_t rowmask, float& m_i, float& l_i, f32x16_t* o,
+                                             PackP (*p)[2], int hf) {
+  using C = MfmaCfg<D, BN>;
   if (MASK || lo > 0 || hi < C::BN) {
 #pragma unroll
     for (int kb = 0; kb < C::NB; ++kb)
@@ -194,7 +209,6 @@ __device__ __forceinline__ void mfma_tile_step(const char* __restrict__ stage, c
   ones[0] = (__bf16)1.f;
   ones[1] = (__bf16)1.f;
   float rs = 0.f;
-  PackP p[C::NB][2];
 #pragma unroll
   for (int kb = 0; kb < C::NB; ++kb)
 #pragma unroll
@@ -219,8 +233,14 @@ __device__ __forceinline__ void mfma_tile_step(const char* __restrict__ stage, c
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
   }
-  // O^T += V^T P^T: key k-step (kb, s2) covers keys 32 kb + 16 s2 + {4 hf + 0..3, 8 + 4 hf + 0..3},
-  // which the V^T layout keeps as chunk 2 (2 kb + s2) + hf of the row
+}
+
+// pv_mfma: O^T += V^T P^T.  Key k-step (kb, s2) covers keys 32 kb + 16 s2 + {4 hf + 0..3,
+// 8 + 4 hf + 0..3}, which the V^T layout keeps as chunk 2 (2 kb + s2) + hf of the row.
+template <int D, int BN>
+__device__ __forceinline__ void pv_mfma(const char* __restrict__ stage, const PackP (*p)[2], f32x16_t* o, int l32,
+                                        int hf) {
+  using C = MfmaCfg<D, BN>;
   const char* vst = stage + C::KBYTES;
 #pragma unroll
   for (int kb = 0; kb < C::NB; ++kb)
@@ -234,6 +254,272 @@ __device__ __forceinline__ void mfma_tile_step(const char* __restrict__ stage, c
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, p[kb][s2].v, o[db], 0, 0, 0);
       }
     }
+}
+
+// The probe rows' softmax: as softmax_step, but the probabilities are split into a bf16
+// high part and a bf16 remainder (p = hi + lo to about 2^-16 relative), both laid out as
+// B operands, and the row sum is formed from the float probabilities, so that the probe
+// rows' O^T += V^T (hi + lo)^T carries no bf16 rounding of P.
+template <int D, int BN, bool MASK>
+__device__ __forceinline__ void softmax_step_split(f32x16_t* sv, int hi_key, float c2,
+                                                   const uint8_t* __restrict__ klab, uint64_t rowmask, float& m_i,
+                                                   float& l_i, f32x16_t* o, PackP (*ph)[2], PackP (*pl)[2],
+                                                   int hf) {
+  using C = MfmaCfg<D, BN>;
+#pragma unroll
+  for (int kb = 0; kb < C::NB; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = 32 * kb + 8 * (r >> 2) + 4 * hf + (r & 3);
+      bool keep = key < hi_key;
+      if constexpr (MASK) keep = keep && ((rowmask >> klab[key]) & 1ull);
+      sv[kb][r] = keep ? sv[kb][r] : -INFINITY;
+    }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < C::NB; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sv[kb][r]);
+  mx = max_xor32(mx) * c2;
+  const float m_use = (mx > m_i + kStaleMax) ? mx : m_i;
+  const float alpha = (m_use == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_i - m_use);
+  const float neg = -m_use;
+  float rs = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < C::NB; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      float e0 = __builtin_amdgcn_exp2f(fmaf(sv[kb][r], c2, neg));
+      float e1 = __builtin_amdgcn_exp2f(fmaf(sv[kb][r + 1], c2, neg));
+      e0 = (sv[kb][r] == -INFINITY) ? 0.f : e0;
+      e1 = (sv[kb][r + 1] == -INFINITY) ? 0.f : e1;
+      bf16x2_t h, l;
+      h[0] = (__bf16)e0;
+      h[1] = (__bf16)e1;
+      l[0] = (__bf16)(e0 - (float)h[0]);
+      l[1] = (__bf16)(e1 - (float)h[1]);
+      ph[kb][r >> 3].h[(r & 7) >> 1] = h;
+      pl[kb][r >> 3].h[(r & 7) >> 1] = l;
+      rs += e0 + e1;
+    }
+  l_i = l_i * alpha + rs;
+  m_i = m_use;
+  if (__ballot(alpha != 1.f)) {
+#pragma unroll
+    for (int db = 0; db < C::DBLK; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+  }
+}
+
+template <int D, int BN, bool MASK>
+__device__ __forceinline__ void probe_tile_step(const char* __restrict__ stage, const bf16x8_t* qreg, int hi_key,
+                                                float c2, const uint8_t* __restrict__ klab, uint64_t rowmask,
+                                                float& m_i, float& l_i, f32x16_t* o, int l32, int hf) {
+  using C = MfmaCfg<D, BN>;
+  f32x16_t sv[C::NB];
+  PackP ph[C::NB][2], pl[C::NB][2];
+  scores_mfma<D, BN>(stage, qreg, sv, l32, hf);
+  softmax_step_split<D, BN, MASK>(sv, hi_key, c2, klab, rowmask, m_i, l_i, o, ph, pl, hf);
+  pv_mfma<D, BN>(stage, ph, o, l32, hf);
+  pv_mfma<D, BN>(stage, pl, o, l32, hf);
+}
+
+// The matrix phase of the anti-phased schedule: O^T += V^T P^T of the previous tile and
+// S^T = K Q^T of the current one as one straight-line block, with the LDS operand reads
+// issued LA products ahead of their use (the partner wave of the SIMD runs its softmax
+// meanwhile, so this wave must hide its own LDS latency).
+template <int D, int BN, int LA>
+__device__ __forceinline__ void matrix_phase(const char* __restrict__ kstage, const char* __restrict__ vstage,
+                                             const bf16x8_t* qreg, const PackP (*p)[2], f32x16_t* o,
+                                             f32x16_t* sv, int l32, int hf) {
+  using C = MfmaCfg<D, BN>;
+  constexpr int NPV = C::NB * 2 * C::DBLK, NS = C::NB * C::KSTEPS, T = NPV + NS;
+  bf16x8_t va[NPV], ka[NS];
+  const char* vst = vstage + C::KBYTES;
+#pragma unroll
+  for (int kb = 0; kb < C::NB; ++kb)
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int db = 0; db < C::DBLK; ++db) {
+        const int d = 32 * db + l32;
+        va[(kb * 2 + s2) * C::DBLK + db] = *reinterpret_cast<const bf16x8_t*>(
+            vst + d * (C::BN * 2) + (((4 * kb + 2 * s2 + hf) ^ C::vswz(d)) << 4));
+      }
+#pragma unroll
+  for (int kk = 0; kk < C::KSTEPS; ++kk)
+#pragma unroll
+    for (int kb = 0; kb < C::NB; ++kb) {
+      const int row = 32 * kb + l32;
+      ka[kk * C::NB + kb] =
+          *reinterpret_cast<const bf16x8_t*>(kstage + row * (D * 2) + (((2 * kk + hf) ^ C::kswz(row)) << 4));
+    }
+#pragma unroll
+  for (int kb = 0; kb < C::NB; ++kb)
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int db = 0; db < C::DBLK; ++db)
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[(kb * 2 + s2) * C::DBLK + db], p[kb][s2].v, o[db], 0, 0, 0);
+#pragma unroll
+  for (int kb = 0; kb < C::NB; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sv[kb][r] = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < C::KSTEPS; ++kk)
+#pragma unroll
+    for (int kb = 0; kb < C::NB; ++kb)
+      sv[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk * C::NB + kb], qreg[kk], sv[kb], 0, 0, 0);
+  __builtin_amdgcn_sched_group_barrier(0x100, LA, 0);   // LA operand reads
+#pragma unroll
+  for (int i = 0; i < T - LA; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one product
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // the read LA products ahead
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, LA, 0);
+}
+
+// The matrix phase for d = 128 and 64-key tiles as two self-contained assembly blocks,
+// each keeping four LDS operand reads in flight with exact partial waits (a read is
+// issued into the buffer the product before it has just consumed, and every block waits
+// for all of its own reads before it ends).  The first block is O^T += V^T P^T of the
+// previous tile (V^T rows d = 32 db + l32 at vaddr[m] + 16384 + 4096 db for key k-step
+// m = 2 kb + s2); the second S^T = K Q^T of the current one (K rows 32 kb + l32 at
+// kaddr[kk] + 8192 kb for d k-step kk).  The leading s_nop covers the wait states between
+// the softmax phase's vector writes (P, the rescaled O) and their first matrix read; the
+// trailing ones those between the last product and the vector reads of S that follow.
+__device__ __forceinline__ void matrix_phase_d128(const uint32_t* kaddr, const uint32_t* vaddr,
+                                                  const bf16x8_t* qreg, const PackP (*p)[2], f32x16_t* o,
+                                                  f32x16_t* sv) {
+  bf16x8_t t0, t1, t2, t3;
+  asm volatile(
+            "s_nop 4\n"
+      "ds_read_b128 %[t0], %[va0] offset:16384\n"
+      "ds_read_b128 %[t1], %[va0] offset:20480\n"
+      "ds_read_b128 %[t2], %[va0] offset:24576\n"
+      "ds_read_b128 %[t3], %[va0] offset:28672\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %[o0], %[t0], %[p0], %[o0]\n"
+      "ds_read_b128 %[t0], %[va1] offset:16384\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %[o1], %[t1], %[p0], %[o1]\n"
+      "ds_read_b128 %[t1], %[va1] offset:20480\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %[o2], %[t2], %[p0], %[o2]\n"
+      "ds_read_b128 %[t2], %[va1] offset:24576\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %[o3], %[t3], %[p0], %[o3]\n"
+      "ds_read_b128 %[t3], %[va1] offset:28672\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %[o0], %[t0], %[p1], %[o0]\n"
+      "ds_read_b128 %[t0], %[va2] offset:16384\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %[o1], %[t1], %[p1], %[o1]\n"
+      "ds_read_b128 %[t1], %[va2] offset:20480\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %[o2], %[t2], %[p1], %[o2]\n"
+      "ds_read_b128 %[t2], %[va2] offset:24576\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %[o3], %[t3], %[p1], %[o3]\n"
+      "ds_read_b128 %[t3], %[va2] offset:28672\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %[o0], %[t0], %[p2], %[o0]\n"
+      "ds_read_b128 %[t0], %[va3] offset:16384\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %[o1], %[t1], %[p2], %[o1]\n"
+      "ds_read_b128 %[t1], %[va3] offset:20480\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %[o2], %[t2], %[p2], %[o2]\n"
+      "ds_read_b128 %[t2], %[va3] offset:24576\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %[o3], %[t3], %[p2], %[o3]\n"
+      "ds_read_b128 %[t3], %[va3] offset:28672\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %[o0], %[t0], %[p3], %[o0]\n"
+      "s_waitcnt lgkmcnt(2)\n"
+      "v_mfma_f32_32x32x16_bf16 %[o1], %[t1], %[p3], %[o1]\n"
+      "s_waitcnt lgkmcnt(1)\n"
+      "v_mfma_f32_32x32x16_bf16 %[o2], %[t2], %[p3], %[o2]\n"
+      "s_waitcnt lgkmcnt(0)\n"
+      "v_mfma_f32_32x32x16_bf16 %[o3], %[t3], %[p3], %[o3]\n"
+      : [o0] "+v"(o[0]), [o1] "+v"(o[1]), [o2] "+v"(o[2]), [o3] "+v"(o[3]), [t0] "=&v"(t0), [t1] "=&v"(t1),
+        [t2] "=&v"(t2), [t3] "=&v"(t3)
+      : [p0] "v"(p[0][0].v), [p1] "v"(p[0][1].v), [p2] "v"(p[1][0].v), [p3] "v"(p[1][1].v), [va0] "v"(vaddr[0]),
+        [va1] "v"(vaddr[1]), [va2] "v"(vaddr[2]), [va3] "v"(vaddr[3])
+      : "memory");
+  asm volatile(
+            "s_nop 4\n"
+      "ds_read_b128 %[t0], %[ka0] offset:0\n"
+      "ds_read_b128 %[t1], %[ka0] offset:8192\n"
+      "ds_read_b128 %[t2], %[ka1] offset:0\n"
+      "ds_read_b128 %[t3], %[ka1] offset:8192\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s0], %[t0], %[q0], 0\n"
+      "ds_read_b128 %[t0], %[ka2] offset:0\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s1], %[t1], %[q0], 0\n"
+      "ds_read_b128 %[t1], %[ka2] offset:8192\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s0], %[t2], %[q1], %[s0]\n"
+      "ds_read_b128 %[t2], %[ka3] offset:0\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s1], %[t3], %[q1], %[s1]\n"
+      "ds_read_b128 %[t3], %[ka3] offset:8192\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s0], %[t0], %[q2], %[s0]\n"
+      "ds_read_b128 %[t0], %[ka4] offset:0\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s1], %[t1], %[q2], %[s1]\n"
+      "ds_read_b128 %[t1], %[ka4] offset:8192\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s0], %[t2], %[q3], %[s0]\n"
+      "ds_read_b128 %[t2], %[ka5] offset:0\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s1], %[t3], %[q3], %[s1]\n"
+      "ds_read_b128 %[t3], %[ka5] offset:8192\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s0], %[t0], %[q4], %[s0]\n"
+      "ds_read_b128 %[t0], %[ka6] offset:0\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s1], %[t1], %[q4], %[s1]\n"
+      "ds_read_b128 %[t1], %[ka6] offset:8192\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s0], %[t2], %[q5], %[s0]\n"
+      "ds_read_b128 %[t2], %[ka7] offset:0\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s1], %[t3], %[q5], %[s1]\n"
+      "ds_read_b128 %[t3], %[ka7] offset:8192\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s0], %[t0], %[q6], %[s0]\n"
+      "s_waitcnt lgkmcnt(2)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s1], %[t1], %[q6], %[s1]\n"
+      "s_waitcnt lgkmcnt(1)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s0], %[t2], %[q7], %[s0]\n"
+      "s_waitcnt lgkmcnt(0)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s1], %[t3], %[q7], %[s1]\n"
+      "s_nop 7\n"
+      "s_nop 7\n"
+      "s_nop 4\n"
+      : [s0] "=&v"(sv[0]), [s1] "=&v"(sv[1]), [t0] "=&v"(t0), [t1] "=&v"(t1), [t2] "=&v"(t2), [t3] "=&v"(t3)
+      : [q0] "v"(qreg[0]), [q1] "v"(qreg[1]), [q2] "v"(qreg[2]), [q3] "v"(qreg[3]), [q4] "v"(qreg[4]),
+        [q5] "v"(qreg[5]), [q6] "v"(qreg[6]), [q7] "v"(qreg[7]), [ka0] "v"(kaddr[0]), [ka1] "v"(kaddr[1]),
+        [ka2] "v"(kaddr[2]), [ka3] "v"(kaddr[3]), [ka4] "v"(kaddr[4]), [ka5] "v"(kaddr[5]), [ka6] "v"(kaddr[6]),
+        [ka7] "v"(kaddr[7])
+      : "memory");
+}
+
+// One whole tile: scores, softmax and O^T += V^T P^T in sequence (the probe rows).
+template <int D, int BN, bool MASK>
+__device__ __forceinline__ void mfma_tile_step(const char* __restrict__ stage, const bf16x8_t* qreg, int lo, int hi,
+                                               float c2, const uint8_t* __restrict__ klab, uint64_t rowmask,
+                                               float& m_i, float& l_i, f32x16_t* o, int l32, int hf) {
+  using C = MfmaCfg<D, BN>;
+  f32x16_t sv[C::NB];
+  PackP p[C::NB][2];
+  scores_mfma<D, BN>(stage, qreg, sv, l32, hf);
+  softmax_step<D, BN, MASK>(sv, lo, hi, c2, klab, rowmask, m_i, l_i, o, p, hf);
+  pv_mfma<D, BN>(stage, p, o, l32, hf);
 }
 
 // Fused write-back for one query head per KV head (summary page of "Partition the
@@ -351,6 +637,7 @@ __device__ __forceinline__ void fused_writeback(const AttnArgs& A, int kv, int v
 
 constexpr int kAttnWaves = 8;    // waves per block of the main attention kernel
 constexpr int kAttnStages = 4;   // K/V tile stages in LDS; tile j + 2 is copied while tile j runs
+constexpr int kMatLookahead = 6; // LDS operand reads in flight ahead of the matrix products
 
 // Waits until at most `later` tiles' copies of this wave are still in flight (each tile is
 // C::KIPW + C::VIPW direct-to-LDS loads, which complete in order for the counter).
@@ -365,7 +652,7 @@ __device__ __forceinline__ void wait_tiles_in_flight(int later) {
   else __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
-template <int D, int BN, typename OutT>
+template <int D, int BN, typename OutT, int PP>
 __global__ __launch_bounds__(64 * kAttnWaves, 1) void attn_mfma_kernel(AttnArgs A) {
   using C = MfmaCfg<D, BN, kAttnWaves>;
   constexpr int PER_TILE = C::KIPW + C::VIPW;
@@ -435,6 +722,83 @@ __global__ __launch_bounds__(64 * kAttnWaves, 1) void attn_mfma_kernel(AttnArgs 
   if (valid) kt = k0 & ~15;
   int fci = ci, fk0 = k0, fk1 = k1, fkt = kt;
   bool fvalid = valid;
+  if constexpr (PP) {
+    // Anti-phased schedule: waves 0-3 and 4-7 (one of each per SIMD) alternate between a
+    // matrix phase (S_j = K_j Q^T and O += V_{j-1} P_{j-1}) and a softmax phase (S_j ->
+    // P_j), waves 4-7 one phase behind, with a block barrier between phases, so that one
+    // wave of every SIMD issues matrix products while the other runs its exponentials.
+    // Phases t = 0, 1, ...: waves 0-3 run the matrix part of tile j in phase 2j and its
+    // softmax in 2j + 1; waves 4-7 in 2j + 1 and 2j + 2.  K_j is read in phases 2j and
+    // 2j + 1, V_j in 2j + 2 and 2j + 3.  Waves 0-3 alone copy the tiles, during their
+    // softmax phases (which read no LDS, so the copies never hold up a matrix phase's
+    // operand reads): tile j + 2 in phase 2j + 1, into the stage of tile j - 2 (free
+    // after phase 2j - 1), and each waits for its copies of tile j + 1 before the
+    // barrier that ends phase 2j + 1.
+    constexpr int CW = kAttnWaves / 2;   // copying waves
+    using CC = MfmaCfg<D, BN, CW>;
+    constexpr int PT = CC::KIPW + CC::VIPW;
+    const bool lag = wu >= CW;
+    const CopyPlan<D, BN, CW> cpa(wu & (CW - 1), lane, A.v_np);
+    int ncopied = 0;
+    for (int i = 0; i < 2 && fvalid; ++i) {
+      if (!lag) stage_copy<D, BN, CW>(cpa, kb, vtb, A.n, A.v_np, fkt, stages[i], wu);
+      ++ncopied;
+      fvalid = next_tile(A, kv, ti, C::BN, fci, fk0, fk1, fkt);
+    }
+    if (!lag) wait_tiles_in_flight<PT>(ncopied - 1);   // tile 0 has landed
+    __syncthreads();
+    if (lag) asm volatile("s_barrier" ::: "memory");   // waves 4-7 sit out phase 0
+    f32x16_t sv[C::NB];
+    PackP pp[C::NB][2];
+#pragma unroll
+    for (int kb = 0; kb < C::NB; ++kb)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pp[kb][s2].v[e] = (__bf16)0.f;
+    // per-lane LDS byte offsets of the matrix phase's operand reads within a stage (d = 128)
+    uint32_t koffs[8], voffs[4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) koffs[i] = (uint32_t)(l32 * 256 + (((2 * i + hf) ^ (l32 & 15)) << 4));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) voffs[i] = (uint32_t)(l32 * 128 + (((2 * i + hf) ^ ((l32 >> 1) & 7)) << 4));
+    int cur = 0, prev = 0, fst = 2;
+    bool have_prev = false;
+    while (valid) {
+      const int lo = max(k0 - kt, 0), hi = min(k1 - kt, BN);
+      if (wave_rows) {   // matrix phase (the first one multiplies tile 0's V by zero probabilities)
+        if constexpr (D == 128 && BN == 64 && PP == 5) {
+          const uint32_t kst = lds_addr(stages[cur]), vst = lds_addr(stages[prev]);
+          uint32_t kaddr[8], vaddr[4];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) kaddr[i] = kst + koffs[i];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) vaddr[i] = vst + voffs[i];
+          matrix_phase_d128(kaddr, vaddr, qreg, pp, o, sv);
+        } else {
+          matrix_phase<D, BN, (PP > 0 ? PP : 4)>(stages[cur], stages[prev], qreg, pp, o, sv, l32, hf);
+        }
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      bool issued = false;
+      if (fvalid) {
+        if (!lag) stage_copy<D, BN, CW>(cpa, kb, vtb, A.n, A.v_np, fkt, stages[fst], wu);
+        issued = true;
+        fst = fst == kAttnStages - 1 ? 0 : fst + 1;
+        fvalid = next_tile(A, kv, ti, C::BN, fci, fk0, fk1, fkt);
+      }
+      if (wave_rows)     // softmax phase
+        softmax_step<D, BN, false>(sv, lo, hi, c2, nullptr, 0ull, m_i, l_i, o, pp, hf);
+      have_prev = true;
+      prev = cur;
+      cur = cur == kAttnStages - 1 ? 0 : cur + 1;
+      valid = next_tile(A, kv, ti, C::BN, ci, k0, k1, kt);
+      if (!lag) wait_tiles_in_flight<PT>(issued ? 1 : 0);   // tile j + 1 has landed
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
+    if (wave_rows && have_prev) pv_mfma<D, BN>(stages[prev], pp, o, l32, hf);
+    if (!lag) asm volatile("s_barrier" ::: "memory");   // matches the lagging waves' first barrier
+  } else {
   int nfront = 0;           // copied tiles not yet computed
   int fst = 0;              // stage of the frontier tile
   for (int i = 0; i < kAttnStages - 2 && fvalid; ++i) {
@@ -465,10 +829,12 @@ __global__ __launch_bounds__(64 * kAttnWaves, 1) void attn_mfma_kernel(AttnArgs 
     ++j;
     cur = cur == kAttnStages - 1 ? 0 : cur + 1;
   }
+  }
 
   const float l_tot = add_xor32(l_i);
   const float inv = 1.f / l_tot;
   if (A.fitA != nullptr) {
+    __syncthreads();   // every wave is done reading its last V tile from the stages
     fused_writeback<D, C::STAGE * kAttnStages, 64 * kAttnWaves>(A, kv, vrow, qvalid, inv, o, &stages[0][0], tid,
                                                                    l32, hf);
     return;
@@ -627,9 +993,9 @@ __global__ __launch_bounds__(256, 2) void probe_attn_mfma_kernel(const bf16_t* _
     }
     const int hi = min(k1 - kt, C::BN);
     if (sparse)
-      mfma_tile_step<D, 32, true>(stages[cur], qreg, 0, hi, c2, klab[cur], rowmask, m_i, l_i, o, l32, hf);
+      probe_tile_step<D, 32, true>(stages[cur], qreg, hi, c2, klab[cur], rowmask, m_i, l_i, o, l32, hf);
     else
-      mfma_tile_step<D, 32, false>(stages[cur], qreg, 0, hi, c2, nullptr, 0ull, m_i, l_i, o, l32, hf);
+      probe_tile_step<D, 32, false>(stages[cur], qreg, hi, c2, nullptr, 0ull, m_i, l_i, o, l32, hf);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     cur ^= 1;
@@ -751,7 +1117,11 @@ void launch_mfma_typed(AttnArgs a, int hkv, hipStream_t s) {
   a.n_heads_kv = hkv;
   int64_t total = (int64_t)a.tiles_per_head * hkv;
   total = ceil_div(total, kXcds) * kXcds;
-  hipLaunchKernelGGL((attn_mfma_kernel<D, kAttnBN, OutT>), dim3((unsigned)total), dim3(64 * kAttnWaves), 0, s, a);
+  static const int pp = getenv("SPARSEPR_ATTN_PP") == nullptr ? 5 : atoi(getenv("SPARSEPR_ATTN_PP"));
+  if (pp == 4) hipLaunchKernelGGL((attn_mfma_kernel<D, kAttnBN, OutT, 4>), dim3((unsigned)total), dim3(64 * kAttnWaves), 0, s, a);
+  else if (pp == 6) hipLaunchKernelGGL((attn_mfma_kernel<D, kAttnBN, OutT, 6>), dim3((unsigned)total), dim3(64 * kAttnWaves), 0, s, a);
+  else if (pp == 5) hipLaunchKernelGGL((attn_mfma_kernel<D, kAttnBN, OutT, 5>), dim3((unsigned)total), dim3(64 * kAttnWaves), 0, s, a);
+  else hipLaunchKernelGGL((attn_mfma_kernel<D, kAttnBN, OutT, 0>), dim3((unsigned)total), dim3(64 * kAttnWaves), 0, s, a);
 }
 
 void launch_attention_mfma(const Dims& dm, AttnArgs a, bool out_is_input_dtype, hipStream_t s) {

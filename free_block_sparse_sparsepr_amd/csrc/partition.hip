@@ -850,19 +850,21 @@ __global__ __launch_bounds__(256) void sem_maxabs_kernel(const T* __restrict__ x
 }
 
 // grid (ceil(n * D / 256), Hkv), block 256: int8 features into Xpad [Hkv][n][D] (and Xout
-// when given), exponent into exps[kv * 2 + slot]
+// when given), exponent into exps[kv * 2 + slot], the summed rows into xsum when given
 template <typename T, int D>
 __global__ __launch_bounds__(256) void sem_quant_kernel(const T* __restrict__ x, int n, int g,
                                                         const uint32_t* __restrict__ maxbits, int slot,
                                                         int8_t* __restrict__ Xout, int8_t* __restrict__ Xpad,
-                                                        int32_t* __restrict__ exps) {
+                                                        int32_t* __restrict__ exps, float* __restrict__ xsum) {
   const int kv = blockIdx.y;
   const int e = pow2_exponent(__uint_as_float(maxbits[kv]), 127.f);
   if (blockIdx.x == 0 && threadIdx.x == 0) exps[kv * 2 + slot] = e;
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= (int64_t)n * D) return;
   const int i = (int)(idx / D), c = (int)(idx % D);
-  const float v = fminf(fmaxf(rintf(ldexpf(sem_value<T, D>(x, n, g, kv, i, c), e)), -127.f), 127.f);
+  const float xv = sem_value<T, D>(x, n, g, kv, i, c);
+  if (xsum) xsum[((int64_t)kv * n + i) * D + c] = xv;
+  const float v = fminf(fmaxf(rintf(ldexpf(xv, e)), -127.f), 127.f);
   const int8_t q = (int8_t)(int)v;
   Xpad[((int64_t)kv * n + i) * D + c] = q;
   if (Xout) Xout[((int64_t)kv * n + i) * D + c] = q;
@@ -870,12 +872,12 @@ __global__ __launch_bounds__(256) void sem_quant_kernel(const T* __restrict__ x,
 
 template <typename T, int D>
 static void launch_semantic_features(const T* x, int n, int hkv, int g, uint32_t* maxbits, int slot, int8_t* Xout,
-                                     int8_t* Xpad, int32_t* exps, hipStream_t s) {
+                                     int8_t* Xpad, int32_t* exps, float* xsum, hipStream_t s) {
   const int64_t total = (int64_t)n * D;
   hipLaunchKernelGGL((sem_maxabs_kernel<T, D>), dim3((unsigned)ceil_div(total, 1024), hkv), dim3(256), 0, s, x, n, g,
                      maxbits);
   hipLaunchKernelGGL((sem_quant_kernel<T, D>), dim3((unsigned)ceil_div(total, 256), hkv), dim3(256), 0, s, x, n, g,
-                     maxbits, slot, Xout, Xpad, exps);
+                     maxbits, slot, Xout, Xpad, exps, xsum);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1016,13 +1018,15 @@ static void partition_typed(const Dims& dm, const Workspace& wp, const T* q, con
   int8_t* xq = reinterpret_cast<int8_t*>(ws + wp.xq);
   int32_t* C = reinterpret_cast<int32_t*>(ws + wp.centroids);
   int32_t* sums = reinterpret_cast<int32_t*>(ws + wp.sums);
-  float* usum = dm.g > 1 ? reinterpret_cast<float*>(ws + wp.usum) : nullptr;
+  // head-summed query coordinate (g > 1): the caller's query_coord_sum when given, else scratch
+  float* usum = dm.g > 1 ? (out.query_coord_sum ? out.query_coord_sum : reinterpret_cast<float*>(ws + wp.usum))
+                        : nullptr;
   int32_t* gm_hist = reinterpret_cast<int32_t*>(ws + wp.gm_hist);
   const int n = dm.n, hkv = dm.hkv;
   fill_u32(maxbits, (size_t)hkv * 2, 0, s);
   // keys
   if (dm.semantic) {
-    launch_semantic_features<T, D>(k, n, hkv, 1, maxbits, 0, nullptr, xk, out.exponents, s);
+    launch_semantic_features<T, D>(k, n, hkv, 1, maxbits, 0, nullptr, xk, out.exponents, nullptr, s);
     run_kmeans(xk, n, hkv, dm.gk, D, D, dm.iters, C, sums, out.key_labels, out.key_centroids_int, s);
   } else {
     if (dm.bf16)
@@ -1046,7 +1050,8 @@ static void partition_typed(const Dims& dm, const Workspace& wp, const T* q, con
   // queries (the semantic features are formed first: the response kernels below reuse the
   // second max slot)
   if (dm.semantic)
-    launch_semantic_features<T, D>(q, n, hkv, dm.g, maxbits + hkv, 1, out.query_features, xq, out.exponents, s);
+    launch_semantic_features<T, D>(q, n, hkv, dm.g, maxbits + hkv, 1, out.query_features, xq, out.exponents,
+                                   dm.g > 1 ? out.query_coord_sum : nullptr, s);
   if (dm.bf16)
     launch_resp_u_mfma(dm, q, out.key_centroids, out.responses_u, usum, maxbits + hkv, s);
   else

@@ -5,7 +5,6 @@
 
 namespace sp {
 
-hipError_t ensure_exp_table();
 
 void launch_resp_s_mfma(const Dims& dm, const void* q, const void* k, float* S, uint32_t* maxbits, hipStream_t s);
 void launch_resp_u_mfma(const Dims& dm, const void* q, const float* Ck, float* U, float* Usum, uint32_t* maxbits,

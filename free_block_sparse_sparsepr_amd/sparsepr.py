@@ -112,6 +112,8 @@ class SparsePR:
             query_offsets=e(c.heads_kv, c.groups_q + 1),
             q_gm=e(c.heads_kv, c.n, c.g, c.d, dt=c.torch_dtype), k_gm=e(c.heads_kv, c.n, c.d, dt=c.torch_dtype),
             v_gm=e(c.heads_kv, c.d, c.n_pad, dt=c.torch_dtype))
+        if c.g > 1:   # the head-summed query coordinate the features quantise (read back by tests)
+            self.part["query_coord_sum"] = e(c.heads_kv, c.n, c.query_feat, dt=f32)
         self.route_buf = dict(
             row_ptr=e(c.heads_kv, c.groups_q + 1), cols=e(c.heads_kv, c.groups_q * c.groups_k),
             kept_mask=e(c.heads_kv, c.groups_q, dt=torch.int64), pairs=e(c.heads_kv, dt=torch.int64),
@@ -125,7 +127,8 @@ class SparsePR:
             r_eff=e(c.heads_q), eig=e(c.heads_q, c.rank + 1, dt=f32))
         self.o_gm = e(c.heads_kv, c.n, c.g, c.d, dt=f32)
         self.lse = e(c.heads_kv, c.n, c.g, dt=f32)
-        self._part_t = B.PartitionT(*[self.part[k].data_ptr() for k in B.PARTITION_FIELDS])
+        self._part_t = B.PartitionT(*[self.part[k].data_ptr() if k in self.part else None
+                                      for k in B.PARTITION_FIELDS])
         self._route_t = B.RouteT(*[self.route_buf[k].data_ptr() for k in B.ROUTE_FIELDS])
         self._fit_t = B.FitT(*[self.fit[k].data_ptr() for k in B.FIT_FIELDS])
 
@@ -230,8 +233,8 @@ class SparsePR:
     def capture(self, q, k, v, out, order="fused"):
         """Records one whole call of the given order ("fused", "unfused" or "overlapped") into
         a HIP graph and returns it (``graph.replay()`` reruns the call on the same buffers).
-        One eager call runs first, on a side stream, so that one-time set-up (the route's
-        exponential table upload) happens outside the capture."""
+        One eager call runs first, on a side stream (the usual warm-up before a capture: torch's
+        own lazy set-up, such as the side stream of the overlapped order, happens outside it)."""
         fn = {"fused": self.fused, "unfused": self.__call__, "overlapped": self.overlapped}[order]
         warm = torch.cuda.Stream(device=out.device)
         warm.wait_stream(torch.cuda.current_stream())

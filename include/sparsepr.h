@@ -19,9 +19,8 @@
  *
  * Conventions for every entry point
  *  - All tensor pointers are DEVICE pointers allocated and owned by the caller; the
- *    library allocates nothing and keeps no state between calls, except an immutable
- *    1024-entry exponential table uploaded once per device on the first call made on
- *    that device (so do not make the very first call inside a stream capture).
+ *    library allocates nothing and keeps no state between calls, so every call may be
+ *    captured into a HIP graph, the first one on a device included.
  *  - `stream` is a hipStream_t (NULL = the null stream).  All work is asynchronous on
  *    it; no entry point synchronises the host.
  *  - Tensors are contiguous, row-major, 16-byte aligned.  Element type of Q/K/V and of
@@ -184,6 +183,13 @@ typedef struct sparsepr_partition_t {
                                 d * n_pad + s(p), where s swaps bits 2 and 3 of p (within each
                                 16-key group the keys are stored as 0-3, 8-11, 4-7, 12-15);
                                 positions n .. n_pad - 1 are zero. */
+  float* query_coord_sum;    /* optional (NULL: not written), read only when g > 1: the head-summed
+                                query coordinate that the query features quantise, fp32 as the
+                                kernels formed it (ascending query head order).  Response
+                                partition: [Hkv, n, G_K], the sum of responses_u over the KV
+                                head's query heads; semantic partition: [Hkv, n, d], the summed
+                                raw query rows.  With g = 1 the features quantise responses_u (or
+                                the raw rows) directly and nothing is written here. */
 } sparsepr_partition_t;
 
 /* Route outputs.  Row a of the CSR lists the kept key groups of query group a,
@@ -244,7 +250,9 @@ sparsepr_status sparsepr_route(const sparsepr_params* params, const sparsepr_par
                                size_t workspace_bytes, void* stream);
 
 /* Block-sparse attention over the kept cells, renormalised over the kept K/V groups
- * (PSRR, execution paragraph).  Reads q_gm, k_gm, v_gm, offsets and the CSR.
+ * (PSRR, execution paragraph).  Reads q_gm, k_gm, v_gm, offsets and the CSR.  After a
+ * partition made with defer_kv_gather = 1, sparsepr_gather_kv must have run (ordered before
+ * this call) or k_gm and v_gm still hold an earlier call's keys and values.
  * o_gm: [Hkv, n, g, d] fp32, group-major rows; lse: [Hkv, n, g] fp32 (natural log).
  * The workspace (sparsepr_workspace_size bytes, 256-byte aligned) holds the tile schedule
  * (each head's query groups longest first) in a region disjoint from the one
@@ -257,14 +265,18 @@ sparsepr_status sparsepr_attend(const sparsepr_params* params, const sparsepr_pa
  * paragraph): n_probe rows per KV head stratified over query groups in radial order
  * about each group centroid, their dense and sparse outputs against all keys,
  * R = O_dense - O_sparse, the group-coverage-weighted ridge fit of R on O_sparse and
- * the rank-r subspace of the probe residuals.  q: [Hq, n, d] token order. */
+ * the rank-r subspace of the probe residuals.  q: [Hq, n, d] token order.  Reads k_gm and
+ * v_gm: after a partition made with defer_kv_gather = 1, sparsepr_gather_kv must have run
+ * (ordered before this call). */
 sparsepr_status sparsepr_probe_fit(const sparsepr_params* params, const void* q,
                                    const sparsepr_partition_t* part, const sparsepr_route_t* route,
                                    const sparsepr_fit_t* out, void* workspace,
                                    size_t workspace_bytes, void* stream);
 
-/* Write-back: o_hat = o + c0 + (o A) B for every row, probe rows replaced by their exact
- * dense output, inverse permutation to token order, cast to dtype.
+/* Write-back (PSRR, execution paragraph, where write-back is one of the timed parts of the
+ * call; the correction is the probe-fit paragraph's affine map projected onto the rank-r
+ * output subspace): o_hat = o + c0 + (o A) B for every row, probe rows replaced by their
+ * exact dense output, inverse permutation to token order, cast to dtype.
  * o_gm: [Hkv, n, g, d] fp32 from sparsepr_attend; o: [Hq, n, d] dtype, token order. */
 sparsepr_status sparsepr_apply(const sparsepr_params* params, const float* o_gm,
                                const sparsepr_partition_t* part, const sparsepr_fit_t* fit, void* o,
@@ -276,7 +288,8 @@ sparsepr_status sparsepr_apply(const sparsepr_params* params, const float* o_gm,
  * fp32 accumulation) without the fp32 group-major intermediate.  For bf16 with one query
  * head per KV head the correction o + c0 + (o A) B runs on the matrix cores inside the
  * attention kernel; otherwise O_gm is formed in the workspace and the write-back follows.
- * Reads the partition, the route and the fit; o: [Hq, n, d] dtype, token order. */
+ * Reads the partition, the route and the fit; o: [Hq, n, d] dtype, token order.  After a
+ * partition made with defer_kv_gather = 1, sparsepr_gather_kv must have run first. */
 sparsepr_status sparsepr_attend_apply(const sparsepr_params* params, const sparsepr_partition_t* part,
                                       const sparsepr_route_t* route, const sparsepr_fit_t* fit, void* o,
                                       void* workspace, size_t workspace_bytes, void* stream);

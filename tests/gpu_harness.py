@@ -33,17 +33,30 @@ def host(t):
     return t.detach().cpu().numpy()
 
 
+OVERLAP_CHECKED = ("k_gm", "v_gm", "key_centroids", "q_gm", "key_perm", "query_perm")
+
+
 def run_gpu(cfg, Q, K, V):
-    """Runs the unfused call and returns every buffer as numpy, plus the dense output."""
+    """Runs the three call orders (unfused, overlapped -- the one bench.py times by default,
+    whose partition defers the K/V gathers to a second stream -- and fused) and the dense
+    baseline; returns every buffer of the unfused call as numpy, the three outputs, the
+    dense output, and whether the overlapped call left the partition buffers bit-identical."""
     import free_block_sparse_sparsepr_amd as S
     torch = torch_mod()
     sp = S.SparsePR(S.config_from_workload(cfg))
     q, k, v = device_tensor(Q, cfg), device_tensor(K, cfg), device_tensor(V, cfg)
-    out = sp(q, k, v)
+    out = sp(q, k, v).clone()
+    snap = {k_: sp.part[k_].clone() for k_ in OVERLAP_CHECKED}
+    out_overlapped = sp.overlapped(q, k, v).clone()
+    torch.cuda.synchronize()
+    overlap_same = {k_: bool(torch.equal(snap[k_], sp.part[k_])) for k_ in OVERLAP_CHECKED}
+    del snap
     out_fused = sp.fused(q, k, v).clone()
     dense = sp.dense(q, k, v)
     torch.cuda.synchronize()
     res = {k_: host(t) for k_, t in {**sp.part, **sp.route_buf, **sp.fit}.items()}
+    res["out_overlapped"] = host(out_overlapped)
+    res["overlap_same"] = overlap_same
     res["o_gm"] = host(sp.o_gm)
     res["lse"] = host(sp.lse)
     res["out"] = host(out)
@@ -71,6 +84,12 @@ def compare_float(got, want, fp32):
     if fp32:
         return err.max() <= FP32_MAX_ABS, err.max(), err.mean()
     return (err.max() <= BF16_MAX_ABS and err.mean() <= BF16_MEAN_ABS), err.max(), err.mean()
+
+
+def gpu_coord_sum(gpu, cfg, kv):
+    """The head-summed query coordinate the GPU quantised (GQA only; None for g = 1, where
+    the features quantise the single head's responses as given)."""
+    return gpu["query_coord_sum"][kv] if cfg.g > 1 else None
 
 
 def oracle_inputs(cfg):

@@ -11,7 +11,7 @@ import pytest
 from oracle import sparsepr as O
 from sparsepr_workloads import CONFIGS, small
 
-from gpu_harness import compare_float, device_tensor, host, kept_from_mask, oracle_inputs, oracle_params
+from gpu_harness import compare_float, device_tensor, host, kept_from_mask, oracle_inputs, oracle_params, gpu_coord_sum
 
 pytestmark = pytest.mark.gpu
 
@@ -139,7 +139,8 @@ def test_semantic_partition_bit_exact(r):
         pytest.skip("response-coupled partition (covered by test_gpu_parity)")
     for kv in range(cfg.heads_kv):
         qh = r["Q"][kv * cfg.g:(kv + 1) * cfg.g]
-        part = O.partition_semantic(qh, r["K"][kv], p, U=gpu["responses_u"][kv * cfg.g:(kv + 1) * cfg.g])
+        part = O.partition_semantic(qh, r["K"][kv], p, U=gpu["responses_u"][kv * cfg.g:(kv + 1) * cfg.g],
+                                    x_sum=gpu_coord_sum(gpu, cfg, kv))
         np.testing.assert_array_equal(gpu["key_labels"][kv], part.k_labels)
         np.testing.assert_array_equal(gpu["key_centroids_int"][kv], part.k_centroids_int)
         np.testing.assert_array_equal(gpu["key_perm"][kv], part.k_perm)

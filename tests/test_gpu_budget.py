@@ -2,21 +2,20 @@
 the Residual", execution paragraph: the router spends a pair budget over indivisible
 cells): tile-padded cell costs, one budget shared by all KV heads, and both.  The route is
 bit-exact against the oracle fed the GPU's response matrices.  The whole call's output
-(overlapped and fused orders) is checked on sampled rows within the bf16 bar: the probe
-rows against the oracle's exact attention on the GPU's labels, cells and probes, and the
-corrected rows against the oracle's float64 fit of the GPU's probe rows.  The ridge
-extrapolates (corrections here reach the size of the output itself), so rounding in the
-probe rows would otherwise be amplified into the comparison; the fit itself is pinned in
-test_gpu_parity at the default route."""
+(overlapped and fused orders) is checked on sampled rows within the bf16 bar against the
+oracle's own probe fit (float64 probe rows, ridge and subspace) on the GPU's labels, cells
+and probes; the probe rows themselves within 1e-3 of the oracle's exact attention."""
 import numpy as np
 import pytest
 
 from oracle import sparsepr as O
 from sparsepr_workloads import CONFIGS, small
 
-from gpu_harness import compare_float, device_tensor, host, kept_from_mask, oracle_inputs, oracle_params
+from gpu_harness import compare_float, device_tensor, host, kept_from_mask, oracle_inputs, oracle_params, gpu_coord_sum
 
 pytestmark = pytest.mark.gpu
+
+PROBE_ROW_MAX_ABS = 1e-3   # probe rows: fp32 scores, probabilities as a bf16 high + remainder pair
 
 CASES = {
     "c2_bf16_mixed_scales": small(CONFIGS[2], (8, 16, 16), heads_q=4, groups=16),
@@ -47,7 +46,8 @@ def run(request):
     gpu = {n: host(t) for n, t in {**sp.part, **sp.route_buf, **sp.fit}.items()}
     p = dataclasses.replace(oracle_params(cfg), tile_cost=64 if cost_mode else 0, global_budget=bool(budget_mode))
     parts = [O.partition(Q[kv * cfg.g:(kv + 1) * cfg.g], K[kv], p, S=gpu["responses_s"][kv],
-                         U=gpu["responses_u"][kv * cfg.g:(kv + 1) * cfg.g]) for kv in range(cfg.heads_kv)]
+                         U=gpu["responses_u"][kv * cfg.g:(kv + 1) * cfg.g], U_sum=gpu_coord_sum(gpu, cfg, kv))
+             for kv in range(cfg.heads_kv)]
     return dict(cfg=cfg, p=p, Q=Q, K=K, V=V, gpu=gpu, out=out, out_fused=out_fused, parts=parts)
 
 
@@ -82,12 +82,11 @@ def test_outputs_follow_the_variant_route(run):
         q, k, v = run["Q"][h], run["K"][kv], run["V"][kv]
         exact = O.probe_fit(q, k, v, scale, probes, ql, kl, kept, p)
         ok, mx, mean = compare_float(gpu["o_dense"][h], exact.o_dense, False)
-        assert ok, ("o_dense", h, mx, mean)
+        assert ok and mx <= PROBE_ROW_MAX_ABS, ("o_dense", h, mx, mean)
         ok, mx, mean = compare_float(gpu["o_sparse"][h], exact.o_sparse, False)
-        assert ok, ("o_sparse", h, mx, mean)
-        fit = O.fit_from_probe_rows(gpu["o_dense"][h], gpu["o_sparse"][h], probes.weights, p)
+        assert ok and mx <= PROBE_ROW_MAX_ABS, ("o_sparse", h, mx, mean)
         o_s, _ = O.sparse_attention(q, k, v, scale, ql, kl, kept, rows=rows)
-        want = O.correct_rows(o_s, fit)
+        want = O.correct_rows(o_s, exact)
         for name in ("out", "out_fused"):
             ok, mx, mean = compare_float(run[name][h][rows], want, False)
             assert ok, (name, h, mx, mean)

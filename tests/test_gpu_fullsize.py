@@ -1,15 +1,19 @@
-"""Full-size GPU parity at the workloads' real shapes, in the launch configuration bench.py
-times (the whole call, all heads, fused and unfused orders).  The oracle checks a subset
-of heads: integer stages bit-exact given the GPU's S and U, float outputs on sampled rows
-(the probe rows, the first and last rows and seeded random rows) with the oracle fed the
-GPU's labels, cells and probes; bf16 bar max-abs <= 2e-2, mean-abs <= 2e-3."""
+"""Full-size GPU parity at the workloads' real shapes: the whole call, all heads, in the three
+call orders -- the overlapped order bench.py times by default (the partition defers the K/V
+gathers, which run on a second stream beside the route, and the probe stage runs beside the
+attention), the unfused and the fused order.  The overlapped call is checked bit-identical to
+the unfused one (output and the group-major K, V, Q, centroids and permutations), and the
+oracle checks a subset of heads: integer stages bit-exact given the GPU's S and U (and the
+head-summed U under GQA), float outputs on sampled rows (the probe rows, the first and last
+rows and seeded random rows) with the oracle fed the GPU's labels, cells and probes; bf16 bar
+max-abs <= 2e-2, mean-abs <= 2e-3."""
 import numpy as np
 import pytest
 
 from oracle import sparsepr as O
 from sparsepr_workloads import CONFIGS
 
-from gpu_harness import compare_float, kept_from_mask, oracle_inputs, oracle_params, run_gpu
+from gpu_harness import compare_float, kept_from_mask, oracle_inputs, oracle_params, run_gpu, gpu_coord_sum
 
 pytestmark = pytest.mark.gpu
 
@@ -32,12 +36,18 @@ def full(request):
     return dict(cfg=cfg, Q=Q, K=K, V=V, gpu=gpu, p=oracle_params(cfg))
 
 
+def test_fullsize_overlapped_order_is_bit_identical(full):
+    gpu = full["gpu"]
+    assert all(gpu["overlap_same"].values()), gpu["overlap_same"]
+    np.testing.assert_array_equal(gpu["out_overlapped"], gpu["out"])
+
+
 def test_fullsize_integer_stages_bit_exact(full):
     cfg, gpu, p = full["cfg"], full["gpu"], full["p"]
     for kv in CHECKED[cfg.cfg_id]:
         qh = full["Q"][kv * cfg.g:(kv + 1) * cfg.g]
         part = O.partition(qh, full["K"][kv], p, S=gpu["responses_s"][kv],
-                           U=gpu["responses_u"][kv * cfg.g:(kv + 1) * cfg.g])
+                           U=gpu["responses_u"][kv * cfg.g:(kv + 1) * cfg.g], U_sum=gpu_coord_sum(gpu, cfg, kv))
         np.testing.assert_array_equal(gpu["key_labels"][kv], part.k_labels)
         np.testing.assert_array_equal(gpu["key_perm"][kv], part.k_perm)
         np.testing.assert_array_equal(gpu["query_features"][kv], part.xq)

@@ -11,7 +11,7 @@ import pytest
 from oracle import sparsepr as O
 from sparsepr_workloads import CONFIGS, small
 
-from gpu_harness import device_tensor, host, oracle_inputs, oracle_params
+from gpu_harness import device_tensor, host, oracle_inputs, oracle_params, gpu_coord_sum
 
 pytestmark = pytest.mark.gpu
 
@@ -37,7 +37,8 @@ def test_kmeans_iterations_bit_exact(path, iters, cfg):
     assert p.kmeans_iters == iters
     for kv in range(cfg.heads_kv):
         qh = Q[kv * cfg.g:(kv + 1) * cfg.g]
-        part = O.partition(qh, K[kv], p, S=gpu["responses_s"][kv], U=gpu["responses_u"][kv * cfg.g:(kv + 1) * cfg.g])
+        part = O.partition(qh, K[kv], p, S=gpu["responses_s"][kv], U=gpu["responses_u"][kv * cfg.g:(kv + 1) * cfg.g],
+                           U_sum=gpu_coord_sum(gpu, cfg, kv))
         np.testing.assert_array_equal(gpu["key_labels"][kv], part.k_labels)
         np.testing.assert_array_equal(gpu["key_centroids_int"][kv], part.k_centroids_int[:, :cfg.r_k])
         np.testing.assert_array_equal(gpu["query_labels"][kv], part.q_labels)

@@ -13,7 +13,7 @@ import pytest
 from oracle import sparsepr as O
 from sparsepr_workloads import CONFIGS, small
 
-from gpu_harness import (compare_float, kept_from_mask, oracle_inputs, oracle_params, run_gpu, vgm_rows)
+from gpu_harness import (gpu_coord_sum, compare_float, kept_from_mask, oracle_inputs, oracle_params, run_gpu, vgm_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -41,7 +41,8 @@ def case(request):
     for kv in range(cfg.heads_kv):
         qh = Q[kv * cfg.g:(kv + 1) * cfg.g]
         parts.append(O.partition(qh, K[kv], p, S=gpu["responses_s"][kv],
-                                 U=gpu["responses_u"][kv * cfg.g:(kv + 1) * cfg.g]))
+                                 U=gpu["responses_u"][kv * cfg.g:(kv + 1) * cfg.g],
+                                 U_sum=gpu_coord_sum(gpu, cfg, kv)))
     return dict(name=request.param, cfg=cfg, Q=Q, K=K, V=V, gpu=gpu, p=p, parts=parts, sp=sp, dev=dev)
 
 
