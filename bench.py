@@ -61,6 +61,56 @@ def cpu_baseline(cfg):
                       f"nproc {os.cpu_count()}"}
 
 
+def dense_oracle_baseline(cfg, rows=1024):
+    """The oracle's dense attention (float64, 1024-row chunks) on a bounded sample of query
+    head 0 -- `rows` evenly spaced rows against all n keys -- scaled to every row of every
+    query head of the call."""
+    import numpy as np
+    from oracle import sparsepr as O
+    from sparsepr_workloads import generator as gen
+    q, k, v = gen.head_inputs(cfg, 0)
+    rows = min(rows, cfg.n)
+    sel = (np.arange(rows) * cfg.n) // rows
+    t0 = time.perf_counter()
+    O.dense_attention(q[0], k, v, 1.0 / np.sqrt(cfg.d), rows=sel)
+    dt = time.perf_counter() - t0
+    per_call = dt * (cfg.n / rows) * cfg.heads_q
+    return {"value": 1.0 / per_call, "unit": "calls/s", "kind": "oracle dense attention",
+            "sample": f"{rows} evenly spaced rows of query head 0 against all {cfg.n} keys in {dt:.2f} s, "
+                      f"scaled x{cfg.n / rows:.1f} rows x{cfg.heads_q} heads"}
+
+
+def executed_tile_pairs(sp, cfg):
+    """Query-key pairs the sparse kernel executes once its work is padded to tiles: per query
+    group, the virtual rows (tokens x query heads of the KV head) rounded up to the 32 rows of
+    one wave (waves past a group's rows skip the tile math), times the keys of the 64-key tiles
+    its kept runs occupy (runs of adjacent kept key groups, each starting on a 16-key
+    boundary), summed over KV heads."""
+    import numpy as np
+    rp = sp.route_buf["row_ptr"].cpu().numpy().astype(np.int64)
+    cols = sp.route_buf["cols"].cpu().numpy().astype(np.int64)
+    ko = sp.part["key_offsets"].cpu().numpy().astype(np.int64)
+    qo = sp.part["query_offsets"].cpu().numpy().astype(np.int64)
+    total = 0
+    for kv in range(cfg.heads_kv):
+        for a in range(cfg.groups_q):
+            rows = (qo[kv, a + 1] - qo[kv, a]) * cfg.g
+            if rows == 0:
+                continue
+            c = cols[kv, rp[kv, a]:rp[kv, a + 1]]
+            keys, i = 0, 0
+            while i < len(c):
+                b = e = c[i]
+                i += 1
+                while i < len(c) and c[i] == e + 1:
+                    e, i = c[i], i + 1
+                k0, k1 = ko[kv, b], ko[kv, e + 1]
+                if k1 > k0:
+                    keys += (k1 - (k0 & ~15) + 63) // 64 * 64
+            total += (rows + 31) // 32 * 32 * keys
+    return int(total)
+
+
 TRAFFIC_PROFILES = {   # call order -> counter summary of that order's attention kernel
     "fused": os.path.join(ROOT, "profiles", "sparse_attention_720p_n118800_h24_hbm_traffic.md"),
     "overlapped": os.path.join(ROOT, "profiles", "sparse_attention_overlapped_720p_n118800_h24_hbm_traffic.md"),
@@ -278,7 +328,8 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=3)
-    ap.add_argument("--dense-steps", type=int, default=2)
+    ap.add_argument("--dense-steps", type=int, default=None,
+                    help="timed dense-attention calls (default: --steps, after --warmup untimed ones)")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--unfused", action="store_true",
@@ -447,17 +498,21 @@ def main():
     rho_route = float(pairs_kv.mean()) / cfg.n ** 2
     rho_exec = rho_route + cfg.n_probe / cfg.n
 
+    padded = executed_tile_pairs(sp, cfg) if pipe is None else None
+
     dense = None
     if not args.no_dense:
-        sp.dense(q, k, v, out)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(args.dense_steps):
+        dsteps = args.dense_steps or args.steps
+        for _ in range(max(1, args.warmup)):
             sp.dense(q, k, v, out)
         torch.cuda.synchronize()
-        dense_ms = (time.perf_counter() - t0) * 1e3 / args.dense_steps
+        t0 = time.perf_counter()
+        for _ in range(dsteps):
+            sp.dense(q, k, v, out)
+        torch.cuda.synchronize()
+        dense_ms = (time.perf_counter() - t0) * 1e3 / dsteps
         dense_flop = 4.0 * cfg.d * cfg.n * cfg.n * cfg.heads_q
-        dense = {"ms_per_call": dense_ms, "tflops": dense_flop / (dense_ms * 1e-3) / 1e12,
+        dense = {"ms_per_call": dense_ms, "steps": dsteps, "tflops": dense_flop / (dense_ms * 1e-3) / 1e12,
                  "speedup_sparsepr_vs_dense": dense_ms / ms_per_step}
         log(f"[bench] dense {dense_ms:.2f} ms/call")
 
@@ -465,6 +520,8 @@ def main():
     if not args.no_cpu:
         log("[bench] timing the CPU oracle on one head")
         cpu = cpu_baseline(cfg)
+        log("[bench] timing the CPU oracle's dense attention on a sample of rows")
+        cpu["dense_attention"] = dense_oracle_baseline(cfg)
 
     res = {
         "metric": METRIC, "value": args.steps / wall, "unit": "calls/s", "n_gpus": 1, "steps": args.steps,
@@ -486,7 +543,11 @@ def main():
         "graph": graph,
         "effective_tflops_call": call_tflops, "effective_frac_call": call_tflops / peak,
         "realised_rho_route": rho_route, "realised_rho_exec": rho_exec,
-        "routed_pairs": routed, "stage_ms": stage_ms, "dense": dense, "cpu_baseline": cpu,
+        "routed_pairs": routed,
+        "tile_padded_pairs": None if padded is None else padded,
+        "routed_over_padded": None if not padded else routed / padded,
+        "attend_tflops_on_padded_pairs": None if not padded else 4.0 * cfg.d * padded / (stage_ms[attn_stage] * 1e-3) / 1e12,
+        "stage_ms": stage_ms, "dense": dense, "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
 

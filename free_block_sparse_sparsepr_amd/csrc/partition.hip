@@ -1018,9 +1018,12 @@ static void partition_typed(const Dims& dm, const Workspace& wp, const T* q, con
   int8_t* xq = reinterpret_cast<int8_t*>(ws + wp.xq);
   int32_t* C = reinterpret_cast<int32_t*>(ws + wp.centroids);
   int32_t* sums = reinterpret_cast<int32_t*>(ws + wp.sums);
-  // head-summed query coordinate (g > 1): the caller's query_coord_sum when given, else scratch
-  float* usum = dm.g > 1 ? (out.query_coord_sum ? out.query_coord_sum : reinterpret_cast<float*>(ws + wp.usum))
-                        : nullptr;
+  // head-summed query responses (g > 1, response partition: the coordinate the query features
+  // quantise): the caller's query_coord_sum when given, else scratch.  The semantic partition
+  // sums the raw query rows instead (into query_coord_sum) and needs no response sum.
+  float* usum = (dm.g > 1 && !dm.semantic)
+                    ? (out.query_coord_sum ? out.query_coord_sum : reinterpret_cast<float*>(ws + wp.usum))
+                    : nullptr;
   int32_t* gm_hist = reinterpret_cast<int32_t*>(ws + wp.gm_hist);
   const int n = dm.n, hkv = dm.hkv;
   fill_u32(maxbits, (size_t)hkv * 2, 0, s);
