@@ -49,6 +49,7 @@ RouteT = _ptr_struct("RouteT", ROUTE_FIELDS)
 FitT = _ptr_struct("FitT", FIT_FIELDS)
 
 EXPORTS = ["sparsepr_workspace_size", "sparsepr_partition", "sparsepr_gather_kv", "sparsepr_route", "sparsepr_attend",
+           "sparsepr_attend_noalloc",
            "sparsepr_probe_fit", "sparsepr_apply", "sparsepr_attend_apply", "sparsepr_dense_attention",
            "sparsepr_diagnostics_workspace_size", "sparsepr_residual_diagnostics",
            "sparsepr_support_workspace_size", "sparsepr_support_diagnostics", "sparsepr_status_string"]
@@ -75,6 +76,7 @@ def load():
         "sparsepr_gather_kv": [P(Params), vp, vp, P(PartitionT), vp],
         "sparsepr_route": [P(Params), P(PartitionT), P(RouteT), vp, sz, vp],
         "sparsepr_attend": [P(Params), P(PartitionT), P(RouteT), vp, vp, vp, sz, vp],
+        "sparsepr_attend_noalloc": [P(Params), P(PartitionT), P(RouteT), vp, vp, vp],
         "sparsepr_probe_fit": [P(Params), vp, P(PartitionT), P(RouteT), P(FitT), vp, sz, vp],
         "sparsepr_apply": [P(Params), vp, P(PartitionT), P(FitT), vp, vp],
         "sparsepr_attend_apply": [P(Params), P(PartitionT), P(RouteT), P(FitT), vp, vp, sz, vp],

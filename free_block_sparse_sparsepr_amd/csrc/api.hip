@@ -1,6 +1,7 @@
 // C ABI of the SparsePR call: argument validation, workspace planning and launch order.
 // The operations themselves are documented in include/sparsepr.h.
 #include <cmath>
+#include <mutex>
 
 #include "sp_common.hpp"
 #include "sp_launch.hpp"
@@ -193,6 +194,29 @@ static AttnArgs dense_args(const Dims& dm, const void* q, const void* k, const v
   return a;
 }
 
+// Scratch of sparsepr_attend_noalloc: the attention's tile schedule (each KV head's query
+// groups longest first) in a file-scope device array instead of the caller's workspace.
+// Every GPU the library runs on holds its own copy until the process ends; host code uses
+// the per-device address from hipGetSymbolAddress, never the array's name.
+constexpr size_t kNoAllocScratchBytes = (size_t)4 << 20;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+// The device address of `scratch` on the current device, looked up once per device.
+static sparsepr_status scratch_address(void** out) {
+  static std::mutex mu;
+  static void* addr[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return SPARSEPR_ERR_HIP;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return SPARSEPR_ERR_HIP;
+    addr[dev] = ptr;
+  }
+  *out = addr[dev];
+  return SPARSEPR_OK;
+}
+
 }  // namespace sp
 
 using namespace sp;
@@ -280,6 +304,32 @@ sparsepr_status sparsepr_attend(const sparsepr_params* params, const sparsepr_pa
   a.lse = lse;
   (void)hipGetLastError();
   if (dm.bf16) launch_tile_order(dm, a, static_cast<char*>(workspace) + wp.attn_order, (hipStream_t)stream);
+  launch_attention(dm, a, false, (hipStream_t)stream);
+  return hip_status();
+}
+
+sparsepr_status sparsepr_attend_noalloc(const sparsepr_params* params, const sparsepr_partition_t* part,
+                                        const sparsepr_route_t* route, float* o_gm, float* lse, void* stream) {
+  sparsepr_status st = check_params(params);
+  if (st != SPARSEPR_OK) return st;
+  if (!part || !route || !o_gm) return SPARSEPR_ERR_NULL;
+  if (!part->q_gm || !part->k_gm || !part->v_gm || !part->query_offsets || !part->key_offsets || !route->row_ptr ||
+      !route->cols)
+    return SPARSEPR_ERR_NULL;
+  if (!aligned16(part->q_gm) || !aligned16(part->k_gm) || !aligned16(part->v_gm) || !aligned16(o_gm))
+    return SPARSEPR_ERR_ALIGN;
+  const Dims dm = dims_of(*params);
+  if (dm.bf16 && attn_order_bytes(dm.n, dm.g, dm.hkv, dm.gq) > kNoAllocScratchBytes) return SPARSEPR_ERR_WORKSPACE;
+  void* scr = nullptr;
+  if (dm.bf16) {
+    st = scratch_address(&scr);
+    if (st != SPARSEPR_OK) return st;
+  }
+  AttnArgs a = sparse_args(dm, *part, *route);
+  a.o = o_gm;
+  a.lse = lse;
+  (void)hipGetLastError();
+  if (dm.bf16) launch_tile_order(dm, a, static_cast<char*>(scr), (hipStream_t)stream);
   launch_attention(dm, a, false, (hipStream_t)stream);
   return hip_status();
 }

@@ -163,6 +163,13 @@ class SparsePR:
                                          ctypes.byref(self._route_t), _p(self.o_gm), _p(self.lse), _p(self.ws),
                                          self.ws.numel(), _stream()))
 
+    def attend_noalloc(self):
+        """attend() through sparsepr_attend_noalloc: no workspace, the schedule in the
+        library's fixed device array."""
+        B.check(self.lib.sparsepr_attend_noalloc(ctypes.byref(self.prm), ctypes.byref(self._part_t),
+                                                 ctypes.byref(self._route_t), _p(self.o_gm), _p(self.lse),
+                                                 _stream()))
+
     def probe_fit(self, q):
         self._check_qkv(q, None, None)
         B.check(self.lib.sparsepr_probe_fit(ctypes.byref(self.prm), _p(q), ctypes.byref(self._part_t),

@@ -19,8 +19,9 @@
  *
  * Conventions for every entry point
  *  - All tensor pointers are DEVICE pointers allocated and owned by the caller; the
- *    library allocates nothing and keeps no state between calls, so every call may be
- *    captured into a HIP graph, the first one on a device included.
+ *    library allocates nothing and keeps no state between calls (the one exception is the
+ *    fixed device array of sparsepr_attend_noalloc), so every call may be captured into a
+ *    HIP graph, the first one on a device included.
  *  - `stream` is a hipStream_t (NULL = the null stream).  All work is asynchronous on
  *    it; no entry point synchronises the host.
  *  - Tensors are contiguous, row-major, 16-byte aligned.  Element type of Q/K/V and of
@@ -260,6 +261,20 @@ sparsepr_status sparsepr_route(const sparsepr_params* params, const sparsepr_par
 sparsepr_status sparsepr_attend(const sparsepr_params* params, const sparsepr_partition_t* part,
                                 const sparsepr_route_t* route, float* o_gm, float* lse,
                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* sparsepr_attend for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same attention with
+ * the same arguments and results, but no workspace.  The tile schedule that sparsepr_attend
+ * keeps in the workspace lives instead in a fixed 4 MiB device array inside the library, one
+ * per GPU, held until the process ends; no call allocates or frees anything.  Limit: the
+ * schedule needs 4 (2 (ceil(n g / 256) + G_Q) H_kv + 64 + H_kv) bytes for bf16 (nothing for
+ * fp32); larger shapes return SPARSEPR_ERR_WORKSPACE before any launch.  Every call on one GPU
+ * shares that GPU's array and overwrites it, so calls that overlap on one GPU (other streams,
+ * other threads, replays of several graphs at once) race and must be ordered by the caller.
+ * The first call on a device looks the array's address up (no allocation, no stream work). */
+sparsepr_status sparsepr_attend_noalloc(const sparsepr_params* params, const sparsepr_partition_t* part,
+                                        const sparsepr_route_t* route, float* o_gm, float* lse,
+                                        void* stream);
 
 /* Probe selection, exact probe rows and the fit (PSRR, probe-fit residual reconstruction
  * paragraph): n_probe rows per KV head stratified over query groups in radial order

@@ -165,3 +165,27 @@ def test_global_budget_route_needs_its_workspace():
     assert lib.sparsepr_route(ctypes.byref(g), ctypes.byref(part), ctypes.byref(route), nul, 0, nul) == -1
     assert lib.sparsepr_route(ctypes.byref(g), ctypes.byref(part), ctypes.byref(route), ctypes.c_void_p(0x1000), 16,
                               nul) == -5
+
+
+def test_noalloc_attend_rejects_before_any_launch():
+    """The allocation-free attention takes no workspace: it checks its pointers and rejects a
+    schedule larger than its fixed device array before it looks anything up or launches."""
+    lib = lib_or_skip()
+    nul = ctypes.c_void_p(0)
+    fake = ctypes.c_void_p(0x1000)
+    odd = ctypes.c_void_p(0x1008)
+    part = B.PartitionT(**{f: 0x2000 for f in B.PARTITION_FIELDS})
+    route = B.RouteT(**{f: 0x3000 for f in B.ROUTE_FIELDS})
+    good = _params()
+    assert lib.sparsepr_attend_noalloc(ctypes.byref(_params(d=96)), ctypes.byref(part), ctypes.byref(route), fake,
+                                       fake, nul) == -2
+    assert lib.sparsepr_attend_noalloc(ctypes.byref(good), ctypes.byref(part), ctypes.byref(route), nul, fake,
+                                       nul) == -1
+    assert lib.sparsepr_attend_noalloc(ctypes.byref(good), ctypes.byref(part), ctypes.byref(route), odd, fake,
+                                       nul) == -4
+    # 16 query heads on each of 8 KV heads at the largest n: the schedule needs
+    # 4 (2 (2^22 16 / 256 + 64) 8 + 64 + 8) bytes, more than the 4 MiB array
+    big = _params(heads_q=128, heads_kv=8, n=1 << 22)
+    assert 4 * (2 * ((1 << 22) * 16 // 256 + 64) * 8 + 64 + 8) > 4 << 20
+    assert lib.sparsepr_attend_noalloc(ctypes.byref(big), ctypes.byref(part), ctypes.byref(route), fake, fake,
+                                       nul) == -5
