@@ -194,11 +194,10 @@ void launch_probe_writeback(const Dims& dm, const sparsepr_fit_t& fit, void* o, 
 
 void launch_apply(const Dims& dm, const float* o_gm, const sparsepr_partition_t& part, const sparsepr_fit_t& fit,
                   void* o, hipStream_t s) {
-  if (dm.bf16 && dm.rc <= kMaxRank && dm.g == 1) {
-    // bf16 output, one query head per KV head and the projected correction (rank <= 32): the
-    // matrix-core write-back (the fused epilogue's arithmetic, bf16 operands), then the exact
-    // probe rows.  Elsewhere the fp32 path: under GQA and for the unprojected ridge the fitted
-    // corrections extrapolate further, and bf16 operand rounding would exceed the output's own.
+  if (dm.bf16 && dm.rc <= kMaxCorrRank) {
+    // bf16 output: the matrix-core write-back (the fused epilogue's arithmetic; with split
+    // hi/lo operands under GQA and for the unprojected ridge, whose corrections can reach the
+    // size of the output), then the exact probe rows
     launch_apply_mfma(dm, o_gm, part, fit, o, s);
     if (dm.ablation != SPARSEPR_ABLATE_HARD_DROP) launch_probe_writeback(dm, fit, o, s);
   } else if (dm.bf16) {

@@ -5,12 +5,15 @@
 //
 // Work decomposition: one block = 256 virtual query rows of one query group (8 waves x
 // 32 rows); the block walks the group's kept key runs in 64-key tiles staged through LDS
-// (four stages, direct global-to-LDS copies two tiles ahead of the tile being consumed).  Each wave computes S^T = K Q^T so that a lane owns one query and 32 of the
-// tile's keys: the row max and sum are in-register plus one exchange with the partner
-// lane (l ^ 32), and the probabilities are already laid out as the B operand of
-// O^T += V^T P^T, so P never leaves registers.  V is stored transposed in LDS for that
-// A operand.  Softmax runs in the log2 domain with scale * log2(e) folded in; P is
-// rounded to bf16 for the second product and accumulation is fp32.
+// (four stages filled by direct global-to-LDS copies two tiles ahead).  Each wave computes
+// S^T = K Q^T so that a lane owns one query and 32 of the tile's keys: the row max and sum
+// are in-register plus one exchange with the partner lane (l ^ 32), and the probabilities
+// are already laid out as the B operand of O^T += V^T P^T, so P never leaves registers.
+// V is stored transposed in LDS for that A operand.  Softmax runs in the log2 domain with
+// scale * log2(e) folded in; P is rounded to bf16 for the second product and accumulation
+// is fp32.  The two waves of every SIMD run anti-phased between block barriers: while one
+// issues a tile's matrix products (with its LDS operand reads kept four deep, as assembly
+// for d = 128), the other runs its softmax and copies the tiles.
 //
 // Blocks are remapped so that consecutive tiles of one query group run on the same XCD
 // (the hardware deals blocks round-robin over the 8 XCDs), keeping a group's key runs
@@ -527,42 +530,63 @@ __device__ __forceinline__ void mfma_tile_step(const char* __restrict__ stage, c
 // o_hat = o + c0 + (o A) B on the matrix cores straight from the output accumulators.
 // O^T's accumulator layout is already a valid B operand over d (the k-index permutation
 // is applied to both operands), so t^T = A^T O^T (k x q) and then O^T += B^T t^T need no
-// data movement; A^T, B^T (bf16) and c0 are staged in the free LDS stages.  Rows are
-// scattered to token order through the query permutation.
-template <int D, int LDS_BYTES, int NT>
+// data movement; A^T, B^T (bf16) and c0 are staged in LDS.  With SPLIT every bf16 operand
+// (O, A, t, B) is carried as a bf16 high part and a bf16 remainder and each product as
+// three (hi hi + hi lo + lo hi), which keeps the correction to about 2^-16 of its size
+// where it grows as large as the output itself (grouped query heads, the unprojected
+// ridge).  Rows are scattered to token order through the query permutation.
+template <int D, bool SPLIT>
+struct FusedLds {
+  static constexpr int RCM = kMaxCorrRank;  // up to 64 correction directions (two 32-row blocks of t)
+  static constexpr int AROW = D + 8;        // At[k][d] bf16, padded rows (conflict-free 16-byte reads)
+  static constexpr int BROW = RCM + 4;      // Bt[d][k] bf16, padded rows (conflict-free 8-byte reads)
+  static constexpr int PART = (RCM * AROW + D * BROW) * 2;   // one copy of At and Bt
+  static constexpr int BYTES = PART * (SPLIT ? 2 : 1) + D * 4;
+};
+
+template <int D, int LDS_BYTES, int NT, bool SPLIT = false>
 __device__ __forceinline__ void fused_stage(const AttnArgs& A, int h, char* lds, int tid) {
-  constexpr int RCM = kMaxCorrRank;  // up to 64 correction directions (two 32-row blocks of t)
-  constexpr int AROW = D + 8;        // At[k][d] bf16, padded rows (conflict-free 16-byte reads)
-  constexpr int BROW = RCM + 4;      // Bt[d][k] bf16, padded rows (conflict-free 8-byte reads)
-  static_assert((RCM * AROW + D * BROW) * 2 + D * 4 <= LDS_BYTES, "fused write-back staging");
+  using F = FusedLds<D, SPLIT>;
+  static_assert(F::BYTES <= LDS_BYTES, "fused write-back staging");
   bf16_t* At = reinterpret_cast<bf16_t*>(lds);
-  bf16_t* Bt = At + RCM * AROW;
-  float* c0s = reinterpret_cast<float*>(Bt + D * BROW);
-  const int re = min(A.r_eff[h], min(A.rank, RCM));
+  bf16_t* Bt = At + F::RCM * F::AROW;
+  float* c0s = reinterpret_cast<float*>(lds + F::PART * (SPLIT ? 2 : 1));
+  const int re = min(A.r_eff[h], min(A.rank, F::RCM));
   const float* Ah = A.fitA + (int64_t)h * D * A.rank;
   const float* Bh = A.fitB + (int64_t)h * A.rank * D;
-  for (int idx = tid; idx < RCM * D; idx += NT) {
+  for (int idx = tid; idx < F::RCM * D; idx += NT) {
     const int k = idx / D, d = idx % D;
-    At[k * AROW + d] = f32_to_bf16(k < re ? Ah[d * A.rank + k] : 0.f);
-    Bt[d * BROW + k] = f32_to_bf16(k < re ? Bh[k * D + d] : 0.f);
+    const float av = k < re ? Ah[d * A.rank + k] : 0.f, bv = k < re ? Bh[k * D + d] : 0.f;
+    const bf16_t ah = f32_to_bf16(av), bh = f32_to_bf16(bv);
+    At[k * F::AROW + d] = ah;
+    Bt[d * F::BROW + k] = bh;
+    if constexpr (SPLIT) {
+      At[F::PART / 2 + k * F::AROW + d] = f32_to_bf16(av - bf16_to_f32(ah));
+      Bt[F::PART / 2 + d * F::BROW + k] = f32_to_bf16(bv - bf16_to_f32(bh));
+    }
   }
   for (int d = tid; d < D; d += NT) c0s[d] = A.fitc0[(int64_t)h * D + d];
   __syncthreads();
 }
 
+// 8 bf16 of a staged row (two 8-byte reads 8 elements apart: the k-permuted operand layout)
+__device__ __forceinline__ bf16x8_t staged8(const bf16_t* r) {
+  const uint2 lo8 = *reinterpret_cast<const uint2*>(r);
+  const uint2 hi8 = *reinterpret_cast<const uint2*>(r + 8);
+  return __builtin_bit_cast(bf16x8_t, make_uint4(lo8.x, lo8.y, hi8.x, hi8.y));
+}
+
 // The correction and scatter of one wave's 32 rows of query head h (group-major position
 // p of KV head kv) from A^T, B^T and c0 staged by fused_stage.
-template <int D>
+template <int D, bool SPLIT = false>
 __device__ __forceinline__ void fused_apply(const AttnArgs& A, int h, int kv, int p, bool qvalid, float inv,
                                             f32x16_t* o, const char* lds, int l32, int hf) {
+  using F = FusedLds<D, SPLIT>;
   constexpr int DBLK = D / 32;
-  constexpr int RCM = kMaxCorrRank;
-  constexpr int AROW = D + 8;
-  constexpr int BROW = RCM + 4;
   const bf16_t* At = reinterpret_cast<const bf16_t*>(lds);
-  const bf16_t* Bt = At + RCM * AROW;
-  const float* c0s = reinterpret_cast<const float*>(Bt + D * BROW);
-  const int re = min(A.r_eff[h], min(A.rank, RCM));
+  const bf16_t* Bt = At + F::RCM * F::AROW;
+  const float* c0s = reinterpret_cast<const float*>(lds + F::PART * (SPLIT ? 2 : 1));
+  const int re = min(A.r_eff[h], min(A.rank, F::RCM));
   // normalise and pack O (bf16) as the B operand over d; t^T = A^T O^T in one or two 32-row
   // blocks of correction directions
   const bool two = re > 32;
@@ -575,28 +599,39 @@ __device__ __forceinline__ void fused_apply(const AttnArgs& A, int h, int kv, in
     for (int r = 0; r < 16; ++r) o[db][r] *= inv;
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
-      bf16x8_t ob;
+      bf16x8_t ob, obl;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) ob[e] = (__bf16)o[db][8 * s2 + e];
+      for (int e = 0; e < 8; ++e) {
+        ob[e] = (__bf16)o[db][8 * s2 + e];
+        if constexpr (SPLIT) obl[e] = (__bf16)(o[db][8 * s2 + e] - (float)ob[e]);
+      }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         if (kb == 1 && !two) break;
-        const bf16_t* ar = At + (32 * kb + l32) * AROW + 32 * db + 16 * s2 + 4 * hf;
-        const uint2 lo8 = *reinterpret_cast<const uint2*>(ar);
-        const uint2 hi8 = *reinterpret_cast<const uint2*>(ar + 8);
-        const uint4 av = make_uint4(lo8.x, lo8.y, hi8.x, hi8.y);
-        t[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av), ob, t[kb], 0, 0, 0);
+        const bf16_t* ar = At + (32 * kb + l32) * F::AROW + 32 * db + 16 * s2 + 4 * hf;
+        const bf16x8_t av = staged8(ar);
+        t[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, ob, t[kb], 0, 0, 0);
+        if constexpr (SPLIT) {
+          t[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(staged8(ar + F::PART / 2), ob, t[kb], 0, 0, 0);
+          t[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, obl, t[kb], 0, 0, 0);
+        }
       }
     }
   }
   // t^T[k][q] in the accumulator layout is the B operand over k of O^T += B^T t^T
-  bf16x8_t tb[4];
+  bf16x8_t tb[4], tbl[4];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     tb[0][e] = (__bf16)t[0][e];
     tb[1][e] = (__bf16)t[0][8 + e];
     tb[2][e] = (__bf16)t[1][e];
     tb[3][e] = (__bf16)t[1][8 + e];
+    if constexpr (SPLIT) {
+      tbl[0][e] = (__bf16)(t[0][e] - (float)tb[0][e]);
+      tbl[1][e] = (__bf16)(t[0][8 + e] - (float)tb[1][e]);
+      tbl[2][e] = (__bf16)(t[1][e] - (float)tb[2][e]);
+      tbl[3][e] = (__bf16)(t[1][8 + e] - (float)tb[3][e]);
+    }
   }
   const int ksteps = (re + 15) / 16;
 #pragma unroll
@@ -604,11 +639,13 @@ __device__ __forceinline__ void fused_apply(const AttnArgs& A, int h, int kv, in
 #pragma unroll
     for (int s2 = 0; s2 < 4; ++s2) {
       if (s2 >= ksteps) break;
-      const bf16_t* br = Bt + (32 * db + l32) * BROW + 16 * s2 + 4 * hf;
-      const uint2 lo8 = *reinterpret_cast<const uint2*>(br);
-      const uint2 hi8 = *reinterpret_cast<const uint2*>(br + 8);
-      const uint4 bv = make_uint4(lo8.x, lo8.y, hi8.x, hi8.y);
-      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, bv), tb[s2], o[db], 0, 0, 0);
+      const bf16_t* br = Bt + (32 * db + l32) * F::BROW + 16 * s2 + 4 * hf;
+      const bf16x8_t bv = staged8(br);
+      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv, tb[s2], o[db], 0, 0, 0);
+      if constexpr (SPLIT) {
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(staged8(br + F::PART / 2), tb[s2], o[db], 0, 0, 0);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv, tbl[s2], o[db], 0, 0, 0);
+      }
     }
   }
   if (qvalid) {
@@ -637,7 +674,7 @@ __device__ __forceinline__ void fused_writeback(const AttnArgs& A, int kv, int v
 
 constexpr int kAttnWaves = 8;    // waves per block of the main attention kernel
 constexpr int kAttnStages = 4;   // K/V tile stages in LDS; tile j + 2 is copied while tile j runs
-constexpr int kMatLookahead = 6; // LDS operand reads in flight ahead of the matrix products
+constexpr int kMatLookahead = 5; // LDS operand reads in flight ahead of the matrix products (d = 64)
 
 // Waits until at most `later` tiles' copies of this wave are still in flight (each tile is
 // C::KIPW + C::VIPW direct-to-LDS loads, which complete in order for the counter).
@@ -652,7 +689,7 @@ __device__ __forceinline__ void wait_tiles_in_flight(int later) {
   else __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
-template <int D, int BN, typename OutT, int PP>
+template <int D, int BN, typename OutT>
 __global__ __launch_bounds__(64 * kAttnWaves, 1) void attn_mfma_kernel(AttnArgs A) {
   using C = MfmaCfg<D, BN, kAttnWaves>;
   constexpr int PER_TILE = C::KIPW + C::VIPW;
@@ -681,7 +718,6 @@ __global__ __launch_bounds__(64 * kAttnWaves, 1) void attn_mfma_kernel(AttnArgs 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
   const int wu = wave_uniform(w);
-  const CopyPlan<D, BN, kAttnWaves> cp(wu, lane, A.v_np);
   const bf16_t* qb = static_cast<const bf16_t*>(A.q);
   const bf16_t* kb = static_cast<const bf16_t*>(A.k) + (int64_t)kv * A.kv_skv;
   const bf16_t* vtb = static_cast<const bf16_t*>(A.v) + (int64_t)kv * A.v_skv;
@@ -708,128 +744,88 @@ __global__ __launch_bounds__(64 * kAttnWaves, 1) void attn_mfma_kernel(AttnArgs 
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
 
-  // Tile iterators: (ci, k0, k1, kt) is the tile being computed; (fci, fk0, fk1, fkt) the
-  // copy frontier, kAttnStages - 2 tiles ahead.  Tile j lives in stage j % kAttnStages.
-  // The block meets at a barrier after every second tile (odd j) and after the last one:
-  // a wave working on tile j has then passed the barrier after tile j - 1 or j - 2, so
-  // every wave is done with tile j - 2, whose stage the copy of tile j + 2 reuses; and
-  // before the barrier after an odd tile j each wave waits for its copies of tiles j + 1
-  // and j + 2, the two tiles computed before the next barrier.  The barrier is a bare
-  // s_barrier after the counted waits: the workgroup fence of __syncthreads() would also
-  // drain the copies still in flight.
+  // Tile iterators: (ci, k0, k1, kt) is the tile being computed, (fci, fk0, fk1, fkt) the
+  // copy frontier two tiles ahead; tile j lives in stage j % kAttnStages.
   int ci = ti.kbeg < 0 ? 0 : ti.kbeg, k0 = 0, k1 = 0, kt = 0;
   bool valid = next_run(A, kv, ti, ci, k0, k1);
   if (valid) kt = k0 & ~15;
   int fci = ci, fk0 = k0, fk1 = k1, fkt = kt;
   bool fvalid = valid;
-  if constexpr (PP) {
-    // Anti-phased schedule: waves 0-3 and 4-7 (one of each per SIMD) alternate between a
-    // matrix phase (S_j = K_j Q^T and O += V_{j-1} P_{j-1}) and a softmax phase (S_j ->
-    // P_j), waves 4-7 one phase behind, with a block barrier between phases, so that one
-    // wave of every SIMD issues matrix products while the other runs its exponentials.
-    // Phases t = 0, 1, ...: waves 0-3 run the matrix part of tile j in phase 2j and its
-    // softmax in 2j + 1; waves 4-7 in 2j + 1 and 2j + 2.  K_j is read in phases 2j and
-    // 2j + 1, V_j in 2j + 2 and 2j + 3.  Waves 0-3 alone copy the tiles, during their
-    // softmax phases (which read no LDS, so the copies never hold up a matrix phase's
-    // operand reads): tile j + 2 in phase 2j + 1, into the stage of tile j - 2 (free
-    // after phase 2j - 1), and each waits for its copies of tile j + 1 before the
-    // barrier that ends phase 2j + 1.
-    constexpr int CW = kAttnWaves / 2;   // copying waves
-    using CC = MfmaCfg<D, BN, CW>;
-    constexpr int PT = CC::KIPW + CC::VIPW;
-    const bool lag = wu >= CW;
-    const CopyPlan<D, BN, CW> cpa(wu & (CW - 1), lane, A.v_np);
-    int ncopied = 0;
-    for (int i = 0; i < 2 && fvalid; ++i) {
-      if (!lag) stage_copy<D, BN, CW>(cpa, kb, vtb, A.n, A.v_np, fkt, stages[i], wu);
-      ++ncopied;
-      fvalid = next_tile(A, kv, ti, C::BN, fci, fk0, fk1, fkt);
-    }
-    if (!lag) wait_tiles_in_flight<PT>(ncopied - 1);   // tile 0 has landed
-    __syncthreads();
-    if (lag) asm volatile("s_barrier" ::: "memory");   // waves 4-7 sit out phase 0
-    f32x16_t sv[C::NB];
-    PackP pp[C::NB][2];
-#pragma unroll
-    for (int kb = 0; kb < C::NB; ++kb)
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pp[kb][s2].v[e] = (__bf16)0.f;
-    // per-lane LDS byte offsets of the matrix phase's operand reads within a stage (d = 128)
-    uint32_t koffs[8], voffs[4];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) koffs[i] = (uint32_t)(l32 * 256 + (((2 * i + hf) ^ (l32 & 15)) << 4));
-#pragma unroll
-    for (int i = 0; i < 4; ++i) voffs[i] = (uint32_t)(l32 * 128 + (((2 * i + hf) ^ ((l32 >> 1) & 7)) << 4));
-    int cur = 0, prev = 0, fst = 2;
-    bool have_prev = false;
-    while (valid) {
-      const int lo = max(k0 - kt, 0), hi = min(k1 - kt, BN);
-      if (wave_rows) {   // matrix phase (the first one multiplies tile 0's V by zero probabilities)
-        if constexpr (D == 128 && BN == 64 && PP == 5) {
-          const uint32_t kst = lds_addr(stages[cur]), vst = lds_addr(stages[prev]);
-          uint32_t kaddr[8], vaddr[4];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) kaddr[i] = kst + koffs[i];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) vaddr[i] = vst + voffs[i];
-          matrix_phase_d128(kaddr, vaddr, qreg, pp, o, sv);
-        } else {
-          matrix_phase<D, BN, (PP > 0 ? PP : 4)>(stages[cur], stages[prev], qreg, pp, o, sv, l32, hf);
-        }
-      }
-      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      bool issued = false;
-      if (fvalid) {
-        if (!lag) stage_copy<D, BN, CW>(cpa, kb, vtb, A.n, A.v_np, fkt, stages[fst], wu);
-        issued = true;
-        fst = fst == kAttnStages - 1 ? 0 : fst + 1;
-        fvalid = next_tile(A, kv, ti, C::BN, fci, fk0, fk1, fkt);
-      }
-      if (wave_rows)     // softmax phase
-        softmax_step<D, BN, false>(sv, lo, hi, c2, nullptr, 0ull, m_i, l_i, o, pp, hf);
-      have_prev = true;
-      prev = cur;
-      cur = cur == kAttnStages - 1 ? 0 : cur + 1;
-      valid = next_tile(A, kv, ti, C::BN, ci, k0, k1, kt);
-      if (!lag) wait_tiles_in_flight<PT>(issued ? 1 : 0);   // tile j + 1 has landed
-      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    }
-    if (wave_rows && have_prev) pv_mfma<D, BN>(stages[prev], pp, o, l32, hf);
-    if (!lag) asm volatile("s_barrier" ::: "memory");   // matches the lagging waves' first barrier
-  } else {
-  int nfront = 0;           // copied tiles not yet computed
-  int fst = 0;              // stage of the frontier tile
-  for (int i = 0; i < kAttnStages - 2 && fvalid; ++i) {
-    stage_copy<D, BN, kAttnWaves>(cp, kb, vtb, A.n, A.v_np, fkt, stages[fst], wu);
-    ++nfront;
-    fst = fst == kAttnStages - 1 ? 0 : fst + 1;
+  // Anti-phased schedule: waves 0-3 and 4-7 (one of each per SIMD) alternate between a
+  // matrix phase (S_j = K_j Q^T and O += V_{j-1} P_{j-1}) and a softmax phase (S_j ->
+  // P_j), waves 4-7 one phase behind, with a block barrier between phases, so that one
+  // wave of every SIMD issues matrix products while the other runs its exponentials.
+  // Phases t = 0, 1, ...: waves 0-3 run the matrix part of tile j in phase 2j and its
+  // softmax in 2j + 1; waves 4-7 in 2j + 1 and 2j + 2.  K_j is read in phases 2j and
+  // 2j + 1, V_j in 2j + 2 and 2j + 3.  Waves 0-3 alone copy the tiles, during their
+  // softmax phases (which read no LDS, so the copies never hold up a matrix phase's
+  // operand reads): tile j + 2 in phase 2j + 1, into the stage of tile j - 2 (free
+  // after phase 2j - 1), and each waits for its copies of tile j + 1 before the
+  // barrier that ends phase 2j + 1.
+  constexpr int CW = kAttnWaves / 2;   // copying waves
+  using CC = MfmaCfg<D, BN, CW>;
+  constexpr int PT = CC::KIPW + CC::VIPW;
+  const bool lag = wu >= CW;
+  const CopyPlan<D, BN, CW> cpa(wu & (CW - 1), lane, A.v_np);
+  int ncopied = 0;
+  for (int i = 0; i < 2 && fvalid; ++i) {
+    if (!lag) stage_copy<D, BN, CW>(cpa, kb, vtb, A.n, A.v_np, fkt, stages[i], wu);
+    ++ncopied;
     fvalid = next_tile(A, kv, ti, C::BN, fci, fk0, fk1, fkt);
   }
-  wait_tiles_in_flight<PER_TILE>(nfront - 2);   // tiles 0 and 1 have landed
+  if (!lag) wait_tiles_in_flight<PT>(ncopied - 1);   // tile 0 has landed
   __syncthreads();
-  int cur = 0, j = 0;
+  if (lag) asm volatile("s_barrier" ::: "memory");   // waves 4-7 sit out phase 0
+  f32x16_t sv[C::NB];
+  PackP pp[C::NB][2];
+#pragma unroll
+  for (int kb = 0; kb < C::NB; ++kb)
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pp[kb][s2].v[e] = (__bf16)0.f;
+  // per-lane LDS byte offsets of the matrix phase's operand reads within a stage (d = 128)
+  uint32_t koffs[8], voffs[4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) koffs[i] = (uint32_t)(l32 * 256 + (((2 * i + hf) ^ (l32 & 15)) << 4));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) voffs[i] = (uint32_t)(l32 * 128 + (((2 * i + hf) ^ ((l32 >> 1) & 7)) << 4));
+  int cur = 0, prev = 0, fst = 2;
+  bool have_prev = false;
   while (valid) {
+    const int lo = max(k0 - kt, 0), hi = min(k1 - kt, BN);
+    if (wave_rows) {   // matrix phase (the first one multiplies tile 0's V by zero probabilities)
+      if constexpr (D == 128 && BN == 64) {
+        const uint32_t kst = lds_addr(stages[cur]), vst = lds_addr(stages[prev]);
+        uint32_t kaddr[8], vaddr[4];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) kaddr[i] = kst + koffs[i];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) vaddr[i] = vst + voffs[i];
+        matrix_phase_d128(kaddr, vaddr, qreg, pp, o, sv);
+      } else {
+        matrix_phase<D, BN, kMatLookahead>(stages[cur], stages[prev], qreg, pp, o, sv, l32, hf);
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    bool issued = false;
     if (fvalid) {
-      stage_copy<D, BN, kAttnWaves>(cp, kb, vtb, A.n, A.v_np, fkt, stages[fst], wu);
-      ++nfront;
+      if (!lag) stage_copy<D, BN, CW>(cpa, kb, vtb, A.n, A.v_np, fkt, stages[fst], wu);
+      issued = true;
       fst = fst == kAttnStages - 1 ? 0 : fst + 1;
       fvalid = next_tile(A, kv, ti, C::BN, fci, fk0, fk1, fkt);
     }
-    const int lo = max(k0 - kt, 0), hi = min(k1 - kt, BN);
-    if (wave_rows)   // a wave whose rows all lie past the tile's end only keeps the copies and barriers
-      mfma_tile_step<D, BN, false>(stages[cur], qreg, lo, hi, c2, nullptr, 0ull, m_i, l_i, o, l32, hf);
-    --nfront;
-    valid = next_tile(A, kv, ti, C::BN, ci, k0, k1, kt);
-    if ((j & 1) || !valid) {
-      wait_tiles_in_flight<PER_TILE>(nfront - 2);   // tiles j + 1 and j + 2 have landed
-      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    }
-    ++j;
+    if (wave_rows)     // softmax phase
+      softmax_step<D, BN, false>(sv, lo, hi, c2, nullptr, 0ull, m_i, l_i, o, pp, hf);
+    have_prev = true;
+    prev = cur;
     cur = cur == kAttnStages - 1 ? 0 : cur + 1;
+    valid = next_tile(A, kv, ti, C::BN, ci, k0, k1, kt);
+    if (!lag) wait_tiles_in_flight<PT>(issued ? 1 : 0);   // tile j + 1 has landed
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   }
-  }
+  if (wave_rows && have_prev) pv_mfma<D, BN>(stages[prev], pp, o, l32, hf);
+  if (!lag) asm volatile("s_barrier" ::: "memory");   // matches the lagging waves' first barrier
 
   const float l_tot = add_xor32(l_i);
   const float inv = 1.f / l_tot;
@@ -871,14 +867,14 @@ __global__ __launch_bounds__(64 * kAttnWaves, 1) void attn_mfma_kernel(AttnArgs 
 // 256 (4 waves x 32 rows per tile); one staging of the correction per block.
 constexpr int kApplyTiles = 4;
 
-template <int D>
+template <int D, bool SPLIT>
 __global__ __launch_bounds__(256) void apply_mfma_kernel(AttnArgs A, const float* __restrict__ o_gm) {
-  constexpr int LDS = (kMaxCorrRank * (D + 8) + D * (kMaxCorrRank + 4)) * 2 + D * 4;
+  constexpr int LDS = FusedLds<D, SPLIT>::BYTES;
   __shared__ __attribute__((aligned(16))) char lds[LDS];
   const int h = blockIdx.y, kv = h / A.g, j = h % A.g;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
-  fused_stage<D, LDS, 256>(A, h, lds, tid);
+  fused_stage<D, LDS, 256, SPLIT>(A, h, lds, tid);
   // the staged A^T, B^T and c0 serve kApplyTiles tiles of 128 rows
   for (int it = 0; it < kApplyTiles; ++it) {
     const int p0 = (blockIdx.x * kApplyTiles + it) * 128;
@@ -898,7 +894,7 @@ __global__ __launch_bounds__(256) void apply_mfma_kernel(AttnArgs A, const float
         o[db][4 * jj + 2] = v.z;
         o[db][4 * jj + 3] = v.w;
       }
-    fused_apply<D>(A, h, kv, p, valid, 1.f, o, lds, l32, hf);
+    fused_apply<D, SPLIT>(A, h, kv, p, valid, 1.f, o, lds, l32, hf);
   }
 }
 
@@ -915,8 +911,17 @@ void launch_apply_mfma(const Dims& dm, const float* o_gm, const sparsepr_partiti
   a.qperm = part.query_perm;
   a.out_tok = o;
   const dim3 grid((unsigned)ceil_div(dm.n, 128 * kApplyTiles), dm.hq);
-  if (dm.d == 128) hipLaunchKernelGGL(apply_mfma_kernel<128>, grid, dim3(256), 0, s, a, o_gm);
-  else hipLaunchKernelGGL(apply_mfma_kernel<64>, grid, dim3(256), 0, s, a, o_gm);
+  // the split operands where the correction may grow as large as the output: grouped query
+  // heads and the unprojected ridge (one query head per KV head with the projected fit keeps
+  // the fused epilogue's single bf16 products)
+  const bool split = dm.g > 1 || dm.rc > kMaxRank;
+  if (dm.d == 128) {
+    if (split) hipLaunchKernelGGL((apply_mfma_kernel<128, true>), grid, dim3(256), 0, s, a, o_gm);
+    else hipLaunchKernelGGL((apply_mfma_kernel<128, false>), grid, dim3(256), 0, s, a, o_gm);
+  } else {
+    if (split) hipLaunchKernelGGL((apply_mfma_kernel<64, true>), grid, dim3(256), 0, s, a, o_gm);
+    else hipLaunchKernelGGL((apply_mfma_kernel<64, false>), grid, dim3(256), 0, s, a, o_gm);
+  }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1117,11 +1122,7 @@ void launch_mfma_typed(AttnArgs a, int hkv, hipStream_t s) {
   a.n_heads_kv = hkv;
   int64_t total = (int64_t)a.tiles_per_head * hkv;
   total = ceil_div(total, kXcds) * kXcds;
-  static const int pp = getenv("SPARSEPR_ATTN_PP") == nullptr ? 5 : atoi(getenv("SPARSEPR_ATTN_PP"));
-  if (pp == 4) hipLaunchKernelGGL((attn_mfma_kernel<D, kAttnBN, OutT, 4>), dim3((unsigned)total), dim3(64 * kAttnWaves), 0, s, a);
-  else if (pp == 6) hipLaunchKernelGGL((attn_mfma_kernel<D, kAttnBN, OutT, 6>), dim3((unsigned)total), dim3(64 * kAttnWaves), 0, s, a);
-  else if (pp == 5) hipLaunchKernelGGL((attn_mfma_kernel<D, kAttnBN, OutT, 5>), dim3((unsigned)total), dim3(64 * kAttnWaves), 0, s, a);
-  else hipLaunchKernelGGL((attn_mfma_kernel<D, kAttnBN, OutT, 0>), dim3((unsigned)total), dim3(64 * kAttnWaves), 0, s, a);
+  hipLaunchKernelGGL((attn_mfma_kernel<D, kAttnBN, OutT>), dim3((unsigned)total), dim3(64 * kAttnWaves), 0, s, a);
 }
 
 void launch_attention_mfma(const Dims& dm, AttnArgs a, bool out_is_input_dtype, hipStream_t s) {
