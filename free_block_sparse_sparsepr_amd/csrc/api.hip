@@ -56,7 +56,7 @@ Workspace plan_workspace(const sparsepr_params& p) {
   o = 0;
   w.probe_alloc = o; o = align_up(o + hkv * n * 4);
   w.partials = o; o = align_up(o + hq * w.nchunks * p.n_probe * 2 * (p.d + 2) * 4);
-  w.fitbuf = o; o = align_up(o + hq * (3 * kMaxProbe * p.d + p.d * kMaxRank) * 8);
+  w.fitbuf = o; o = align_up(o + hq * (size_t)FitBuf::per_head(p.d) * 8);
   w.total_probe = o;
   w.dense_meta = 0;
   w.total_dense = align_up(hkv * (size_t)p.d * (size_t)vt_pad(p.n) * (p.dtype == SPARSEPR_BF16 ? 2 : 4));

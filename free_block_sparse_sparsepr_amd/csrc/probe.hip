@@ -350,123 +350,112 @@ __global__ __launch_bounds__(D) void probe_merge_kernel(const float* __restrict_
   }
   o_dense[((int64_t)h * M + r) * D + c] = (float)res[0];
   o_sparse[((int64_t)h * M + r) * D + c] = (float)res[1];
-  double* X = fbuf + (size_t)h * (3 * kMaxProbe * D + D * kMaxRank);
-  X[r * D + c] = res[1];
-  X[kMaxProbe * D + r * D + c] = res[0] - res[1];
+  double* fb = fbuf + (size_t)h * FitBuf::per_head(D);
+  fb[FitBuf::x(D) + r * D + c] = res[1];
+  fb[FitBuf::y(D) + r * D + c] = res[0] - res[1];
 }
 
-// ridge_only: write the unprojected ridge map as A = Xt^T [d, M], B = Z [M, d] (leading
-// dimension M) and skip the subspace (PSRR, ablation paragraph).
+// The fit of each query head in float64, as three kernels.
+//
+// fit_gram_kernel, grid (4, Hq), block 256: blocks 0-1 stage X = O_sparse of the probe
+// rows in LDS, form the weighted mean xbar and Xt = sqrt(w) (X - xbar) and each compute 32
+// rows of the dual matrix K = Xt Xt^T + lambda I; blocks 2-3 do the same for the residuals
+// Y (ybar, Yt) and the Gram matrix G = Yt Yt^T (zero-padded to 64 x 64).  Blocks 0 and 2
+// also store Xt, xbar and Yt, ybar.
 template <int D>
-__global__ __launch_bounds__(256) void probe_fit_kernel(const float* __restrict__ partials, int nch,
-                                                        const double* __restrict__ pw, int g, int M,
-                                                        int rank, int ridge_only, double lam,
-                                                        double* __restrict__ fbuf,
-                                                        float* __restrict__ o_dense,
-                                                        float* __restrict__ o_sparse, float* __restrict__ Aout,
-                                                        float* __restrict__ Bout, float* __restrict__ c0out,
-                                                        int32_t* __restrict__ r_eff_out,
-                                                        float* __restrict__ eig_out) {
+__global__ __launch_bounds__(256) void fit_gram_kernel(const double* __restrict__ pw, int g, int M, double lam,
+                                                       double* __restrict__ fbuf) {
   constexpr int MM = kMaxProbe;
-  __shared__ double Km[MM][MM + 1];
-  __shared__ double Vm[MM][MM + 1];
-  __shared__ double w[MM], xbar[D], ybar[D], rc[32], rs[32], ev[MM], xa[kMaxRank], red[256];
-  __shared__ int pp[32], qq[32], ord[MM];
-  __shared__ int reff_s;
-  __shared__ int stop_s;
-  const int h = blockIdx.x, kv = h / g, tid = threadIdx.x;
-  double* X = fbuf + (size_t)h * (3 * MM * D + D * kMaxRank);
-  double* Y = X + MM * D;
-  double* Z = Y + MM * D;
-  double* Vr = Z + MM * D;
-  if (tid < M) w[tid] = pw[kv * M + tid];
+  __shared__ double S[MM][D + 1];
+  __shared__ double w[MM], mean[D];
+  const int h = blockIdx.y, kv = h / g, part = blockIdx.x, tid = threadIdx.x;
+  const bool isK = part < 2;
+  double* fb = fbuf + (size_t)h * FitBuf::per_head(D);
+  const double* src = fb + (isK ? FitBuf::x(D) : FitBuf::y(D));
+  if (tid < MM) w[tid] = tid < M ? pw[kv * M + tid] : 0.0;
   __syncthreads();
-  // 2. weighted centring and sqrt(w) scaling
   double sw = 0.0;
   for (int r = 0; r < M; ++r) sw += w[r];
   for (int c = tid; c < D; c += 256) {
-    double sx = 0.0, sy = 0.0;
-    for (int r = 0; r < M; ++r) { sx += w[r] * X[r * D + c]; sy += w[r] * Y[r * D + c]; }
-    xbar[c] = sx / sw;
-    ybar[c] = sy / sw;
+    double sx = 0.0;
+    for (int r = 0; r < M; ++r) sx += w[r] * src[r * D + c];
+    mean[c] = sx / sw;
   }
   __syncthreads();
-  for (int idx = tid; idx < M * D; idx += 256) {
+  for (int idx = tid; idx < MM * D; idx += 256) {
     const int r = idx / D, c = idx % D;
-    const double sq = sqrt(w[r]);
-    X[idx] = sq * (X[idx] - xbar[c]);
-    Y[idx] = sq * (Y[idx] - ybar[c]);
+    S[r][c] = r < M ? sqrt(w[r]) * (src[idx] - mean[c]) : 0.0;
   }
   __syncthreads();
-  // 3. K = Xt Xt^T + lambda I
-  for (int idx = tid; idx < M * M; idx += 256) {
-    const int i = idx / M, j = idx % M;
-    double s = 0.0;
-    for (int c = 0; c < D; ++c) s += X[i * D + c] * X[j * D + c];
-    Km[i][j] = s + (i == j ? lam : 0.0);
+  if ((part & 1) == 0) {
+    double* dst = fb + (isK ? FitBuf::xt(D) : FitBuf::yt(D));
+    for (int idx = tid; idx < M * D; idx += 256) dst[idx] = S[idx / D][idx % D];
+    for (int c = tid; c < D; c += 256) fb[(isK ? FitBuf::xbar(D) : FitBuf::ybar(D)) + c] = mean[c];
   }
-  __syncthreads();
-  // 4. Cholesky K = L L^T (lower triangle of Km)
-  for (int k = 0; k < M; ++k) {
-    if (tid == 0) Km[k][k] = sqrt(Km[k][k]);
-    __syncthreads();
-    for (int i = k + 1 + tid; i < M; i += 256) Km[i][k] /= Km[k][k];
-    __syncthreads();
-    const int rem = M - k - 1;
-    for (int idx = tid; idx < rem * rem; idx += 256) {
-      const int i = k + 1 + idx / rem, j = k + 1 + idx % rem;
-      if (j <= i) Km[i][j] -= Km[i][k] * Km[j][k];
-    }
-    __syncthreads();
+  double* out = fb + (isK ? FitBuf::k(D) : FitBuf::g(D));
+  const int r0 = 32 * (part & 1);
+  for (int idx = tid; idx < 32 * MM; idx += 256) {
+    const int i = r0 + idx / MM, j = idx % MM;
+    double v = 0.0;
+    if (i < M && j < M)
+      for (int c = 0; c < D; ++c) v += S[i][c] * S[j][c];
+    if (isK && i == j) v += lam;
+    out[i * MM + j] = v;
   }
-  // 5. Z = K^{-1} Yt, one thread per column
-  for (int c = tid; c < D; c += 256) {
-    for (int i = 0; i < M; ++i) {
-      double s = Y[i * D + c];
-      for (int k = 0; k < i; ++k) s -= Km[i][k] * Z[k * D + c];
-      Z[i * D + c] = s / Km[i][i];
-    }
-    for (int i = M - 1; i >= 0; --i) {
-      double s = Z[i * D + c];
-      for (int k = i + 1; k < M; ++k) s -= Km[k][i] * Z[k * D + c];
-      Z[i * D + c] = s / Km[i][i];
-    }
-  }
-  __syncthreads();
-  if (ridge_only) {
-    // xa[k] = xbar . Xt[k]; c0 = ybar - xa Z; A = Xt^T, B = Z (leading dimension M)
-    double* xam = &Vm[0][0];
-    for (int k = tid; k < M; k += 256) {
-      double acc = 0.0;
-      for (int c = 0; c < D; ++c) acc += xbar[c] * X[k * D + c];
-      xam[k] = acc;
-    }
+}
+
+// fit_factor_kernel, grid (2, Hq), block 256: block 0 factors K = L L^T (Cholesky, lower
+// triangle in place); block 1 diagonalises G by parallel cyclic Jacobi (round-robin
+// pairing: 32 disjoint rotations per step), orders the eigenvalues (descending, ties by
+// index), keeps those above 1e-8 of the largest (at most rank) and stores them with their
+// eigenvectors a.  With ridge_only (the unprojected ridge) block 1 writes r_eff = M and
+// zero eigenvalues.
+template <int D>
+__global__ __launch_bounds__(256) void fit_factor_kernel(int M, int rank, int ridge_only, double* __restrict__ fbuf,
+                                                         int32_t* __restrict__ r_eff_out,
+                                                         float* __restrict__ eig_out) {
+  constexpr int MM = kMaxProbe;
+  __shared__ double Km[MM][MM + 1];
+  __shared__ double Vm[MM][MM + 1];
+  __shared__ double rc[32], rs[32], ev[MM], red[256];
+  __shared__ int pp[32], qq[32], ord[MM];
+  __shared__ int stop_s;
+  const int h = blockIdx.y, tid = threadIdx.x;
+  double* fb = fbuf + (size_t)h * FitBuf::per_head(D);
+  if (blockIdx.x == 0) {
+    double* K = fb + FitBuf::k(D);
+    for (int idx = tid; idx < MM * MM; idx += 256) Km[idx / MM][idx % MM] = K[idx];
     __syncthreads();
-    for (int idx = tid; idx < D * M; idx += 256) {
-      const int c = idx / M, k = idx % M;
-      Aout[(int64_t)h * D * M + idx] = (float)X[k * D + c];
-      Bout[(int64_t)h * M * D + (int64_t)k * D + c] = (float)Z[k * D + c];
+    for (int k = 0; k < M; ++k) {
+      if (tid == 0) Km[k][k] = sqrt(Km[k][k]);
+      __syncthreads();
+      for (int i = k + 1 + tid; i < M; i += 256) Km[i][k] /= Km[k][k];
+      __syncthreads();
+      const int rem = M - k - 1;
+      for (int idx = tid; idx < rem * rem; idx += 256) {
+        const int i = k + 1 + idx / rem, j = k + 1 + idx % rem;
+        if (j <= i) Km[i][j] -= Km[i][k] * Km[j][k];
+      }
+      __syncthreads();
     }
-    for (int c = tid; c < D; c += 256) {
-      double acc = ybar[c];
-      for (int k = 0; k < M; ++k) acc -= xam[k] * Z[k * D + c];
-      c0out[(int64_t)h * D + c] = (float)acc;
-    }
-    for (int k = tid; k <= rank; k += 256) eig_out[(int64_t)h * (rank + 1) + k] = 0.f;
-    if (tid == 0) r_eff_out[h] = M;
+    for (int idx = tid; idx < MM * MM; idx += 256) K[idx] = Km[idx / MM][idx % MM];
     return;
   }
-  // 6. G = Yt Yt^T (zero-padded to 64 x 64), V = I
+  if (ridge_only) {
+    for (int k = tid; k <= rank; k += 256) eig_out[(int64_t)h * (rank + 1) + k] = 0.f;
+    if (tid == 0) {
+      r_eff_out[h] = M;
+      fb[FitBuf::reff(D)] = (double)M;
+    }
+    return;
+  }
+  const double* G = fb + FitBuf::g(D);
   for (int idx = tid; idx < MM * MM; idx += 256) {
     const int i = idx / MM, j = idx % MM;
-    double s = 0.0;
-    if (i < M && j < M)
-      for (int c = 0; c < D; ++c) s += Y[i * D + c] * Y[j * D + c];
-    Km[i][j] = s;
+    Km[i][j] = G[idx];
     Vm[i][j] = (i == j) ? 1.0 : 0.0;
   }
   __syncthreads();
-  // 7. parallel cyclic Jacobi (round-robin pairing: 32 disjoint rotations per step)
   for (int sweep = 0; sweep < 30; ++sweep) {
     double off = 0.0, dg = 0.0;
     for (int idx = tid; idx < MM * MM; idx += 256) {
@@ -524,7 +513,6 @@ __global__ __launch_bounds__(256) void probe_fit_kernel(const float* __restrict_
       __syncthreads();
     }
   }
-  // 8. order the eigenvalues (descending, ties by index) and choose r_eff
   if (tid < MM) ev[tid] = Km[tid][tid];
   __syncthreads();
   if (tid < MM) {
@@ -538,58 +526,126 @@ __global__ __launch_bounds__(256) void probe_fit_kernel(const float* __restrict_
     int re = 0;
     for (int k = 0; k < rank && k < M; ++k)
       if (l1 > 0.0 && ev[ord[k]] > 1e-8 * l1) ++re; else break;
-    reff_s = re;
     r_eff_out[h] = re;
+    fb[FitBuf::reff(D)] = (double)re;
   }
   for (int k = tid; k <= rank; k += 256) eig_out[(int64_t)h * (rank + 1) + k] = k < MM ? (float)ev[ord[k]] : 0.f;
+  for (int idx = tid; idx < MM * kMaxRank; idx += 256) {
+    const int i = idx / kMaxRank, k = idx % kMaxRank;
+    fb[FitBuf::a(D) + idx] = Vm[i][ord[k]];
+  }
+  for (int k = tid; k < MM; k += 256) fb[FitBuf::ev(D) + k] = ev[ord[k]];
+}
+
+// fit_solve_kernel, grid Hq, block 256: Z = K^{-1} Yt by forward and back substitution
+// with L and Z resident in LDS (one thread per output column), then either the
+// unprojected ridge (A = Xt^T, B = Z, c0 = ybar - (xbar Xt^T) Z) or the projected fit:
+// V_r[:, k] = Yt^T a_k / sqrt(lambda_k), A = Xt^T (Z V_r), B = V_r^T, c0 = ybar - (xbar A) B.
+template <int D>
+__global__ __launch_bounds__(256) void fit_solve_kernel(int M, int rank, int ridge_only,
+                                                        const double* __restrict__ fbuf, float* __restrict__ Aout,
+                                                        float* __restrict__ Bout, float* __restrict__ c0out) {
+  constexpr int MM = kMaxProbe;
+  __shared__ double La[MM][MM + 1];         // L, then a, then Z V_r
+  __shared__ double Zs[MM * D];             // Z, then A
+  __shared__ double Vr[D][kMaxRank + 1];
+  __shared__ double xa[MM];
+  const int h = blockIdx.x, tid = threadIdx.x;
+  const double* fb = fbuf + (size_t)h * FitBuf::per_head(D);
+  const double* Xt = fb + FitBuf::xt(D);
+  const double* Yt = fb + FitBuf::yt(D);
+  const double* xbar = fb + FitBuf::xbar(D);
+  const double* ybar = fb + FitBuf::ybar(D);
+  for (int idx = tid; idx < MM * MM; idx += 256) La[idx / MM][idx % MM] = fb[FitBuf::k(D) + idx];
+  for (int idx = tid; idx < M * D; idx += 256) Zs[idx] = Yt[idx];
   __syncthreads();
-  const int re = reff_s;
-  // 9. V_r[:, k] = Yt^T a_k / sqrt(lambda_k)
-  for (int idx = tid; idx < D * kMaxRank; idx += 256) {
-    const int c = idx / kMaxRank, k = idx % kMaxRank;
-    double s = 0.0;
-    if (k < re) {
-      const int e = ord[k];
-      for (int i = 0; i < M; ++i) s += Y[i * D + c] * Vm[i][e];
-      s /= sqrt(ev[e]);
+  for (int c = tid; c < D; c += 256) {
+    for (int i = 0; i < M; ++i) {
+      double s = Zs[i * D + c];
+      for (int k = 0; k < i; ++k) s -= La[i][k] * Zs[k * D + c];
+      Zs[i * D + c] = s / La[i][i];
     }
-    Vr[c * kMaxRank + k] = s;
+    for (int i = M - 1; i >= 0; --i) {
+      double s = Zs[i * D + c];
+      for (int k = i + 1; k < M; ++k) s -= La[k][i] * Zs[k * D + c];
+      Zs[i * D + c] = s / La[i][i];
+    }
   }
   __syncthreads();
-  // 10. ZV = Z V_r (M x r) into Km
+  if (ridge_only) {
+    // xa[k] = xbar . Xt[k]; c0 = ybar - xa Z; A = Xt^T, B = Z (leading dimension M)
+    for (int k = tid; k < M; k += 256) {
+      double acc = 0.0;
+      for (int c = 0; c < D; ++c) acc += xbar[c] * Xt[k * D + c];
+      xa[k] = acc;
+    }
+    __syncthreads();
+    for (int idx = tid; idx < D * M; idx += 256) {
+      const int c = idx / M, k = idx % M;
+      Aout[(int64_t)h * D * M + idx] = (float)Xt[k * D + c];
+      Bout[(int64_t)h * M * D + (int64_t)k * D + c] = (float)Zs[k * D + c];
+    }
+    for (int c = tid; c < D; c += 256) {
+      double acc = ybar[c];
+      for (int k = 0; k < M; ++k) acc -= xa[k] * Zs[k * D + c];
+      c0out[(int64_t)h * D + c] = (float)acc;
+    }
+    return;
+  }
+  const int re = (int)fb[FitBuf::reff(D)];
+  for (int idx = tid; idx < MM * kMaxRank; idx += 256) La[idx / kMaxRank][idx % kMaxRank] = fb[FitBuf::a(D) + idx];
+  __syncthreads();
+  for (int c = tid; c < D; c += 256) {
+    double acc[kMaxRank];
+#pragma unroll
+    for (int k = 0; k < kMaxRank; ++k) acc[k] = 0.0;
+    for (int i = 0; i < M; ++i) {
+      const double y = Yt[i * D + c];
+#pragma unroll
+      for (int k = 0; k < kMaxRank; ++k) acc[k] += y * La[i][k];
+    }
+#pragma unroll
+    for (int k = 0; k < kMaxRank; ++k) Vr[c][k] = k < re ? acc[k] / sqrt(fb[FitBuf::ev(D) + k]) : 0.0;
+  }
+  __syncthreads();
+  // Z V_r (M x r) into La
   for (int idx = tid; idx < M * kMaxRank; idx += 256) {
     const int i = idx / kMaxRank, k = idx % kMaxRank;
     double s = 0.0;
     if (k < re)
-      for (int c = 0; c < D; ++c) s += Z[i * D + c] * Vr[c * kMaxRank + k];
-    Km[i][k] = s;
+      for (int c = 0; c < D; ++c) s += Zs[i * D + c] * Vr[c][k];
+    La[i][k] = s;
   }
   __syncthreads();
-  // 11. A = Xt^T ZV (D x r) into Vm rows (D <= 128 rows -> two halves of 64 columns)
-  double* Al = &Vm[0][0];  // D * kMaxRank doubles fit in Vm (64 * 65)
-  for (int idx = tid; idx < D * kMaxRank; idx += 256) {
-    const int c = idx / kMaxRank, k = idx % kMaxRank;
-    double s = 0.0;
-    if (k < re)
-      for (int i = 0; i < M; ++i) s += X[i * D + c] * Km[i][k];
-    Al[c * kMaxRank + k] = s;
+  // A = Xt^T (Z V_r) (D x r) into Zs
+  for (int c = tid; c < D; c += 256) {
+    double acc[kMaxRank];
+#pragma unroll
+    for (int k = 0; k < kMaxRank; ++k) acc[k] = 0.0;
+    for (int i = 0; i < M; ++i) {
+      const double x = Xt[i * D + c];
+#pragma unroll
+      for (int k = 0; k < kMaxRank; ++k) acc[k] += x * La[i][k];
+    }
+#pragma unroll
+    for (int k = 0; k < kMaxRank; ++k) Zs[c * kMaxRank + k] = k < re ? acc[k] : 0.0;
   }
   __syncthreads();
   for (int k = tid; k < kMaxRank; k += 256) {
     double s = 0.0;
-    for (int c = 0; c < D; ++c) s += xbar[c] * Al[c * kMaxRank + k];
+    for (int c = 0; c < D; ++c) s += xbar[c] * Zs[c * kMaxRank + k];
     xa[k] = s;
   }
   __syncthreads();
-  // 12. outputs: A [D][rank], B [rank][D], c0 = ybar - (xbar A) B
+  // outputs: A [D][rank], B [rank][D], c0 = ybar - (xbar A) B
   for (int idx = tid; idx < D * rank; idx += 256) {
     const int c = idx / rank, k = idx % rank;
-    Aout[(int64_t)h * D * rank + idx] = k < re ? (float)Al[c * kMaxRank + k] : 0.f;
-    Bout[(int64_t)h * rank * D + (int64_t)k * D + c] = k < re ? (float)Vr[c * kMaxRank + k] : 0.f;
+    Aout[(int64_t)h * D * rank + idx] = k < re ? (float)Zs[c * kMaxRank + k] : 0.f;
+    Bout[(int64_t)h * rank * D + (int64_t)k * D + c] = k < re ? (float)Vr[c][k] : 0.f;
   }
   for (int c = tid; c < D; c += 256) {
     double s = ybar[c];
-    for (int k = 0; k < re; ++k) s -= xa[k] * Vr[c * kMaxRank + k];
+    for (int k = 0; k < re; ++k) s -= xa[k] * Vr[c][k];
     c0out[(int64_t)h * D + c] = (float)s;
   }
 }
@@ -643,16 +699,22 @@ void launch_probe_fit(const Dims& dm, const Workspace& wp, const void* q, const 
   else
     hipLaunchKernelGGL(probe_merge_kernel<64>, dim3(dm.m, dm.hq), dim3(64), 0, s, partials, wp.nchunks, dm.m,
                        fbuf, out.o_dense, out.o_sparse);
-  if (dm.d == 128)
-    hipLaunchKernelGGL(probe_fit_kernel<128>, dim3(dm.hq), dim3(256), 0, s, partials, wp.nchunks,
-                       out.probe_weights, dm.g, dm.m, dm.r,
-                       dm.ablation == SPARSEPR_ABLATE_RIDGE_ONLY ? 1 : 0, (double)dm.lambda, fbuf, out.o_dense, out.o_sparse,
-                       out.A, out.B, out.c0, out.r_eff, out.eig);
-  else
-    hipLaunchKernelGGL(probe_fit_kernel<64>, dim3(dm.hq), dim3(256), 0, s, partials, wp.nchunks,
-                       out.probe_weights, dm.g, dm.m, dm.r,
-                       dm.ablation == SPARSEPR_ABLATE_RIDGE_ONLY ? 1 : 0, (double)dm.lambda, fbuf, out.o_dense, out.o_sparse,
-                       out.A, out.B, out.c0, out.r_eff, out.eig);
+  const int ridge = dm.ablation == SPARSEPR_ABLATE_RIDGE_ONLY ? 1 : 0;
+  if (dm.d == 128) {
+    hipLaunchKernelGGL(fit_gram_kernel<128>, dim3(4, dm.hq), dim3(256), 0, s, out.probe_weights, dm.g, dm.m,
+                       (double)dm.lambda, fbuf);
+    hipLaunchKernelGGL(fit_factor_kernel<128>, dim3(2, dm.hq), dim3(256), 0, s, dm.m, dm.r, ridge, fbuf, out.r_eff,
+                       out.eig);
+    hipLaunchKernelGGL(fit_solve_kernel<128>, dim3(dm.hq), dim3(256), 0, s, dm.m, dm.r, ridge, fbuf, out.A, out.B,
+                       out.c0);
+  } else {
+    hipLaunchKernelGGL(fit_gram_kernel<64>, dim3(4, dm.hq), dim3(256), 0, s, out.probe_weights, dm.g, dm.m,
+                       (double)dm.lambda, fbuf);
+    hipLaunchKernelGGL(fit_factor_kernel<64>, dim3(2, dm.hq), dim3(256), 0, s, dm.m, dm.r, ridge, fbuf, out.r_eff,
+                       out.eig);
+    hipLaunchKernelGGL(fit_solve_kernel<64>, dim3(dm.hq), dim3(256), 0, s, dm.m, dm.r, ridge, fbuf, out.A, out.B,
+                       out.c0);
+  }
 }
 
 }  // namespace sp

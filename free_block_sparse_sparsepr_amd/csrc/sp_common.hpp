@@ -23,6 +23,27 @@ constexpr int kGmChunk = 1024;      // tokens per chunk of the group-major count
 
 __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Per-query-head float64 scratch of the probe fit (probe_merge_kernel and the three fit
+// kernels), in doubles from the head's base: raw X = O_sparse and Y = O_dense - O_sparse
+// rows, their weighted centred and scaled copies Xt, Yt, the dual matrix K (Cholesky factor
+// in place) and the residual Gram matrix G, the ordered leading eigenvectors a and
+// eigenvalues ev of G, the weighted means xbar and ybar, and r_eff.
+struct FitBuf {
+  static constexpr int MM = kMaxProbe;
+  __host__ __device__ static int64_t x(int) { return 0; }
+  __host__ __device__ static int64_t y(int d) { return (int64_t)MM * d; }
+  __host__ __device__ static int64_t xt(int d) { return 2 * (int64_t)MM * d; }
+  __host__ __device__ static int64_t yt(int d) { return 3 * (int64_t)MM * d; }
+  __host__ __device__ static int64_t k(int d) { return 4 * (int64_t)MM * d; }
+  __host__ __device__ static int64_t g(int d) { return k(d) + MM * MM; }
+  __host__ __device__ static int64_t a(int d) { return g(d) + MM * MM; }
+  __host__ __device__ static int64_t ev(int d) { return a(d) + MM * kMaxRank; }
+  __host__ __device__ static int64_t xbar(int d) { return ev(d) + MM; }
+  __host__ __device__ static int64_t ybar(int d) { return xbar(d) + d; }
+  __host__ __device__ static int64_t reff(int d) { return ybar(d) + d; }
+  __host__ __device__ static int64_t per_head(int d) { return reff(d) + 8; }
+};
+
 // Group-major V is stored transposed (d-major) as [Hkv][d][n_pad], n_pad = n rounded up to
 // 16.  Within every 16-key group the keys are stored in the order 0-3, 8-11, 4-7, 12-15
 // (bits 2 and 3 of the position swapped), which is the order in which the matrix cores'

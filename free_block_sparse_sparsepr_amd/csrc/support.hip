@@ -8,8 +8,9 @@
 //  2. per row, the threshold key of its support by a four-pass radix select over the
 //     order-preserving 32-bit key of f, from the largest down, with each key weighted
 //     by its probability in 2^-40 fixed point relative to the row maximum, m =
-//     floor(2^40 exp(scale (f - max))), summed in 64-bit integers (LDS atomics; lanes of
-//     a wave that share a bin are summed first).  The target is ceil(mass * sum m).
+//     floor(2^40 exp((f - max) scale)) formed in double precision, summed in 64-bit
+//     integers (LDS atomics; lanes of a wave that share a bin are summed first).  The
+//     target is min(ceil(mass * sum m), sum m), at least 1, with sum m as a double.
 //     Keys above the threshold all belong to the support; of the keys equal to it, the
 //     lowest indices are taken until the target is met;
 //  3. the support count of each row and the size of the union over the set.
@@ -33,8 +34,10 @@ __device__ __forceinline__ uint32_t okey(float f) {
 __device__ __forceinline__ float from_okey(uint32_t u) {
   return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
 }
-__device__ __forceinline__ uint64_t mass_fixed(float f, float fmax, float c) {
-  return (uint64_t)(exp2f((f - fmax) * c) * 1099511627776.f);   // 2^40
+// floor(2^40 exp((f - fmax) scale)) from the fp32 scores in double precision (the
+// difference and the product are the double operations a float64 reference performs)
+__device__ __forceinline__ uint64_t mass_fixed(float f, float fmax, double scale) {
+  return (uint64_t)ldexp(exp(((double)f - (double)fmax) * scale), 40);
 }
 
 template <typename T>
@@ -94,7 +97,7 @@ __device__ __forceinline__ void hist_add(bool part, int b, uint64_t m, unsigned 
 template <typename T, int D>
 __global__ __launch_bounds__(kSupThreads) void support_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                               const int32_t* __restrict__ sets, int n, int hq, int g,
-                                                              int n_sets, int S, float c, double mass,
+                                                              int n_sets, int S, double c, double mass,
                                                               float* __restrict__ scratch, int32_t* __restrict__ row_out,
                                                               int32_t* __restrict__ union_out) {
   __shared__ __attribute__((aligned(16))) float qs[kSupportMaxSet][D];
@@ -315,7 +318,7 @@ void launch_support(const Dims& dm, const void* q, const void* k, const int32_t*
   const int64_t items = (int64_t)dm.hq * n_sets;
   if (items == 0) return;
   const int grid = (int)(items < kSupportSlots ? items : kSupportSlots);
-  const float c = dm.scale * 1.4426950408889634f;
+  const double c = (double)dm.scale;
   float* sc = static_cast<float*>(ws);
 #define SUP_LAUNCH(T, DD)                                                                                      \
   hipLaunchKernelGGL((support_kernel<T, DD>), dim3(grid), dim3(kSupThreads), 0, s, static_cast<const T*>(q), \

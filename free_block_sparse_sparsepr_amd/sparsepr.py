@@ -269,10 +269,12 @@ class SparsePR:
                                                        _p(out), _p(ws), ws.numel(), _stream()))
         return out
 
-    def support_diagnostics(self, q, k, sets, mass=0.9):
+    def support_diagnostics(self, q, k, sets, mass=0.9, with_scores=False):
         """90 %-mass supports: ``sets`` [Hq, n_sets, s] int32 query tokens (device).  Returns
         (row_support [Hq, n_sets, s], shared_support [Hq, n_sets]) int32 key counts; needs
-        only Q and K (allocates its own workspace for the call)."""
+        only Q and K (allocates its own workspace for the call).  With ``with_scores`` (at
+        most 512 items) also the fp32 scores the decisions were taken on, [Hq, n_sets, s, n],
+        read back from the workspace."""
         c = self.cfg
         if sets.dtype != torch.int32 or sets.dim() != 3 or sets.shape[0] != c.heads_q or not sets.is_contiguous():
             raise ValueError("sets must be a contiguous int32 tensor [heads_q, n_sets, set_size]")
@@ -287,6 +289,12 @@ class SparsePR:
         B.check(self.lib.sparsepr_support_diagnostics(ctypes.byref(self.prm), _p(q), _p(k), _p(sets), n_sets, s,
                                                       float(mass), _p(rows), _p(union), _p(ws), ws.numel(),
                                                       _stream()))
+        if with_scores:
+            if c.heads_q * n_sets > 512:
+                raise ValueError("scores are kept for at most 512 (head, set) items")
+            nsc = c.heads_q * n_sets * s * c.n
+            scores = ws[:nsc * 4].view(torch.float32).view(c.heads_q, n_sets, s, c.n)
+            return rows, union, scores
         return rows, union
 
     def dense(self, q, k, v, out=None):

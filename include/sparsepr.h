@@ -346,10 +346,13 @@ sparsepr_status sparsepr_residual_diagnostics(const sparsepr_params* params, con
  *          marks that row invalid: its row_support is -1 and it is left out of the union.
  *   row_support [Hq, n_sets, set_size], shared_support [Hq, n_sets]: int32 (device).
  *   1 <= set_size <= 16, n_sets >= 0 (0: nothing to do), 0 < mass <= 1.
- * Scores are fp32 dot products of the stored Q and K values; probabilities enter the
- * decision as floor(2^40 p / p_max) in 64-bit integers, so keys below 2^-40 of the row's
- * largest probability carry no mass.  The workspace (sparsepr_support_workspace_size)
- * holds set_size * n fp32 scores for each of up to 512 concurrent (head, set) items.
+ * Scores f are fp32 dot products of the stored Q and K values; each key's probability
+ * enters the decision as the 64-bit integer floor(2^40 exp((f - f_max) scale)), formed in
+ * double precision from the fp32 scores, so keys below 2^-40 of the row's largest
+ * probability carry no mass.  The workspace (sparsepr_support_workspace_size) holds
+ * set_size * n fp32 scores for each of up to 512 concurrent (head, set) items; when
+ * Hq * n_sets <= 512 it still holds them after the call, item i = h * n_sets + s at float
+ * offset i * set_size * n as [set_size][n] (rows of invalid tokens unspecified).
  * Needs only params, Q and K (no partition).  Not part of the timed call. */
 sparsepr_status sparsepr_support_workspace_size(const sparsepr_params* params, int n_sets, int set_size,
                                                 size_t* bytes);

@@ -41,6 +41,34 @@ def row_supports(q, k, scale, rows, mass=0.9):
     return count, member
 
 
+def supports_from_scores(scores, scale, mass=0.9):
+    """The same support definition with each key's probability taken as an integer mass,
+    decided in double precision from given float32 scores f (e.g. another implementation's):
+    m = floor(2^40 exp((f - f_max) scale)) with the difference and product as float64
+    operations; the target is min(ceil(mass * S), S) with S = sum m as a float64, at least 1;
+    keys by decreasing score, ties by the smaller index, and the count is the shortest
+    prefix whose integer sum reaches the target.  ``scores`` [R, N]; returns (count per row
+    [R] int64, member mask [R, N] bool)."""
+    f = np.asarray(scores, dtype=np.float32)
+    count = np.empty(f.shape[0], dtype=np.int64)
+    member = np.zeros(f.shape, dtype=bool)
+    n = f.shape[1]
+    for r in range(f.shape[0]):
+        fr = f[r].astype(np.float64) + 0.0          # -0 and +0 are one score
+        x = (fr - fr.max()) * float(np.float32(scale))
+        m = np.floor(np.ldexp(np.exp(x), 40)).astype(np.int64)
+        total = int(m.sum())
+        want = float(np.ceil(float(total) * mass))
+        tgt = total if want >= float(total) else int(want)
+        tgt = max(tgt, 1)
+        order = np.lexsort((np.arange(n), -fr))
+        c = np.cumsum(m[order])
+        k = int(np.searchsorted(c, tgt, side="left")) + 1
+        count[r] = min(k, n)
+        member[r, order[:count[r]]] = True
+    return count, member
+
+
 def shared_supports(q, k, scale, sets, mass=0.9):
     """Queries that share one route must keep the union of their single-row supports (same
     paragraph: eight queries per route).  ``sets`` [S, s] holds token indices; returns

@@ -1,13 +1,14 @@
 """GPU parity of the support diagnostics (summary page of "Partition the Support,
 Reconstruct the Residual", support paragraph: single-row 90 %-mass supports and their
-union over queries that share a route) against the oracle's float64 definition.
+union over queries that share a route) against the oracle.
 
-The count is an integer decided from floating-point probabilities (fp32 scores and
-2^-40 fixed-point masses on the GPU, float64 in the oracle), so each GPU count is checked
-to be a valid answer in float64 within 2e-5 of the mass (the smallest prefix of the sorted
-probabilities reaching it), at least 95 % of counts must equal the oracle's, and each union
-may differ from the oracle's only by the rows whose counts differ or whose boundary keys are
-within 1e-5 relative of each other.  Exact ties (identical keys) are checked exactly."""
+The counts are integers decided from floating-point scores, so they are checked the way the
+partition's integer stages are: the GPU's fp32 scores (read back from the workspace) are
+within 1e-5 relative of the oracle's float64 scores, and given those scores the oracle's
+integer decisions (fixed-point masses formed in double precision,
+``supports_from_scores``) give every row count and every union bit-exact.  Each count is
+also checked to be a valid float64 answer within 2e-5 of the mass.  Exact ties
+(identical keys) are checked against their closed form."""
 import math
 
 import numpy as np
@@ -61,14 +62,33 @@ def _check(cfg, Q, K, sets, rows_gpu, union_gpu, mass):
     assert equal >= 0.95 * total, (equal, total)
 
 
-def _run(cfg, Q, K, sets, mass):
+def _run(cfg, Q, K, sets, mass, with_scores=False):
     import torch
     import free_block_sparse_sparsepr_amd as S
     sp = S.SparsePR(S.config_from_workload(cfg))
     q, k = device_tensor(Q, cfg), device_tensor(K, cfg)
-    rows, union = sp.support_diagnostics(q, k, torch.from_numpy(sets.astype(np.int32)).cuda(), mass)
+    res = sp.support_diagnostics(q, k, torch.from_numpy(sets.astype(np.int32)).cuda(), mass, with_scores=with_scores)
     torch.cuda.synchronize()
-    return host(rows), host(union)
+    return tuple(host(t) for t in res)
+
+
+def _check_exact(cfg, Q, K, sets, rows_gpu, union_gpu, scores, mass):
+    """Bit-exact counts and unions given the GPU's fp32 scores; the scores themselves against
+    the float64 dot products."""
+    scale = np.float32(1 / math.sqrt(cfg.d))
+    for h in range(cfg.heads_q):
+        kv = h // cfg.g
+        for si in range(sets.shape[1]):
+            toks = sets[h, si]
+            valid = (toks >= 0) & (toks < cfg.n)
+            if not valid.any():
+                continue
+            f = scores[h, si][valid]
+            ref = np.asarray(Q[h], np.float64)[toks[valid]] @ np.asarray(K[kv], np.float64).T
+            np.testing.assert_allclose(f, ref, rtol=1e-5, atol=1e-5 * np.abs(ref).max())
+            cnt, member = Dg.supports_from_scores(f, scale, mass)
+            np.testing.assert_array_equal(rows_gpu[h, si][valid], cnt)
+            assert int(union_gpu[h, si]) == int(member.any(axis=0).sum()), (h, si)
 
 
 def _consecutive_sets(cfg, n_sets, s, rng):
@@ -99,7 +119,8 @@ def test_support_matches_oracle(cname, kind, mass):
         sets = _consecutive_sets(cfg, n_sets, s, rng)
     else:
         sets = rng.integers(0, cfg.n, (cfg.heads_q, n_sets, s))
-    rows, union = _run(cfg, Q, K, sets, mass)
+    rows, union, scores = _run(cfg, Q, K, sets, mass, with_scores=True)
+    _check_exact(cfg, Q, K, sets, rows, union, scores, mass)
     _check(cfg, Q, K, sets, rows, union, mass)
 
 
@@ -122,7 +143,8 @@ def test_support_invalid_tokens_and_many_items():
     _check(cfg, Q, K, sets, rows, union, 0.9)
     for s in (1, 16):
         sets = rng.integers(0, cfg.n, (1, 5, s))
-        rows, union = _run(cfg, Q, K, sets, 0.9)
+        rows, union, scores = _run(cfg, Q, K, sets, 0.9, with_scores=True)
+        _check_exact(cfg, Q, K, sets, rows, union, scores, 0.9)
         _check(cfg, Q, K, sets, rows, union, 0.9)
         if s == 1:
             np.testing.assert_array_equal(union[0], rows[0, :, 0])

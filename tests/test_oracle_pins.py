@@ -9,6 +9,7 @@ import numpy as np
 import pytest
 from scipy.special import logsumexp, softmax
 
+from oracle import diagnostics as Dg
 from oracle import sparsepr as O
 
 RNG = np.random.default_rng(1234)
@@ -821,3 +822,51 @@ def test_global_budget_is_a_feasible_maximal_prefix(tile):
     if first_drop < len(opt):
         _, h, c, _ = opt[first_drop]
         assert total + int(costs[h][c // 6, c % 6]) > 3 * O.route_budget(0.2, n, 4)
+
+
+# ------------------------------------------------------------ support from given scores
+def test_supports_from_scores_closed_forms_and_subset_brute_force():
+    """Integer-mass supports on given float32 scores: uniform scores need ceil(mass n) keys
+    (the lowest indices), a dominant score needs one key, and on tiny random rows the count
+    is the smallest k for which some k-subset's integer mass reaches the target (subset
+    enumeration, no sorting), with members the highest scores, ties to lower indices."""
+    f = np.zeros((1, 8), np.float32)
+    cnt, mem = Dg.supports_from_scores(f, 1.0, 0.75)
+    assert cnt[0] == 6 and mem[0].tolist() == [True] * 6 + [False] * 2
+    f = np.array([[0.0, 100.0, 0.0, 0.0]], np.float32)
+    cnt, mem = Dg.supports_from_scores(f, 1.0, 0.9)
+    assert cnt[0] == 1 and mem[0].tolist() == [False, True, False, False]
+    rng = np.random.default_rng(11)
+    for _ in range(40):
+        n = int(rng.integers(2, 8))
+        row = (rng.integers(-3, 4, n) * 0.5).astype(np.float32)   # repeated values -> ties
+        scale = float(np.float32(rng.uniform(0.3, 2.0)))
+        mass = float(rng.choice([0.5, 0.75, 0.9]))
+        cnt, mem = Dg.supports_from_scores(row[None], scale, mass)
+        x = (row.astype(np.float64) - float(row.max())) * scale
+        m = [int(v) for v in np.floor(np.ldexp(np.exp(x), 40))]
+        total = sum(m)
+        want = math.ceil(float(total) * mass)
+        tgt = max(total if want >= total else want, 1)
+        best = min(k for k in range(1, n + 1)
+                   if max(sum(m[i] for i in c) for c in itertools.combinations(range(n), k)) >= tgt)
+        assert cnt[0] == best, (row, mass, cnt[0], best)
+        keep = sorted(range(n), key=lambda i: (-float(row[i]), i))[:best]
+        assert sorted(np.nonzero(mem[0])[0].tolist()) == sorted(keep)
+
+
+def test_supports_from_scores_agree_with_float64_probabilities():
+    """On random float32 scores the integer-mass count equals the float64-probability count
+    except where the mass threshold falls within the 2^-40 quantisation of a boundary."""
+    rng = np.random.default_rng(12)
+    q, k = rng.standard_normal((40, 16)), rng.standard_normal((300, 16))
+    scale = 0.25
+    f = (q @ k.T).astype(np.float32)
+    cnt, _ = Dg.supports_from_scores(f, scale, 0.9)
+    p = np.exp((f.astype(np.float64) - f.max(axis=1, keepdims=True)) * scale)
+    p /= p.sum(axis=1, keepdims=True)
+    for r in range(40):
+        srt = -np.sort(-p[r])
+        c = np.cumsum(srt)
+        want = int((c < 0.9).sum()) + 1
+        assert abs(int(cnt[r]) - want) <= 1 and (cnt[r] == want or abs(c[want - 1] - 0.9) < 1e-9)
