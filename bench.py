@@ -112,7 +112,7 @@ def executed_tile_pairs(sp, cfg):
 
 
 TRAFFIC_PROFILES = {   # call order -> counter summary of that order's attention kernel
-    "fused": os.path.join(ROOT, "profiles", "sparse_attention_720p_n118800_h24_hbm_traffic.md"),
+    "fused": os.path.join(ROOT, "profiles", "sparse_attention_fused_720p_n118800_h24_hbm_traffic.md"),
     "overlapped": os.path.join(ROOT, "profiles", "sparse_attention_overlapped_720p_n118800_h24_hbm_traffic.md"),
 }
 KERNEL_SOURCES = ["free_block_sparse_sparsepr_amd/csrc/attend_mfma.hip", "free_block_sparse_sparsepr_amd/csrc/sp_attn.hpp",

@@ -90,3 +90,31 @@ def test_outputs_match_oracle(case):
             ok, mx, mean = compare_float(gpu["dense"][h], od, False)
             assert ok, (case["name"], "dense", h, mx, mean)
     np.testing.assert_array_equal(gpu["out_overlapped"], gpu["out"])
+
+
+def test_route_budget_at_the_largest_n():
+    """The route's budget floor(rho_ppm n^2 / 10^6) - M n at the largest accepted n (2^22) and
+    rho_exec = 1, where rho_ppm n^2 exceeds the 64-bit range: partition and route on seeded
+    random bf16 inputs, then the kept cells and the realised pairs against the oracle's
+    selection (Python integers) on the GPU's cell masses and group sizes."""
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import free_block_sparse_sparsepr_amd as S
+    n, d = 1 << 22, 64
+    print(f"\n[edge largest n] N={n} d={d} rho_exec=1", flush=True)
+    cfg = S.Config(heads_q=1, heads_kv=1, n=n, d=d, rho_exec=1.0)
+    sp = S.SparsePR(cfg)
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    q, k, v = (torch.randn((1, n, d), generator=gen, device="cuda").to(torch.bfloat16) for _ in range(3))
+    sp.partition(q, k, v)
+    sp.route()
+    torch.cuda.synchronize()
+    m = host(sp.route_buf["cell_mass"])[0].astype(np.int64)      # cell masses < 2^42
+    qc = np.diff(host(sp.part["query_offsets"])[0].astype(np.int64))
+    kc = np.diff(host(sp.part["key_offsets"])[0].astype(np.int64))
+    r = O.select_cells(m, qc, kc, 1.0, n, cfg.n_probe)
+    assert r.budget == n * n - cfg.n_probe * n
+    np.testing.assert_array_equal(kept_from_mask(host(sp.route_buf["kept_mask"])[0], 64, 64), r.kept)
+    assert int(host(sp.route_buf["pairs"])[0]) == r.pairs
+    assert r.pairs > r.budget - n * n // 8
