@@ -62,13 +62,52 @@ struct MfmaCfg {
 
 // Key tiles walk the kept runs of a query tile (uniform across the block).  Tiles start
 // on 16-key boundaries so that the transposed V's 16-key groups are aligned; keys of a
-// tile outside its run [k0, k1) are masked.  Advances (ci, k0, k1, kt) to the next tile;
-// returns false after the last one.
-__device__ __forceinline__ bool next_tile(const AttnArgs& A, int kv, const TileInfo& ti, int BN, int& ci, int& k0,
-                                          int& k1, int& kt) {
+// tile outside its run [k0, k1) are masked.
+// The runs of next_run, listed once per block in LDS by one wave: lane t takes CSR column t
+// of the query group; a column starts a run unless it follows its predecessor's group, a run
+// ends before the next start, and runs without keys are dropped (ballot + rank).  The
+// block's iterators then read one LDS entry per run: loads of the CSR columns from global
+// memory would wait behind the tile copies in flight (the counter of vector memory
+// operations is in order).
+__device__ __forceinline__ void build_runs(const AttnArgs& A, int kv, const TileInfo& ti, int lane, int2* runs,
+                                           int* nruns) {
+  if (ti.kbeg < 0) {   // the dense schedule: one run over every key
+    if (lane == 0) {
+      runs[0] = make_int2(0, A.n);
+      *nruns = 1;
+    }
+    return;
+  }
+  const int32_t* cl = A.cols + (int64_t)kv * A.gq * A.gk;
+  const int32_t* ko = A.koff + (int64_t)kv * (A.gk + 1);
+  const int cnt = ti.kend - ti.kbeg;   // <= G_K <= 64
+  const int b = lane < cnt ? cl[ti.kbeg + lane] : 0;
+  const int pb = __shfl(b, lane > 0 ? lane - 1 : 0);
+  const bool start = lane < cnt && (lane == 0 || pb + 1 != b);
+  const uint64_t sm = __ballot(start);
+  const uint64_t after = sm & ~((2ull << lane) - 1ull);   // starts above this lane
+  const int e = after ? __ffsll((unsigned long long)after) - 2 : cnt - 1;
+  const int be = __shfl(b, e < 0 ? 0 : e);
+  int k0 = 0, k1 = 0;
+  if (start) {
+    k0 = ko[b];
+    k1 = ko[be + 1];
+  }
+  const bool keep = start && k1 > k0;
+  const uint64_t km = __ballot(keep);
+  if (keep) runs[__popcll(km & ((1ull << lane) - 1ull))] = make_int2(k0, k1);
+  if (lane == 0) *nruns = __popcll(km);
+}
+
+// Advances (ri, k0, k1, kt) to the next tile (ri: the next run); false after the last one.
+__device__ __forceinline__ bool next_tile_lds(const int2* runs, int nruns, int BN, int& ri, int& k0, int& k1,
+                                              int& kt) {
   kt += BN;
   if (kt < k1) return true;
-  if (!next_run(A, kv, ti, ci, k0, k1)) return false;
+  if (ri >= nruns) return false;
+  const int2 r = runs[ri++];
+  k0 = __builtin_amdgcn_readfirstlane(r.x);
+  k1 = __builtin_amdgcn_readfirstlane(r.y);
   kt = k0 & ~15;
   return true;
 }
@@ -744,11 +783,15 @@ __global__ __launch_bounds__(64 * kAttnWaves, 1) void attn_mfma_kernel(AttnArgs 
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
 
-  // Tile iterators: (ci, k0, k1, kt) is the tile being computed, (fci, fk0, fk1, fkt) the
-  // copy frontier two tiles ahead; tile j lives in stage j % kAttnStages.
-  int ci = ti.kbeg < 0 ? 0 : ti.kbeg, k0 = 0, k1 = 0, kt = 0;
-  bool valid = next_run(A, kv, ti, ci, k0, k1);
-  if (valid) kt = k0 & ~15;
+  // Tile iterators: (ci, k0, k1, kt) is the tile being computed (ci: its next run), (fci, fk0,
+  // fk1, fkt) the copy frontier two tiles ahead; tile j lives in stage j % kAttnStages.
+  __shared__ int2 runs[kMaxGroups];
+  __shared__ int nruns_s;
+  if (wu == 0) build_runs(A, kv, ti, lane, runs, &nruns_s);
+  __syncthreads();
+  const int nruns = __builtin_amdgcn_readfirstlane(nruns_s);
+  int ci = 0, k0 = 0, k1 = 0, kt = -BN;
+  bool valid = next_tile_lds(runs, nruns, BN, ci, k0, k1, kt);
   int fci = ci, fk0 = k0, fk1 = k1, fkt = kt;
   bool fvalid = valid;
   // Anti-phased schedule: waves 0-3 and 4-7 (one of each per SIMD) alternate between a
@@ -771,7 +814,7 @@ __global__ __launch_bounds__(64 * kAttnWaves, 1) void attn_mfma_kernel(AttnArgs 
   for (int i = 0; i < 2 && fvalid; ++i) {
     if (!lag) stage_copy<D, BN, CW>(cpa, kb, vtb, A.n, A.v_np, fkt, stages[i], wu);
     ++ncopied;
-    fvalid = next_tile(A, kv, ti, C::BN, fci, fk0, fk1, fkt);
+    fvalid = next_tile_lds(runs, nruns, BN, fci, fk0, fk1, fkt);
   }
   if (!lag) wait_tiles_in_flight<PT>(ncopied - 1);   // tile 0 has landed
   __syncthreads();
@@ -813,14 +856,14 @@ __global__ __launch_bounds__(64 * kAttnWaves, 1) void attn_mfma_kernel(AttnArgs 
       if (!lag) stage_copy<D, BN, CW>(cpa, kb, vtb, A.n, A.v_np, fkt, stages[fst], wu);
       issued = true;
       fst = fst == kAttnStages - 1 ? 0 : fst + 1;
-      fvalid = next_tile(A, kv, ti, C::BN, fci, fk0, fk1, fkt);
+      fvalid = next_tile_lds(runs, nruns, BN, fci, fk0, fk1, fkt);
     }
     if (wave_rows)     // softmax phase
       softmax_step<D, BN, false>(sv, lo, hi, c2, nullptr, 0ull, m_i, l_i, o, pp, hf);
     have_prev = true;
     prev = cur;
     cur = cur == kAttnStages - 1 ? 0 : cur + 1;
-    valid = next_tile(A, kv, ti, C::BN, ci, k0, k1, kt);
+    valid = next_tile_lds(runs, nruns, BN, ci, k0, k1, kt);
     if (!lag) wait_tiles_in_flight<PT>(issued ? 1 : 0);   // tile j + 1 has landed
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   }

@@ -211,8 +211,9 @@ constexpr int kAssignChunk = 256;       // points per chunk: 64 per wave
 // on which feature (or point) each byte stands for.
 //  * scores^T = C X^T: a lane owns one point and 16 of each 32-group block (its partner
 //    lane l ^ 32 the other 16).  key = 64 (||c_g||^2 - 2 <x, c_g>) + g orders by score,
-//    then by g; the minimum over the lane and its partner is the label (key mod 64).
-//    Groups beyond G carry a key above every real one.
+//    then by g; it is held negated, 128 <x, c_g> - (64 ||c_g||^2 + g) (one shift-add per
+//    score, |key| < 2^28), and the maximum over the lane and its partner gives the label
+//    (-key mod 64).  Groups beyond G carry a key below every real one.
 //  * transpose: the same X operand times an identity slice puts the features on the lanes
 //    and the points in the accumulator registers.
 //  * sums: S^T += X^T onehot(labels), byte e of both operands standing for the point in
@@ -262,7 +263,7 @@ __global__ __launch_bounds__(256, FP > 64 ? 1 : 2) void kmeans_assign_mfma_kerne
   }
   for (int idx = tid; idx < kMaxGroups * SROW; idx += 256) ssum[idx] = 0;
   __syncthreads();
-  {  // 64 ||c_g||^2 + g, four lanes per group
+  {  // -(64 ||c_g||^2 + g), four lanes per group
     const int gi = tid >> 2, q = tid & 3;
     int s2 = 0;
 #pragma unroll
@@ -272,7 +273,7 @@ __global__ __launch_bounds__(256, FP > 64 ? 1 : 2) void kmeans_assign_mfma_kerne
     }
     s2 += __shfl_xor(s2, 1);
     s2 += __shfl_xor(s2, 2);
-    if (q == 0) cnk[gi] = gi < G ? 64 * s2 + gi : (1 << 30) + gi;
+    if (q == 0) cnk[gi] = -(gi < G ? 64 * s2 + gi : (1 << 30) + gi);
   }
   __syncthreads();
   // identity slice: byte e of lane (j, hf) is 1 where 16 hf + e == j
@@ -307,7 +308,7 @@ __global__ __launch_bounds__(256, FP > 64 ? 1 : 2) void kmeans_assign_mfma_kerne
   ki32x4_t nraw[KB];
   load32(pbeg + w * 64 + l32, nraw);
   for (int pbase = pbeg + w * 64; pbase < pend; pbase += kAssignChunk) {
-#pragma unroll 1
+#pragma unroll
     for (int pb = 0; pb < 2; ++pb) {
       const int pt = pbase + pb * 32 + l32;
       const bool pv = pt < pend;
@@ -316,7 +317,7 @@ __global__ __launch_bounds__(256, FP > 64 ? 1 : 2) void kmeans_assign_mfma_kerne
       for (int kb = 0; kb < KB; ++kb) xo[kb] = nraw[kb];
       load32(pb == 0 ? pt + 32 : pt - 32 + kAssignChunk, nraw);
       // -- assignment
-      int best = 0x7fffffff;
+      int best = (int)0x80000000u;
 #pragma unroll
       for (int gb = 0; gb < 2; ++gb) {
         ki32x16_t sc;
@@ -330,11 +331,11 @@ __global__ __launch_bounds__(256, FP > 64 ? 1 : 2) void kmeans_assign_mfma_kerne
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int gi = 32 * gb + 8 * (r >> 2) + 4 * hf + (r & 3);
-          best = min(best, cnk[gi] - 128 * sc[r]);
+          best = max(best, (int)(((uint32_t)sc[r] << 7) + (uint32_t)cnk[gi]));   // one shift-add
         }
       }
-      best = min(best, __shfl_xor(best, 32));
-      const int bg = best & 63;
+      best = max(best, __shfl_xor(best, 32));
+      const int bg = (-best) & 63;
       const int lab = pv ? bg : kMaxGroups;          // points past the end: no group
       if (pv && hf == 0) labels[(int64_t)h * n + pt] = bg;
       if constexpr (!SUMS) continue;

@@ -406,8 +406,10 @@ __global__ __launch_bounds__(256) void fit_gram_kernel(const double* __restrict_
 
 // fit_factor_kernel, grid (2, Hq), block 256: block 0 factors K = L L^T (Cholesky, lower
 // triangle in place); block 1 diagonalises G by parallel cyclic Jacobi (round-robin
-// pairing: 32 disjoint rotations per step), orders the eigenvalues (descending, ties by
-// index), keeps those above 1e-8 of the largest (at most rank) and stores them with their
+// pairing: 32 disjoint rotations per step; a thread applies a step to four 2x2 blocks of G
+// and to one pair's two columns in eight rows of V, every read issued before its writes),
+// orders the eigenvalues (descending, ties by index), keeps those above 1e-8 of the largest
+// (at most rank) and stores them with their
 // eigenvectors a.  With ridge_only (the unprojected ridge) block 1 writes r_eff = M and
 // zero eigenvalues.
 template <int D>
@@ -418,7 +420,7 @@ __global__ __launch_bounds__(256) void fit_factor_kernel(int M, int rank, int ri
   __shared__ double Km[MM][MM + 1];
   __shared__ double Vm[MM][MM + 1];
   __shared__ double rc[32], rs[32], ev[MM], red[256];
-  __shared__ int pp[32], qq[32], ord[MM];
+  __shared__ int ord[MM];
   __shared__ int stop_s;
   const int h = blockIdx.y, tid = threadIdx.x;
   double* fb = fbuf + (size_t)h * FitBuf::per_head(D);
@@ -486,29 +488,49 @@ __global__ __launch_bounds__(256) void fit_factor_kernel(int M, int rank, int ri
           c = 1.0 / sqrt(1.0 + tt * tt);
           s = tt * c;
         }
-        pp[tid] = p; qq[tid] = q; rc[tid] = c; rs[tid] = s;
+        rc[tid] = c;
+        rs[tid] = s;
       }
       __syncthreads();
-      for (int blk = tid; blk < 32 * 32; blk += 256) {
-        const int bi = blk >> 5, bj = blk & 31;
-        const int pi = pp[bi], qi = qq[bi], pj = pp[bj], qj = qq[bj];
-        const double ci = rc[bi], si = rs[bi], cj = rc[bj], sj = rs[bj];
-        const double a00 = Km[pi][pj], a01 = Km[pi][qj], a10 = Km[qi][pj], a11 = Km[qi][qj];
-        const double t00 = a00 * cj - a01 * sj, t01 = a00 * sj + a01 * cj;
-        const double t10 = a10 * cj - a11 * sj, t11 = a10 * sj + a11 * cj;
-        Km[pi][pj] = ci * t00 - si * t10;
-        Km[pi][qj] = ci * t01 - si * t11;
-        Km[qi][pj] = si * t00 + ci * t10;
-        Km[qi][qj] = si * t01 + ci * t11;
-        if (bi == bj) { Km[pi][qj] = 0.0; Km[qi][pj] = 0.0; }
-      }
-      for (int idx = tid; idx < MM * 32; idx += 256) {
-        const int row = idx >> 5, j = idx & 31;
-        const int pj = pp[j], qj = qq[j];
-        const double cj = rc[j], sj = rs[j];
-        const double vp = Vm[row][pj], vq = Vm[row][qj];
-        Vm[row][pj] = cj * vp - sj * vq;
-        Vm[row][qj] = sj * vp + cj * vq;
+      {  // thread: column pair bj, row pairs r0 + 8k of G and rows r0 + 8m of V; every
+         // operand read is issued before the first write (the blocks are disjoint)
+        const int bj = tid & 31, r0 = tid >> 5;
+        int pj, qj;
+        jacobi_pair(t, bj, pj, qj);
+        const double cj = rc[bj], sj = rs[bj];
+        int pi[4], qi[4];
+        double ci[4], si[4], a[4][4], vp[8], vq[8];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int bi = r0 + 8 * k;
+          jacobi_pair(t, bi, pi[k], qi[k]);
+          ci[k] = rc[bi];
+          si[k] = rs[bi];
+          a[k][0] = Km[pi[k]][pj];
+          a[k][1] = Km[pi[k]][qj];
+          a[k][2] = Km[qi[k]][pj];
+          a[k][3] = Km[qi[k]][qj];
+        }
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          vp[m] = Vm[r0 + 8 * m][pj];
+          vq[m] = Vm[r0 + 8 * m][qj];
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const double t00 = a[k][0] * cj - a[k][1] * sj, t01 = a[k][0] * sj + a[k][1] * cj;
+          const double t10 = a[k][2] * cj - a[k][3] * sj, t11 = a[k][2] * sj + a[k][3] * cj;
+          const bool diag = r0 + 8 * k == bj;
+          Km[pi[k]][pj] = ci[k] * t00 - si[k] * t10;
+          Km[pi[k]][qj] = diag ? 0.0 : ci[k] * t01 - si[k] * t11;
+          Km[qi[k]][pj] = diag ? 0.0 : si[k] * t00 + ci[k] * t10;
+          Km[qi[k]][qj] = si[k] * t01 + ci[k] * t11;
+        }
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          Vm[r0 + 8 * m][pj] = cj * vp[m] - sj * vq[m];
+          Vm[r0 + 8 * m][qj] = sj * vp[m] + cj * vq[m];
+        }
       }
       __syncthreads();
     }
