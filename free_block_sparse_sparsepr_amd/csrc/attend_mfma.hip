@@ -593,15 +593,38 @@ __device__ __forceinline__ void fused_stage(const AttnArgs& A, int h, char* lds,
   const int re = min(A.r_eff[h], min(A.rank, F::RCM));
   const float* Ah = A.fitA + (int64_t)h * D * A.rank;
   const float* Bh = A.fitB + (int64_t)h * A.rank * D;
-  for (int idx = tid; idx < F::RCM * D; idx += NT) {
-    const int k = idx / D, d = idx % D;
-    const float av = k < re ? Ah[d * A.rank + k] : 0.f, bv = k < re ? Bh[k * D + d] : 0.f;
-    const bf16_t ah = f32_to_bf16(av), bh = f32_to_bf16(bv);
-    At[k * F::AROW + d] = ah;
-    Bt[d * F::BROW + k] = bh;
-    if constexpr (SPLIT) {
-      At[F::PART / 2 + k * F::AROW + d] = f32_to_bf16(av - bf16_to_f32(ah));
-      Bt[F::PART / 2 + d * F::BROW + k] = f32_to_bf16(bv - bf16_to_f32(bh));
+  // only the rows of A^T (columns of B^T) the products read: one 32-row block of t, or two
+  const int kr = re > 32 ? F::RCM : 32;
+  auto put = [&](bf16_t* dst, int off, float v) {
+    const bf16_t hi = f32_to_bf16(v);
+    dst[off] = hi;
+    if constexpr (SPLIT) dst[F::PART / 2 + off] = f32_to_bf16(v - bf16_to_f32(hi));
+  };
+  if ((A.rank & 3) == 0) {   // 16-byte loads: four k of a row of A, four d of a row of B
+    const int kq = kr / 4;
+    for (int idx = tid; idx < kq * D; idx += NT) {
+      const int d = idx / kq, k = 4 * (idx % kq);
+      const float4 a4 = k < re ? *reinterpret_cast<const float4*>(Ah + (int64_t)d * A.rank + k)
+                               : make_float4(0.f, 0.f, 0.f, 0.f);
+      put(At, k * F::AROW + d, a4.x);
+      put(At, (k + 1) * F::AROW + d, k + 1 < re ? a4.y : 0.f);
+      put(At, (k + 2) * F::AROW + d, k + 2 < re ? a4.z : 0.f);
+      put(At, (k + 3) * F::AROW + d, k + 3 < re ? a4.w : 0.f);
+    }
+    for (int idx = tid; idx < kr * (D / 4); idx += NT) {
+      const int k = idx / (D / 4), d = 4 * (idx % (D / 4));
+      const float4 b4 = k < re ? *reinterpret_cast<const float4*>(Bh + (int64_t)k * D + d)
+                               : make_float4(0.f, 0.f, 0.f, 0.f);
+      put(Bt, d * F::BROW + k, b4.x);
+      put(Bt, (d + 1) * F::BROW + k, b4.y);
+      put(Bt, (d + 2) * F::BROW + k, b4.z);
+      put(Bt, (d + 3) * F::BROW + k, b4.w);
+    }
+  } else {
+    for (int idx = tid; idx < kr * D; idx += NT) {
+      const int k = idx / D, d = idx % D;
+      put(At, k * F::AROW + d, k < re ? Ah[d * A.rank + k] : 0.f);
+      put(Bt, d * F::BROW + k, k < re ? Bh[k * D + d] : 0.f);
     }
   }
   for (int d = tid; d < D; d += NT) c0s[d] = A.fitc0[(int64_t)h * D + d];

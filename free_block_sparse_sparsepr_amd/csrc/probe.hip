@@ -480,13 +480,20 @@ __global__ __launch_bounds__(256) void fit_factor_kernel(int M, int rank, int ri
       if (tid < 32) {
         int p, q;
         jacobi_pair(t, tid, p, q);
+        // t = tan(theta), the smaller root of t^2 + 2 tau t - 1 = 0 with tau = (a_qq - a_pp) /
+        // (2 a_pq), written as |2 a_pq| / (|a_qq - a_pp| + hypot) with the sign of tau (+ for
+        // tau = 0): one square root and one division, then c = 1 / sqrt(1 + t^2), s = t c
         const double apq = Km[p][q];
         double c = 1.0, s = 0.0;
         if (apq != 0.0) {
-          const double tau = (Km[q][q] - Km[p][p]) / (2.0 * apq);
-          const double tt = tau >= 0.0 ? 1.0 / (tau + sqrt(1.0 + tau * tau)) : -1.0 / (-tau + sqrt(1.0 + tau * tau));
-          c = 1.0 / sqrt(1.0 + tt * tt);
-          s = tt * c;
+          const double dd = Km[q][q] - Km[p][p], a2 = 2.0 * apq;
+          const double r = sqrt(fma(dd, dd, a2 * a2));
+          if (r > 0.0) {
+            double tt = fabs(a2) / (fabs(dd) + r);
+            if (dd != 0.0 && ((dd < 0.0) != (a2 < 0.0))) tt = -tt;
+            c = rsqrt(fma(tt, tt, 1.0));
+            s = tt * c;
+          }
         }
         rc[tid] = c;
         rs[tid] = s;
