@@ -423,60 +423,66 @@ __device__ __forceinline__ void matrix_phase(const char* __restrict__ kstage, co
 }
 
 // The matrix phase for d = 128 and 64-key tiles as two self-contained assembly blocks,
-// each keeping four LDS operand reads in flight with exact partial waits (a read is
-// issued into the buffer the product before it has just consumed, and every block waits
-// for all of its own reads before it ends).  The first block is O^T += V^T P^T of the
-// previous tile (V^T rows d = 32 db + l32 at vaddr[m] + 16384 + 4096 db for key k-step
-// m = 2 kb + s2); the second S^T = K Q^T of the current one (K rows 32 kb + l32 at
-// kaddr[kk] + 8192 kb for d k-step kk).  The leading s_nop covers the wait states between
-// the softmax phase's vector writes (P, the rescaled O) and their first matrix read; the
-// trailing ones those between the last product and the vector reads of S that follow.
-__device__ __forceinline__ void matrix_phase_d128(const uint32_t* kaddr, const uint32_t* vaddr,
-                                                  const bf16x8_t* qreg, const PackP (*p)[2], f32x16_t* o,
-                                                  f32x16_t* sv) {
-  bf16x8_t t0, t1, t2, t3;
+// each keeping six LDS operand reads in flight with exact partial waits (a read is issued
+// into the buffer the product before it has just consumed, and every block waits for all
+// of its own reads before it ends).  With one wave per SIMD in this phase, a 16-byte
+// operand read per 32x32x16 product keeps the matrix pipe about 69 % busy at four reads in
+// flight and 76 % at six (deeper rings add nothing), measured on MI355X.  The first block
+// is O^T += V^T P^T of the previous tile (V^T rows d = 32 db + l32 at (vb ^ 32 m) + 16384 +
+// 4096 db for key k-step m = 2 kb + s2); the second S^T = K Q^T of the current one (K rows
+// 32 kb + l32 at (kb ^ 32 kk) + 8192 kb for d k-step kk); the xor-ed addresses are formed
+// in two temporaries just before their first read.  The leading s_nop covers the wait
+// states between the softmax phase's vector writes (P, the rescaled O) and their first
+// matrix read; the trailing ones those between the last product and the vector reads of S.
+__device__ __forceinline__ void matrix_phase_d128(uint32_t kb, uint32_t vb, const bf16x8_t* qreg,
+                                                  const PackP (*p)[2], f32x16_t* o, f32x16_t* sv) {
+  bf16x8_t t0, t1, t2, t3, t4, t5;
+  uint32_t ta, tb;
   asm volatile(
-            "s_nop 4\n"
-      "ds_read_b128 %[t0], %[va0] offset:16384\n"
-      "ds_read_b128 %[t1], %[va0] offset:20480\n"
-      "ds_read_b128 %[t2], %[va0] offset:24576\n"
-      "ds_read_b128 %[t3], %[va0] offset:28672\n"
-      "s_waitcnt lgkmcnt(3)\n"
+      "s_nop 4\n"
+      "ds_read_b128 %[t0], %[vb] offset:16384\n"
+      "ds_read_b128 %[t1], %[vb] offset:20480\n"
+      "ds_read_b128 %[t2], %[vb] offset:24576\n"
+      "ds_read_b128 %[t3], %[vb] offset:28672\n"
+      "v_xor_b32 %[tb], 32, %[vb]\n"
+      "ds_read_b128 %[t4], %[tb] offset:16384\n"
+      "ds_read_b128 %[t5], %[tb] offset:20480\n"
+      "s_waitcnt lgkmcnt(5)\n"
       "v_mfma_f32_32x32x16_bf16 %[o0], %[t0], %[p0], %[o0]\n"
-      "ds_read_b128 %[t0], %[va1] offset:16384\n"
-      "s_waitcnt lgkmcnt(3)\n"
+      "ds_read_b128 %[t0], %[tb] offset:24576\n"
+      "s_waitcnt lgkmcnt(5)\n"
       "v_mfma_f32_32x32x16_bf16 %[o1], %[t1], %[p0], %[o1]\n"
-      "ds_read_b128 %[t1], %[va1] offset:20480\n"
-      "s_waitcnt lgkmcnt(3)\n"
+      "ds_read_b128 %[t1], %[tb] offset:28672\n"
+      "s_waitcnt lgkmcnt(5)\n"
       "v_mfma_f32_32x32x16_bf16 %[o2], %[t2], %[p0], %[o2]\n"
-      "ds_read_b128 %[t2], %[va1] offset:24576\n"
-      "s_waitcnt lgkmcnt(3)\n"
+      "v_xor_b32 %[ta], 64, %[vb]\n"
+      "ds_read_b128 %[t2], %[ta] offset:16384\n"
+      "s_waitcnt lgkmcnt(5)\n"
       "v_mfma_f32_32x32x16_bf16 %[o3], %[t3], %[p0], %[o3]\n"
-      "ds_read_b128 %[t3], %[va1] offset:28672\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %[o0], %[t0], %[p1], %[o0]\n"
-      "ds_read_b128 %[t0], %[va2] offset:16384\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %[o1], %[t1], %[p1], %[o1]\n"
-      "ds_read_b128 %[t1], %[va2] offset:20480\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %[o2], %[t2], %[p1], %[o2]\n"
-      "ds_read_b128 %[t2], %[va2] offset:24576\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %[o3], %[t3], %[p1], %[o3]\n"
-      "ds_read_b128 %[t3], %[va2] offset:28672\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %[o0], %[t0], %[p2], %[o0]\n"
-      "ds_read_b128 %[t0], %[va3] offset:16384\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %[o1], %[t1], %[p2], %[o1]\n"
-      "ds_read_b128 %[t1], %[va3] offset:20480\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %[o2], %[t2], %[p2], %[o2]\n"
-      "ds_read_b128 %[t2], %[va3] offset:24576\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %[o3], %[t3], %[p2], %[o3]\n"
-      "ds_read_b128 %[t3], %[va3] offset:28672\n"
+      "ds_read_b128 %[t3], %[ta] offset:20480\n"
+      "s_waitcnt lgkmcnt(5)\n"
+      "v_mfma_f32_32x32x16_bf16 %[o0], %[t4], %[p1], %[o0]\n"
+      "ds_read_b128 %[t4], %[ta] offset:24576\n"
+      "s_waitcnt lgkmcnt(5)\n"
+      "v_mfma_f32_32x32x16_bf16 %[o1], %[t5], %[p1], %[o1]\n"
+      "ds_read_b128 %[t5], %[ta] offset:28672\n"
+      "s_waitcnt lgkmcnt(5)\n"
+      "v_mfma_f32_32x32x16_bf16 %[o2], %[t0], %[p1], %[o2]\n"
+      "v_xor_b32 %[tb], 96, %[vb]\n"
+      "ds_read_b128 %[t0], %[tb] offset:16384\n"
+      "s_waitcnt lgkmcnt(5)\n"
+      "v_mfma_f32_32x32x16_bf16 %[o3], %[t1], %[p1], %[o3]\n"
+      "ds_read_b128 %[t1], %[tb] offset:20480\n"
+      "s_waitcnt lgkmcnt(5)\n"
+      "v_mfma_f32_32x32x16_bf16 %[o0], %[t2], %[p2], %[o0]\n"
+      "ds_read_b128 %[t2], %[tb] offset:24576\n"
+      "s_waitcnt lgkmcnt(5)\n"
+      "v_mfma_f32_32x32x16_bf16 %[o1], %[t3], %[p2], %[o1]\n"
+      "ds_read_b128 %[t3], %[tb] offset:28672\n"
+      "s_waitcnt lgkmcnt(5)\n"
+      "v_mfma_f32_32x32x16_bf16 %[o2], %[t4], %[p2], %[o2]\n"
+      "s_waitcnt lgkmcnt(4)\n"
+      "v_mfma_f32_32x32x16_bf16 %[o3], %[t5], %[p2], %[o3]\n"
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %[o0], %[t0], %[p3], %[o0]\n"
       "s_waitcnt lgkmcnt(2)\n"
@@ -486,52 +492,58 @@ __device__ __forceinline__ void matrix_phase_d128(const uint32_t* kaddr, const u
       "s_waitcnt lgkmcnt(0)\n"
       "v_mfma_f32_32x32x16_bf16 %[o3], %[t3], %[p3], %[o3]\n"
       : [o0] "+v"(o[0]), [o1] "+v"(o[1]), [o2] "+v"(o[2]), [o3] "+v"(o[3]), [t0] "=&v"(t0), [t1] "=&v"(t1),
-        [t2] "=&v"(t2), [t3] "=&v"(t3)
-      : [p0] "v"(p[0][0].v), [p1] "v"(p[0][1].v), [p2] "v"(p[1][0].v), [p3] "v"(p[1][1].v), [va0] "v"(vaddr[0]),
-        [va1] "v"(vaddr[1]), [va2] "v"(vaddr[2]), [va3] "v"(vaddr[3])
+        [t2] "=&v"(t2), [t3] "=&v"(t3), [t4] "=&v"(t4), [t5] "=&v"(t5), [ta] "=&v"(ta), [tb] "=&v"(tb)
+      : [p0] "v"(p[0][0].v), [p1] "v"(p[0][1].v), [p2] "v"(p[1][0].v), [p3] "v"(p[1][1].v), [vb] "v"(vb)
       : "memory");
   asm volatile(
-            "s_nop 4\n"
-      "ds_read_b128 %[t0], %[ka0] offset:0\n"
-      "ds_read_b128 %[t1], %[ka0] offset:8192\n"
-      "ds_read_b128 %[t2], %[ka1] offset:0\n"
-      "ds_read_b128 %[t3], %[ka1] offset:8192\n"
-      "s_waitcnt lgkmcnt(3)\n"
+      "s_nop 4\n"
+      "ds_read_b128 %[t0], %[kb] offset:0\n"
+      "ds_read_b128 %[t1], %[kb] offset:8192\n"
+      "v_xor_b32 %[tb], 32, %[kb]\n"
+      "ds_read_b128 %[t2], %[tb] offset:0\n"
+      "ds_read_b128 %[t3], %[tb] offset:8192\n"
+      "v_xor_b32 %[ta], 64, %[kb]\n"
+      "ds_read_b128 %[t4], %[ta] offset:0\n"
+      "ds_read_b128 %[t5], %[ta] offset:8192\n"
+      "s_waitcnt lgkmcnt(5)\n"
       "v_mfma_f32_32x32x16_bf16 %[s0], %[t0], %[q0], 0\n"
-      "ds_read_b128 %[t0], %[ka2] offset:0\n"
-      "s_waitcnt lgkmcnt(3)\n"
+      "v_xor_b32 %[tb], 96, %[kb]\n"
+      "ds_read_b128 %[t0], %[tb] offset:0\n"
+      "s_waitcnt lgkmcnt(5)\n"
       "v_mfma_f32_32x32x16_bf16 %[s1], %[t1], %[q0], 0\n"
-      "ds_read_b128 %[t1], %[ka2] offset:8192\n"
-      "s_waitcnt lgkmcnt(3)\n"
+      "ds_read_b128 %[t1], %[tb] offset:8192\n"
+      "s_waitcnt lgkmcnt(5)\n"
       "v_mfma_f32_32x32x16_bf16 %[s0], %[t2], %[q1], %[s0]\n"
-      "ds_read_b128 %[t2], %[ka3] offset:0\n"
-      "s_waitcnt lgkmcnt(3)\n"
+      "v_xor_b32 %[ta], 128, %[kb]\n"
+      "ds_read_b128 %[t2], %[ta] offset:0\n"
+      "s_waitcnt lgkmcnt(5)\n"
       "v_mfma_f32_32x32x16_bf16 %[s1], %[t3], %[q1], %[s1]\n"
-      "ds_read_b128 %[t3], %[ka3] offset:8192\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s0], %[t0], %[q2], %[s0]\n"
-      "ds_read_b128 %[t0], %[ka4] offset:0\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s1], %[t1], %[q2], %[s1]\n"
-      "ds_read_b128 %[t1], %[ka4] offset:8192\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s0], %[t2], %[q3], %[s0]\n"
-      "ds_read_b128 %[t2], %[ka5] offset:0\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s1], %[t3], %[q3], %[s1]\n"
-      "ds_read_b128 %[t3], %[ka5] offset:8192\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s0], %[t0], %[q4], %[s0]\n"
-      "ds_read_b128 %[t0], %[ka6] offset:0\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s1], %[t1], %[q4], %[s1]\n"
-      "ds_read_b128 %[t1], %[ka6] offset:8192\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s0], %[t2], %[q5], %[s0]\n"
-      "ds_read_b128 %[t2], %[ka7] offset:0\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s1], %[t3], %[q5], %[s1]\n"
-      "ds_read_b128 %[t3], %[ka7] offset:8192\n"
+      "ds_read_b128 %[t3], %[ta] offset:8192\n"
+      "s_waitcnt lgkmcnt(5)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s0], %[t4], %[q2], %[s0]\n"
+      "v_xor_b32 %[tb], 160, %[kb]\n"
+      "ds_read_b128 %[t4], %[tb] offset:0\n"
+      "s_waitcnt lgkmcnt(5)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s1], %[t5], %[q2], %[s1]\n"
+      "ds_read_b128 %[t5], %[tb] offset:8192\n"
+      "s_waitcnt lgkmcnt(5)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s0], %[t0], %[q3], %[s0]\n"
+      "v_xor_b32 %[ta], 192, %[kb]\n"
+      "ds_read_b128 %[t0], %[ta] offset:0\n"
+      "s_waitcnt lgkmcnt(5)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s1], %[t1], %[q3], %[s1]\n"
+      "ds_read_b128 %[t1], %[ta] offset:8192\n"
+      "s_waitcnt lgkmcnt(5)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s0], %[t2], %[q4], %[s0]\n"
+      "v_xor_b32 %[tb], 224, %[kb]\n"
+      "ds_read_b128 %[t2], %[tb] offset:0\n"
+      "s_waitcnt lgkmcnt(5)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s1], %[t3], %[q4], %[s1]\n"
+      "ds_read_b128 %[t3], %[tb] offset:8192\n"
+      "s_waitcnt lgkmcnt(5)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s0], %[t4], %[q5], %[s0]\n"
+      "s_waitcnt lgkmcnt(4)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s1], %[t5], %[q5], %[s1]\n"
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %[s0], %[t0], %[q6], %[s0]\n"
       "s_waitcnt lgkmcnt(2)\n"
@@ -543,11 +555,10 @@ __device__ __forceinline__ void matrix_phase_d128(const uint32_t* kaddr, const u
       "s_nop 7\n"
       "s_nop 7\n"
       "s_nop 4\n"
-      : [s0] "=&v"(sv[0]), [s1] "=&v"(sv[1]), [t0] "=&v"(t0), [t1] "=&v"(t1), [t2] "=&v"(t2), [t3] "=&v"(t3)
+      : [s0] "=&v"(sv[0]), [s1] "=&v"(sv[1]), [t0] "=&v"(t0), [t1] "=&v"(t1), [t2] "=&v"(t2), [t3] "=&v"(t3),
+        [t4] "=&v"(t4), [t5] "=&v"(t5), [ta] "=&v"(ta), [tb] "=&v"(tb)
       : [q0] "v"(qreg[0]), [q1] "v"(qreg[1]), [q2] "v"(qreg[2]), [q3] "v"(qreg[3]), [q4] "v"(qreg[4]),
-        [q5] "v"(qreg[5]), [q6] "v"(qreg[6]), [q7] "v"(qreg[7]), [ka0] "v"(kaddr[0]), [ka1] "v"(kaddr[1]),
-        [ka2] "v"(kaddr[2]), [ka3] "v"(kaddr[3]), [ka4] "v"(kaddr[4]), [ka5] "v"(kaddr[5]), [ka6] "v"(kaddr[6]),
-        [ka7] "v"(kaddr[7])
+        [q5] "v"(qreg[5]), [q6] "v"(qreg[6]), [q7] "v"(qreg[7]), [kb] "v"(kb)
       : "memory");
 }
 
@@ -850,25 +861,19 @@ __global__ __launch_bounds__(64 * kAttnWaves, 1) void attn_mfma_kernel(AttnArgs 
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
       for (int e = 0; e < 8; ++e) pp[kb][s2].v[e] = (__bf16)0.f;
-  // per-lane LDS byte offsets of the matrix phase's operand reads within a stage (d = 128)
-  uint32_t koffs[8], voffs[4];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) koffs[i] = (uint32_t)(l32 * 256 + (((2 * i + hf) ^ (l32 & 15)) << 4));
-#pragma unroll
-  for (int i = 0; i < 4; ++i) voffs[i] = (uint32_t)(l32 * 128 + (((2 * i + hf) ^ ((l32 >> 1) & 7)) << 4));
+  // per-lane LDS byte offsets of the matrix phase's first K and V^T operand reads within a
+  // stage (d = 128); k-step i reads at the offset xor 32 i (the swizzles of K rows and V^T
+  // rows act on the chunk's low bit and the lane only, so the k-step moves bits 5-7 alone)
+  const uint32_t koff0 = (uint32_t)(l32 * 256 + ((hf ^ (l32 & 15)) << 4));
+  const uint32_t voff0 = (uint32_t)(l32 * 128 + ((hf ^ ((l32 >> 1) & 7)) << 4));
   int cur = 0, prev = 0, fst = 2;
   bool have_prev = false;
   while (valid) {
     const int lo = max(k0 - kt, 0), hi = min(k1 - kt, BN);
     if (wave_rows) {   // matrix phase (the first one multiplies tile 0's V by zero probabilities)
       if constexpr (D == 128 && BN == 64) {
-        const uint32_t kst = lds_addr(stages[cur]), vst = lds_addr(stages[prev]);
-        uint32_t kaddr[8], vaddr[4];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) kaddr[i] = kst + koffs[i];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) vaddr[i] = vst + voffs[i];
-        matrix_phase_d128(kaddr, vaddr, qreg, pp, o, sv);
+        // stages are 1024-byte aligned, so adding the stage base commutes with the xor
+        matrix_phase_d128(lds_addr(stages[cur]) + koff0, lds_addr(stages[prev]) + voff0, qreg, pp, o, sv);
       } else {
         matrix_phase<D, BN, kMatLookahead>(stages[cur], stages[prev], qreg, pp, o, sv, l32, hf);
       }
