@@ -422,16 +422,16 @@ __device__ __forceinline__ void matrix_phase(const char* __restrict__ kstage, co
   __builtin_amdgcn_sched_group_barrier(0x008, LA, 0);
 }
 
-// The matrix phase for d = 128 and 64-key tiles as two self-contained assembly blocks,
-// each keeping six LDS operand reads in flight with exact partial waits (a read is issued
-// into the buffer the product before it has just consumed, and every block waits for all
-// of its own reads before it ends).  With one wave per SIMD in this phase, a 16-byte
-// operand read per 32x32x16 product keeps the matrix pipe about 69 % busy at four reads in
-// flight and 76 % at six (deeper rings add nothing), measured on MI355X.  The first block
-// is O^T += V^T P^T of the previous tile (V^T rows d = 32 db + l32 at (vb ^ 32 m) + 16384 +
-// 4096 db for key k-step m = 2 kb + s2); the second S^T = K Q^T of the current one (K rows
-// 32 kb + l32 at (kb ^ 32 kk) + 8192 kb for d k-step kk); the xor-ed addresses are formed
-// in two temporaries just before their first read.  The leading s_nop covers the wait
+// The matrix phase for d = 128 and 64-key tiles as one self-contained assembly block: O^T +=
+// V^T P^T of the previous tile (V^T rows d = 32 db + l32 at (vb ^ 32 m) + 16384 + 4096 db for
+// key k-step m = 2 kb + s2), then S^T = K Q^T of the current one (K rows 32 kb + l32 at
+// (kb ^ 32 kk) + 8192 kb for d k-step kk), with six LDS operand reads in flight across both
+// products and exact partial waits (a read is issued into the buffer the product before it
+// has just consumed; the xor-ed addresses are formed in two temporaries just before their
+// first read; the block waits for all of its reads before it ends).  With one wave per SIMD
+// in this phase, a 16-byte operand read per 32x32x16 product keeps the matrix pipe about
+// 69 % busy at four reads in flight and 76 % at six (deeper rings add nothing), measured on
+// MI355X with the ring restarted every 16 products.  The leading s_nop covers the wait
 // states between the softmax phase's vector writes (P, the rescaled O) and their first
 // matrix read; the trailing ones those between the last product and the vector reads of S.
 __device__ __forceinline__ void matrix_phase_d128(uint32_t kb, uint32_t vb, const bf16x8_t* qreg,
@@ -444,121 +444,117 @@ __device__ __forceinline__ void matrix_phase_d128(uint32_t kb, uint32_t vb, cons
       "ds_read_b128 %[t1], %[vb] offset:20480\n"
       "ds_read_b128 %[t2], %[vb] offset:24576\n"
       "ds_read_b128 %[t3], %[vb] offset:28672\n"
-      "v_xor_b32 %[tb], 32, %[vb]\n"
-      "ds_read_b128 %[t4], %[tb] offset:16384\n"
-      "ds_read_b128 %[t5], %[tb] offset:20480\n"
+      "v_xor_b32 %[ta], 32, %[vb]\n"
+      "ds_read_b128 %[t4], %[ta] offset:16384\n"
+      "ds_read_b128 %[t5], %[ta] offset:20480\n"
       "s_waitcnt lgkmcnt(5)\n"
       "v_mfma_f32_32x32x16_bf16 %[o0], %[t0], %[p0], %[o0]\n"
-      "ds_read_b128 %[t0], %[tb] offset:24576\n"
+      "ds_read_b128 %[t0], %[ta] offset:24576\n"
       "s_waitcnt lgkmcnt(5)\n"
       "v_mfma_f32_32x32x16_bf16 %[o1], %[t1], %[p0], %[o1]\n"
-      "ds_read_b128 %[t1], %[tb] offset:28672\n"
+      "ds_read_b128 %[t1], %[ta] offset:28672\n"
       "s_waitcnt lgkmcnt(5)\n"
       "v_mfma_f32_32x32x16_bf16 %[o2], %[t2], %[p0], %[o2]\n"
-      "v_xor_b32 %[ta], 64, %[vb]\n"
-      "ds_read_b128 %[t2], %[ta] offset:16384\n"
+      "v_xor_b32 %[tb], 64, %[vb]\n"
+      "ds_read_b128 %[t2], %[tb] offset:16384\n"
       "s_waitcnt lgkmcnt(5)\n"
       "v_mfma_f32_32x32x16_bf16 %[o3], %[t3], %[p0], %[o3]\n"
-      "ds_read_b128 %[t3], %[ta] offset:20480\n"
+      "ds_read_b128 %[t3], %[tb] offset:20480\n"
       "s_waitcnt lgkmcnt(5)\n"
       "v_mfma_f32_32x32x16_bf16 %[o0], %[t4], %[p1], %[o0]\n"
-      "ds_read_b128 %[t4], %[ta] offset:24576\n"
+      "ds_read_b128 %[t4], %[tb] offset:24576\n"
       "s_waitcnt lgkmcnt(5)\n"
       "v_mfma_f32_32x32x16_bf16 %[o1], %[t5], %[p1], %[o1]\n"
-      "ds_read_b128 %[t5], %[ta] offset:28672\n"
+      "ds_read_b128 %[t5], %[tb] offset:28672\n"
       "s_waitcnt lgkmcnt(5)\n"
       "v_mfma_f32_32x32x16_bf16 %[o2], %[t0], %[p1], %[o2]\n"
-      "v_xor_b32 %[tb], 96, %[vb]\n"
-      "ds_read_b128 %[t0], %[tb] offset:16384\n"
+      "v_xor_b32 %[ta], 96, %[vb]\n"
+      "ds_read_b128 %[t0], %[ta] offset:16384\n"
       "s_waitcnt lgkmcnt(5)\n"
       "v_mfma_f32_32x32x16_bf16 %[o3], %[t1], %[p1], %[o3]\n"
-      "ds_read_b128 %[t1], %[tb] offset:20480\n"
+      "ds_read_b128 %[t1], %[ta] offset:20480\n"
       "s_waitcnt lgkmcnt(5)\n"
       "v_mfma_f32_32x32x16_bf16 %[o0], %[t2], %[p2], %[o0]\n"
-      "ds_read_b128 %[t2], %[tb] offset:24576\n"
+      "ds_read_b128 %[t2], %[ta] offset:24576\n"
       "s_waitcnt lgkmcnt(5)\n"
       "v_mfma_f32_32x32x16_bf16 %[o1], %[t3], %[p2], %[o1]\n"
-      "ds_read_b128 %[t3], %[tb] offset:28672\n"
+      "ds_read_b128 %[t3], %[ta] offset:28672\n"
       "s_waitcnt lgkmcnt(5)\n"
       "v_mfma_f32_32x32x16_bf16 %[o2], %[t4], %[p2], %[o2]\n"
-      "s_waitcnt lgkmcnt(4)\n"
-      "v_mfma_f32_32x32x16_bf16 %[o3], %[t5], %[p2], %[o3]\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %[o0], %[t0], %[p3], %[o0]\n"
-      "s_waitcnt lgkmcnt(2)\n"
-      "v_mfma_f32_32x32x16_bf16 %[o1], %[t1], %[p3], %[o1]\n"
-      "s_waitcnt lgkmcnt(1)\n"
-      "v_mfma_f32_32x32x16_bf16 %[o2], %[t2], %[p3], %[o2]\n"
-      "s_waitcnt lgkmcnt(0)\n"
-      "v_mfma_f32_32x32x16_bf16 %[o3], %[t3], %[p3], %[o3]\n"
-      : [o0] "+v"(o[0]), [o1] "+v"(o[1]), [o2] "+v"(o[2]), [o3] "+v"(o[3]), [t0] "=&v"(t0), [t1] "=&v"(t1),
-        [t2] "=&v"(t2), [t3] "=&v"(t3), [t4] "=&v"(t4), [t5] "=&v"(t5), [ta] "=&v"(ta), [tb] "=&v"(tb)
-      : [p0] "v"(p[0][0].v), [p1] "v"(p[0][1].v), [p2] "v"(p[1][0].v), [p3] "v"(p[1][1].v), [vb] "v"(vb)
-      : "memory");
-  asm volatile(
-      "s_nop 4\n"
-      "ds_read_b128 %[t0], %[kb] offset:0\n"
-      "ds_read_b128 %[t1], %[kb] offset:8192\n"
-      "v_xor_b32 %[tb], 32, %[kb]\n"
-      "ds_read_b128 %[t2], %[tb] offset:0\n"
-      "ds_read_b128 %[t3], %[tb] offset:8192\n"
-      "v_xor_b32 %[ta], 64, %[kb]\n"
-      "ds_read_b128 %[t4], %[ta] offset:0\n"
-      "ds_read_b128 %[t5], %[ta] offset:8192\n"
+      "ds_read_b128 %[t4], %[kb] offset:0\n"
       "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s0], %[t0], %[q0], 0\n"
-      "v_xor_b32 %[tb], 96, %[kb]\n"
+      "v_mfma_f32_32x32x16_bf16 %[o3], %[t5], %[p2], %[o3]\n"
+      "ds_read_b128 %[t5], %[kb] offset:8192\n"
+      "s_waitcnt lgkmcnt(5)\n"
+      "v_mfma_f32_32x32x16_bf16 %[o0], %[t0], %[p3], %[o0]\n"
+      "v_xor_b32 %[tb], 32, %[kb]\n"
       "ds_read_b128 %[t0], %[tb] offset:0\n"
       "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s1], %[t1], %[q0], 0\n"
+      "v_mfma_f32_32x32x16_bf16 %[o1], %[t1], %[p3], %[o1]\n"
       "ds_read_b128 %[t1], %[tb] offset:8192\n"
       "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s0], %[t2], %[q1], %[s0]\n"
-      "v_xor_b32 %[ta], 128, %[kb]\n"
+      "v_mfma_f32_32x32x16_bf16 %[o2], %[t2], %[p3], %[o2]\n"
+      "v_xor_b32 %[ta], 64, %[kb]\n"
       "ds_read_b128 %[t2], %[ta] offset:0\n"
       "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s1], %[t3], %[q1], %[s1]\n"
+      "v_mfma_f32_32x32x16_bf16 %[o3], %[t3], %[p3], %[o3]\n"
       "ds_read_b128 %[t3], %[ta] offset:8192\n"
       "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s0], %[t4], %[q2], %[s0]\n"
-      "v_xor_b32 %[tb], 160, %[kb]\n"
+      "v_mfma_f32_32x32x16_bf16 %[s0], %[t4], %[q0], 0\n"
+      "v_xor_b32 %[tb], 96, %[kb]\n"
       "ds_read_b128 %[t4], %[tb] offset:0\n"
       "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s1], %[t5], %[q2], %[s1]\n"
+      "v_mfma_f32_32x32x16_bf16 %[s1], %[t5], %[q0], 0\n"
       "ds_read_b128 %[t5], %[tb] offset:8192\n"
       "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s0], %[t0], %[q3], %[s0]\n"
-      "v_xor_b32 %[ta], 192, %[kb]\n"
+      "v_mfma_f32_32x32x16_bf16 %[s0], %[t0], %[q1], %[s0]\n"
+      "v_xor_b32 %[ta], 128, %[kb]\n"
       "ds_read_b128 %[t0], %[ta] offset:0\n"
       "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s1], %[t1], %[q3], %[s1]\n"
+      "v_mfma_f32_32x32x16_bf16 %[s1], %[t1], %[q1], %[s1]\n"
       "ds_read_b128 %[t1], %[ta] offset:8192\n"
       "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s0], %[t2], %[q4], %[s0]\n"
-      "v_xor_b32 %[tb], 224, %[kb]\n"
+      "v_mfma_f32_32x32x16_bf16 %[s0], %[t2], %[q2], %[s0]\n"
+      "v_xor_b32 %[tb], 160, %[kb]\n"
       "ds_read_b128 %[t2], %[tb] offset:0\n"
       "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s1], %[t3], %[q4], %[s1]\n"
+      "v_mfma_f32_32x32x16_bf16 %[s1], %[t3], %[q2], %[s1]\n"
       "ds_read_b128 %[t3], %[tb] offset:8192\n"
       "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s0], %[t4], %[q5], %[s0]\n"
+      "v_mfma_f32_32x32x16_bf16 %[s0], %[t4], %[q3], %[s0]\n"
+      "v_xor_b32 %[ta], 192, %[kb]\n"
+      "ds_read_b128 %[t4], %[ta] offset:0\n"
+      "s_waitcnt lgkmcnt(5)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s1], %[t5], %[q3], %[s1]\n"
+      "ds_read_b128 %[t5], %[ta] offset:8192\n"
+      "s_waitcnt lgkmcnt(5)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s0], %[t0], %[q4], %[s0]\n"
+      "v_xor_b32 %[tb], 224, %[kb]\n"
+      "ds_read_b128 %[t0], %[tb] offset:0\n"
+      "s_waitcnt lgkmcnt(5)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s1], %[t1], %[q4], %[s1]\n"
+      "ds_read_b128 %[t1], %[tb] offset:8192\n"
+      "s_waitcnt lgkmcnt(5)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s0], %[t2], %[q5], %[s0]\n"
       "s_waitcnt lgkmcnt(4)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s1], %[t5], %[q5], %[s1]\n"
+      "v_mfma_f32_32x32x16_bf16 %[s1], %[t3], %[q5], %[s1]\n"
       "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s0], %[t0], %[q6], %[s0]\n"
+      "v_mfma_f32_32x32x16_bf16 %[s0], %[t4], %[q6], %[s0]\n"
       "s_waitcnt lgkmcnt(2)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s1], %[t1], %[q6], %[s1]\n"
+      "v_mfma_f32_32x32x16_bf16 %[s1], %[t5], %[q6], %[s1]\n"
       "s_waitcnt lgkmcnt(1)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s0], %[t2], %[q7], %[s0]\n"
+      "v_mfma_f32_32x32x16_bf16 %[s0], %[t0], %[q7], %[s0]\n"
       "s_waitcnt lgkmcnt(0)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s1], %[t3], %[q7], %[s1]\n"
+      "v_mfma_f32_32x32x16_bf16 %[s1], %[t1], %[q7], %[s1]\n"
       "s_nop 7\n"
       "s_nop 7\n"
       "s_nop 4\n"
-      : [s0] "=&v"(sv[0]), [s1] "=&v"(sv[1]), [t0] "=&v"(t0), [t1] "=&v"(t1), [t2] "=&v"(t2), [t3] "=&v"(t3),
-        [t4] "=&v"(t4), [t5] "=&v"(t5), [ta] "=&v"(ta), [tb] "=&v"(tb)
-      : [q0] "v"(qreg[0]), [q1] "v"(qreg[1]), [q2] "v"(qreg[2]), [q3] "v"(qreg[3]), [q4] "v"(qreg[4]),
-        [q5] "v"(qreg[5]), [q6] "v"(qreg[6]), [q7] "v"(qreg[7]), [kb] "v"(kb)
+      : [o0] "+v"(o[0]), [o1] "+v"(o[1]), [o2] "+v"(o[2]), [o3] "+v"(o[3]), [s0] "=&v"(sv[0]), [s1] "=&v"(sv[1]),
+        [t0] "=&v"(t0), [t1] "=&v"(t1), [t2] "=&v"(t2), [t3] "=&v"(t3), [t4] "=&v"(t4), [t5] "=&v"(t5),
+        [ta] "=&v"(ta), [tb] "=&v"(tb)
+      : [p0] "v"(p[0][0].v), [p1] "v"(p[0][1].v), [p2] "v"(p[1][0].v), [p3] "v"(p[1][1].v), [q0] "v"(qreg[0]),
+        [q1] "v"(qreg[1]), [q2] "v"(qreg[2]), [q3] "v"(qreg[3]), [q4] "v"(qreg[4]), [q5] "v"(qreg[5]),
+        [q6] "v"(qreg[6]), [q7] "v"(qreg[7]), [vb] "v"(vb), [kb] "v"(kb)
       : "memory");
 }
 
