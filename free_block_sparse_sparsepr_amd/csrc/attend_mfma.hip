@@ -826,15 +826,15 @@ __global__ __launch_bounds__(64 * kAttnWaves, 1) void attn_mfma_kernel(AttnArgs 
   bool fvalid = valid;
   // Anti-phased schedule: waves 0-3 and 4-7 (one of each per SIMD) alternate between a
   // matrix phase (S_j = K_j Q^T and O += V_{j-1} P_{j-1}) and a softmax phase (S_j ->
-  // P_j), waves 4-7 one phase behind, with a block barrier between phases, so that one
-  // wave of every SIMD issues matrix products while the other runs its exponentials.
-  // Phases t = 0, 1, ...: waves 0-3 run the matrix part of tile j in phase 2j and its
-  // softmax in 2j + 1; waves 4-7 in 2j + 1 and 2j + 2.  K_j is read in phases 2j and
-  // 2j + 1, V_j in 2j + 2 and 2j + 3.  Waves 0-3 alone copy the tiles, during their
-  // softmax phases (which read no LDS, so the copies never hold up a matrix phase's
-  // operand reads): tile j + 2 in phase 2j + 1, into the stage of tile j - 2 (free
-  // after phase 2j - 1), and each waits for its copies of tile j + 1 before the
-  // barrier that ends phase 2j + 1.
+  // P_j), so that one wave of every SIMD issues matrix products while the other runs its
+  // exponentials.  One block barrier per tile: between barriers j and j + 1, waves 0-3 run
+  // the matrix phase of tile j and then its softmax; waves 4-7 run the softmax of tile
+  // j - 1 and then the matrix phase of tile j (their first interval has no softmax, and the
+  // last tile's softmax follows the loop).  K_j and V_{j-1} are the only stages read in
+  // interval j.  Waves 0-3 alone copy the tiles, between their matrix phase and their
+  // softmax (which reads no LDS): tile j + 2 in interval j, into the stage of tile j - 2
+  // (last read in interval j - 1), and each waits for its copies of tile j + 1 before the
+  // barrier that ends interval j.
   constexpr int CW = kAttnWaves / 2;   // copying waves
   using CC = MfmaCfg<D, BN, CW>;
   constexpr int PT = CC::KIPW + CC::VIPW;
@@ -848,7 +848,6 @@ __global__ __launch_bounds__(64 * kAttnWaves, 1) void attn_mfma_kernel(AttnArgs 
   }
   if (!lag) wait_tiles_in_flight<PT>(ncopied - 1);   // tile 0 has landed
   __syncthreads();
-  if (lag) asm volatile("s_barrier" ::: "memory");   // waves 4-7 sit out phase 0
   f32x16_t sv[C::NB];
   PackP pp[C::NB][2];
 #pragma unroll
@@ -864,8 +863,11 @@ __global__ __launch_bounds__(64 * kAttnWaves, 1) void attn_mfma_kernel(AttnArgs 
   const uint32_t voff0 = (uint32_t)(l32 * 128 + ((hf ^ ((l32 >> 1) & 7)) << 4));
   int cur = 0, prev = 0, fst = 2;
   bool have_prev = false;
+  int plo = 0, phi = 0;   // valid keys of the previous tile (the lagging waves' softmax)
   while (valid) {
     const int lo = max(k0 - kt, 0), hi = min(k1 - kt, BN);
+    if (lag && have_prev && wave_rows)   // waves 4-7: the previous tile's softmax first
+      softmax_step<D, BN, false>(sv, plo, phi, c2, nullptr, 0ull, m_i, l_i, o, pp, hf);
     if (wave_rows) {   // matrix phase (the first one multiplies tile 0's V by zero probabilities)
       if constexpr (D == 128 && BN == 64) {
         // stages are 1024-byte aligned, so adding the stage base commutes with the xor
@@ -874,7 +876,6 @@ __global__ __launch_bounds__(64 * kAttnWaves, 1) void attn_mfma_kernel(AttnArgs 
         matrix_phase<D, BN, kMatLookahead>(stages[cur], stages[prev], qreg, pp, o, sv, l32, hf);
       }
     }
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     bool issued = false;
     if (fvalid) {
       if (!lag) stage_copy<D, BN, CW>(cpa, kb, vtb, A.n, A.v_np, fkt, stages[fst], wu);
@@ -882,17 +883,19 @@ __global__ __launch_bounds__(64 * kAttnWaves, 1) void attn_mfma_kernel(AttnArgs 
       fst = fst == kAttnStages - 1 ? 0 : fst + 1;
       fvalid = next_tile_lds(runs, nruns, BN, fci, fk0, fk1, fkt);
     }
-    if (wave_rows)     // softmax phase
+    if (!lag && wave_rows)   // waves 0-3: this tile's softmax
       softmax_step<D, BN, false>(sv, lo, hi, c2, nullptr, 0ull, m_i, l_i, o, pp, hf);
     have_prev = true;
+    plo = lo;
+    phi = hi;
     prev = cur;
     cur = cur == kAttnStages - 1 ? 0 : cur + 1;
     valid = next_tile_lds(runs, nruns, BN, ci, k0, k1, kt);
     if (!lag) wait_tiles_in_flight<PT>(issued ? 1 : 0);   // tile j + 1 has landed
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   }
+  if (lag && have_prev && wave_rows) softmax_step<D, BN, false>(sv, plo, phi, c2, nullptr, 0ull, m_i, l_i, o, pp, hf);
   if (wave_rows && have_prev) pv_mfma<D, BN>(stages[prev], pp, o, l32, hf);
-  if (!lag) asm volatile("s_barrier" ::: "memory");   // matches the lagging waves' first barrier
 
   const float l_tot = add_xor32(l_i);
   const float inv = 1.f / l_tot;
