@@ -938,21 +938,18 @@ __global__ __launch_bounds__(64 * kAttnWaves, 1) void attn_mfma_kernel(AttnArgs 
 constexpr int kApplyTiles = 4;
 
 template <int D, bool SPLIT>
-__global__ __launch_bounds__(256) void apply_mfma_kernel(AttnArgs A, const float* __restrict__ o_gm) {
+__global__ __launch_bounds__(256, 2) void apply_mfma_kernel(AttnArgs A, const float* __restrict__ o_gm) {
   constexpr int LDS = FusedLds<D, SPLIT>::BYTES;
   __shared__ __attribute__((aligned(16))) char lds[LDS];
   const int h = blockIdx.y, kv = h / A.g, j = h % A.g;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
-  fused_stage<D, LDS, 256, SPLIT>(A, h, lds, tid);
-  // the staged A^T, B^T and c0 serve kApplyTiles tiles of 128 rows
-  for (int it = 0; it < kApplyTiles; ++it) {
-    const int p0 = (blockIdx.x * kApplyTiles + it) * 128;
-    if (p0 >= A.n) break;
-    const int p = p0 + 32 * w + l32;
+  // rows of tile it in the accumulator layout (the next tile's loads are issued before the
+  // current tile's products, and the first tile's before the staging, to hide HBM latency)
+  auto load_tile = [&](int it, f32x16_t* o) {
+    const int p = (blockIdx.x * kApplyTiles + it) * 128 + 32 * w + l32;
     const bool valid = p < A.n;
     const float* row = o_gm + (((int64_t)kv * A.n + (valid ? p : 0)) * A.g + j) * D;
-    f32x16_t o[D / 32];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -964,7 +961,19 @@ __global__ __launch_bounds__(256) void apply_mfma_kernel(AttnArgs A, const float
         o[db][4 * jj + 2] = v.z;
         o[db][4 * jj + 3] = v.w;
       }
-    fused_apply<D, SPLIT>(A, h, kv, p, valid, 1.f, o, lds, l32, hf);
+  };
+  f32x16_t ob[2][D / 32];
+  load_tile(0, ob[0]);
+  fused_stage<D, LDS, 256, SPLIT>(A, h, lds, tid);
+  // the staged A^T, B^T and c0 serve kApplyTiles tiles of 128 rows
+#pragma unroll
+  for (int it = 0; it < kApplyTiles; ++it) {
+    const int p0 = (blockIdx.x * kApplyTiles + it) * 128;
+    if (p0 < A.n) {
+      if (it + 1 < kApplyTiles && p0 + 128 < A.n) load_tile(it + 1, ob[(it + 1) & 1]);
+      const int p = p0 + 32 * w + l32;
+      fused_apply<D, SPLIT>(A, h, kv, p, p < A.n, 1.f, ob[it & 1], lds, l32, hf);
+    }
   }
 }
 
