@@ -305,73 +305,93 @@ __global__ __launch_bounds__(256, FP > 64 ? 1 : 2) void kmeans_assign_mfma_kerne
       raw[kb] = in ? *reinterpret_cast<const ki32x4_t*>(xr + 32 * kb) : ki32x4_t{0, 0, 0, 0};
     }
   };
-  ki32x4_t nraw[KB];
-  load32(pbeg + w * 64 + l32, nraw);
+  // both 32-point halves of a wave's 64 points go through each step together (two
+  // independent instruction streams for the scheduler); the next 64 points are in flight
+  ki32x4_t nraw[2][KB];
+  load32(pbeg + w * 64 + l32, nraw[0]);
+  load32(pbeg + w * 64 + 32 + l32, nraw[1]);
   for (int pbase = pbeg + w * 64; pbase < pend; pbase += kAssignChunk) {
+    ki32x4_t xo[2][KB];
+    int pt[2], lab[2];
+    bool pv[2];
 #pragma unroll
     for (int pb = 0; pb < 2; ++pb) {
-      const int pt = pbase + pb * 32 + l32;
-      const bool pv = pt < pend;
-      ki32x4_t xo[KB];
+      pt[pb] = pbase + pb * 32 + l32;
+      pv[pb] = pt[pb] < pend;
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) xo[kb] = nraw[kb];
-      load32(pb == 0 ? pt + 32 : pt - 32 + kAssignChunk, nraw);
-      // -- assignment
-      int best = (int)0x80000000u;
+      for (int kb = 0; kb < KB; ++kb) xo[pb][kb] = nraw[pb][kb];
+      load32(pt[pb] + kAssignChunk, nraw[pb]);
+    }
+    // -- assignment
+    int best[2] = {(int)0x80000000u, (int)0x80000000u};
 #pragma unroll
-      for (int gb = 0; gb < 2; ++gb) {
+    for (int gb = 0; gb < 2; ++gb) {
+      const int8_t* crow = cs + (32 * gb + l32) * CROW + 16 * hf;
+#pragma unroll
+      for (int pb = 0; pb < 2; ++pb) {
         ki32x16_t sc;
 #pragma unroll
         for (int r = 0; r < 16; ++r) sc[r] = 0;
-        const int8_t* crow = cs + (32 * gb + l32) * CROW + 16 * hf;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
-          sc = __builtin_amdgcn_mfma_i32_32x32x32_i8(*reinterpret_cast<const ki32x4_t*>(crow + 32 * kb), xo[kb], sc,
-                                                     0, 0, 0);
+          sc = __builtin_amdgcn_mfma_i32_32x32x32_i8(*reinterpret_cast<const ki32x4_t*>(crow + 32 * kb), xo[pb][kb],
+                                                     sc, 0, 0, 0);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int gi = 32 * gb + 8 * (r >> 2) + 4 * hf + (r & 3);
-          best = max(best, (int)(((uint32_t)sc[r] << 7) + (uint32_t)cnk[gi]));   // one shift-add
+          best[pb] = max(best[pb], (int)(((uint32_t)sc[r] << 7) + (uint32_t)cnk[gi]));   // one shift-add
         }
       }
-      best = max(best, __shfl_xor(best, 32));
-      const int bg = (-best) & 63;
-      const int lab = pv ? bg : kMaxGroups;          // points past the end: no group
-      if (pv && hf == 0) labels[(int64_t)h * n + pt] = bg;
-      if constexpr (!SUMS) continue;
-      // -- counts: one add per run of equal labels among the 32 points
-      const int prev = __shfl(lab, lane - (l32 > 0 ? 1 : 0));
-      const int next = __shfl(lab, lane + (l32 < 31 ? 1 : 0));
-      const uint64_t startm = __ballot(l32 == 0 || prev != lab);
+    }
+#pragma unroll
+    for (int pb = 0; pb < 2; ++pb) {
+      best[pb] = max(best[pb], __shfl_xor(best[pb], 32));
+      const int bg = (-best[pb]) & 63;
+      lab[pb] = pv[pb] ? bg : kMaxGroups;          // points past the end: no group
+      if (pv[pb] && hf == 0) labels[(int64_t)h * n + pt[pb]] = bg;
+    }
+    if constexpr (!SUMS) continue;
+    // -- counts: one add per run of equal labels among each half's 32 points
+#pragma unroll
+    for (int pb = 0; pb < 2; ++pb) {
+      const int prev = __shfl(lab[pb], lane - (l32 > 0 ? 1 : 0));
+      const int next = __shfl(lab[pb], lane + (l32 < 31 ? 1 : 0));
+      const uint64_t startm = __ballot(l32 == 0 || prev != lab[pb]);
       if (hf == 0) {
-        lab_s[w][pb][l32] = (uint8_t)lab;
-        if (lab < kMaxGroups && (l32 == 31 || next != lab)) {
+        lab_s[w][pb][l32] = (uint8_t)lab[pb];
+        if (lab[pb] < kMaxGroups && (l32 == 31 || next != lab[pb])) {
           const uint32_t m = (uint32_t)startm & (0xffffffffu >> (31 - l32));
           const int first = 31 - __builtin_clz(m);
-          atomicAdd(&ssum[lab * SROW + FP], l32 - first + 1);
+          atomicAdd(&ssum[lab[pb] * SROW + FP], l32 - first + 1);
         }
       }
-      // -- onehot: byte e of lane (g, hf) is [label of point 8 (e / 4) + 4 hf + e % 4 == g]
+    }
+    // -- onehot: byte e of lane (g, hf) is [label of point 8 (e / 4) + 4 hf + e % 4 == g]
+    ki32x4_t oh[2][2];
+#pragma unroll
+    for (int pb = 0; pb < 2; ++pb) {
       const uint32_t* lw = reinterpret_cast<const uint32_t*>(lab_s[w][pb]);
       uint32_t lq[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) lq[q] = lw[2 * q + hf];
-      ki32x4_t oh[2];
 #pragma unroll
       for (int gb = 0; gb < 2; ++gb)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           // label bytes are <= 64 and g < 64, so x + 0x7f per byte never carries
           const uint32_t x = lq[q] ^ ((uint32_t)(32 * gb + l32) * 0x01010101u);
-          oh[gb][q] = (int32_t)((~(x + 0x7f7f7f7fu) >> 7) & 0x01010101u);
+          oh[pb][gb][q] = (int32_t)((~(x + 0x7f7f7f7fu) >> 7) & 0x01010101u);
         }
-      // -- transpose and sums: tx[r] = X[8 (r / 4) + 4 hf + r % 4][32 fb + l32]
+    }
+    // -- transpose and sums: tx[r] = X[8 (r / 4) + 4 hf + r % 4][32 fb + l32]
 #pragma unroll
-      for (int fb = 0; fb < KB; ++fb) {
+    for (int fb = 0; fb < KB; ++fb) {
+#pragma unroll
+      for (int pb = 0; pb < 2; ++pb) {
         ki32x16_t tx;
 #pragma unroll
         for (int r = 0; r < 16; ++r) tx[r] = 0;
-        tx = __builtin_amdgcn_mfma_i32_32x32x32_i8(xo[fb], ident, tx, 0, 0, 0);
+        tx = __builtin_amdgcn_mfma_i32_32x32x32_i8(xo[pb][fb], ident, tx, 0, 0, 0);
         ki32x4_t xa;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -381,7 +401,7 @@ __global__ __launch_bounds__(256, FP > 64 ? 1 : 2) void kmeans_assign_mfma_kerne
         }
 #pragma unroll
         for (int gb = 0; gb < 2; ++gb)
-          acc[fb][gb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(xa, oh[gb], acc[fb][gb], 0, 0, 0);
+          acc[fb][gb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(xa, oh[pb][gb], acc[fb][gb], 0, 0, 0);
       }
     }
   }
