@@ -11,9 +11,10 @@
 // are already laid out as the B operand of O^T += V^T P^T, so P never leaves registers.
 // V is stored transposed in LDS for that A operand.  Softmax runs in the log2 domain with
 // scale * log2(e) folded in; P is rounded to bf16 for the second product and accumulation
-// is fp32.  The two waves of every SIMD run anti-phased between block barriers: while one
-// issues a tile's matrix products (with its LDS operand reads kept four deep, as assembly
-// for d = 128), the other runs its softmax and copies the tiles.
+// is fp32.  The two waves of every SIMD run anti-phased, one block barrier per tile: while
+// one issues a tile's matrix products (with its LDS operand reads kept six deep, as one
+// assembly block for d = 128), the other runs its softmax; one of the two also copies the
+// tiles.
 //
 // Blocks are remapped so that consecutive tiles of one query group run on the same XCD
 // (the hardware deals blocks round-robin over the 8 XCDs), keeping a group's key runs
