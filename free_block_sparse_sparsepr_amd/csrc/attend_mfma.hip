@@ -759,6 +759,25 @@ __device__ __forceinline__ void wait_tiles_in_flight(int later) {
   else __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
+// Claims the next unstarted tile of the tail of XCD x's range, else of the other XCDs' ranges
+// in turn; -1 when none is left.  A claimed slot past a head's tiles (its padding) moves that
+// counter on to the next head's first slot.
+__device__ int claim_tile(const AttnArgs& A, int x) {
+  for (int k = 0; k < kXcds; ++k) {
+    const int y = (x + k) & (kXcds - 1);
+    for (;;) {
+      const int j = atomicAdd(&A.claim[y], 1);
+      if (j >= A.per_xcd) break;
+      const int logical = y * A.per_xcd + j;
+      const int kv = logical / A.tiles_per_head;
+      if (kv >= A.n_heads_kv) break;   // the grid's rounding past the last head
+      if (logical % A.tiles_per_head < A.order_count[kv]) return logical;
+      atomicMax(&A.claim[y], (kv + 1) * A.tiles_per_head - y * A.per_xcd);
+    }
+  }
+  return -1;
+}
+
 template <int D, int BN, typename OutT>
 __global__ __launch_bounds__(64 * kAttnWaves, 1) void attn_mfma_kernel(AttnArgs A) {
   using C = MfmaCfg<D, BN, kAttnWaves>;
@@ -766,10 +785,19 @@ __global__ __launch_bounds__(64 * kAttnWaves, 1) void attn_mfma_kernel(AttnArgs 
   __shared__ __attribute__((aligned(1024))) char stages[kAttnStages][C::STAGE];
 
   // XCD-aware remap of the linear block id (consecutive logical tiles on one XCD)
-  const int total = gridDim.x;
-  const int per_xcd = total / kXcds;
   const int b = blockIdx.x;
-  const int logical = (b % kXcds) * per_xcd + b / kXcds;
+  int logical;
+  if (A.claim == nullptr) {
+    logical = (b % kXcds) * (gridDim.x / kXcds) + b / kXcds;
+  } else if (b / kXcds < A.tail_start) {
+    logical = (b % kXcds) * A.per_xcd + b / kXcds;
+  } else {   // the tail of the XCD's range, then of the others' ranges (block-uniform branch)
+    __shared__ int claimed_s;
+    if (threadIdx.x == 0) claimed_s = claim_tile(A, b % kXcds);
+    __syncthreads();
+    logical = claimed_s;
+    if (logical < 0) return;
+  }
   int kv;
   TileInfo ti;
   if (A.order != nullptr) {   // the head's groups longest first
@@ -1133,10 +1161,12 @@ __global__ __launch_bounds__(64) void tile_order_kernel(const int32_t* __restric
                                                         const int32_t* __restrict__ row_ptr,
                                                         const int32_t* __restrict__ cols, int gq, int gk, int g,
                                                         int BM, int BN, int tiles_per_head,
-                                                        int32_t* __restrict__ order, int32_t* __restrict__ count) {
+                                                        int32_t* __restrict__ order, int32_t* __restrict__ count,
+                                                        int* __restrict__ claim, int tail_start) {
   __shared__ int nkt[kMaxGroups], nqt[kMaxGroups], start[kMaxGroups];
   __shared__ int cl[kMaxGroups * kMaxGroups], ko[kMaxGroups + 1], rp[kMaxGroups + 1];
   const int kv = blockIdx.x, a = threadIdx.x;
+  if (kv == 0 && a < kXcds) claim[a] = tail_start;   // the attention's tile claims start afresh
   // the head's CSR and key offsets, staged with coalesced loads
   for (int i = a; i <= gk; i += 64) ko[i] = koff[(int64_t)kv * (gk + 1) + i];
   for (int i = a; i <= gq; i += 64) rp[i] = row_ptr[(int64_t)kv * (gq + 1) + i];
@@ -1190,10 +1220,18 @@ void launch_tile_order(const Dims& dm, AttnArgs& a, char* region, hipStream_t s)
   const int tph = attn_tiles_per_head(dm.n, dm.g, dm.gq);
   int32_t* order = reinterpret_cast<int32_t*>(region);
   int32_t* count = order + 2 * (int64_t)tph * dm.hkv;
+  int* claim = count + dm.hkv;   // kXcds counters in the region's last 64 words
+  // the last eighth of each XCD's range is claimed, with half as many spare blocks per XCD
+  const int per_xcd = (int)ceil_div((int64_t)tph * dm.hkv, kXcds);
+  const int tail = per_xcd / 8;
   hipLaunchKernelGGL(tile_order_kernel, dim3(dm.hkv), dim3(64), 0, s, a.qoff, a.koff, a.row_ptr, a.cols, dm.gq, dm.gk,
-                     dm.g, MfmaCfg<128, kAttnBN, kAttnWaves>::BM, kAttnBN, tph, order, count);
+                     dm.g, MfmaCfg<128, kAttnBN, kAttnWaves>::BM, kAttnBN, tph, order, count, claim,
+                     per_xcd - tail);
   a.order = order;
   a.order_count = count;
+  a.claim = claim;
+  a.per_xcd = per_xcd;
+  a.tail_start = per_xcd - tail;
 }
 
 template <int D, typename OutT>
@@ -1202,6 +1240,8 @@ void launch_mfma_typed(AttnArgs a, int hkv, hipStream_t s) {
   a.n_heads_kv = hkv;
   int64_t total = (int64_t)a.tiles_per_head * hkv;
   total = ceil_div(total, kXcds) * kXcds;
+  if (a.claim != nullptr)   // spare blocks: half the claimed tail of each XCD
+    total = (int64_t)kXcds * (a.per_xcd + (a.per_xcd - a.tail_start) / 2);
   hipLaunchKernelGGL((attn_mfma_kernel<D, kAttnBN, OutT>), dim3((unsigned)total), dim3(64 * kAttnWaves), 0, s, a);
 }
 

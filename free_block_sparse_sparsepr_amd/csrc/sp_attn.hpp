@@ -28,6 +28,14 @@ struct AttnArgs {
   int n_heads_kv;
   const int32_t* order;        // NULL, or [Hkv][tiles_per_head][2]: (query group, tile of the group)
   const int32_t* order_count;  // [Hkv] tiles of each head in order
+  // With an order: the grid's blocks go to the XCDs in turn, XCD x owning logical tiles
+  // [x per_xcd, (x + 1) per_xcd).  Its first tail_start blocks take their tiles in place;
+  // its later blocks (and a few spare ones) claim the rest of its range through claim[x],
+  // then the rest of the other XCDs' ranges, so that a faster XCD takes over tiles that a
+  // slower one has not started.  claim: NULL (every block in place) or [8] counters, each
+  // set to tail_start before the launch.
+  int* claim;
+  int per_xcd, tail_start;
   // fused write-back (one query head per KV head): o_hat = o + c0 + (o A) B written to
   // out_tok[h][qperm[p]] in the input dtype
   const float* fitA;           // [Hq][d][rank] or NULL (no fused write-back)
