@@ -59,7 +59,8 @@ Workspace plan_workspace(const sparsepr_params& p) {
   w.fitbuf = o; o = align_up(o + hq * (size_t)FitBuf::per_head(p.d) * 8);
   w.total_probe = o;
   w.dense_meta = 0;
-  w.total_dense = align_up(hkv * (size_t)p.d * (size_t)vt_pad(p.n) * (p.dtype == SPARSEPR_BF16 ? 2 : 4));
+  w.dense_claim = align_up(hkv * (size_t)p.d * (size_t)vt_pad(p.n) * (p.dtype == SPARSEPR_BF16 ? 2 : 4));
+  w.total_dense = align_up(w.dense_claim + 64);   // the attention's eight tile-claim counters
   // the fused write-back runs in the attention epilogue for bf16 with one query head per KV
   // head; otherwise attend writes O_gm into the workspace and apply follows
   w.fused_ogm = 0;
@@ -422,6 +423,9 @@ sparsepr_status sparsepr_dense_attention(const sparsepr_params* params, const vo
   launch_transpose_v(dm, v, vt, (hipStream_t)stream);
   AttnArgs a = dense_args(dm, q, k, vt);
   a.o = o;
+  if (dm.bf16)
+    launch_dense_claims(dm, a, reinterpret_cast<int*>(static_cast<char*>(workspace) + wp.dense_claim),
+                        (hipStream_t)stream);
   (void)hipGetLastError();
   launch_attention(dm, a, true, (hipStream_t)stream);
   return hip_status();

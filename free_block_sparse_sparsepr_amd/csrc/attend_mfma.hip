@@ -771,7 +771,7 @@ __device__ int claim_tile(const AttnArgs& A, int x) {
       const int logical = y * A.per_xcd + j;
       const int kv = logical / A.tiles_per_head;
       if (kv >= A.n_heads_kv) break;   // the grid's rounding past the last head
-      if (logical % A.tiles_per_head < A.order_count[kv]) return logical;
+      if (A.order_count == nullptr || logical % A.tiles_per_head < A.order_count[kv]) return logical;
       atomicMax(&A.claim[y], (kv + 1) * A.tiles_per_head - y * A.per_xcd);
     }
   }
@@ -1216,22 +1216,33 @@ size_t attn_order_bytes(int n, int g, int hkv, int gq) {
   return (size_t)(2 * (int64_t)attn_tiles_per_head(n, g, gq) * hkv + 64 + hkv) * 4;
 }
 
+// XCD ranges of tph tiles per head over hkv heads: the last eighth of each XCD's range is
+// claimed, with half as many spare blocks per XCD (launch_mfma_typed).
+static void claim_plan(int tph, int hkv, AttnArgs& a) {
+  a.per_xcd = (int)ceil_div((int64_t)tph * hkv, kXcds);
+  a.tail_start = a.per_xcd - a.per_xcd / 8;
+}
+
 void launch_tile_order(const Dims& dm, AttnArgs& a, char* region, hipStream_t s) {
   const int tph = attn_tiles_per_head(dm.n, dm.g, dm.gq);
   int32_t* order = reinterpret_cast<int32_t*>(region);
   int32_t* count = order + 2 * (int64_t)tph * dm.hkv;
   int* claim = count + dm.hkv;   // kXcds counters in the region's last 64 words
-  // the last eighth of each XCD's range is claimed, with half as many spare blocks per XCD
-  const int per_xcd = (int)ceil_div((int64_t)tph * dm.hkv, kXcds);
-  const int tail = per_xcd / 8;
+  claim_plan(tph, dm.hkv, a);
   hipLaunchKernelGGL(tile_order_kernel, dim3(dm.hkv), dim3(64), 0, s, a.qoff, a.koff, a.row_ptr, a.cols, dm.gq, dm.gk,
-                     dm.g, MfmaCfg<128, kAttnBN, kAttnWaves>::BM, kAttnBN, tph, order, count, claim,
-                     per_xcd - tail);
+                     dm.g, MfmaCfg<128, kAttnBN, kAttnWaves>::BM, kAttnBN, tph, order, count, claim, a.tail_start);
   a.order = order;
   a.order_count = count;
   a.claim = claim;
-  a.per_xcd = per_xcd;
-  a.tail_start = per_xcd - tail;
+}
+
+// The dense schedule (every tile of a head, no order) with the same claimed XCD tails; the
+// counters are set by a fill kernel on the call's stream.
+void launch_dense_claims(const Dims& dm, AttnArgs& a, int* claim, hipStream_t s) {
+  const int tph = (int)ceil_div((int64_t)dm.n * dm.g, MfmaCfg<128, kAttnBN, kAttnWaves>::BM);
+  claim_plan(tph, dm.hkv, a);
+  fill_u32(reinterpret_cast<uint32_t*>(claim), kXcds, (uint32_t)a.tail_start, s);
+  a.claim = claim;
 }
 
 template <int D, typename OutT>

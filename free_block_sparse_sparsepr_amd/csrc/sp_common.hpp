@@ -175,7 +175,7 @@ void fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t s);
 struct Workspace {
   size_t maxbits, xk, xq, centroids, sums, usum, gm_hist, total_partition;
   size_t partials, fitbuf, probe_alloc, total_probe;
-  size_t dense_meta, total_dense;
+  size_t dense_meta, dense_claim, total_dense;
   size_t fused_ogm, total_fused;
   size_t rt_order, rt_pos, rt_prefix, rt_cost, rt_kept, rt_head, total_route;   // global route budget
   size_t attn_order;   // attention tile order, past every other region (attend may run beside probe_fit)

@@ -25,6 +25,7 @@ void launch_attention_mfma(const Dims& dm, AttnArgs a, bool out_is_input_dtype, 
 // its workspace region, and the kernel that fills it and points `a` at it.
 size_t attn_order_bytes(int n, int g, int hkv, int gq);
 void launch_tile_order(const Dims& dm, AttnArgs& a, char* region, hipStream_t s);
+void launch_dense_claims(const Dims& dm, AttnArgs& a, int* claim, hipStream_t s);
 void launch_probe_attn_mfma(const Dims& dm, const void* q, const sparsepr_partition_t& part,
                             const sparsepr_route_t& route, const sparsepr_fit_t& fit, int chunk, int nchunks,
                             float* partials, hipStream_t s);
