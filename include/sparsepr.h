@@ -256,8 +256,9 @@ sparsepr_status sparsepr_route(const sparsepr_params* params, const sparsepr_par
  * this call) or k_gm and v_gm still hold an earlier call's keys and values.
  * o_gm: [Hkv, n, g, d] fp32, group-major rows; lse: [Hkv, n, g] fp32 (natural log).
  * The workspace (sparsepr_workspace_size bytes, 256-byte aligned) holds the tile schedule
- * (each head's query groups longest first) in a region disjoint from the one
- * sparsepr_probe_fit uses, so the two may run concurrently on one workspace. */
+ * (each head's query groups longest first, and eight counters through which the last blocks
+ * of each XCD's share claim their tiles, reset by every call) in a region disjoint from the
+ * one sparsepr_probe_fit uses, so the two may run concurrently on one workspace. */
 sparsepr_status sparsepr_attend(const sparsepr_params* params, const sparsepr_partition_t* part,
                                 const sparsepr_route_t* route, float* o_gm, float* lse,
                                 void* workspace, size_t workspace_bytes, void* stream);
@@ -311,7 +312,8 @@ sparsepr_status sparsepr_attend_apply(const sparsepr_params* params, const spars
 
 /* Dense softmax attention O = softmax(Q K^T * scale) V on the same tile machinery (the
  * baseline; dense formula as in the lmnt.cn SparsePR article, section 2.1).  V is first
- * transposed into the workspace (part of the call).
+ * transposed into the workspace (part of the call), which also holds the eight tile-claim
+ * counters of the sparse schedule, reset by every call.
  * q: [Hq, n, d]; k, v: [Hkv, n, d]; o: [Hq, n, d], all dtype and token order. */
 sparsepr_status sparsepr_dense_attention(const sparsepr_params* params, const void* q,
                                          const void* k, const void* v, void* o,
