@@ -331,20 +331,42 @@ template <int D>
 __global__ __launch_bounds__(D) void probe_merge_kernel(const float* __restrict__ partials, int nch, int M,
                                                         double* __restrict__ fbuf, float* __restrict__ o_dense,
                                                         float* __restrict__ o_sparse) {
+  // each chunk's scale exp(m - max) is formed once, by one thread, into LDS; every thread
+  // then adds its column over the chunks in chunk order (chunks without keys skipped)
+  __shared__ double red[D], scs[D];
   const int r = blockIdx.x, h = blockIdx.y, c = threadIdx.x;
+  const int64_t cstride = (int64_t)M * 2 * (D + 2);
   double res[2];
   for (int which = 0; which < 2; ++which) {
+    const float* base = partials + (((int64_t)h * nch) * M + r) * 2 * (D + 2) + which * (D + 2);
     double mx = -INFINITY;
-    for (int ch = 0; ch < nch; ++ch)
-      mx = fmax(mx, (double)partials[(((int64_t)h * nch + ch) * M + r) * 2 * (D + 2) + which * (D + 2) + D]);
+    for (int ch = c; ch < nch; ch += D) mx = fmax(mx, (double)base[ch * cstride + D]);
+    red[c] = mx;
+    __syncthreads();
+    for (int s2 = D / 2; s2 > 0; s2 >>= 1) {
+      if (c < s2) red[c] = fmax(red[c], red[c + s2]);
+      __syncthreads();
+    }
+    mx = red[0];
     double L = 0.0, O = 0.0;
-    for (int ch = 0; ch < nch; ++ch) {
-      const float* pb = partials + (((int64_t)h * nch + ch) * M + r) * 2 * (D + 2) + which * (D + 2);
-      const double m = pb[D];
-      if (m == -INFINITY) continue;
-      const double sc = exp(m - mx);
-      L += (double)pb[D + 1] * sc;
-      O += (double)pb[c] * sc;
+    for (int b0 = 0; b0 < nch; b0 += D) {
+      const int ch = b0 + c;
+      double sc = -1.0;   // no keys in the chunk
+      if (ch < nch) {
+        const double m = base[ch * cstride + D];
+        if (m != -INFINITY) sc = exp(m - mx);
+      }
+      scs[c] = sc;
+      __syncthreads();
+      const int lim = min(D, nch - b0);
+      for (int k = 0; k < lim; ++k) {
+        const double s2 = scs[k];
+        if (s2 < 0.0) continue;
+        const float* pb = base + (int64_t)(b0 + k) * cstride;
+        L += (double)pb[D + 1] * s2;
+        O += (double)pb[c] * s2;
+      }
+      __syncthreads();   // scs and red are rewritten by the next pass
     }
     res[which] = O / L;
   }
