@@ -53,7 +53,6 @@ __global__ __launch_bounds__(256) void probe_select_kernel(const int8_t* __restr
   __shared__ int alloc[kMaxGroups], start[kMaxGroups], tgt[kMaxProbe];
   __shared__ int sz[kMaxGroups];
   __shared__ int cent[kMaxSemFeat];
-  __shared__ int lrad[1024];
   __shared__ uint64_t skey[kSortMax];
   const int a = blockIdx.x, kv = blockIdx.y, tid = threadIdx.x;
   const int32_t* qo = qoff + (int64_t)kv * (Gq + 1);
@@ -120,65 +119,97 @@ __global__ __launch_bounds__(256) void probe_select_kernel(const int8_t* __restr
     rad[i] = s;
   }
   __syncthreads();
-  if (na <= kSortMax) {
-    // members fit in LDS: bitonic sort of (radius << 13 | position) keys, then read the
-    // target ranks directly
-    int P = 1;
-    while (P < na) P <<= 1;
-    for (int i = tid; i < P; i += 256)
-      skey[i] = i < na ? (((uint64_t)(uint32_t)rad[i]) << 13) | (uint64_t)i : ~0ull;
-    __syncthreads();
-    for (int size = 2; size <= P; size <<= 1) {
-      for (int stride = size >> 1; stride > 0; stride >>= 1) {
-        for (int t = tid; t < P / 2; t += 256) {
-          const int lo = 2 * t - (t & (stride - 1));
-          const int hi = lo + stride;
-          const bool up = (lo & size) == 0;
-          const uint64_t x = skey[lo], y = skey[hi];
-          if ((x > y) == up) { skey[lo] = y; skey[hi] = x; }
+  const double wgt = (double)M * (double)na / ((double)ma * (double)n);
+  if (ma <= 4 || na > kSortMax) {
+    // A few probes, or more members than the sort holds: each target rank of the order
+    // (radius, position) by radix selection, four 8-bit digit passes over the radius (a
+    // histogram of the members that match the digits found so far, then the bin that holds
+    // the rank), then the ordered count, by position, of the members at that radius.
+    __shared__ uint32_t hist[256];
+    __shared__ int pick[2], wtot[4];
+    const int lane = tid & 63, wv = tid >> 6;
+    for (int k = 0; k < ma; ++k) {
+      int r = tgt[k];
+      uint32_t prefix = 0;
+      for (int shift = 24; shift >= 0; shift -= 8) {
+        hist[tid] = 0u;
+        __syncthreads();
+        for (int i = tid; i < na; i += 256) {
+          const uint32_t x = (uint32_t)rad[i];
+          if (shift == 24 || (x >> (shift + 8)) == prefix) atomicAdd(&hist[(x >> shift) & 255u], 1u);
         }
         __syncthreads();
+        if (tid < 64) {   // bins 4 tid .. 4 tid + 3 per lane, prefix sums across the wave
+          const uint32_t hs[4] = {hist[4 * tid], hist[4 * tid + 1], hist[4 * tid + 2], hist[4 * tid + 3]};
+          const uint32_t own = hs[0] + hs[1] + hs[2] + hs[3];
+          uint32_t incl = own;
+          for (int o = 1; o < 64; o <<= 1) {
+            const uint32_t u = __shfl_up(incl, o);
+            if (tid >= o) incl += u;
+          }
+          uint32_t c = incl - own;   // members in the bins below 4 tid
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            if ((uint32_t)r >= c && (uint32_t)r < c + hs[j]) {
+              pick[0] = 4 * tid + j;
+              pick[1] = (int)c;
+            }
+            c += hs[j];
+          }
+        }
+        __syncthreads();
+        prefix = (prefix << 8) | (uint32_t)pick[0];
+        r -= pick[1];
+        __syncthreads();   // hist and pick are rewritten by the next pass
       }
-    }
-    for (int k = tid; k < ma; k += 256) {
-      const int i = (int)(skey[tgt[k]] & (kSortMax - 1));
-      const int slot = kv * M + start[a] + k;
-      ptok[slot] = qperm[(int64_t)kv * n + off + i];
-      pgrp[slot] = a;
-      pw[slot] = (double)M * (double)na / ((double)ma * (double)n);
+      int base = 0;   // members at radius prefix among the positions before this chunk
+      for (int i0 = 0; i0 < na; i0 += 256) {
+        const int i = i0 + tid;
+        const bool hit = i < na && (uint32_t)rad[i] == prefix;
+        const uint64_t bal = __ballot(hit);
+        if (lane == 0) wtot[wv] = __popcll(bal);
+        __syncthreads();
+        int woff = 0;
+        for (int u = 0; u < wv; ++u) woff += wtot[u];
+        const int tot = wtot[0] + wtot[1] + wtot[2] + wtot[3];
+        if (hit && base + woff + __popcll(bal & ((1ull << lane) - 1ull)) == r) {
+          const int slot = kv * M + start[a] + k;
+          ptok[slot] = qperm[(int64_t)kv * n + off + i];
+          pgrp[slot] = a;
+          pw[slot] = wgt;
+        }
+        base += tot;
+        __syncthreads();   // wtot is rewritten by the next chunk
+        if (base > r) break;
+      }
     }
     return;
   }
-  // large group: rank of every member by counting smaller keys, tiled through LDS
-  for (int i0 = 0; i0 < na; i0 += 256) {
-    const int i = i0 + tid;
-    const int my = i < na ? rad[i] : 0;
-    int cnt = 0;
-    for (int c0 = 0; c0 < na; c0 += 1024) {
+  // members fit in LDS: bitonic sort of (radius << 13 | position) keys, then read the
+  // target ranks directly
+  int P = 1;
+  while (P < na) P <<= 1;
+  for (int i = tid; i < P; i += 256)
+    skey[i] = i < na ? (((uint64_t)(uint32_t)rad[i]) << 13) | (uint64_t)i : ~0ull;
+  __syncthreads();
+  for (int size = 2; size <= P; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int t = tid; t < P / 2; t += 256) {
+        const int lo = 2 * t - (t & (stride - 1));
+        const int hi = lo + stride;
+        const bool up = (lo & size) == 0;
+        const uint64_t x = skey[lo], y = skey[hi];
+        if ((x > y) == up) { skey[lo] = y; skey[hi] = x; }
+      }
       __syncthreads();
-      for (int t = tid; t < 1024; t += 256) lrad[t] = (c0 + t < na) ? rad[c0 + t] : 0;
-      __syncthreads();
-      const int lim = min(1024, na - c0);
-      if (i < na) {
-        for (int t = 0; t < lim; ++t) {
-          const int r2 = lrad[t];
-          cnt += (r2 < my) || (r2 == my && c0 + t < i);
-        }
-      }
     }
-    if (i < na) {
-      int lo = 0, hi = ma - 1;
-      while (lo < hi) {  // first target >= cnt
-        int mid = (lo + hi) >> 1;
-        if (tgt[mid] < cnt) lo = mid + 1; else hi = mid;
-      }
-      if (tgt[lo] == cnt) {
-        const int slot = kv * M + start[a] + lo;
-        ptok[slot] = qperm[(int64_t)kv * n + off + i];
-        pgrp[slot] = a;
-        pw[slot] = (double)M * (double)na / ((double)ma * (double)n);
-      }
-    }
+  }
+  for (int k = tid; k < ma; k += 256) {
+    const int i = (int)(skey[tgt[k]] & (kSortMax - 1));
+    const int slot = kv * M + start[a] + k;
+    ptok[slot] = qperm[(int64_t)kv * n + off + i];
+    pgrp[slot] = a;
+    pw[slot] = wgt;
   }
 }
 
