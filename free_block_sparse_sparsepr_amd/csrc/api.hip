@@ -61,11 +61,11 @@ Workspace plan_workspace(const sparsepr_params& p) {
   w.dense_meta = 0;
   w.dense_claim = align_up(hkv * (size_t)p.d * (size_t)vt_pad(p.n) * (p.dtype == SPARSEPR_BF16 ? 2 : 4));
   w.total_dense = align_up(w.dense_claim + 64);   // the attention's eight tile-claim counters
-  // the fused write-back runs in the attention epilogue for bf16 with one query head per KV
-  // head; otherwise attend writes O_gm into the workspace and apply follows
+  // the fused write-back runs in the attention epilogue for bf16 (under GQA with the query
+  // heads' corrections applied in turn); for fp32 attend writes O_gm into the workspace and
+  // apply follows
   w.fused_ogm = 0;
-  w.total_fused = (p.dtype == SPARSEPR_BF16 && p.heads_q == p.heads_kv)
-                      ? 0 : align_up(hkv * n * (size_t)(p.heads_q / p.heads_kv) * p.d * 4);
+  w.total_fused = p.dtype == SPARSEPR_BF16 ? 0 : align_up(hkv * n * (size_t)(p.heads_q / p.heads_kv) * p.d * 4);
   {
     const size_t cells = hkv * (size_t)p.groups_q * (size_t)p.groups_k;
     size_t r = 0;

@@ -173,11 +173,15 @@ __device__ __forceinline__ void stage_copy(const CopyPlan<D, BN, NW>& cp, const 
                                        (lds_void_t*)(vst + (wu * C::VIPW + i) * 1024), 16, 0, 0);
     return;
   }
+  // ragged tail: rows past n read row n - 1.  Byte offsets from the head's base are formed in
+  // 32 bits (wrapping; the sums are the in-bounds offsets, below 2^30 at the largest n), so
+  // that only koff / voff stay in registers across the loop.
 #pragma unroll
   for (int i = 0; i < C::KIPW; ++i) {
     const int kr = cp.krow(i);
     const int row = min(kt + kr, n - 1);
-    const char* src = reinterpret_cast<const char*>(kb + (int64_t)(row - kr) * D) + cp.koff[i];
+    const uint32_t off = cp.koff[i] + (uint32_t)(row - kr) * (uint32_t)(D * 2);
+    const char* src = reinterpret_cast<const char*>(kb) + off;
     __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)(stage + (wu * C::KIPW + i) * 1024), 16, 0, 0);
   }
 #pragma unroll
@@ -185,7 +189,8 @@ __device__ __forceinline__ void stage_copy(const CopyPlan<D, BN, NW>& cp, const 
     const int vc = cp.vcol(i);
     const int pos = kt + vc;
     const int base = pos + 8 <= np ? kt : -vc;   // chunks past n_pad read the row's first chunk
-    const char* src = reinterpret_cast<const char*>(vtb + base) + cp.voff[i];
+    const uint32_t off = cp.voff[i] + (uint32_t)base * 2u;
+    const char* src = reinterpret_cast<const char*>(vtb) + off;
     __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)(vst + (wu * C::VIPW + i) * 1024), 16, 0, 0);
   }
 }
@@ -742,6 +747,106 @@ __device__ __forceinline__ void fused_writeback(const AttnArgs& A, int kv, int v
   fused_apply<D>(A, kv, kv, vrow, qvalid, inv, o, lds, l32, hf);
 }
 
+// The fused write-back under GQA (summary page of "Partition the Support, Reconstruct the
+// Residual", execution paragraph: the route is shared by the query heads of a KV head, so
+// one attention block holds rows of all of them; virtual row v is query head v mod g at
+// group-major position v / g).  The g heads' corrections are applied in turn: head j's A^T,
+// B^T (split into a bf16 high part and remainder, as the GQA write-back kernel does) are
+// staged, t^T = A_j^T O^T is formed for the wave's 32 columns and the columns of other heads'
+// rows are zeroed, so O^T += B_j^T t^T changes only head j's columns (a column of the
+// products depends on that column of O^T alone).  Then c0 of each row's head is added and
+// the rows are scattered to token order.
+template <int D, int LDS_BYTES, int NT>
+__device__ __forceinline__ void fused_writeback_gqa(const AttnArgs& A, int kv, int vrow, bool qvalid, float inv,
+                                                    f32x16_t* o, char* lds, int tid, int l32, int hf) {
+  using F = FusedLds<D, true>;
+  constexpr int DBLK = D / 32;
+  const bf16_t* At = reinterpret_cast<const bf16_t*>(lds);
+  const bf16_t* Bt = At + F::RCM * F::AROW;
+  const int jrow = vrow % A.g;
+#pragma unroll
+  for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[db][r] *= inv;
+  for (int j = 0; j < A.g; ++j) {
+    const int h = kv * A.g + j;
+    if (j > 0) __syncthreads();   // every wave is done reading head j - 1's staging
+    fused_stage<D, LDS_BYTES, NT, true>(A, h, lds, tid);
+    const int re = min(A.r_eff[h], min(A.rank, F::RCM));
+    const bool two = re > 32;
+    f32x16_t t[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) { t[0][r] = 0.f; t[1][r] = 0.f; }
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        bf16x8_t ob, obl;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          ob[e] = (__bf16)o[db][8 * s2 + e];
+          obl[e] = (__bf16)(o[db][8 * s2 + e] - (float)ob[e]);
+        }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          if (kb == 1 && !two) break;
+          const bf16_t* ar = At + (32 * kb + l32) * F::AROW + 32 * db + 16 * s2 + 4 * hf;
+          const bf16x8_t av = staged8(ar);
+          t[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, ob, t[kb], 0, 0, 0);
+          t[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(staged8(ar + F::PART / 2), ob, t[kb], 0, 0, 0);
+          t[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, obl, t[kb], 0, 0, 0);
+        }
+      }
+    const bool mine = jrow == j;   // lane l32's column is this head's row
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      t[0][r] = mine ? t[0][r] : 0.f;
+      t[1][r] = mine ? t[1][r] : 0.f;
+    }
+    bf16x8_t tb[4], tbl[4];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      tb[0][e] = (__bf16)t[0][e];
+      tb[1][e] = (__bf16)t[0][8 + e];
+      tb[2][e] = (__bf16)t[1][e];
+      tb[3][e] = (__bf16)t[1][8 + e];
+      tbl[0][e] = (__bf16)(t[0][e] - (float)tb[0][e]);
+      tbl[1][e] = (__bf16)(t[0][8 + e] - (float)tb[1][e]);
+      tbl[2][e] = (__bf16)(t[1][e] - (float)tb[2][e]);
+      tbl[3][e] = (__bf16)(t[1][8 + e] - (float)tb[3][e]);
+    }
+    const int ksteps = (re + 15) / 16;
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2) {
+        if (s2 >= ksteps) break;
+        const bf16_t* br = Bt + (32 * db + l32) * F::BROW + 16 * s2 + 4 * hf;
+        const bf16x8_t bv = staged8(br);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv, tb[s2], o[db], 0, 0, 0);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(staged8(br + F::PART / 2), tb[s2], o[db], 0, 0, 0);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv, tbl[s2], o[db], 0, 0, 0);
+      }
+  }
+  if (qvalid) {
+    const int h = kv * A.g + jrow;
+    const int64_t tok = A.qperm[(int64_t)kv * A.n + vrow / A.g];
+    const float* c0 = A.fitc0 + (int64_t)h * D;
+    bf16_t* orow = static_cast<bf16_t*>(A.out_tok) + ((int64_t)h * A.n + tok) * D;
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d0 = 32 * db + 8 * j + 4 * hf;
+        uint2 v2 = make_uint2((uint32_t)f32_to_bf16(o[db][4 * j] + c0[d0]) |
+                                  ((uint32_t)f32_to_bf16(o[db][4 * j + 1] + c0[d0 + 1]) << 16),
+                              (uint32_t)f32_to_bf16(o[db][4 * j + 2] + c0[d0 + 2]) |
+                                  ((uint32_t)f32_to_bf16(o[db][4 * j + 3] + c0[d0 + 3]) << 16));
+        *reinterpret_cast<uint2*>(orow + d0) = v2;
+      }
+  }
+}
+
 constexpr int kAttnWaves = 8;    // waves per block of the main attention kernel
 constexpr int kAttnStages = 4;   // K/V tile stages in LDS; tile j + 2 is copied while tile j runs
 constexpr int kMatLookahead = 5; // LDS operand reads in flight ahead of the matrix products (d = 64)
@@ -930,8 +1035,12 @@ __global__ __launch_bounds__(64 * kAttnWaves, 1) void attn_mfma_kernel(AttnArgs 
   const float inv = 1.f / l_tot;
   if (A.fitA != nullptr) {
     __syncthreads();   // every wave is done reading its last V tile from the stages
-    fused_writeback<D, C::STAGE * kAttnStages, 64 * kAttnWaves>(A, kv, vrow, qvalid, inv, o, &stages[0][0], tid,
-                                                                   l32, hf);
+    if (A.g == 1)
+      fused_writeback<D, C::STAGE * kAttnStages, 64 * kAttnWaves>(A, kv, vrow, qvalid, inv, o, &stages[0][0], tid,
+                                                                     l32, hf);
+    else
+      fused_writeback_gqa<D, C::STAGE * kAttnStages, 64 * kAttnWaves>(A, kv, vrow, qvalid, inv, o, &stages[0][0],
+                                                                         tid, l32, hf);
     return;
   }
   // epilogue: O / l, LSE; lane writes query l32's d = 32 db + 8 j + 4 hf + 0..3

@@ -301,9 +301,10 @@ sparsepr_status sparsepr_apply(const sparsepr_params* params, const float* o_gm,
 /* Block-sparse attention with the write-back fused into its epilogue: the fused call order
  * partition -> route -> probe_fit -> attend_apply produces the same output as the unfused
  * order (up to the rounding of the correction, which is formed from bf16 operands with
- * fp32 accumulation) without the fp32 group-major intermediate.  For bf16 with one query
- * head per KV head the correction o + c0 + (o A) B runs on the matrix cores inside the
- * attention kernel; otherwise O_gm is formed in the workspace and the write-back follows.
+ * fp32 accumulation) without the fp32 group-major intermediate.  For bf16 the correction
+ * o + c0 + (o A) B runs on the matrix cores inside the attention kernel (under GQA with A and
+ * B split into a bf16 high part and remainder, the g query heads of a KV head corrected in
+ * turn); for fp32 O_gm is formed in the workspace and the write-back follows.
  * Reads the partition, the route and the fit; o: [Hq, n, d] dtype, token order.  After a
  * partition made with defer_kv_gather = 1, sparsepr_gather_kv must have run first. */
 sparsepr_status sparsepr_attend_apply(const sparsepr_params* params, const sparsepr_partition_t* part,
