@@ -336,7 +336,10 @@ def main():
                     help="time the unfused order (attend -> probe_fit -> apply) instead of the fused one")
     ap.add_argument("--chunks", type=int, default=4,
                     help="KV-head chunks of the pipelined order")
-    ap.add_argument("--order", choices=["fused", "unfused", "overlapped", "pipelined"], default=None,
+    ap.add_argument("--split-kv", type=int, default=None,
+                    help="split order: KV heads whose attention runs beside the probe stage "
+                         "(default: SparsePR.split_point())")
+    ap.add_argument("--order", choices=["fused", "unfused", "overlapped", "pipelined", "split"], default=None,
                     help="call order to time: fused (probe_fit -> attend_apply), unfused (attend -> probe_fit "
                          "-> apply), overlapped (probe_fit on a second stream beside attend, then apply) or "
                          "pipelined (the fused order over --chunks chunks of KV heads on three streams, each "
@@ -409,6 +412,8 @@ def main():
         nch = len(pipe.parts)
     if order == "pipelined":
         pass
+    elif order == "split":
+        stages = S.SparsePR.SPLIT_STAGES
     elif order == "unfused":
         stages = STAGES_UNFUSED
         fns = [lambda: sp.partition(q, k, v), sp.route, sp.attend, lambda: sp.probe_fit(q), lambda: sp.apply(out)]
@@ -428,6 +433,10 @@ def main():
     def step(ev=None):
         if pipe is not None:
             pipe(q, k, v, out, events=None if ev is None else {name: ev[i] for i, name in enumerate(stages)})
+            return
+        if order == "split":
+            sp.split(q, k, v, out, first_kv=args.split_kv,
+                     events=None if ev is None else {name: ev[i] for i, name in enumerate(stages)})
             return
         for i, fn in enumerate(fns):
             st = streams[i]
@@ -468,6 +477,8 @@ def main():
         stage_ms = {name: float(np.mean([events[s][i][0].elapsed_time(events[s][i][1]) for s in range(args.steps)]))
                     for i, name in enumerate(stages)}
     ms_per_step = wall * 1e3 / args.steps
+    if order == "split":   # the attention's two launches, each timed on its own stream
+        stage_ms["attend"] = stage_ms[stages[4]] + stage_ms[stages[5]]
 
     graph = None
     if args.graph:
@@ -532,12 +543,17 @@ def main():
                    "heads_kv": cfg.heads_kv, "d": cfg.d, "rho_exec_target": cfg.rho_exec,
                    "groups_q": cfg.groups_q, "groups_k": cfg.groups_k, "n_probe": cfg.n_probe,
                    "rank": cfg.rank, "r_k": cfg.r_k, "r_q": cfg.r_q, "lambda": cfg.lam},
-        "call_order": order if pipe is None else f"pipelined over {nch} chunks of KV heads (fused order per chunk)",
+        "call_order": (order if order != "split" else
+                       f"split at KV head {args.split_kv or sp.split_point()} of {cfg.heads_kv}")
+                      if pipe is None else f"pipelined over {nch} chunks of KV heads (fused order per chunk)",
         "route_variant": {"budget_mode": ["per_kv_head", "global"][args.budget_mode],
                           "cost_mode": ["pairs", "tile_padded"][args.cost_mode]},
-        "roofline": {"bound": "mfma", "kernel": "sparse attention (" + ("sparsepr_attend" if order != "fused" else
+        "roofline": {"bound": "mfma", "kernel": "sparse attention (" + (
+                     "sparsepr_attend" if order not in ("fused", "split") else
                      "sparsepr_attend_apply: attention with the fused write-back epilogue, plus the 64-row probe "
-                     "write-back kernel") + ")",
+                     "write-back kernel" if order == "fused" else
+                     "sparsepr_attend on the first KV heads plus sparsepr_attend_apply on the others, their "
+                     "durations on their own streams summed") + ")",
                      "achieved": attend_tflops, "peak": peak, "unit": "TFLOP/s", "frac": attend_tflops / peak,
                      "traffic": measured_traffic(cfg.name, order)},
         "graph": graph,

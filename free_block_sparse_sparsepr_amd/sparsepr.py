@@ -237,12 +237,104 @@ class SparsePR:
         main.wait_stream(side)
         return self.apply(out)
 
+    def _head_views(self, kv0, kv1):
+        """The call's buffers restricted to KV heads [kv0, kv1) (every buffer is head-major):
+        params and partition / route / fit structs of that sub-call, its O_gm and LSE rows,
+        and a workspace of the sub-call's size of its own (the attention keeps its tile
+        schedule there, so two head ranges can run at once)."""
+        views = self.__dict__.setdefault("_views", {})
+        if (kv0, kv1) in views:
+            return views[(kv0, kv1)]
+        c = self.cfg
+        h0, h1 = kv0 * c.g, kv1 * c.g
+        sub = dataclasses.replace(c, heads_kv=kv1 - kv0, heads_q=h1 - h0)
+        per_query_head = {"responses_u", "o_dense", "o_sparse", "A", "B", "c0", "r_eff", "eig"}
+        cut = lambda name, t: t[h0:h1] if name in per_query_head else t[kv0:kv1]  # noqa: E731
+        part = {k: cut(k, t) for k, t in self.part.items()}
+        route = {k: cut(k, t) for k, t in self.route_buf.items()}
+        fit = {k: cut(k, t) for k, t in self.fit.items()}
+        v = dict(prm=sub.params(), h0=h0, h1=h1, o_gm=self.o_gm[kv0:kv1], lse=self.lse[kv0:kv1],
+                 ws=torch.empty(max(workspace_bytes(sub), 256), dtype=torch.uint8, device=self.ws.device),
+                 part=B.PartitionT(*[part[k].data_ptr() if k in part else None for k in B.PARTITION_FIELDS]),
+                 route=B.RouteT(*[route[k].data_ptr() for k in B.ROUTE_FIELDS]),
+                 fit=B.FitT(*[fit[k].data_ptr() for k in B.FIT_FIELDS]))
+        views[(kv0, kv1)] = v
+        return v
+
+    def third_stream(self):
+        """The third stream of the split order (default priority), created on first use."""
+        if getattr(self, "_third", None) is None:
+            self._third = torch.cuda.Stream(device=self.o_gm.device)
+        return self._third
+
+    def split_point(self):
+        """KV heads whose attention runs beside the probe stage in the split order: a sixth of
+        them (the fastest of 4, 6 and 8 of 24 at the 720p shape), at least one, and at least
+        one left for the fused part."""
+        return max(1, min(self.cfg.heads_kv - 1, self.cfg.heads_kv // 6))
+
+    SPLIT_STAGES = ["partition", "gather_kv (second stream)", "route", "probe_fit (second stream)",
+                    "attend (first KV heads)", "attend_apply (other KV heads, third stream)",
+                    "apply (first KV heads)"]
+
+    def split(self, q, k, v, out=None, first_kv=None, events=None):
+        """The overlapped order with the write-back fused where the fit is already there: the
+        attention of the first ``first_kv`` KV heads (fp32 group-major rows) runs beside
+        probe_fit, as in ``overlapped``; as soon as the fit is done, attend_apply runs the
+        other heads' attention with the correction in its epilogue on a third stream (it
+        shares no buffer with the first heads' attention, so its blocks fill the CUs as the
+        first launch drains), and apply writes back the first heads' rows.  Every head's
+        arithmetic is that of the unfused call (the fused heads as in ``fused``).  ``events``:
+        optional dict stage (``SPLIT_STAGES``) -> (start, end) torch events, recorded on the
+        stream that runs the stage (for timing)."""
+        c = self.cfg
+        if out is None:
+            out = torch.empty((c.heads_q, c.n, c.d), dtype=c.torch_dtype, device=self.o_gm.device)
+        first = self.split_point() if first_kv is None else int(first_kv)
+        if not 0 < first < c.heads_kv:
+            raise ValueError(f"first_kv must leave heads on both sides: 0 < {first} < {c.heads_kv}")
+        a, b = self._head_views(0, first), self._head_views(first, c.heads_kv)
+        main, side, third = torch.cuda.current_stream(), self.side_stream(), self.third_stream()
+
+        def stage(i, stream, fn):
+            with torch.cuda.stream(stream):
+                if events is not None:
+                    events[self.SPLIT_STAGES[i]][0].record(stream)
+                fn()
+                if events is not None:
+                    events[self.SPLIT_STAGES[i]][1].record(stream)
+
+        stage(0, main, lambda: self.partition(q, k, v, defer_kv=True))
+        side.wait_stream(main)
+        stage(1, side, lambda: self.gather_kv(k, v))
+        kv_ready = torch.cuda.Event()
+        kv_ready.record(side)
+        stage(2, main, self.route)
+        side.wait_stream(main)
+        stage(3, side, lambda: self.probe_fit(q))
+        fit_done = torch.cuda.Event()
+        fit_done.record(side)
+        main.wait_event(kv_ready)
+        stage(4, main, lambda: B.check(self.lib.sparsepr_attend(
+            ctypes.byref(a["prm"]), ctypes.byref(a["part"]), ctypes.byref(a["route"]), _p(a["o_gm"]),
+            _p(a["lse"]), _p(a["ws"]), a["ws"].numel(), _stream())))
+        third.wait_event(fit_done)
+        stage(5, third, lambda: B.check(self.lib.sparsepr_attend_apply(
+            ctypes.byref(b["prm"]), ctypes.byref(b["part"]), ctypes.byref(b["route"]), ctypes.byref(b["fit"]),
+            _p(out[b["h0"]:b["h1"]]), _p(b["ws"]), b["ws"].numel(), _stream())))
+        main.wait_event(fit_done)
+        stage(6, main, lambda: B.check(self.lib.sparsepr_apply(
+            ctypes.byref(a["prm"]), _p(a["o_gm"]), ctypes.byref(a["part"]), ctypes.byref(a["fit"]),
+            _p(out[a["h0"]:a["h1"]]), _stream())))
+        main.wait_stream(third)
+        return out
+
     def capture(self, q, k, v, out, order="fused"):
-        """Records one whole call of the given order ("fused", "unfused" or "overlapped") into
+        """Records one whole call of the given order ("fused", "unfused", "overlapped" or "split") into
         a HIP graph and returns it (``graph.replay()`` reruns the call on the same buffers).
         One eager call runs first, on a side stream (the usual warm-up before a capture: torch's
         own lazy set-up, such as the side stream of the overlapped order, happens outside it)."""
-        fn = {"fused": self.fused, "unfused": self.__call__, "overlapped": self.overlapped}[order]
+        fn = {"fused": self.fused, "unfused": self.__call__, "overlapped": self.overlapped, "split": self.split}[order]
         warm = torch.cuda.Stream(device=out.device)
         warm.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(warm):

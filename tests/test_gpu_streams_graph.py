@@ -109,6 +109,41 @@ def test_graph_replays_match_eager(cname, order):
         np.testing.assert_array_equal(host(out), want2u)
 
 
+@pytest.mark.parametrize("cname", sorted(CASES))
+def test_split_order_matches_overlapped_and_fused(cname):
+    """The split order (the first KV heads' attention beside the probe stage, the other heads'
+    attention with the fused write-back on a third stream once the fit is done): the first
+    heads equal the overlapped call and the others the fused call, bit for bit, at every
+    split point, eager (twice) and as graph replays with eager work between them."""
+    import torch
+    print(f"\n[split {cname}]", flush=True)
+    cfg, sp, q, k, v = _setup(cname)
+    if cfg.heads_kv < 2:
+        pytest.skip("one KV head: nothing to split")
+    over = host(sp.overlapped(q, k, v).clone())
+    fused = host(sp.fused(q, k, v).clone())
+    for first in range(1, cfg.heads_kv):
+        h0 = first * cfg.g
+        for _ in range(2):
+            got = host(sp.split(q, k, v, first_kv=first))
+            torch.cuda.synchronize()
+            np.testing.assert_array_equal(got[:h0], over[:h0], err_msg=f"first heads, split {first}")
+            np.testing.assert_array_equal(got[h0:], fused[h0:], err_msg=f"other heads, split {first}")
+    out = torch.empty((cfg.heads_q, cfg.n, cfg.d), dtype=q.dtype, device=q.device)
+    graph = sp.capture(q, k, v, out, "split")
+    h0 = sp.split_point() * cfg.g
+    _, sp2, q2, k2, v2 = _setup(cname, seed_shift=5)
+    for rep in range(3):
+        out.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = host(out)
+        np.testing.assert_array_equal(got[:h0], over[:h0], err_msg=f"replay {rep}")
+        np.testing.assert_array_equal(got[h0:], fused[h0:], err_msg=f"replay {rep}")
+        (sp2.fused(q2, k2, v2).float() * 2).sum().item()
+        torch.cuda.synchronize()
+
+
 @pytest.mark.parametrize("fused", [True, False], ids=["fused", "unfused"])
 @pytest.mark.parametrize("cname", sorted(CASES))
 def test_head_chunk_pipeline_matches_one_call(cname, fused):
