@@ -52,7 +52,7 @@ Workspace plan_workspace(const sparsepr_params& p) {
   w.usum = o; if (p.heads_q != p.heads_kv) o = align_up(o + hkv * n * p.groups_k * 4);
   w.gm_hist = o; o = align_up(o + hkv * (size_t)ceil_div(p.n, kGmChunk) * kMaxGroups * 4);
   w.total_partition = o;
-  w.nchunks = (int)ceil_div(p.n, kProbeChunk);
+  w.nchunks = (int)ceil_div(p.n, probe_chunk(p.n));
   o = 0;
   w.probe_alloc = o; o = align_up(o + hkv * n * 4);
   w.partials = o; o = align_up(o + hq * w.nchunks * p.n_probe * 2 * (p.d + 2) * 4);

@@ -762,18 +762,18 @@ void launch_probe_fit(const Dims& dm, const Workspace& wp, const void* q, const 
                        out.probe_weights);
   const dim3 pgrid(wp.nchunks, dm.hq);
   if (dm.bf16) {
-    launch_probe_attn_mfma(dm, q, part, route, out, kProbeChunk, wp.nchunks, partials, s);
+    launch_probe_attn_mfma(dm, q, part, route, out, probe_chunk(dm.n), wp.nchunks, partials, s);
   } else {
     if (dm.d == 128)
       hipLaunchKernelGGL((probe_attn_kernel<float, 128>), pgrid, dim3(256), 0, s, (const float*)q,
                          (const float*)part.k_gm, (const float*)part.v_gm, part.key_offsets, route.kept_mask,
                          out.probe_tokens, out.probe_groups, dm.n, dm.g, dm.gq, dm.gk, dm.m, dm.scale,
-                         kProbeChunk, partials);
+                         probe_chunk(dm.n), partials);
     else
       hipLaunchKernelGGL((probe_attn_kernel<float, 64>), pgrid, dim3(256), 0, s, (const float*)q,
                          (const float*)part.k_gm, (const float*)part.v_gm, part.key_offsets, route.kept_mask,
                          out.probe_tokens, out.probe_groups, dm.n, dm.g, dm.gq, dm.gk, dm.m, dm.scale,
-                         kProbeChunk, partials);
+                         probe_chunk(dm.n), partials);
   }
   if (dm.d == 128)
     hipLaunchKernelGGL(probe_merge_kernel<128>, dim3(dm.m, dm.hq), dim3(128), 0, s, partials, wp.nchunks, dm.m,

@@ -18,7 +18,16 @@ constexpr int kMaxProbe = 64;
 constexpr int kMaxRank = 32;
 constexpr int kMaxCorrRank = 64;   // columns of A / rows of B: rank, or n_probe for the unprojected ridge
 constexpr int kExpTable = 1024;     // route exponential table entries
-constexpr int kProbeChunk = 1024;   // keys per probe-attention work item
+constexpr int kProbeChunk = 1024;   // keys per probe-attention work item, at most
+
+// Keys per probe-attention work item: an eighth of the keys rounded up to 64, between 64
+// and kProbeChunk, so that short sequences still spread over several blocks.  It depends on
+// n alone, so a head's probe rows (their per-chunk rounding) do not depend on how many heads
+// a call holds.
+inline int probe_chunk(int n) {
+  const int c = ((n + 7) / 8 + 63) / 64 * 64;
+  return c < 64 ? 64 : (c > kProbeChunk ? kProbeChunk : c);
+}
 constexpr int kGmChunk = 1024;      // tokens per chunk of the group-major counting sort
 
 __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
