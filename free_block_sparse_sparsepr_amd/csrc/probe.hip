@@ -526,7 +526,11 @@ __global__ __launch_bounds__(256) void fit_factor_kernel(int M, int rank, int ri
     red[tid] = dg;
     __syncthreads();
     for (int s = 128; s > 0; s >>= 1) { if (tid < s) red[tid] += red[tid + s]; __syncthreads(); }
-    if (tid == 0) stop_s = (off_all <= 1e-24 * red[0]) || (off_all == 0.0);
+    // stop once the off-diagonal energy is below 1e-12 of the diagonal's (a relative norm
+    // of 1e-6): on real probe residuals the rank-16 projector then agrees with a full
+    // eigendecomposition to about 1e-7, and the sweeps that would tidy the small
+    // eigenvalues' block (up to three of eleven) are skipped
+    if (tid == 0) stop_s = (off_all <= 1e-12 * red[0]) || (off_all == 0.0);
     __syncthreads();
     if (stop_s) break;
     for (int t = 0; t < MM - 1; ++t) {
