@@ -2,6 +2,7 @@
 // The operations themselves are documented in include/sparsepr.h.
 #include <cmath>
 #include <mutex>
+#include <unordered_set>
 
 #include "sp_common.hpp"
 #include "sp_launch.hpp"
@@ -232,6 +233,24 @@ sparsepr_status sparsepr_workspace_size(const sparsepr_params* params, size_t* b
   return SPARSEPR_OK;
 }
 
+// Partitions made with defer_kv_gather = 1 whose K/V gathers have not been enqueued yet,
+// keyed by their k_gm buffer: the entry points that read k_gm and v_gm refuse them
+// (SPARSEPR_ERR_PARAM) instead of reading the previous call's rows.  Host-side and in call
+// order, so a graph captured from a valid order replays without consulting it.
+static std::mutex g_deferred_mu;
+static std::unordered_set<const void*> g_deferred;
+
+static void set_deferred(const void* k_gm, bool deferred) {
+  std::lock_guard<std::mutex> lk(g_deferred_mu);
+  if (deferred) g_deferred.insert(k_gm);
+  else g_deferred.erase(k_gm);
+}
+
+static bool gathers_pending(const sparsepr_partition_t* part) {
+  std::lock_guard<std::mutex> lk(g_deferred_mu);
+  return part && g_deferred.count(part->k_gm) != 0;
+}
+
 sparsepr_status sparsepr_partition(const sparsepr_params* params, const void* q, const void* k, const void* v,
                                    const sparsepr_partition_t* out, void* workspace, size_t workspace_bytes,
                                    void* stream) {
@@ -252,7 +271,9 @@ sparsepr_status sparsepr_partition(const sparsepr_params* params, const void* q,
   (void)hipGetLastError();
   launch_partition(dims_of(*params), wp, q, k, v, o, static_cast<char*>(workspace), params->defer_kv_gather != 0,
                    (hipStream_t)stream);
-  return hip_status();
+  st = hip_status();
+  if (st == SPARSEPR_OK) set_deferred(o.k_gm, params->defer_kv_gather != 0);
+  return st;
 }
 
 sparsepr_status sparsepr_gather_kv(const sparsepr_params* params, const void* k, const void* v,
@@ -264,7 +285,9 @@ sparsepr_status sparsepr_gather_kv(const sparsepr_params* params, const void* k,
   if (!aligned16(k) || !aligned16(v) || !aligned16(part->k_gm) || !aligned16(part->v_gm)) return SPARSEPR_ERR_ALIGN;
   (void)hipGetLastError();
   launch_gather_kv(dims_of(*params), k, v, *part, (hipStream_t)stream);
-  return hip_status();
+  st = hip_status();
+  if (st == SPARSEPR_OK) set_deferred(part->k_gm, false);
+  return st;
 }
 
 sparsepr_status sparsepr_route(const sparsepr_params* params, const sparsepr_partition_t* part,
@@ -296,6 +319,7 @@ sparsepr_status sparsepr_attend(const sparsepr_params* params, const sparsepr_pa
     return SPARSEPR_ERR_NULL;
   if (!aligned16(part->q_gm) || !aligned16(part->k_gm) || !aligned16(part->v_gm) || !aligned16(o_gm))
     return SPARSEPR_ERR_ALIGN;
+  if (gathers_pending(part)) return SPARSEPR_ERR_PARAM;   // sparsepr_gather_kv has not run
   const Workspace wp = plan_workspace(*params);
   st = check_ws(params, workspace, workspace_bytes, wp.total);
   if (st != SPARSEPR_OK) return st;
@@ -319,6 +343,7 @@ sparsepr_status sparsepr_attend_noalloc(const sparsepr_params* params, const spa
     return SPARSEPR_ERR_NULL;
   if (!aligned16(part->q_gm) || !aligned16(part->k_gm) || !aligned16(part->v_gm) || !aligned16(o_gm))
     return SPARSEPR_ERR_ALIGN;
+  if (gathers_pending(part)) return SPARSEPR_ERR_PARAM;   // sparsepr_gather_kv has not run
   const Dims dm = dims_of(*params);
   if (dm.bf16 && attn_order_bytes(dm.n, dm.g, dm.hkv, dm.gq) > kNoAllocScratchBytes) return SPARSEPR_ERR_WORKSPACE;
   void* scr = nullptr;
@@ -347,6 +372,7 @@ sparsepr_status sparsepr_attend_apply(const sparsepr_params* params, const spars
   if (!fit->A || !fit->B || !fit->c0 || !fit->r_eff || !fit->o_dense || !fit->probe_tokens) return SPARSEPR_ERR_NULL;
   if (!aligned16(part->q_gm) || !aligned16(part->k_gm) || !aligned16(part->v_gm) || !aligned16(o))
     return SPARSEPR_ERR_ALIGN;
+  if (gathers_pending(part)) return SPARSEPR_ERR_PARAM;   // sparsepr_gather_kv has not run
   const Workspace wp = plan_workspace(*params);
   st = check_ws(params, workspace, workspace_bytes, wp.total);
   if (st != SPARSEPR_OK) return st;
@@ -386,6 +412,7 @@ sparsepr_status sparsepr_probe_fit(const sparsepr_params* params, const void* q,
       !out->A || !out->B || !out->c0 || !out->r_eff || !out->eig)
     return SPARSEPR_ERR_NULL;
   if (!aligned16(q) || !aligned16(part->k_gm) || !aligned16(part->v_gm)) return SPARSEPR_ERR_ALIGN;
+  if (gathers_pending(part)) return SPARSEPR_ERR_PARAM;   // sparsepr_gather_kv has not run
   const Workspace wp = plan_workspace(*params);
   st = check_ws(params, workspace, workspace_bytes, wp.total_probe);
   if (st != SPARSEPR_OK) return st;
@@ -452,6 +479,7 @@ sparsepr_status sparsepr_residual_diagnostics(const sparsepr_params* params, con
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(part->q_gm) || !aligned16(part->k_gm) ||
       !aligned16(part->v_gm) || ((uintptr_t)out & 7u) != 0)
     return SPARSEPR_ERR_ALIGN;
+  if (gathers_pending(part)) return SPARSEPR_ERR_PARAM;   // sparsepr_gather_kv has not run
   const Dims dm = dims_of(*params);
   const DiagWorkspace w = plan_diagnostics(dm);
   st = check_ws(params, workspace, workspace_bytes, w.total);

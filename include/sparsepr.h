@@ -60,7 +60,8 @@ typedef enum {
   SPARSEPR_ERR_DTYPE = -3,     /* dtype not bf16 / fp32 */
   SPARSEPR_ERR_ALIGN = -4,     /* a tensor pointer is not 16-byte aligned */
   SPARSEPR_ERR_WORKSPACE = -5, /* workspace smaller than sparsepr_workspace_size() */
-  SPARSEPR_ERR_PARAM = -6,     /* r_k, r_q, n_probe, rank, lambda, rho_exec, iters, block */
+  SPARSEPR_ERR_PARAM = -6,     /* r_k, r_q, n_probe, rank, lambda, rho_exec, iters, block;
+                                  or K/V gathers deferred by the partition not yet enqueued */
   SPARSEPR_ERR_HIP = -7        /* a HIP runtime call or kernel launch failed */
 } sparsepr_status;
 
@@ -253,7 +254,9 @@ sparsepr_status sparsepr_route(const sparsepr_params* params, const sparsepr_par
 /* Block-sparse attention over the kept cells, renormalised over the kept K/V groups
  * (PSRR, execution paragraph).  Reads q_gm, k_gm, v_gm, offsets and the CSR.  After a
  * partition made with defer_kv_gather = 1, sparsepr_gather_kv must have run (ordered before
- * this call) or k_gm and v_gm still hold an earlier call's keys and values.
+ * this call); until it has been called the call returns SPARSEPR_ERR_PARAM (the library
+ * records deferred partitions by their k_gm buffer), since k_gm and v_gm would still hold
+ * an earlier call's keys and values.
  * o_gm: [Hkv, n, g, d] fp32, group-major rows; lse: [Hkv, n, g] fp32 (natural log).
  * The workspace (sparsepr_workspace_size bytes, 256-byte aligned) holds the tile schedule
  * (each head's query groups longest first, and eight counters through which the last blocks
@@ -283,7 +286,7 @@ sparsepr_status sparsepr_attend_noalloc(const sparsepr_params* params, const spa
  * R = O_dense - O_sparse, the group-coverage-weighted ridge fit of R on O_sparse and
  * the rank-r subspace of the probe residuals.  q: [Hq, n, d] token order.  Reads k_gm and
  * v_gm: after a partition made with defer_kv_gather = 1, sparsepr_gather_kv must have run
- * (ordered before this call). */
+ * (ordered before this call; until it has been called the call returns SPARSEPR_ERR_PARAM). */
 sparsepr_status sparsepr_probe_fit(const sparsepr_params* params, const void* q,
                                    const sparsepr_partition_t* part, const sparsepr_route_t* route,
                                    const sparsepr_fit_t* out, void* workspace,
@@ -306,7 +309,8 @@ sparsepr_status sparsepr_apply(const sparsepr_params* params, const float* o_gm,
  * B split into a bf16 high part and remainder, the g query heads of a KV head corrected in
  * turn); for fp32 O_gm is formed in the workspace and the write-back follows.
  * Reads the partition, the route and the fit; o: [Hq, n, d] dtype, token order.  After a
- * partition made with defer_kv_gather = 1, sparsepr_gather_kv must have run first. */
+ * partition made with defer_kv_gather = 1, sparsepr_gather_kv must have run first (until it
+ * has been called the call returns SPARSEPR_ERR_PARAM). */
 sparsepr_status sparsepr_attend_apply(const sparsepr_params* params, const sparsepr_partition_t* part,
                                       const sparsepr_route_t* route, const sparsepr_fit_t* fit, void* o,
                                       void* workspace, size_t workspace_bytes, void* stream);

@@ -57,6 +57,26 @@ def test_deferred_kv_gather_is_bit_identical(cname):
         np.testing.assert_array_equal(host(t), want[n], err_msg=n)
 
 
+def test_deferred_gathers_are_required():
+    """A partition that defers the K/V gathers is refused by the entry points that read the
+    gathered K and V (SPARSEPR_ERR_PARAM) until sparsepr_gather_kv has been enqueued."""
+    import torch
+    print("\n[deferred gathers required]", flush=True)
+    cfg, sp, q, k, v = _setup("c3_bf16_ragged")
+    sp.partition(q, k, v, defer_kv=True)
+    sp.route()
+    for name, call in (("attend", sp.attend), ("attend_apply", sp.attend_apply),
+                       ("probe_fit", lambda: sp.probe_fit(q))):
+        with pytest.raises(RuntimeError, match="status -6"):
+            call()
+    sp.gather_kv(k, v)
+    sp.probe_fit(q)
+    out = sp.attend_apply()
+    torch.cuda.synchronize()
+    want = host(sp.fused(q, k, v).clone())
+    np.testing.assert_array_equal(host(out), want)
+
+
 @pytest.mark.parametrize("cname", sorted(CASES))
 def test_overlapped_order_matches_unfused(cname):
     import torch
